@@ -1,0 +1,23 @@
+"""Seeded synthetic workloads for the predictor-gated sparse FFN.
+
+This package only *draws* inputs: weights, biases, thresholds, token vectors
+and integer-grid fixtures.  It holds none of the method's arithmetic (no
+prediction, no compaction, no FFN) so that both the CPU oracle and the HIP
+path can consume the very same bytes without sharing any computation.
+"""
+from .workload import (  # noqa: F401
+    CONFIGS,
+    LayerSpec,
+    Layer,
+    config,
+    make_layer,
+    make_tokens,
+    make_grid_layer,
+    make_grid_tokens,
+    zipf_probs,
+    uniform_probs,
+    union_density,
+    quant_int4_g128,
+    random_masks,
+    pack_bits,
+)
