@@ -1,0 +1,280 @@
+// C ABI of libsfnn.so: argument validation, workspace layout and the launch
+// sequence of each entry point.  No allocation, no host<->device copies, no
+// synchronisation: everything is enqueued on the caller's stream.
+#include <algorithm>
+#include <numeric>
+#include <vector>
+
+#include "../../include/sfnn.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+using namespace sfnn;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool al16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+
+struct Layout {
+  size_t z = 0, h = 0, partial = 0, cnt = 0, mask = 0, ids = 0, count = 0, total = 0;
+};
+
+Layout layout(const sfnn_pred* p, const sfnn_ffn* f, int batch) {
+  Layout L;
+  size_t off = 0;
+  if (p) {
+    L.z = off;
+    off += up((size_t)batch * p->rank * 4);
+  }
+  const int ff = f ? f->d_ff : (p ? p->d_ff : 0);
+  if (f) {
+    const int R = ffn_row_blocks(f->d_model, f->d_ff);
+    const int tiles = (f->d_model + 255) / 256;
+    L.h = off;
+    off += up((size_t)batch * f->d_ff * 4);
+    L.partial = off;
+    off += up((size_t)R * kMaxNT * f->d_model * 4);
+    L.cnt = off;
+    off += up((size_t)tiles * 4);
+  }
+  L.mask = off;
+  off += up((size_t)batch * (ff / 64) * 8);
+  L.ids = off;
+  off += up((size_t)ff * 4);
+  L.count = off;
+  off += up(4);
+  L.total = off;
+  return L;
+}
+
+bool batch_ok(int b) { return b >= 1 && b <= 64; }
+bool dff_ok(int f) { return f >= 64 && f <= 65536 && f % 64 == 0; }
+bool dmodel_ok(int d) { return d >= 128 && d <= 16384 && d % 128 == 0; }
+
+sfnn_status check_pred(const sfnn_pred* p) {
+  if (!p || !p->w1_t || !p->w2_t || !p->tau) return SFNN_E_NULL;
+  if (p->wtype != SFNN_F32 && p->wtype != SFNN_F16) return SFNN_E_DTYPE;
+  if (!dmodel_ok(p->d_model) || !dff_ok(p->d_ff) || p->rank < 8 || p->rank > 2048 || p->rank % 8)
+    return SFNN_E_SHAPE;
+  if (!al16(p->w1_t) || !al16(p->w2_t) || !al16(p->tau)) return SFNN_E_ALIGN;
+  return SFNN_OK;
+}
+
+sfnn_status check_ffn(const sfnn_ffn* f) {
+  if (!f || !f->w_up || !f->w_down_t) return SFNN_E_NULL;
+  if (f->wtype != SFNN_F32 && f->wtype != SFNN_F16 && f->wtype != SFNN_I4G128) return SFNN_E_DTYPE;
+  if (f->act != SFNN_RELU && f->act != SFNN_REGLU) return SFNN_E_DTYPE;
+  if (f->act == SFNN_REGLU && !f->w_gate) return SFNN_E_NULL;
+  if (f->wtype == SFNN_I4G128 && (!f->s_up || !f->s_down_t || (f->act == SFNN_REGLU && !f->s_gate)))
+    return SFNN_E_NULL;
+  if (!dmodel_ok(f->d_model) || !dff_ok(f->d_ff)) return SFNN_E_SHAPE;
+  const void* ps[] = {f->w_up, f->w_gate, f->w_down_t, f->s_up, f->s_gate, f->s_down_t,
+                      f->b_up, f->b_gate, f->b_down};
+  for (const void* q : ps)
+    if (!al16(q)) return SFNN_E_ALIGN;
+  return SFNN_OK;
+}
+
+int x_type_of_ffn(const sfnn_ffn* f) { return f->wtype == SFNN_F32 ? SFNN_F32 : SFNN_F16; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+sfnn_status hip_status(hipError_t e) { return e == hipSuccess ? SFNN_OK : SFNN_E_HIP; }
+
+sfnn_status do_predict(const sfnn_pred* p, const void* x, int batch, uint64_t* mask, float* logits, float* z,
+                       hipStream_t s) {
+  PredLaunch L;
+  L.wt = p->wtype == SFNN_F32 ? WT_F32 : WT_F16;
+  L.d = p->d_model;
+  L.f = p->d_ff;
+  L.r = p->rank;
+  L.w1_t = p->w1_t;
+  L.w2_t = p->w2_t;
+  L.tau = p->tau;
+  L.x = x;
+  L.batch = batch;
+  L.z = z;
+  L.mask = mask;
+  L.logits = logits;
+  return hip_status(launch_predict(L, s));
+}
+
+sfnn_status do_ffn(const sfnn_ffn* f, const void* x, int batch, const int32_t* ids, const int32_t* count,
+                   const uint64_t* mask, float* y, char* ws, const Layout& Lw, hipStream_t s) {
+  FfnLaunch L;
+  L.wt = f->wtype == SFNN_F32 ? WT_F32 : (f->wtype == SFNN_F16 ? WT_F16 : WT_I4);
+  L.act = f->act == SFNN_RELU ? ACT_RELU : ACT_REGLU;
+  L.d = f->d_model;
+  L.f = f->d_ff;
+  L.w_up = f->w_up;
+  L.w_gate = f->w_gate;
+  L.w_down_t = f->w_down_t;
+  L.s_up = f->s_up;
+  L.s_gate = f->s_gate;
+  L.s_down_t = f->s_down_t;
+  L.b_up = f->b_up;
+  L.b_gate = f->b_gate;
+  L.b_down = f->b_down;
+  L.x = x;
+  L.batch = batch;
+  L.ids = ids;
+  L.count = count;
+  L.mask = mask;
+  L.y = y;
+  L.h = reinterpret_cast<float*>(ws + Lw.h);
+  L.partial = reinterpret_cast<float*>(ws + Lw.partial);
+  L.tile_cnt = reinterpret_cast<int32_t*>(ws + Lw.cnt);
+  L.row_blocks = ffn_row_blocks(f->d_model, f->d_ff);
+  return hip_status(launch_ffn(L, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sfnn_workspace_bytes(const sfnn_pred* pred, const sfnn_ffn* ffn, int32_t batch) {
+  if (!batch_ok(batch) || (!pred && !ffn)) return 0;
+  if (pred && check_pred(pred) == SFNN_E_SHAPE) return 0;
+  if (ffn && check_ffn(ffn) == SFNN_E_SHAPE) return 0;
+  return layout(pred, ffn, batch).total;
+}
+
+sfnn_status sfnn_predict(const sfnn_pred* pred, const void* x, int32_t batch, uint64_t* mask, float* logits,
+                         void* ws, size_t ws_bytes, void* stream) {
+  sfnn_status st = check_pred(pred);
+  if (st != SFNN_OK) return st;
+  if (!x || !mask || !ws) return SFNN_E_NULL;
+  if (!batch_ok(batch)) return SFNN_E_SHAPE;
+  if (!al16(x) || !al16(mask) || !al16(logits) || !al16(ws)) return SFNN_E_ALIGN;
+  const Layout Lw = layout(pred, nullptr, batch);
+  if (ws_bytes < Lw.total) return SFNN_E_WORKSPACE;
+  return do_predict(pred, x, batch, mask, logits, reinterpret_cast<float*>((char*)ws + Lw.z), as_stream(stream));
+}
+
+sfnn_status sfnn_compact(const uint64_t* mask, int32_t batch, int32_t d_ff, int32_t* ids, int32_t* count,
+                         uint64_t* union_mask, void* stream) {
+  if (!mask || !ids || !count) return SFNN_E_NULL;
+  if (!batch_ok(batch) || !dff_ok(d_ff)) return SFNN_E_SHAPE;
+  if (!al16(mask) || !al16(ids) || !al16(count) || !al16(union_mask)) return SFNN_E_ALIGN;
+  return hip_status(launch_compact(mask, batch, d_ff, ids, count, union_mask, as_stream(stream)));
+}
+
+sfnn_status sfnn_sparse_ffn(const sfnn_ffn* ffn, const void* x, int32_t batch, const int32_t* ids,
+                            const int32_t* count, const uint64_t* mask, float* y, void* ws, size_t ws_bytes,
+                            void* stream) {
+  sfnn_status st = check_ffn(ffn);
+  if (st != SFNN_OK) return st;
+  if (!x || !ids || !count || !y || !ws) return SFNN_E_NULL;
+  if (!batch_ok(batch)) return SFNN_E_SHAPE;
+  if (!al16(x) || !al16(ids) || !al16(count) || !al16(mask) || !al16(y) || !al16(ws)) return SFNN_E_ALIGN;
+  const Layout Lw = layout(nullptr, ffn, batch);
+  if (ws_bytes < Lw.total) return SFNN_E_WORKSPACE;
+  return do_ffn(ffn, x, batch, ids, count, mask, y, (char*)ws, Lw, as_stream(stream));
+}
+
+sfnn_status sfnn_dense_ffn(const sfnn_ffn* ffn, const void* x, int32_t batch, float* y, void* ws,
+                           size_t ws_bytes, void* stream) {
+  sfnn_status st = check_ffn(ffn);
+  if (st != SFNN_OK) return st;
+  if (!x || !y || !ws) return SFNN_E_NULL;
+  if (!batch_ok(batch)) return SFNN_E_SHAPE;
+  if (!al16(x) || !al16(y) || !al16(ws)) return SFNN_E_ALIGN;
+  const Layout Lw = layout(nullptr, ffn, batch);
+  if (ws_bytes < Lw.total) return SFNN_E_WORKSPACE;
+  return do_ffn(ffn, x, batch, nullptr, nullptr, nullptr, y, (char*)ws, Lw, as_stream(stream));
+}
+
+sfnn_status sfnn_layer(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x, int32_t batch, float* y,
+                       uint64_t* mask, int32_t* ids, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  sfnn_status st = check_pred(pred);
+  if (st != SFNN_OK) return st;
+  st = check_ffn(ffn);
+  if (st != SFNN_OK) return st;
+  if (!x || !y || !ws) return SFNN_E_NULL;
+  if (!batch_ok(batch)) return SFNN_E_SHAPE;
+  if (pred->d_model != ffn->d_model || pred->d_ff != ffn->d_ff) return SFNN_E_SHAPE;
+  if (pred->wtype != x_type_of_ffn(ffn)) return SFNN_E_DTYPE;
+  if (!al16(x) || !al16(y) || !al16(mask) || !al16(ids) || !al16(count) || !al16(ws)) return SFNN_E_ALIGN;
+  const Layout Lw = layout(pred, ffn, batch);
+  if (ws_bytes < Lw.total) return SFNN_E_WORKSPACE;
+  char* w = (char*)ws;
+  if (!mask) mask = reinterpret_cast<uint64_t*>(w + Lw.mask);
+  if (!ids) ids = reinterpret_cast<int32_t*>(w + Lw.ids);
+  if (!count) count = reinterpret_cast<int32_t*>(w + Lw.count);
+  hipStream_t s = as_stream(stream);
+  st = do_predict(pred, x, batch, mask, nullptr, reinterpret_cast<float*>(w + Lw.z), s);
+  if (st != SFNN_OK) return st;
+  st = hip_status(launch_compact(mask, batch, ffn->d_ff, ids, count, nullptr, s));
+  if (st != SFNN_OK) return st;
+  return do_ffn(ffn, x, batch, ids, count, batch > 1 ? mask : nullptr, y, w, Lw, s);
+}
+
+sfnn_status sfnn_residual_rmsnorm(const float* r_in, const float* y, float* r_out, int32_t batch,
+                                  int32_t d_model, float eps, void* x_out, int32_t xtype, void* stream) {
+  if (!r_in || !r_out || !x_out) return SFNN_E_NULL;
+  if (!batch_ok(batch) || !dmodel_ok(d_model)) return SFNN_E_SHAPE;
+  if (xtype != SFNN_F32 && xtype != SFNN_F16) return SFNN_E_DTYPE;
+  if (!al16(r_in) || !al16(y) || !al16(r_out) || !al16(x_out)) return SFNN_E_ALIGN;
+  return hip_status(launch_residual_rmsnorm(r_in, y, r_out, batch, d_model, eps, x_out,
+                                            xtype == SFNN_F32 ? WT_F32 : WT_F16, as_stream(stream)));
+}
+
+sfnn_status sfnn_fire_counts(const uint64_t* masks, int32_t n_masks, int32_t d_ff, uint32_t* counts,
+                             void* stream) {
+  if (!masks || !counts) return SFNN_E_NULL;
+  if (n_masks < 1 || !dff_ok(d_ff)) return SFNN_E_SHAPE;
+  if (!al16(masks) || !al16(counts)) return SFNN_E_ALIGN;
+  return hip_status(launch_fire_counts(masks, n_masks, d_ff, counts, as_stream(stream)));
+}
+
+sfnn_status sfnn_hot_first_perm(const uint32_t* counts, int32_t d_ff, int32_t* perm) {
+  if (!counts || !perm) return SFNN_E_NULL;
+  if (d_ff < 1) return SFNN_E_SHAPE;
+  std::vector<int32_t> idx((size_t)d_ff);
+  std::iota(idx.begin(), idx.end(), 0);
+  std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) { return counts[a] > counts[b]; });
+  std::copy(idx.begin(), idx.end(), perm);
+  return SFNN_OK;
+}
+
+sfnn_status sfnn_gather_rows(const void* src, const int32_t* perm, int32_t n_rows, int64_t row_bytes, void* dst,
+                             void* stream) {
+  if (!src || !perm || !dst) return SFNN_E_NULL;
+  if (n_rows < 1 || row_bytes < 2 || (row_bytes & 1)) return SFNN_E_SHAPE;
+  if (!al16(src) || !al16(perm) || !al16(dst)) return SFNN_E_ALIGN;
+  return hip_status(launch_gather_rows(src, perm, n_rows, row_bytes, dst, as_stream(stream)));
+}
+
+sfnn_status sfnn_probe_read(const void* buf, size_t bytes, float* sink, void* stream) {
+  if (!buf || !sink) return SFNN_E_NULL;
+  if (bytes < 16 || bytes % 16) return SFNN_E_SHAPE;
+  if (!al16(buf) || !al16(sink)) return SFNN_E_ALIGN;
+  return hip_status(launch_probe_read(buf, bytes, sink, as_stream(stream)));
+}
+
+sfnn_status sfnn_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst) return SFNN_E_NULL;
+  if (bytes < 16 || bytes % 16) return SFNN_E_SHAPE;
+  if (!al16(src) || !al16(dst)) return SFNN_E_ALIGN;
+  return hip_status(launch_probe_copy(src, dst, bytes, as_stream(stream)));
+}
+
+const char* sfnn_status_str(sfnn_status s) {
+  switch (s) {
+    case SFNN_OK: return "ok";
+    case SFNN_E_NULL: return "required pointer is NULL";
+    case SFNN_E_SHAPE: return "size outside the supported limits";
+    case SFNN_E_ALIGN: return "pointer not 16-byte aligned";
+    case SFNN_E_DTYPE: return "unknown or inconsistent data type";
+    case SFNN_E_WORKSPACE: return "workspace too small";
+    case SFNN_E_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int32_t sfnn_version(void) { return 100; }
+
+}  // extern "C"

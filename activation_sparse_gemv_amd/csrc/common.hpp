@@ -1,0 +1,199 @@
+// Device helpers shared by the sfnn kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace sfnn {
+
+enum { WT_F32 = 0, WT_F16 = 1, WT_I4 = 2 };
+enum { ACT_RELU = 0, ACT_REGLU = 1 };
+
+constexpr int kWave = 64;
+
+template <typename T>
+__device__ __forceinline__ T bitcast(uint32_t u) { return __builtin_bit_cast(T, u); }
+
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Weight rows are read once per call: stream them past the caches.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(bitcast<f16x2>(a), bitcast<f16x2>(b), c, false);
+}
+
+// Sum over aligned groups of G consecutive lanes (G a power of two <= 64).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// INT4 nibbles of one dword as four fp16 pairs (e0,e4) (e1,e5) (e2,e6) (e3,e7).
+// Each nibble t is two's complement; (t ^ 8) is t + 8 in offset binary, and
+// the fp16 bit pattern 0x6400 | n is 1024 + n, so subtracting 1032 leaves t.
+__device__ __forceinline__ void int4_pairs(uint32_t u, uint32_t out[4]) {
+  const uint32_t v = u ^ 0x88888888u;
+  const f16x2 bias = {(f16)1032.0f, (f16)1032.0f};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t p = ((v >> (4 * k)) & 0x000F000Fu) | 0x64006400u;
+    const f16x2 q = bitcast<f16x2>(p) - bias;
+    out[k] = __builtin_bit_cast(uint32_t, q);
+  }
+}
+
+// Where element c (0..7) of an 8-element chunk sits when x is staged for the
+// INT4 pairing above: order (0,4,1,5,2,6,3,7).
+__device__ __forceinline__ int int4_slot(int c) { return c < 4 ? 2 * c : 2 * (c - 4) + 1; }
+
+// Stage tokens [tok0, tok0+nt) of x [*, K] into LDS xs [NT][K]; rows of
+// tokens >= nt are zero.  PERM8 applies the INT4 pairing order.
+template <typename XT, bool PERM8>
+__device__ __forceinline__ void stage_rows(XT* xs, const XT* __restrict__ x, int K, int tok0, int nt,
+                                           int NT) {
+  const int total = NT * K;
+  for (int e = threadIdx.x; e < total; e += blockDim.x) {
+    const int t = e / K;
+    const int k = e - t * K;
+    const XT v = (t < nt) ? x[(size_t)(tok0 + t) * K + k] : (XT)0;
+    int kk = k;
+    if (PERM8) kk = (k & ~7) + int4_slot(k & 7);
+    xs[t * K + kk] = v;
+  }
+}
+
+// ---- one 16-byte weight vector against NT token rows of staged x ----------
+// xs points at element (vector start) of token 0; xstride is the LDS row
+// stride in elements.
+
+// fp32 weights (4 elements) x fp32 activations.
+template <int NT>
+__device__ __forceinline__ void vec_f32(const u32x4 w, const float* xs, int xstride, float* acc) {
+  const float w0 = bitcast<float>(w.x), w1 = bitcast<float>(w.y);
+  const float w2 = bitcast<float>(w.z), w3 = bitcast<float>(w.w);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const f32x4 xv = *reinterpret_cast<const f32x4*>(xs + t * xstride);
+    float a = acc[t];
+    a = __builtin_fmaf(w0, xv.x, a);
+    a = __builtin_fmaf(w1, xv.y, a);
+    a = __builtin_fmaf(w2, xv.z, a);
+    a = __builtin_fmaf(w3, xv.w, a);
+    acc[t] = a;
+  }
+}
+
+// fp16 weights (8 elements) x fp16 activations, fp32 accumulation.
+template <int NT>
+__device__ __forceinline__ void vec_f16(const u32x4 w, const f16* xs, int xstride, float* acc) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + t * xstride);
+    float a = acc[t];
+    a = dot2(w.x, xv.x, a);
+    a = dot2(w.y, xv.y, a);
+    a = dot2(w.z, xv.z, a);
+    a = dot2(w.w, xv.w, a);
+    acc[t] = a;
+  }
+}
+
+// fp16 weights (8 elements) x fp32 activations (the predictor's second stage).
+template <int NT>
+__device__ __forceinline__ void vec_f16_f32x(const u32x4 w, const float* xs, int xstride, float* acc) {
+  float wf[8];
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f16x2 h = bitcast<f16x2>(ww[k]);
+    wf[2 * k] = (float)h.x;
+    wf[2 * k + 1] = (float)h.y;
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const f32x4 xa = *reinterpret_cast<const f32x4*>(xs + t * xstride);
+    const f32x4 xb = *reinterpret_cast<const f32x4*>(xs + t * xstride + 4);
+    float a = acc[t];
+    a = __builtin_fmaf(wf[0], xa.x, a);
+    a = __builtin_fmaf(wf[1], xa.y, a);
+    a = __builtin_fmaf(wf[2], xa.z, a);
+    a = __builtin_fmaf(wf[3], xa.w, a);
+    a = __builtin_fmaf(wf[4], xb.x, a);
+    a = __builtin_fmaf(wf[5], xb.y, a);
+    a = __builtin_fmaf(wf[6], xb.z, a);
+    a = __builtin_fmaf(wf[7], xb.w, a);
+    acc[t] = a;
+  }
+}
+
+// INT4 weights (32 elements, one 128-group scale) x fp16 activations staged
+// in the INT4 pairing order.
+template <int NT>
+__device__ __forceinline__ void vec_i4(const u32x4 w, float scale, const f16* xs, int xstride,
+                                       float* acc) {
+  uint32_t q[4][4];
+  int4_pairs(w.x, q[0]);
+  int4_pairs(w.y, q[1]);
+  int4_pairs(w.z, q[2]);
+  int4_pairs(w.w, q[3]);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float d = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + t * xstride + 8 * j);
+      d = dot2(q[j][0], xv.x, d);
+      d = dot2(q[j][1], xv.y, d);
+      d = dot2(q[j][2], xv.z, d);
+      d = dot2(q[j][3], xv.w, d);
+    }
+    acc[t] = __builtin_fmaf(d, scale, acc[t]);
+  }
+}
+
+// Elements per 16-byte weight vector.
+template <int WT>
+constexpr int vec_elems() { return WT == WT_F32 ? 4 : (WT == WT_F16 ? 8 : 32); }
+
+// Partial dot products of one weight row against NT staged token rows: lane
+// li of an LPR-lane group takes vectors li, li+LPR, ...  XT is the staged type.
+template <int WT, int LPR, int NT, typename XT>
+__device__ __forceinline__ void row_partial(const uint8_t* __restrict__ row,
+                                            const f16* __restrict__ srow, int nvec, int li,
+                                            const XT* xs, int xstride, float* acc) {
+  constexpr int E = vec_elems<WT>();
+#pragma unroll 8
+  for (int v = li; v < nvec; v += LPR) {
+    const u32x4 w = ld16_stream(row + 16 * (size_t)v);
+    if constexpr (WT == WT_F32) {
+      vec_f32<NT>(w, reinterpret_cast<const float*>(xs) + E * v, xstride, acc);
+    } else if constexpr (WT == WT_F16) {
+      if constexpr (sizeof(XT) == 4)
+        vec_f16_f32x<NT>(w, reinterpret_cast<const float*>(xs) + E * v, xstride, acc);
+      else
+        vec_f16<NT>(w, reinterpret_cast<const f16*>(xs) + E * v, xstride, acc);
+    } else {
+      const float s = (float)srow[v >> 2];
+      vec_i4<NT>(w, s, reinterpret_cast<const f16*>(xs) + E * v, xstride, acc);
+    }
+  }
+}
+
+template <typename XT>
+__device__ __forceinline__ float load_as_float(const void* p, int i) {
+  return (float)reinterpret_cast<const XT*>(p)[i];
+}
+
+}  // namespace sfnn

@@ -1,0 +1,284 @@
+"""Throughput of the predictor-gated sparse FFN decode stack on one MI355X.
+
+Default workload: the OPT-6.7B-shaped FFN stack (32 layers, d_model 4096,
+d_ff 16384, fp16 weights N(0, 0.02), ReLU at ~90% per-token sparsity, rank-1024
+fp16 predictor per layer), batch 1, 256 decode steps of fresh x ~ N(0, I)
+through the RMS-normalised residual chain.  One step = for every layer:
+predict -> compact -> sparse FFN, then residual + RMSNorm.  Weights are drawn
+on the host from seeded streams and copied to HBM before timing; a step is
+captured once in a HIP graph and replayed, the next token copied in between.
+
+Prints one JSON line (metric/value/unit, ms_per_step, roofline of the sparse
+FFN kernel pair, CPU-oracle baseline, and a breakdown under "extra").
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--config", default="c2", help="workload: c2 (default) | c3 | c4 | c5")
+    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--rho", type=float, default=None, help="override the mean fire probability")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--no-extra", action="store_true", help="skip per-kernel, dense and probe timings")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+HBM_PEAK_GBS = 8000.0
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        msg = ("bench.py measures one GPU only: the hot path has no inter-GPU step; "
+               f"--gpus {args.gpus} is not supported")
+        print(msg, file=sys.stderr)
+        print(json.dumps({"error": msg, "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import synth
+    import activation_sparse_gemv_amd as sg
+    from activation_sparse_gemv_amd.device import to_dev, upload_layer, workspace
+
+    dev = "cuda"
+    over = {}
+    if args.rho is not None:
+        over["rho"] = args.rho
+    spec = synth.config(args.config, **over)
+    B, L = args.batch, spec.n_layers
+    d, f, r = spec.d_model, spec.d_ff, spec.rank
+    t0 = time.time()
+
+    # ---- weights: drawn per layer on the host, resident in HBM -------------
+    layers = []
+    host0 = None
+    for l in range(L):
+        lay = synth.make_layer(spec, layer=l)
+        layers.append(upload_layer(lay, device=dev))
+        if l == 0:
+            host0 = lay
+        del lay
+    torch.cuda.synchronize()
+    t_setup = time.time() - t0
+    print(f"# {L} layers of {spec.name} resident in HBM after {t_setup:.1f}s", file=sys.stderr, flush=True)
+
+    # ---- hot-first relayout for power-law workloads -------------------------
+    if spec.profile == "zipf":
+        _hot_first(sg, layers, spec, B, dev)
+
+    xdt = torch.float32 if spec.wtype == "f32" else torch.float16
+    ntok = args.steps + args.warmup
+    tokens = to_dev(synth.make_tokens(spec, ntok * B, stream=7, dtype=np.float32)).view(ntok, B, d)
+    stage = torch.empty((B, d), dtype=torch.float32, device=dev)
+    rbuf = torch.empty((B, d), dtype=torch.float32, device=dev)
+    xbuf = torch.empty((B, d), dtype=xdt, device=dev)
+    ybuf = torch.empty((B, d), dtype=torch.float32, device=dev)
+    masks = torch.zeros((L, B, f // 64), dtype=torch.uint64, device=dev)
+    ids = torch.zeros((L, f), dtype=torch.int32, device=dev)
+    counts = torch.zeros((L, 4), dtype=torch.int32, device=dev)
+    ws = workspace(layers[0][0], layers[0][1], B)
+
+    def step():
+        sg.sfnn_residual_rmsnorm(stage, None, rbuf, B, d, 1e-6, xbuf)
+        for l, (pred, ffn) in enumerate(layers):
+            sg.sfnn_layer(pred, ffn, xbuf, B, ybuf, masks[l], ids[l], counts[l], ws)
+            sg.sfnn_residual_rmsnorm(rbuf, ybuf, rbuf, B, d, 1e-6, xbuf)
+
+    # eager warm-up on a side stream, then capture one step
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        stage.copy_(tokens[0])
+        step()
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    for t in range(args.warmup):
+        stage.copy_(tokens[t])
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(args.steps):
+        stage.copy_(tokens[args.warmup + t])
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed_ms = e0.elapsed_time(e1)
+    ms_per_step = elapsed_ms / args.steps
+    tok_s = B * args.steps / (elapsed_ms / 1e3)
+    cnt = counts[:, 0].cpu().numpy().astype(np.float64)
+    mean_u = float(cnt.mean())
+
+    # ---- algorithmic bytes ----------------------------------------------------
+    wb = {"f32": 4.0, "f16": 2.0, "i4g128": d / 2 / d + 2.0 / 128}[spec.wtype]
+    row_bytes = d * wb
+    xb = 4 if spec.wtype == "f32" else 2
+    pb = 4 if spec.pred_dtype == "f32" else 2
+    nmat = spec.n_mat
+    ffn_bytes_u = lambda u: u * nmat * row_bytes + u * (nmat - 1) * xb          # noqa: E731
+    pred_bytes = (d * r + r * f) * pb + 4 * f
+    ffn_bytes = ffn_bytes_u(mean_u)
+
+    out = {
+        "metric": "sparse-FFN decode tokens/sec at batch 1 + effective HBM GB/s on active bytes",
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if spec.wtype == "f16" else ("f32" if spec.wtype == "f32" else "i4g128+f16"),
+        "data": "synthetic (seeded N(0,0.02) weights, calibrated biases/thresholds, x~N(0,1))",
+        "config": {"workload": f"{spec.name} FFN stack: {L} layers, d_model {d}, d_ff {f}, "
+                               f"rank-{r} predictor, {spec.act}, {spec.wtype}, "
+                               f"{'zipf phi=%.2f ' % spec.phi if spec.profile == 'zipf' else ''}rho={spec.rho}",
+                   "global_batch": B, "decode_steps": args.steps, "layers": L},
+    }
+
+    extra = {"mean_active_neurons": round(mean_u, 1), "active_fraction": round(mean_u / f, 4),
+             "ffn_active_bytes_per_layer": int(ffn_bytes), "predictor_bytes_per_layer": int(pred_bytes),
+             "setup_s": round(t_setup, 1)}
+    extra["layer_GBps_stack"] = round(L * (ffn_bytes + pred_bytes) / (ms_per_step / 1e3) / 1e9, 1)
+
+    # ---- per-call timings (HIP events over back-to-back launches) -----------
+    if not args.no_extra:
+        reps = 4
+        xs = xbuf
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / (reps * L) * 1e3  # us per layer call
+
+        y2 = torch.empty_like(ybuf)
+        t_ffn = timed(lambda: [sg.sfnn_sparse_ffn(ffn, xs, B, ids[l], counts[l], masks[l] if B > 1 else None, y2, ws)
+                               for l, (_, ffn) in enumerate(layers)])
+        t_pred = timed(lambda: [sg.sfnn_predict(pred, xs, B, masks[l], None, ws) for l, (pred, _) in enumerate(layers)])
+        t_comp = timed(lambda: [sg.sfnn_compact(masks[l], B, f, ids[l], counts[l]) for l in range(L)])
+        t_dense = timed(lambda: [sg.sfnn_dense_ffn(ffn, xs, B, y2, ws) for _, ffn in layers])
+        t_layer = timed(lambda: [sg.sfnn_layer(pred, ffn, xs, B, y2, masks[l], ids[l], counts[l], ws)
+                                 for l, (pred, ffn) in enumerate(layers)])
+        dense_bytes = f * nmat * row_bytes + f * (nmat - 1) * xb
+        extra.update({
+            "us_sparse_ffn": round(t_ffn, 2), "us_predict": round(t_pred, 2), "us_compact": round(t_comp, 2),
+            "us_layer_eager": round(t_layer, 2), "us_dense_ffn": round(t_dense, 2),
+            "GBps_ffn_active": round(ffn_bytes / t_ffn / 1e3, 1),
+            "GBps_predict": round(pred_bytes / t_pred / 1e3, 1),
+            "GBps_dense_ffn": round(dense_bytes / t_dense / 1e3, 1),
+            "speedup_sparse_vs_dense_ffn": round(t_dense / t_ffn, 2),
+            "tokens_s_dense_ffn_stack_only": round(B / (L * t_dense * 1e-6), 1),
+        })
+        # read-bandwidth probe over 4 GiB (same 16-byte load width)
+        buf = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(4, dtype=torch.float32, device=dev)
+        sg.sfnn_probe_read(buf, buf.numel(), sink)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(5):
+            sg.sfnn_probe_read(buf, buf.numel(), sink)
+        b.record()
+        torch.cuda.synchronize()
+        probe = 5 * buf.numel() / (a.elapsed_time(b) / 1e3) / 1e9
+        extra["probe_read_GBps"] = round(probe, 1)
+        del buf
+        out["roofline"] = {
+            "bound": "hbm", "achieved": round(ffn_bytes / t_ffn / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ffn_bytes / t_ffn / 1e3 / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "sfnn_sparse_ffn (k_up + k_down)",
+            "bytes_per_launch": int(ffn_bytes), "us_per_launch": round(t_ffn, 2),
+        }
+
+    # ---- CPU oracle baseline (bounded sample) ---------------------------------
+    if not args.no_cpu:
+        out["cpu_baseline"] = _cpu_baseline(host0, spec, B, L, args.cpu_seconds)
+
+    out["extra"] = extra
+    print(json.dumps(out), flush=True)
+
+
+def _hot_first(sg, layers, spec, B, dev):
+    """Profile fire counts on seeded tokens, then relayout each layer hot-first."""
+    import torch
+    import synth
+    from activation_sparse_gemv_amd.device import to_dev, workspace
+    f, d = spec.d_ff, spec.d_model
+    nprof = 256
+    xs = to_dev(synth.make_tokens(spec, nprof, stream=99))
+    for pred, ffn in layers:
+        ws = workspace(pred, None, 8)
+        m = torch.zeros((nprof, f // 64), dtype=torch.uint64, device=dev)
+        for i in range(0, nprof, 8):
+            sg.sfnn_predict(pred, xs[i:i + 8], 8, m[i:i + 8], None, ws)
+        counts = torch.zeros(f, dtype=torch.int32, device=dev)
+        sg.sfnn_fire_counts(m, nprof, f, counts)
+        ch = counts.cpu().numpy().view(np.uint32).copy()
+        perm = np.empty(f, dtype=np.int32)
+        sg.sfnn_hot_first_perm(ch, f, perm)
+        pd = to_dev(perm)
+        for t in [ffn.t[k] for k in ("w_up", "w_gate", "w_down_t", "s_up", "s_gate", "s_down_t", "b_up",
+                                     "b_gate")] + [pred.w2_t, pred.tau]:
+            if t is None:
+                continue
+            src = t.clone()
+            rb = t.numel() * t.element_size() // f
+            sg.sfnn_gather_rows(src, pd, f, rb, t)
+        torch.cuda.synchronize()
+
+
+def _cpu_baseline(lay, spec, B, L, budget_s):
+    """The float64 oracle (as it stands) on a bounded sample of the same workload."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    xs = synth.make_tokens(spec, 64 * B, stream=123)
+    n, t_total = 0, 0.0
+    while n < 64 and (t_total < budget_s or n < 2):
+        x = xs[n * B:(n + 1) * B]
+        t = time.perf_counter()
+        _, m = oracle.predict(lay.w1_t, lay.w2_t, lay.tau, x)
+        ids, c, _ = oracle.compact(oracle.pack_mask(m), B, spec.d_ff)
+        oracle.masked_ffn(lay, x, m)
+        t_total += time.perf_counter() - t
+        n += 1
+    per_layer = t_total / n
+    return {"value": round(B / (per_layer * L), 4), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} decode steps x 1 layer (layer 0) of the same stack, batch {B}, float64 NumPy "
+                      f"predict+compact+masked_ffn; tokens/s extrapolated x{L} layers; {t_total:.1f}s of CPU work"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * sfnn.h -- predictor-gated activation-sparse FFN for MI355X (gfx950).
+ *
+ * One decode step of one FFN layer, as the pages describe it:
+ *   1. a small per-layer predictor says which FFN neurons will fire
+ *      (53ai.com sparsity survey, PowerInfer section "自适应稀疏预测器",
+ *      adaptive sparse predictor; the hexiedandong.com PowerInfer repost:
+ *      a small routing module per layer predicts the neurons an input fires);
+ *   2. the predicted neurons are collected (53ai.com survey, "单层计算优化",
+ *      the one-layer example where neurons 3, 4 and 5 are predicted);
+ *   3. only those neurons' rows of W_up (and W_gate) and columns of W_down are
+ *      read and multiplied (53ai.com survey, "激活稀疏": a zero activation zeroes
+ *      the whole row it multiplies, so that row need not be loaded).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every array argument is a DEVICE pointer owned by the caller; the library
+ *    allocates nothing, keeps no mutable global state, and never reads a device
+ *    value back to the host (no implicit synchronisation; calls can be captured
+ *    in a HIP graph).  Descriptor structs are host memory, read during the call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call is asynchronous on it and uses the caller's current device.
+ *  - Arguments are validated on the host before anything is launched; a bad
+ *    argument returns an error status and launches nothing.  SFNN_E_HIP means a
+ *    launch failed (hipGetLastError).  Faults inside kernels surface at the
+ *    caller's next synchronisation.
+ *  - Shapes: d_ff % 64 == 0, d_model % 128 == 0, rank % 8 == 0,
+ *    8 <= rank <= 2048, 1 <= batch <= 64, d_ff <= 65536, d_model <= 16384.  Every pointer must be
+ *    16-byte aligned (SFNN_E_ALIGN).
+ *  - Weight layout is neuron-major: W_up, W_gate and W_down^T are
+ *    [d_ff][d_model] row-major, so neuron i owns one contiguous row of each
+ *    (row i of W_down^T is column i of the conventional W_down[d_model][d_ff]).
+ *  - Activations x: [batch][d_model] row-major, fp32 when the weights are
+ *    SFNN_F32, else fp16.  Outputs y: [batch][d_model] fp32.
+ *  - Masks: [batch][d_ff/64] uint64, neuron i is bit (i % 64) of word i / 64
+ *    (LSB first).
+ *  - SFNN_I4G128: weights are two's-complement INT4, element 2k in the low
+ *    nibble of byte k of the row ([d_ff][d_model/2] uint8), with one fp16
+ *    scale per row and 128 consecutive elements ([d_ff][d_model/128]);
+ *    w = q * s (the weight-only scheme of the ciyundata.com survey, section
+ *    2.2 量化, dequantised inside the kernel).
+ */
+#ifndef SFNN_H
+#define SFNN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SFNN_OK = 0,
+  SFNN_E_NULL = 1,      /* a required pointer is NULL                        */
+  SFNN_E_SHAPE = 2,     /* a size is outside the limits listed above         */
+  SFNN_E_ALIGN = 3,     /* a pointer is not 16-byte aligned                  */
+  SFNN_E_DTYPE = 4,     /* unknown or inconsistent weight / activation types */
+  SFNN_E_WORKSPACE = 5, /* workspace smaller than sfnn_workspace_bytes()     */
+  SFNN_E_HIP = 6        /* a HIP launch reported an error                    */
+} sfnn_status;
+
+typedef enum { SFNN_F32 = 0, SFNN_F16 = 1, SFNN_I4G128 = 2 } sfnn_wtype;
+typedef enum { SFNN_RELU = 0, SFNN_REGLU = 1 } sfnn_act;
+
+/* Per-layer low-rank predictor.  logit = W2^T (W1^T x); neuron i is predicted
+ * active iff logit_i > tau_i (strict).  wtype is SFNN_F32 or SFNN_F16 and
+ * must match the activation type of x. */
+typedef struct sfnn_pred {
+  int32_t d_model, d_ff, rank;
+  int32_t wtype;       /* sfnn_wtype: F32 or F16                         */
+  const void* w1_t;    /* [rank][d_model]                                */
+  const void* w2_t;    /* [d_ff][rank]                                   */
+  const float* tau;    /* [d_ff]                                         */
+} sfnn_pred;
+
+/* One FFN layer.  ReLU:  y = b_down + sum_i relu(W_up[i].x + b_up[i]) W_down[:, i]
+ *                ReGLU: y = b_down + sum_i relu(W_gate[i].x + b_gate[i])
+ *                                         * (W_up[i].x + b_up[i]) W_down[:, i]
+ * Biases have x's type (fp32 for F32 weights, else fp16); NULL means zero. */
+typedef struct sfnn_ffn {
+  int32_t d_model, d_ff;
+  int32_t wtype;       /* sfnn_wtype                                     */
+  int32_t act;         /* sfnn_act                                       */
+  const void* w_up;    /* [d_ff][d_model]  (I4G128: [d_ff][d_model/2])   */
+  const void* w_gate;  /* ReGLU only, same layout; NULL for ReLU         */
+  const void* w_down_t;/* [d_ff][d_model]  (I4G128: [d_ff][d_model/2])   */
+  const void* s_up;    /* I4G128 only: fp16 [d_ff][d_model/128]          */
+  const void* s_gate;
+  const void* s_down_t;
+  const void* b_up;    /* [d_ff]     or NULL                             */
+  const void* b_gate;  /* [d_ff]     or NULL                             */
+  const void* b_down;  /* [d_model]  or NULL                             */
+} sfnn_ffn;
+
+/* Bytes of device workspace needed by sfnn_predict / sfnn_sparse_ffn /
+ * sfnn_dense_ffn / sfnn_layer for this layer and batch (either descriptor may
+ * be NULL when only the other's calls are used).  0 on invalid input.  The
+ * workspace needs no initialisation and may be reused by the next call on the
+ * same stream. */
+size_t sfnn_workspace_bytes(const sfnn_pred* pred, const sfnn_ffn* ffn, int32_t batch);
+
+/* Predictor (steps 1 of the header comment).  Writes mask [batch][d_ff/64]
+ * and, if logits != NULL, the fp32 logits [batch][d_ff].  The mask equals
+ * (logits > tau) evaluated on those fp32 logits. */
+sfnn_status sfnn_predict(const sfnn_pred* pred, const void* x, int32_t batch,
+                         uint64_t* mask, float* logits,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Compaction (step 2): union U of the batch's masks, ids[0..count) = the set
+ * bits of U in ascending order, *count = |U| (device int32).  Entries of ids
+ * past count are left untouched.  union_mask [d_ff/64] is written if not NULL.
+ * ids must have room for d_ff entries. */
+sfnn_status sfnn_compact(const uint64_t* mask, int32_t batch, int32_t d_ff,
+                         int32_t* ids, int32_t* count, uint64_t* union_mask,
+                         void* stream);
+
+/* Sparse FFN (step 3) over the neurons ids[0..*count) (ascending, unique,
+ * < d_ff; entries >= d_ff are skipped and *count is clamped to d_ff).
+ * If mask != NULL each token b only takes neuron i when bit i of mask[b] is
+ * set (a select, not a multiply); with mask == NULL every token takes every
+ * listed neuron.  Writes y [batch][d_model] fp32. */
+sfnn_status sfnn_sparse_ffn(const sfnn_ffn* ffn, const void* x, int32_t batch,
+                            const int32_t* ids, const int32_t* count,
+                            const uint64_t* mask, float* y,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* The same FFN over all d_ff neurons with no gather: the dense baseline. */
+sfnn_status sfnn_dense_ffn(const sfnn_ffn* ffn, const void* x, int32_t batch, float* y,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/* predict -> compact -> sparse_ffn for one layer.  mask/ids/count are outputs
+ * the caller may inspect; any of them may be NULL, then they live in ws.
+ * pred and ffn must agree on d_model, d_ff and the activation type. */
+sfnn_status sfnn_layer(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x,
+                       int32_t batch, float* y, uint64_t* mask, int32_t* ids,
+                       int32_t* count, void* ws, size_t ws_bytes, void* stream);
+
+/* Stack step between layers (pre-norm residual chain, no gain):
+ * r_out = r_in + y (y may be NULL: r_out = r_in; r_out may alias r_in);
+ * x_out = r_out / sqrt(mean(r_out^2) + eps) written as xtype (F32 or F16).
+ * r_in, y, r_out: [batch][d_model] fp32. */
+sfnn_status sfnn_residual_rmsnorm(const float* r_in, const float* y, float* r_out, int32_t batch,
+                                  int32_t d_model, float eps, void* x_out, int32_t xtype, void* stream);
+
+/* Offline profiling (hexiedandong.com PowerInfer repost, power-law paragraph:
+ * neuron firing follows a power law, so hot neurons are found ahead of time).
+ * counts[i] += number of the n_masks masks ([n_masks][d_ff/64]) with bit i set. */
+sfnn_status sfnn_fire_counts(const uint64_t* masks, int32_t n_masks, int32_t d_ff,
+                             uint32_t* counts, void* stream);
+
+/* Hot-first order (HOST memory in and out): perm[new] = original neuron id,
+ * by descending count, ties by ascending id. */
+sfnn_status sfnn_hot_first_perm(const uint32_t* counts, int32_t d_ff, int32_t* perm);
+
+/* dst row k = src row perm[k] for k < n_rows, rows of row_bytes bytes
+ * (row_bytes % 2 == 0; applies a relayout to weights, scales and biases). */
+sfnn_status sfnn_gather_rows(const void* src, const int32_t* perm, int32_t n_rows,
+                             int64_t row_bytes, void* dst, void* stream);
+
+/* Measurement helpers: read `bytes` (multiple of 16) with 16-byte loads and
+ * fold them into sink[0] (read-bandwidth probe), and copy `bytes` from src to
+ * dst (reference copy for traffic counters). */
+sfnn_status sfnn_probe_read(const void* buf, size_t bytes, float* sink, void* stream);
+sfnn_status sfnn_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+const char* sfnn_status_str(sfnn_status s);
+int32_t sfnn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SFNN_H */

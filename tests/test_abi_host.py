@@ -1,0 +1,96 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every symbol the header declares, validates arguments before launching, and
+the host-only hot-first ordering matches the oracle's."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_symbols():
+    txt = open(os.path.join(ROOT, "include", "sfnn.h")).read()
+    return sorted(set(re.findall(r"\b(sfnn_[a-z_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import activation_sparse_gemv_amd as m
+    return m.load()
+
+
+def test_exports_match_header(L):
+    import activation_sparse_gemv_amd as m
+    syms = header_symbols()
+    assert len(syms) >= 14
+    assert sorted(m.EXPORTS) == syms
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_version_and_status_strings(L):
+    import activation_sparse_gemv_amd as m
+    assert m.sfnn_version() >= 100
+    assert m.sfnn_status_str(0) == "ok"
+    assert "workspace" in m.sfnn_status_str(5)
+
+
+def test_validation_rejects_without_launching(L):
+    import activation_sparse_gemv_amd as m
+    P = m._lib.sfnn_pred
+    F = m._lib.sfnn_ffn
+    fake = 1 << 20  # aligned non-null host value; never dereferenced because validation fails first
+    # null descriptor
+    assert L.sfnn_predict(None, fake, 1, fake, None, fake, 1 << 30, None) == 1
+    # bad shapes
+    p = P(768, 3000, 128, 0, fake, fake, fake)          # d_ff % 64 != 0
+    assert L.sfnn_predict(ctypes.byref(p), fake, 1, fake, None, fake, 1 << 30, None) == 2
+    p = P(768, 3072, 128, 0, fake, fake, fake)
+    assert L.sfnn_predict(ctypes.byref(p), fake, 0, fake, None, fake, 1 << 30, None) == 2   # batch 0
+    assert L.sfnn_predict(ctypes.byref(p), fake, 65, fake, None, fake, 1 << 30, None) == 2  # batch 65
+    assert L.sfnn_predict(ctypes.byref(p), fake + 4, 1, fake, None, fake, 1 << 30, None) == 3  # misaligned
+    assert L.sfnn_predict(ctypes.byref(p), fake, 1, fake, None, fake, 16, None) == 5          # workspace
+    p.wtype = 2
+    assert L.sfnn_predict(ctypes.byref(p), fake, 1, fake, None, fake, 1 << 30, None) == 4     # INT4 predictor
+    f = F(768, 3072, 1, 1, fake, None, fake, None, None, None, None, None, None)         # ReGLU w/o gate
+    assert L.sfnn_sparse_ffn(ctypes.byref(f), fake, 1, fake, fake, None, fake, fake, 1 << 30, None) == 1
+    f = F(700, 3072, 1, 0, fake, None, fake, None, None, None, None, None, None)         # d_model % 128
+    assert L.sfnn_sparse_ffn(ctypes.byref(f), fake, 1, fake, fake, None, fake, fake, 1 << 30, None) == 2
+    f = F(768, 3072, 2, 0, fake, None, fake, None, None, None, None, None, None)         # INT4 w/o scales
+    assert L.sfnn_dense_ffn(ctypes.byref(f), fake, 1, fake, fake, 1 << 30, None) == 1
+    assert L.sfnn_compact(fake, 1, 100, fake, fake, None, None) == 2
+    assert L.sfnn_compact(None, 1, 128, fake, fake, None, None) == 1
+    # layer: predictor / ffn type mismatch
+    p = P(768, 3072, 128, 1, fake, fake, fake)
+    f = F(768, 3072, 0, 0, fake, None, fake, None, None, None, None, None, None)
+    assert L.sfnn_layer(ctypes.byref(p), ctypes.byref(f), fake, 1, fake, None, None, None, fake, 1 << 30,
+                        None) == 4
+
+
+def test_workspace_bytes(L):
+    import activation_sparse_gemv_amd as m
+    P, F = m._lib.sfnn_pred, m._lib.sfnn_ffn
+    fake = 1 << 20
+    p = P(4096, 16384, 1024, 1, fake, fake, fake)
+    f = F(4096, 16384, 1, 0, fake, None, fake, None, None, None, None, None, None)
+    n1 = L.sfnn_workspace_bytes(ctypes.byref(p), ctypes.byref(f), 1)
+    n8 = L.sfnn_workspace_bytes(ctypes.byref(p), ctypes.byref(f), 8)
+    assert n1 >= 1024 * 4 + 16384 * 4 + 16384 * 4 and n8 > n1 and n1 % 256 == 0
+    assert L.sfnn_workspace_bytes(ctypes.byref(p), ctypes.byref(f), 0) == 0
+    assert L.sfnn_workspace_bytes(None, None, 1) == 0
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_hot_first_perm_host_matches_oracle(L, seed):
+    import activation_sparse_gemv_amd as m
+    g = np.random.default_rng(seed)
+    f = 4096
+    counts = g.integers(0, 20, size=f).astype(np.uint32)    # many ties
+    perm = np.empty(f, dtype=np.int32)
+    m.sfnn_hot_first_perm(counts, f, perm)
+    assert np.array_equal(perm, oracle.hot_first_perm(counts))
