@@ -19,7 +19,7 @@ size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool al16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
-  size_t z = 0, h = 0, partial = 0, cnt = 0, mask = 0, ids = 0, count = 0, total = 0;
+  size_t z = 0, h = 0, partial = 0, mask = 0, ids = 0, count = 0, total = 0;
 };
 
 Layout layout(const sfnn_pred* p, const sfnn_ffn* f, int batch) {
@@ -32,13 +32,10 @@ Layout layout(const sfnn_pred* p, const sfnn_ffn* f, int batch) {
   const int ff = f ? f->d_ff : (p ? p->d_ff : 0);
   if (f) {
     const int R = ffn_row_blocks(f->d_model, f->d_ff);
-    const int tiles = (f->d_model + 255) / 256;
     L.h = off;
     off += up((size_t)batch * f->d_ff * 4);
     L.partial = off;
     off += up((size_t)R * kMaxNT * f->d_model * 4);
-    L.cnt = off;
-    off += up((size_t)tiles * 4);
   }
   L.mask = off;
   off += up((size_t)batch * (ff / 64) * 8);
@@ -126,7 +123,6 @@ sfnn_status do_ffn(const sfnn_ffn* f, const void* x, int batch, const int32_t* i
   L.y = y;
   L.h = reinterpret_cast<float*>(ws + Lw.h);
   L.partial = reinterpret_cast<float*>(ws + Lw.partial);
-  L.tile_cnt = reinterpret_cast<int32_t*>(ws + Lw.cnt);
   L.row_blocks = ffn_row_blocks(f->d_model, f->d_ff);
   return hip_status(launch_ffn(L, s));
 }

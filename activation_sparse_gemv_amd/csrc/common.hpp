@@ -54,23 +54,39 @@ __device__ __forceinline__ void int4_pairs(uint32_t u, uint32_t out[4]) {
   }
 }
 
-// Where element c (0..7) of an 8-element chunk sits when x is staged for the
-// INT4 pairing above: order (0,4,1,5,2,6,3,7).
-__device__ __forceinline__ int int4_slot(int c) { return c < 4 ? 2 * c : 2 * (c - 4) + 1; }
-
 // Stage tokens [tok0, tok0+nt) of x [*, K] into LDS xs [NT][K]; rows of
-// tokens >= nt are zero.  PERM8 applies the INT4 pairing order.
+// tokens >= nt are zero.  16-byte vectors, four loads in flight per thread
+// before any store.  PERM8 applies the INT4 pairing order inside every
+// 8-element (16-byte fp16) vector.  K * sizeof(XT) must be a multiple of 16.
 template <typename XT, bool PERM8>
 __device__ __forceinline__ void stage_rows(XT* xs, const XT* __restrict__ x, int K, int tok0, int nt,
                                            int NT) {
-  const int total = NT * K;
-  for (int e = threadIdx.x; e < total; e += blockDim.x) {
-    const int t = e / K;
-    const int k = e - t * K;
-    const XT v = (t < nt) ? x[(size_t)(tok0 + t) * K + k] : (XT)0;
-    int kk = k;
-    if (PERM8) kk = (k & ~7) + int4_slot(k & 7);
-    xs[t * K + kk] = v;
+  const int vpr = K * (int)sizeof(XT) / 16;  // vectors per token row
+  const int total = NT * vpr;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x);
+  u32x4* dst = reinterpret_cast<u32x4*>(xs);
+  for (int base = threadIdx.x; base < total; base += 4 * blockDim.x) {
+    u32x4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = base + j * blockDim.x;
+      const int t = e / vpr;
+      v[j] = (e < total && t < nt) ? src[(size_t)(tok0 + t) * vpr + (e - t * vpr)] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = base + j * blockDim.x;
+      if (e < total) {
+        u32x4 o = v[j];
+        if (PERM8) {  // (x0x1, x2x3, x4x5, x6x7) -> (x0x4, x1x5, x2x6, x3x7)
+          o.x = (v[j].x & 0xFFFFu) | (v[j].z << 16);
+          o.y = (v[j].x >> 16) | (v[j].z & 0xFFFF0000u);
+          o.z = (v[j].y & 0xFFFFu) | (v[j].w << 16);
+          o.w = (v[j].y >> 16) | (v[j].w & 0xFFFF0000u);
+        }
+        dst[e] = o;
+      }
+    }
   }
 }
 
@@ -169,24 +185,47 @@ constexpr int vec_elems() { return WT == WT_F32 ? 4 : (WT == WT_F16 ? 8 : 32); }
 
 // Partial dot products of one weight row against NT staged token rows: lane
 // li of an LPR-lane group takes vectors li, li+LPR, ...  XT is the staged type.
-template <int WT, int LPR, int NT, typename XT>
+// UB loads are issued back to back before any arithmetic; vectors past the
+// row end re-read a valid vector of the same row and are zeroed by a select,
+// so the batch has no branches between its loads.
+template <int WT, int LPR, int NT, int UB, typename XT>
 __device__ __forceinline__ void row_partial(const uint8_t* __restrict__ row,
                                             const f16* __restrict__ srow, int nvec, int li,
                                             const XT* xs, int xstride, float* acc) {
   constexpr int E = vec_elems<WT>();
-#pragma unroll 8
-  for (int v = li; v < nvec; v += LPR) {
-    const u32x4 w = ld16_stream(row + 16 * (size_t)v);
-    if constexpr (WT == WT_F32) {
-      vec_f32<NT>(w, reinterpret_cast<const float*>(xs) + E * v, xstride, acc);
-    } else if constexpr (WT == WT_F16) {
-      if constexpr (sizeof(XT) == 4)
-        vec_f16_f32x<NT>(w, reinterpret_cast<const float*>(xs) + E * v, xstride, acc);
-      else
-        vec_f16<NT>(w, reinterpret_cast<const f16*>(xs) + E * v, xstride, acc);
-    } else {
-      const float s = (float)srow[v >> 2];
-      vec_i4<NT>(w, s, reinterpret_cast<const f16*>(xs) + E * v, xstride, acc);
+  for (int v0 = li; v0 < nvec; v0 += UB * LPR) {
+    u32x4 w[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int v = v0 + u * LPR;
+      w[u] = ld16_stream(row + 16 * (size_t)(v < nvec ? v : v0));
+    }
+    float sc[UB];
+    if constexpr (WT == WT_I4) {
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int v = v0 + u * LPR;
+        sc[u] = (float)srow[(v < nvec ? v : v0) >> 2];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the whole batch of loads ahead of the math
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int v = v0 + u * LPR;
+      const bool ok = v < nvec;
+      const int vc = ok ? v : v0;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const u32x4 wv = ok ? w[u] : z;
+      if constexpr (WT == WT_F32) {
+        vec_f32<NT>(wv, reinterpret_cast<const float*>(xs) + E * vc, xstride, acc);
+      } else if constexpr (WT == WT_F16) {
+        if constexpr (sizeof(XT) == 4)
+          vec_f16_f32x<NT>(wv, reinterpret_cast<const float*>(xs) + E * vc, xstride, acc);
+        else
+          vec_f16<NT>(wv, reinterpret_cast<const f16*>(xs) + E * vc, xstride, acc);
+      } else {
+        vec_i4<NT>(w[u], ok ? sc[u] : 0.0f, reinterpret_cast<const f16*>(xs) + E * vc, xstride, acc);
+      }
     }
   }
 }

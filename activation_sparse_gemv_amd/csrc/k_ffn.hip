@@ -10,11 +10,10 @@
 //          activations staged in LDS, ReLU / ReGLU and the per-token gate fused;
 //          writes h[tok][slot] (fp32).
 // k_down : column-scatter down projection.  Workgroup (tile, row block) sums
-//          h * W_down^T[ids] over its block of slots for 256 output columns,
-//          writes one fp32 partial per row block, and the last workgroup of a
-//          column tile to arrive adds the partials in row-block order (integer
-//          arrival counter, no floating-point atomics: results are
-//          run-to-run deterministic).
+//          h * W_down^T[ids] over its block of slots for 256 output columns and
+//          writes one fp32 partial per row block.
+// k_reduce: y = b_down + the row-block partials added in row-block order.  No
+//          atomics anywhere, so results are run-to-run deterministic.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -27,13 +26,10 @@ __global__ __launch_bounds__(256) void k_up(
     const uint8_t* __restrict__ w_up, const uint8_t* __restrict__ w_gate, const f16* __restrict__ s_up,
     const f16* __restrict__ s_gate, const void* __restrict__ b_up, const void* __restrict__ b_gate,
     const void* __restrict__ x, const int32_t* __restrict__ ids, const int32_t* __restrict__ count,
-    const uint64_t* __restrict__ mask, float* __restrict__ h, int32_t* __restrict__ tile_cnt, int ntiles,
-    int d, int f, int tok0, int nt) {
+    const uint64_t* __restrict__ mask, float* __restrict__ h, int d, int f, int tok0, int nt) {
   using XT = typename std::conditional<WT == WT_F32, float, f16>::type;
   extern __shared__ __align__(16) unsigned char smem[];
   XT* xs = reinterpret_cast<XT*>(smem);
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < ntiles; i += blockDim.x) tile_cnt[i] = 0;
   int n = f;
   if (ids) {
     n = *count;
@@ -58,10 +54,10 @@ __global__ __launch_bounds__(256) void k_up(
 #pragma unroll
     for (int t = 0; t < NT; ++t) au[t] = ag[t] = 0.0f;
     if (ok) {
-      row_partial<WT, kWave, NT, XT>(w_up + (size_t)i * row_bytes, s_up ? s_up + (size_t)i * ngroups : nullptr,
+      row_partial<WT, kWave, NT, 8, XT>(w_up + (size_t)i * row_bytes, s_up ? s_up + (size_t)i * ngroups : nullptr,
                                       nvec, lane, xs, d, au);
       if (ACT == ACT_REGLU)
-        row_partial<WT, kWave, NT, XT>(w_gate + (size_t)i * row_bytes,
+        row_partial<WT, kWave, NT, 8, XT>(w_gate + (size_t)i * row_bytes,
                                         s_gate ? s_gate + (size_t)i * ngroups : nullptr, nvec, lane, xs, d, ag);
     }
 #pragma unroll
@@ -116,26 +112,31 @@ __device__ __forceinline__ void load8(const uint8_t* __restrict__ w_down_t, cons
         reinterpret_cast<const uint32_t*>(w_down_t + (size_t)i * (d / 2) + col / 2));
     const float s = (float)s_down_t[(size_t)i * (d / 128) + col / 128];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) w[k] = (float)__builtin_amdgcn_sbfe(u, 4 * k, 4) * s;
+    for (int k = 0; k < 8; ++k) {
+      const int q = (int)(u << (28 - 4 * k)) >> 28;  // sign-extended nibble k
+      w[k] = (float)q * s;
+    }
   }
 }
 
+constexpr int kChunk = 256;  // slots staged in LDS per step of the down projection
+constexpr int kUnroll = 4;   // independent row loads in flight per lane
+
 template <int WT, int NT>
 __global__ __launch_bounds__(256) void k_down(const uint8_t* __restrict__ w_down_t,
-                                              const f16* __restrict__ s_down_t, const void* __restrict__ b_down,
-                                              const float* __restrict__ h, const int32_t* __restrict__ ids,
-                                              const int32_t* __restrict__ count, float* __restrict__ partial,
-                                              int32_t* __restrict__ tile_cnt, float* __restrict__ y, int d, int f,
-                                              int tok0, int nt) {
-  using XT = typename std::conditional<WT == WT_F32, float, f16>::type;
+                                              const f16* __restrict__ s_down_t, const float* __restrict__ h,
+                                              const int32_t* __restrict__ ids, const int32_t* __restrict__ count,
+                                              float* __restrict__ partial, int d, int f, int tok0, int nt) {
   __shared__ float red[4][NT][kTile];
-  __shared__ int last;
+  __shared__ int s_ids[kChunk];
+  __shared__ float s_h[NT][kChunk];
   const int tile = blockIdx.x, rb = blockIdx.y, R = gridDim.y;
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int rg = wave * 2 + (lane >> 5);          // row group 0..7
   const int cl = (lane & 31) * 8;                 // column offset inside the tile
-  const int col = tile * kTile + cl;
-  const bool colok = col < d;
+  const int col0 = tile * kTile + cl;
+  const bool colok = col0 < d;
+  const int col = colok ? col0 : 0;               // keeps every address in bounds
 
   int n = f;
   if (ids) {
@@ -152,18 +153,42 @@ __global__ __launch_bounds__(256) void k_down(const uint8_t* __restrict__ w_down
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[t][k] = 0.0f;
 
-#pragma unroll 4
-  for (int s = s0 + rg; s < s1; s += 8) {
-    const int i = ids ? ids[s] : s;
-    if ((unsigned)i >= (unsigned)f || !colok) continue;
-    float w[8];
-    load8<WT>(w_down_t, s_down_t, i, col, d, w);
+  for (int c0 = s0; c0 < s1; c0 += kChunk) {
+    const int cn = (s1 - c0 < kChunk) ? s1 - c0 : kChunk;
+    for (int j = threadIdx.x; j < cn; j += blockDim.x) {
+      const int i = ids ? ids[c0 + j] : c0 + j;
+      s_ids[j] = ((unsigned)i < (unsigned)f) ? i : -1;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float hv = (t < nt) ? h[(size_t)(tok0 + t) * f + s] : 0.0f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[t][k] = __builtin_fmaf(hv, w[k], acc[t][k]);
+      for (int t = 0; t < NT; ++t) s_h[t][j] = (t < nt) ? h[(size_t)(tok0 + t) * f + c0 + j] : 0.0f;
     }
+    __syncthreads();
+    const int ilast = s_ids[cn - 1];
+    for (int j = rg; j < cn; j += 8 * kUnroll) {
+      float w[kUnroll][8];
+      bool ok[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int jj = j + 8 * u;
+        const int iu = jj < cn ? s_ids[jj] : ilast;  // tail slots re-read a row this block loads anyway
+        ok[u] = (jj < cn) && (iu >= 0) && colok;
+        load8<WT>(w_down_t, s_down_t, iu >= 0 ? iu : 0, col, d, w[u]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // all row loads of the batch issue before any FMA
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int jj = (j + 8 * u < cn) ? j + 8 * u : cn - 1;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const float hv = s_h[t][jj];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float wk = ok[u] ? w[u][k] : 0.0f;  // select: skipped rows add exactly nothing
+            acc[t][k] = __builtin_fmaf(ok[u] ? hv : 0.0f, wk, acc[t][k]);
+          }
+        }
+      }
+    }
+    __syncthreads();
   }
   // lanes l and l+32 hold the same columns for neighbouring row groups
 #pragma unroll
@@ -188,26 +213,28 @@ __global__ __launch_bounds__(256) void k_down(const uint8_t* __restrict__ w_down
       }
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&tile_cnt[tile], 1);
-    last = (prev == R - 1);
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  if (c < d) {
-    const float bd = b_down ? load_as_float<XT>(b_down, c) : 0.0f;
+}
+
+// y[tok][c] = b_down[c] + sum over row blocks q = 0..R-1 (in order) of partial[q][t][c].
+template <typename XT>
+__global__ __launch_bounds__(64) void k_reduce(const float* __restrict__ partial, const void* __restrict__ b_down,
+                                               float* __restrict__ y, int d, int R, int tok0, int nt) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;  // (t, c) pairs
+  if (e >= nt * d) return;
+  const int t = e / d, c = e - t * d;
+  float v = b_down ? load_as_float<XT>(b_down, c) : 0.0f;
+  for (int q0 = 0; q0 < R; q0 += 16) {
+    float p[16];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t < nt) {
-        float v = bd;
-        for (int q = 0; q < R; ++q) v += __builtin_nontemporal_load(&partial[((size_t)q * kMaxNT + t) * d + c]);
-        y[(size_t)(tok0 + t) * d + c] = v;
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int q = (q0 + j < R) ? q0 + j : q0;
+      p[j] = partial[((size_t)q * kMaxNT + t) * d + c];
     }
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (q0 + j < R) v += p[j];
   }
+  y[(size_t)(tok0 + t) * d + c] = v;
 }
 
 int ffn_row_blocks(int d, int f) {
@@ -228,10 +255,11 @@ static void ffn_pass(const FfnLaunch& p, int tok0, int nt, hipStream_t s) {
   if (blocks > 1024) blocks = 1024;
   hipLaunchKernelGGL((k_up<WT, ACT, NT>), dim3(blocks), dim3(256), sh, s, (const uint8_t*)p.w_up,
                      (const uint8_t*)p.w_gate, (const f16*)p.s_up, (const f16*)p.s_gate, p.b_up, p.b_gate, p.x,
-                     p.ids, p.count, p.mask, p.h, p.tile_cnt, ntiles, p.d, p.f, tok0, nt);
+                     p.ids, p.count, p.mask, p.h, p.d, p.f, tok0, nt);
   hipLaunchKernelGGL((k_down<WT, NT>), dim3(ntiles, p.row_blocks), dim3(256), 0, s, (const uint8_t*)p.w_down_t,
-                     (const f16*)p.s_down_t, p.b_down, p.h, p.ids, p.count, p.partial, p.tile_cnt, p.y, p.d,
-                     p.f, tok0, nt);
+                     (const f16*)p.s_down_t, p.h, p.ids, p.count, p.partial, p.d, p.f, tok0, nt);
+  hipLaunchKernelGGL((k_reduce<XT>), dim3((nt * p.d + 63) / 64), dim3(64), 0, s, p.partial, p.b_down, p.y, p.d,
+                     p.row_blocks, tok0, nt);
 }
 
 template <int WT, int ACT>

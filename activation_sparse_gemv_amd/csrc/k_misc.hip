@@ -7,28 +7,21 @@ namespace sfnn {
 
 // Union of the batch's masks and the ascending list of its set bits
 // (53ai.com sparsity survey, PowerInfer one-layer example 单层计算优化: only the
-// predicted set {3, 4, 5} is computed).  One workgroup: every thread owns a
-// run of consecutive words, a popcount + workgroup prefix sum gives each run
-// its output offset, and bits are emitted lowest first, so ids come out in
-// ascending order with no sort.
+// predicted set {3, 4, 5} is computed).  One workgroup: every thread owns one
+// mask word, a popcount + workgroup prefix sum gives each word its output
+// offset, and bits are emitted lowest first, so ids come out in ascending
+// order with no sort.
 __global__ __launch_bounds__(1024) void k_compact(const uint64_t* __restrict__ mask, int batch, int words,
                                                   int32_t* __restrict__ ids, int32_t* __restrict__ count,
                                                   uint64_t* __restrict__ union_mask) {
+  // words <= 1024 (d_ff <= 65536): thread w owns mask word w
   __shared__ int wsum[16];
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
-  const int per = (words + blockDim.x - 1) / blockDim.x;
-  const int w0 = tid * per;
-
-  int local = 0;
-  for (int k = 0; k < per; ++k) {
-    const int w = w0 + k;
-    if (w < words) {
-      uint64_t u = 0;
-      for (int b = 0; b < batch; ++b) u |= mask[(size_t)b * words + w];
-      local += __popcll(u);
-    }
-  }
+  const int w = threadIdx.x;
+  const int lane = w & (kWave - 1), wave = w / kWave;
+  uint64_t u = 0;
+  if (w < words)
+    for (int b = 0; b < batch; ++b) u |= mask[(size_t)b * words + w];
+  const int local = __popcll(u);
   int v = local;  // inclusive scan inside the wave
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
@@ -49,20 +42,15 @@ __global__ __launch_bounds__(1024) void k_compact(const uint64_t* __restrict__ m
   }
   __syncthreads();
   int off = v - local + (wave > 0 ? wsum[wave - 1] : 0);
-  for (int k = 0; k < per; ++k) {
-    const int w = w0 + k;
-    if (w < words) {
-      uint64_t u = 0;
-      for (int b = 0; b < batch; ++b) u |= mask[(size_t)b * words + w];
-      if (union_mask) union_mask[w] = u;
-      while (u) {
-        const int bit = __builtin_ctzll(u);
-        ids[off++] = w * 64 + bit;
-        u &= u - 1;
-      }
+  if (w < words) {
+    if (union_mask) union_mask[w] = u;
+    while (u) {
+      const int bit = __builtin_ctzll(u);
+      ids[off++] = w * 64 + bit;
+      u &= u - 1;
     }
   }
-  if (tid == blockDim.x - 1) *count = off;
+  if (w == blockDim.x - 1) *count = off;
 }
 
 // counts[i] += number of masks with bit i set (offline hot/cold profiling).
@@ -106,25 +94,59 @@ __device__ __forceinline__ float block_sum256(float v, float* sh) {
 }
 
 // r_out = r_in + y (y optional); x = r_out / sqrt(mean(r_out^2) + eps).
-// One workgroup per token.
+// One workgroup per token; each thread keeps up to 64 values in registers
+// (d_model <= 16384), loaded as 16-byte vectors.
 __global__ __launch_bounds__(256) void k_residual_rmsnorm(const float* r_in, const float* y, float* r_out, int d,
                                                           float eps, void* __restrict__ xo, int xtype) {
+  constexpr int kMaxV = 16;  // float4 vectors per thread
   __shared__ float sh[4];
   const size_t base = (size_t)blockIdx.x * d;
+  const int nv = d / 4;
+  const f32x4* ri = reinterpret_cast<const f32x4*>(r_in + base);
+  const f32x4* yi = reinterpret_cast<const f32x4*>(y + base);
+  f32x4 v[kMaxV];
+#pragma unroll
+  for (int j = 0; j < kMaxV; ++j) {
+    const int e = threadIdx.x + j * blockDim.x;
+    v[j] = (e < nv) ? ri[e] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (y) {
+#pragma unroll
+    for (int j = 0; j < kMaxV; ++j) {
+      const int e = threadIdx.x + j * blockDim.x;
+      if (e < nv) v[j] += yi[e];
+    }
+  }
   float ss = 0.0f;
-  for (int k = threadIdx.x; k < d; k += blockDim.x) {
-    const float v = r_in[base + k] + (y ? y[base + k] : 0.0f);
-    r_out[base + k] = v;
-    ss = __builtin_fmaf(v, v, ss);
+  f32x4* ro = reinterpret_cast<f32x4*>(r_out + base);
+#pragma unroll
+  for (int j = 0; j < kMaxV; ++j) {
+    const int e = threadIdx.x + j * blockDim.x;
+    if (e < nv) {
+      ro[e] = v[j];
+      ss = __builtin_fmaf(v[j].x, v[j].x, ss);
+      ss = __builtin_fmaf(v[j].y, v[j].y, ss);
+      ss = __builtin_fmaf(v[j].z, v[j].z, ss);
+      ss = __builtin_fmaf(v[j].w, v[j].w, ss);
+    }
   }
   const float tot = block_sum256(ss, sh);
   const float inv = 1.0f / __builtin_sqrtf(tot / (float)d + eps);
-  for (int k = threadIdx.x; k < d; k += blockDim.x) {
-    const float v = r_out[base + k] * inv;
-    if (xtype == WT_F32)
-      reinterpret_cast<float*>(xo)[base + k] = v;
-    else
-      reinterpret_cast<f16*>(xo)[base + k] = (f16)v;
+#pragma unroll
+  for (int j = 0; j < kMaxV; ++j) {
+    const int e = threadIdx.x + j * blockDim.x;
+    if (e < nv) {
+      const f32x4 o = v[j] * inv;
+      if (xtype == WT_F32) {
+        reinterpret_cast<f32x4*>(xo)[base / 4 + e] = o;
+      } else {
+        const f16x2 a = {(f16)o.x, (f16)o.y}, b = {(f16)o.z, (f16)o.w};
+        uint2 pk;
+        pk.x = __builtin_bit_cast(uint32_t, a);
+        pk.y = __builtin_bit_cast(uint32_t, b);
+        reinterpret_cast<uint2*>(xo)[base / 4 + e] = pk;
+      }
+    }
   }
 }
 

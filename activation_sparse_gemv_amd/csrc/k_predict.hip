@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void k_pred1(const uint8_t* __restrict__ w1_t,
     float acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
-    if (j < r) row_partial<WT, LPR, NT, XT>(w1_t + (size_t)j * row_bytes, nullptr, nvec, li, xs, d, acc);
+    if (j < r) row_partial<WT, LPR, NT, 8, XT>(w1_t + (size_t)j * row_bytes, nullptr, nvec, li, xs, d, acc);
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = group_sum<LPR>(acc[t]);
     if (li == 0 && j < r) {
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(512) void k_pred2(const uint8_t* __restrict__ w2_t,
   float acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
-  row_partial<WT, LPR, NT, float>(w2_t + (size_t)i * row_bytes, nullptr, nvec, li, zs, r, acc);
+  row_partial<WT, LPR, NT, 16, float>(w2_t + (size_t)i * row_bytes, nullptr, nvec, li, zs, r, acc);
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = group_sum<LPR>(acc[t]);
   if (li == 0) {

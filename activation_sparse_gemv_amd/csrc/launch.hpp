@@ -40,7 +40,6 @@ struct FfnLaunch {
   float* y;               // [B][d]
   float* h;               // [B][f] workspace
   float* partial;         // [R][kMaxNT][d] workspace
-  int32_t* tile_cnt;      // [ceil(d/256)] workspace
   int row_blocks;         // R
 };
 hipError_t launch_ffn(const FfnLaunch& p, hipStream_t s);
