@@ -24,7 +24,7 @@ STATUS = {0: "SFNN_OK", 1: "SFNN_E_NULL", 2: "SFNN_E_SHAPE", 3: "SFNN_E_ALIGN", 
 
 EXPORTS = [
     "sfnn_workspace_bytes", "sfnn_predict", "sfnn_compact", "sfnn_sparse_ffn", "sfnn_dense_ffn",
-    "sfnn_layer", "sfnn_residual_rmsnorm", "sfnn_fire_counts", "sfnn_hot_first_perm",
+    "sfnn_layer", "sfnn_stack_decode", "sfnn_residual_rmsnorm", "sfnn_fire_counts", "sfnn_hot_first_perm",
     "sfnn_gather_rows", "sfnn_probe_read", "sfnn_probe_copy", "sfnn_status_str", "sfnn_version",
 ]
 
@@ -70,6 +70,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sfnn_sparse_ffn": (i32, [F, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
         "sfnn_dense_ffn": (i32, [F, vp, i32, vp, vp, sz, vp]),
         "sfnn_layer": (i32, [P, F, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "sfnn_stack_decode": (i32, [i32, P, F, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, sz, vp]),
         "sfnn_residual_rmsnorm": (i32, [vp, vp, vp, i32, i32, ctypes.c_float, vp, i32, vp]),
         "sfnn_fire_counts": (i32, [vp, i32, i32, vp, vp]),
         "sfnn_hot_first_perm": (i32, [vp, i32, vp]),
@@ -191,6 +192,26 @@ def sfnn_dense_ffn(ffn: FFN, x, batch: int, y, ws, stream=None):
 def sfnn_layer(pred: Pred, ffn: FFN, x, batch: int, y, mask=None, ids=None, count=None, ws=None, stream=None):
     _check("sfnn_layer", load().sfnn_layer(pred.ref, ffn.ref, _p(x), batch, _p(y), _p(mask), _p(ids), _p(count),
                                             _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+
+
+class Stack:
+    """Host arrays of per-layer descriptors for sfnn_stack_decode (keeps the layers alive)."""
+
+    def __init__(self, layers):
+        self.layers = list(layers)  # [(Pred, FFN)]
+        n = len(self.layers)
+        self.preds = (sfnn_pred * n)(*[p.c for p, _ in self.layers])
+        self.ffns = (sfnn_ffn * n)(*[f.c for _, f in self.layers])
+
+    def __len__(self):
+        return len(self.layers)
+
+
+def sfnn_stack_decode(stack: Stack, batch: int, r_in, r_out, eps: float, ws, x_cap=None, y_cap=None, mask_cap=None,
+                      ids_cap=None, count_cap=None, stream=None):
+    _check("sfnn_stack_decode", load().sfnn_stack_decode(
+        len(stack), stack.preds, stack.ffns, batch, _p(r_in), _p(r_out), eps, _p(x_cap), _p(y_cap),
+        _p(mask_cap), _p(ids_cap), _p(count_cap), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
 
 
 def sfnn_residual_rmsnorm(r_in, y, r_out, batch: int, d_model: int, eps: float, x_out, stream=None):

@@ -17,32 +17,45 @@ constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool al16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
+bool al4(const void* p) { return p == nullptr || ((uintptr_t)p & 3u) == 0; }
 
 struct Layout {
-  size_t z = 0, h = 0, partial = 0, mask = 0, ids = 0, count = 0, total = 0;
+  size_t z = 0, h = 0, partial = 0, mask = 0, uni = 0, ids = 0, count = 0, rbuf = 0, xbuf = 0, total = 0;
+  int R = 0;
 };
 
+// Workspace: predictor stage-1 output z, the up projection's h, the down
+// projection's row-block partials, masks, union mask, ids, count, and the
+// residual chain's two fp32 rows and layer input.
 Layout layout(const sfnn_pred* p, const sfnn_ffn* f, int batch) {
   Layout L;
   size_t off = 0;
+  const int ff = f ? f->d_ff : (p ? p->d_ff : 0);
+  const int dm = f ? f->d_model : (p ? p->d_model : 0);
   if (p) {
     L.z = off;
     off += up((size_t)batch * p->rank * 4);
   }
-  const int ff = f ? f->d_ff : (p ? p->d_ff : 0);
   if (f) {
-    const int R = ffn_row_blocks(f->d_model, f->d_ff);
+    L.R = ffn_row_blocks(f->wtype == SFNN_F32 ? WT_F32 : (f->wtype == SFNN_F16 ? WT_F16 : WT_I4), f->d_model,
+                         f->d_ff);
     L.h = off;
     off += up((size_t)batch * f->d_ff * 4);
     L.partial = off;
-    off += up((size_t)R * kMaxNT * f->d_model * 4);
+    off += up((size_t)L.R * batch * f->d_model * 4);
   }
   L.mask = off;
   off += up((size_t)batch * (ff / 64) * 8);
+  L.uni = off;
+  off += up((size_t)(ff / 64) * 8);
   L.ids = off;
   off += up((size_t)ff * 4);
   L.count = off;
   off += up(4);
+  L.rbuf = off;
+  off += up((size_t)2 * batch * dm * 4);
+  L.xbuf = off;
+  off += up((size_t)batch * dm * 4);
   L.total = off;
   return L;
 }
@@ -81,8 +94,8 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 sfnn_status hip_status(hipError_t e) { return e == hipSuccess ? SFNN_OK : SFNN_E_HIP; }
 
-sfnn_status do_predict(const sfnn_pred* p, const void* x, int batch, uint64_t* mask, float* logits, float* z,
-                       hipStream_t s) {
+PredLaunch pred_launch(const sfnn_pred* p, const void* x, int batch, uint64_t* mask, uint64_t* uni,
+                       float* logits, float* z) {
   PredLaunch L;
   L.wt = p->wtype == SFNN_F32 ? WT_F32 : WT_F16;
   L.d = p->d_model;
@@ -95,12 +108,18 @@ sfnn_status do_predict(const sfnn_pred* p, const void* x, int batch, uint64_t* m
   L.batch = batch;
   L.z = z;
   L.mask = mask;
+  L.union_mask = uni;
   L.logits = logits;
-  return hip_status(launch_predict(L, s));
+  return L;
 }
 
-sfnn_status do_ffn(const sfnn_ffn* f, const void* x, int batch, const int32_t* ids, const int32_t* count,
-                   const uint64_t* mask, float* y, char* ws, const Layout& Lw, hipStream_t s) {
+sfnn_status do_predict(const sfnn_pred* p, const void* x, int batch, uint64_t* mask, uint64_t* uni,
+                       float* logits, float* z, hipStream_t s) {
+  return hip_status(launch_predict(pred_launch(p, x, batch, mask, uni, logits, z), s));
+}
+
+FfnLaunch ffn_launch(const sfnn_ffn* f, const void* x, int batch, const uint64_t* mask, float* y, char* ws,
+                     const Layout& Lw) {
   FfnLaunch L;
   L.wt = f->wtype == SFNN_F32 ? WT_F32 : (f->wtype == SFNN_F16 ? WT_F16 : WT_I4);
   L.act = f->act == SFNN_RELU ? ACT_RELU : ACT_REGLU;
@@ -117,14 +136,18 @@ sfnn_status do_ffn(const sfnn_ffn* f, const void* x, int batch, const int32_t* i
   L.b_down = f->b_down;
   L.x = x;
   L.batch = batch;
-  L.ids = ids;
-  L.count = count;
+  L.src = SRC_DENSE;
+  L.ids = nullptr;
+  L.count = nullptr;
+  L.union_mask = nullptr;
+  L.ids_out = nullptr;
+  L.count_out = nullptr;
   L.mask = mask;
   L.y = y;
   L.h = reinterpret_cast<float*>(ws + Lw.h);
   L.partial = reinterpret_cast<float*>(ws + Lw.partial);
-  L.row_blocks = ffn_row_blocks(f->d_model, f->d_ff);
-  return hip_status(launch_ffn(L, s));
+  L.row_blocks = Lw.R;
+  return L;
 }
 
 }  // namespace
@@ -147,14 +170,16 @@ sfnn_status sfnn_predict(const sfnn_pred* pred, const void* x, int32_t batch, ui
   if (!al16(x) || !al16(mask) || !al16(logits) || !al16(ws)) return SFNN_E_ALIGN;
   const Layout Lw = layout(pred, nullptr, batch);
   if (ws_bytes < Lw.total) return SFNN_E_WORKSPACE;
-  return do_predict(pred, x, batch, mask, logits, reinterpret_cast<float*>((char*)ws + Lw.z), as_stream(stream));
+  char* w = (char*)ws;
+  return do_predict(pred, x, batch, mask, reinterpret_cast<uint64_t*>(w + Lw.uni), logits,
+                    reinterpret_cast<float*>(w + Lw.z), as_stream(stream));
 }
 
 sfnn_status sfnn_compact(const uint64_t* mask, int32_t batch, int32_t d_ff, int32_t* ids, int32_t* count,
                          uint64_t* union_mask, void* stream) {
   if (!mask || !ids || !count) return SFNN_E_NULL;
   if (!batch_ok(batch) || !dff_ok(d_ff)) return SFNN_E_SHAPE;
-  if (!al16(mask) || !al16(ids) || !al16(count) || !al16(union_mask)) return SFNN_E_ALIGN;
+  if (!al16(mask) || !al16(ids) || !al4(count) || !al16(union_mask)) return SFNN_E_ALIGN;
   return hip_status(launch_compact(mask, batch, d_ff, ids, count, union_mask, as_stream(stream)));
 }
 
@@ -165,10 +190,14 @@ sfnn_status sfnn_sparse_ffn(const sfnn_ffn* ffn, const void* x, int32_t batch, c
   if (st != SFNN_OK) return st;
   if (!x || !ids || !count || !y || !ws) return SFNN_E_NULL;
   if (!batch_ok(batch)) return SFNN_E_SHAPE;
-  if (!al16(x) || !al16(ids) || !al16(count) || !al16(mask) || !al16(y) || !al16(ws)) return SFNN_E_ALIGN;
+  if (!al16(x) || !al16(ids) || !al4(count) || !al16(mask) || !al16(y) || !al16(ws)) return SFNN_E_ALIGN;
   const Layout Lw = layout(nullptr, ffn, batch);
   if (ws_bytes < Lw.total) return SFNN_E_WORKSPACE;
-  return do_ffn(ffn, x, batch, ids, count, mask, y, (char*)ws, Lw, as_stream(stream));
+  FfnLaunch L = ffn_launch(ffn, x, batch, mask, y, (char*)ws, Lw);
+  L.src = SRC_IDS;
+  L.ids = ids;
+  L.count = count;
+  return hip_status(launch_ffn(L, as_stream(stream)));
 }
 
 sfnn_status sfnn_dense_ffn(const sfnn_ffn* ffn, const void* x, int32_t batch, float* y, void* ws,
@@ -180,32 +209,114 @@ sfnn_status sfnn_dense_ffn(const sfnn_ffn* ffn, const void* x, int32_t batch, fl
   if (!al16(x) || !al16(y) || !al16(ws)) return SFNN_E_ALIGN;
   const Layout Lw = layout(nullptr, ffn, batch);
   if (ws_bytes < Lw.total) return SFNN_E_WORKSPACE;
-  return do_ffn(ffn, x, batch, nullptr, nullptr, nullptr, y, (char*)ws, Lw, as_stream(stream));
+  return hip_status(launch_ffn(ffn_launch(ffn, x, batch, nullptr, y, (char*)ws, Lw), as_stream(stream)));
 }
 
-sfnn_status sfnn_layer(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x, int32_t batch, float* y,
-                       uint64_t* mask, int32_t* ids, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+static sfnn_status check_pair(const sfnn_pred* pred, const sfnn_ffn* ffn) {
   sfnn_status st = check_pred(pred);
   if (st != SFNN_OK) return st;
   st = check_ffn(ffn);
   if (st != SFNN_OK) return st;
-  if (!x || !y || !ws) return SFNN_E_NULL;
-  if (!batch_ok(batch)) return SFNN_E_SHAPE;
   if (pred->d_model != ffn->d_model || pred->d_ff != ffn->d_ff) return SFNN_E_SHAPE;
   if (pred->wtype != x_type_of_ffn(ffn)) return SFNN_E_DTYPE;
-  if (!al16(x) || !al16(y) || !al16(mask) || !al16(ids) || !al16(count) || !al16(ws)) return SFNN_E_ALIGN;
+  return SFNN_OK;
+}
+
+sfnn_status sfnn_layer(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x, int32_t batch, float* y,
+                       uint64_t* mask, int32_t* ids, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  sfnn_status st = check_pair(pred, ffn);
+  if (st != SFNN_OK) return st;
+  if (!x || !y || !ws) return SFNN_E_NULL;
+  if (!batch_ok(batch)) return SFNN_E_SHAPE;
+  if (!al16(x) || !al16(y) || !al16(mask) || !al16(ids) || !al4(count) || !al16(ws)) return SFNN_E_ALIGN;
   const Layout Lw = layout(pred, ffn, batch);
   if (ws_bytes < Lw.total) return SFNN_E_WORKSPACE;
   char* w = (char*)ws;
   if (!mask) mask = reinterpret_cast<uint64_t*>(w + Lw.mask);
   if (!ids) ids = reinterpret_cast<int32_t*>(w + Lw.ids);
   if (!count) count = reinterpret_cast<int32_t*>(w + Lw.count);
+  uint64_t* uni = reinterpret_cast<uint64_t*>(w + Lw.uni);
   hipStream_t s = as_stream(stream);
-  st = do_predict(pred, x, batch, mask, nullptr, reinterpret_cast<float*>(w + Lw.z), s);
+  // predictor (writes the batch's union mask), then the FFN compacts the
+  // union in its first kernel and writes ids/count on the way
+  st = do_predict(pred, x, batch, mask, uni, nullptr, reinterpret_cast<float*>(w + Lw.z), s);
   if (st != SFNN_OK) return st;
-  st = hip_status(launch_compact(mask, batch, ffn->d_ff, ids, count, nullptr, s));
-  if (st != SFNN_OK) return st;
-  return do_ffn(ffn, x, batch, ids, count, batch > 1 ? mask : nullptr, y, w, Lw, s);
+  FfnLaunch L = ffn_launch(ffn, x, batch, batch > 1 ? mask : nullptr, y, w, Lw);
+  L.src = SRC_UNION;
+  L.union_mask = uni;
+  L.ids_out = ids;
+  L.count_out = count;
+  return hip_status(launch_ffn(L, s));
+}
+
+sfnn_status sfnn_stack_decode(int32_t n_layers, const sfnn_pred* preds, const sfnn_ffn* ffns, int32_t batch,
+                              const float* r_in, float* r_out, float eps, void* x_cap, float* y_cap,
+                              uint64_t* mask_cap, int32_t* ids_cap, int32_t* count_cap, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!preds || !ffns || !r_in || !r_out || !ws) return SFNN_E_NULL;
+  if (n_layers < 1 || !batch_ok(batch)) return SFNN_E_SHAPE;
+  for (int l = 0; l < n_layers; ++l) {
+    const sfnn_status st = check_pair(&preds[l], &ffns[l]);
+    if (st != SFNN_OK) return st;
+    if (preds[l].d_model != preds[0].d_model || preds[l].d_ff != preds[0].d_ff || preds[l].rank != preds[0].rank ||
+        preds[l].wtype != preds[0].wtype || ffns[l].wtype != ffns[0].wtype || ffns[l].act != ffns[0].act)
+      return SFNN_E_SHAPE;
+  }
+  if (!(eps > 0.0f)) return SFNN_E_SHAPE;
+  if (!al16(r_in) || !al16(r_out) || !al16(x_cap) || !al16(y_cap) || !al16(mask_cap) || !al16(ids_cap) ||
+      !al4(count_cap) || !al16(ws))
+    return SFNN_E_ALIGN;
+  const Layout Lw = layout(&preds[0], &ffns[0], batch);
+  if (ws_bytes < Lw.total) return SFNN_E_WORKSPACE;
+  char* w = (char*)ws;
+  hipStream_t s = as_stream(stream);
+  const int d = preds[0].d_model, f = preds[0].d_ff, W = f / 64;
+  const int xb = preds[0].wtype == SFNN_F32 ? 4 : 2;
+  const int xt = preds[0].wtype == SFNN_F32 ? WT_F32 : WT_F16;
+  float* rbuf[2] = {reinterpret_cast<float*>(w + Lw.rbuf),
+                    reinterpret_cast<float*>(w + Lw.rbuf) + (size_t)batch * d};
+  float* partial = reinterpret_cast<float*>(w + Lw.partial);
+  // the previous layer's partials are summed inside the next predictor when
+  // few enough; otherwise by a separate reduce launch
+  const bool fuse = Lw.R <= kChainFuseMaxR;
+  for (int l = 0; l < n_layers; ++l) {
+    void* xl = x_cap ? (char*)x_cap + (size_t)l * batch * d * xb : (void*)(w + Lw.xbuf);
+    uint64_t* ml = mask_cap ? mask_cap + (size_t)l * batch * W : reinterpret_cast<uint64_t*>(w + Lw.mask);
+    int32_t* il = ids_cap ? ids_cap + (size_t)l * f : reinterpret_cast<int32_t*>(w + Lw.ids);
+    int32_t* cl = count_cap ? count_cap + l : reinterpret_cast<int32_t*>(w + Lw.count);
+    uint64_t* uni = reinterpret_cast<uint64_t*>(w + Lw.uni);
+    PredLaunch P = pred_launch(&preds[l], nullptr, batch, ml, uni, nullptr, reinterpret_cast<float*>(w + Lw.z));
+    P.norm.eps = eps;
+    P.norm.x_out = xl;
+    float* yprev = (l > 0 && y_cap) ? y_cap + (size_t)(l - 1) * batch * d : nullptr;
+    if (l == 0) {
+      P.norm.r_in = r_in;
+      P.norm.r_out = rbuf[0];
+    } else if (fuse) {
+      P.norm.r_in = rbuf[(l - 1) & 1];
+      P.norm.partial = partial;
+      P.norm.R = Lw.R;
+      P.norm.b_down = ffns[l - 1].b_down;
+      P.norm.r_out = rbuf[l & 1];
+      P.norm.y_out = yprev;
+    } else {
+      hipError_t e = launch_reduce(partial, Lw.R, batch, d, ffns[l - 1].b_down, xt, yprev, rbuf[(l - 1) & 1],
+                                   rbuf[l & 1], s);
+      if (e != hipSuccess) return SFNN_E_HIP;
+      P.norm.r_in = rbuf[l & 1];
+      P.norm.r_out = nullptr;
+    }
+    if (launch_predict(P, s) != hipSuccess) return SFNN_E_HIP;
+    FfnLaunch F = ffn_launch(&ffns[l], xl, batch, batch > 1 ? ml : nullptr, nullptr, w, Lw);
+    F.src = SRC_UNION;
+    F.union_mask = uni;
+    F.ids_out = il;
+    F.count_out = cl;
+    if (launch_ffn(F, s) != hipSuccess) return SFNN_E_HIP;
+  }
+  float* ylast = y_cap ? y_cap + (size_t)(n_layers - 1) * batch * d : nullptr;
+  return hip_status(launch_reduce(partial, Lw.R, batch, d, ffns[n_layers - 1].b_down, xt, ylast,
+                                  rbuf[(n_layers - 1) & 1], r_out, s));
 }
 
 sfnn_status sfnn_residual_rmsnorm(const float* r_in, const float* y, float* r_out, int32_t batch,
@@ -271,6 +382,6 @@ const char* sfnn_status_str(sfnn_status s) {
   return "unknown status";
 }
 
-int32_t sfnn_version(void) { return 100; }
+int32_t sfnn_version(void) { return 200; }
 
 }  // extern "C"

@@ -183,32 +183,38 @@ __device__ __forceinline__ void vec_i4(const u32x4 w, float scale, const f16* xs
 template <int WT>
 constexpr int vec_elems() { return WT == WT_F32 ? 4 : (WT == WT_F16 ? 8 : 32); }
 
-// Partial dot products of one weight row against NT staged token rows: lane
-// li of an LPR-lane group takes vectors li, li+LPR, ...  XT is the staged type.
-// UB loads are issued back to back before any arithmetic; vectors past the
-// row end re-read a valid vector of the same row and are zeroed by a select,
-// so the batch has no branches between its loads.
-template <int WT, int LPR, int NT, int UB, typename XT>
-__device__ __forceinline__ void row_partial(const uint8_t* __restrict__ row,
-                                            const f16* __restrict__ srow, int nvec, int li,
-                                            const XT* xs, int xstride, float* acc) {
-  constexpr int E = vec_elems<WT>();
-  for (int v0 = li; v0 < nvec; v0 += UB * LPR) {
-    u32x4 w[UB];
+// One batch of a weight row's 16-byte vectors held in registers.  Lane li of
+// an LPR-lane group takes vectors v0, v0 + LPR, ..., v0 + (UB-1) LPR with
+// v0 = li + k UB LPR.  issue() starts every load of the batch before any is
+// used, so a caller can issue the batch, stage activations in LDS while the
+// loads are in flight, and only then consume().  A vector past the row end
+// re-reads vector v0 of the same row (in bounds) and is zeroed by a select at
+// use, so the batch has no branches between its loads.  Requires v0 < nvec.
+template <int WT, int LPR, int UB>
+struct RowLoads {
+  u32x4 w[UB];
+  float sc[UB];
+
+  __device__ __forceinline__ void issue(const uint8_t* __restrict__ row, const f16* __restrict__ srow, int nvec,
+                                        int v0) {
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
       const int v = v0 + u * LPR;
       w[u] = ld16_stream(row + 16 * (size_t)(v < nvec ? v : v0));
     }
-    float sc[UB];
     if constexpr (WT == WT_I4) {
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const int v = v0 + u * LPR;
-        sc[u] = (float)srow[(v < nvec ? v : v0) >> 2];
+        sc[u] = (float)srow[(v < nvec ? v : v0) >> 2];  // one scale per 4 vectors (128 elements)
       }
     }
-    __builtin_amdgcn_sched_barrier(0);  // keep the whole batch of loads ahead of the math
+  }
+
+  // acc[t] += (this batch of the row) . (staged row t of xs); XT is the staged type.
+  template <int NT, typename XT>
+  __device__ __forceinline__ void consume(int nvec, int v0, const XT* xs, int xstride, float* acc) const {
+    constexpr int E = vec_elems<WT>();
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
       const int v = v0 + u * LPR;
@@ -227,6 +233,20 @@ __device__ __forceinline__ void row_partial(const uint8_t* __restrict__ row,
         vec_i4<NT>(w[u], ok ? sc[u] : 0.0f, reinterpret_cast<const f16*>(xs) + E * vc, xstride, acc);
       }
     }
+  }
+};
+
+// Whole-row partial dot products: acc[t] += row . xs[t] over this lane's
+// vectors.  `first` says whether the first batch (v0 = li) was already issued
+// into L by the caller.
+template <int WT, int LPR, int UB, int NT, typename XT>
+__device__ __forceinline__ void row_dot(RowLoads<WT, LPR, UB>& L, bool first, const uint8_t* __restrict__ row,
+                                        const f16* __restrict__ srow, int nvec, int li, const XT* xs, int xstride,
+                                        float* acc) {
+  for (int v0 = li; v0 < nvec; v0 += UB * LPR) {
+    if (!(first && v0 == li)) L.issue(row, srow, nvec, v0);
+    __builtin_amdgcn_sched_barrier(0);  // keep the whole batch of loads ahead of the math
+    L.template consume<NT>(nvec, v0, xs, xstride, acc);
   }
 }
 

@@ -3,10 +3,11 @@
 Default workload: the OPT-6.7B-shaped FFN stack (32 layers, d_model 4096,
 d_ff 16384, fp16 weights N(0, 0.02), ReLU at ~90% per-token sparsity, rank-1024
 fp16 predictor per layer), batch 1, 256 decode steps of fresh x ~ N(0, I)
-through the RMS-normalised residual chain.  One step = for every layer:
-predict -> compact -> sparse FFN, then residual + RMSNorm.  Weights are drawn
-on the host from seeded streams and copied to HBM before timing; a step is
-captured once in a HIP graph and replayed, the next token copied in between.
+through the RMS-normalised residual chain.  One step = one sfnn_stack_decode
+call: for every layer, predict -> compact -> sparse FFN, joined by the
+residual + RMSNorm chain.  Weights are drawn on the host from seeded streams
+and copied to HBM before timing; a step is captured once in a HIP graph and
+replayed, the next token copied in between.
 
 Prints one JSON line (metric/value/unit, ms_per_step, roofline of the sparse
 FFN kernel pair, CPU-oracle baseline, and a breakdown under "extra").
@@ -84,18 +85,14 @@ def main():
     tokens = to_dev(synth.make_tokens(spec, ntok * B, stream=7, dtype=np.float32)).view(ntok, B, d)
     stage = torch.empty((B, d), dtype=torch.float32, device=dev)
     rbuf = torch.empty((B, d), dtype=torch.float32, device=dev)
-    xbuf = torch.empty((B, d), dtype=xdt, device=dev)
-    ybuf = torch.empty((B, d), dtype=torch.float32, device=dev)
-    masks = torch.zeros((L, B, f // 64), dtype=torch.uint64, device=dev)
-    ids = torch.zeros((L, f), dtype=torch.int32, device=dev)
-    counts = torch.zeros((L, 4), dtype=torch.int32, device=dev)
+    counts = torch.zeros((L + 4,), dtype=torch.int32, device=dev)
     ws = workspace(layers[0][0], layers[0][1], B)
+    stack = sg.Stack(layers)
 
     def step():
-        sg.sfnn_residual_rmsnorm(stage, None, rbuf, B, d, 1e-6, xbuf)
-        for l, (pred, ffn) in enumerate(layers):
-            sg.sfnn_layer(pred, ffn, xbuf, B, ybuf, masks[l], ids[l], counts[l], ws)
-            sg.sfnn_residual_rmsnorm(rbuf, ybuf, rbuf, B, d, 1e-6, xbuf)
+        # one decode step: every layer's predict -> compact -> sparse FFN, joined
+        # by the residual chain (r += y; x = RMSNorm(r)), all inside the library
+        sg.sfnn_stack_decode(stack, B, stage, rbuf, 1e-6, ws, count_cap=counts)
 
     # eager warm-up on a side stream, then capture one step
     s = torch.cuda.Stream()
@@ -125,8 +122,15 @@ def main():
     elapsed_ms = e0.elapsed_time(e1)
     ms_per_step = elapsed_ms / args.steps
     tok_s = B * args.steps / (elapsed_ms / 1e3)
-    cnt = counts[:, 0].cpu().numpy().astype(np.float64)
+    cnt = counts[:L].cpu().numpy().astype(np.float64)
     mean_u = float(cnt.mean())
+    # the layer inputs of the last step, for the per-call timings below
+    xcap = torch.empty((L, B, d), dtype=xdt, device=dev)
+    masks = torch.zeros((L, B, f // 64), dtype=torch.uint64, device=dev)
+    ids = torch.zeros((L, f), dtype=torch.int32, device=dev)
+    sg.sfnn_stack_decode(stack, B, stage, rbuf, 1e-6, ws, x_cap=xcap, mask_cap=masks, ids_cap=ids,
+                         count_cap=counts)
+    torch.cuda.synchronize()
 
     # ---- algorithmic bytes ----------------------------------------------------
     wb = {"f32": 4.0, "f16": 2.0, "i4g128": d / 2 / d + 2.0 / 128}[spec.wtype]
@@ -162,36 +166,45 @@ def main():
              "setup_s": round(t_setup, 1)}
     extra["layer_GBps_stack"] = round(L * (ffn_bytes + pred_bytes) / (ms_per_step / 1e3) / 1e9, 1)
 
-    # ---- per-call timings (HIP events over back-to-back launches) -----------
+    # ---- per-call timings: each call captured for all layers in one graph ----
     if not args.no_extra:
-        reps = 4
-        xs = xbuf
+        reps = 8
+        y2 = torch.empty((B, d), dtype=torch.float32, device=dev)
 
         def timed(fn):
+            """Average duration of one layer's call, us (HIP events around graph replays)."""
             fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            g.replay()
             torch.cuda.synchronize()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             for _ in range(reps):
-                fn()
+                g.replay()
             b.record()
             torch.cuda.synchronize()
-            return a.elapsed_time(b) / (reps * L) * 1e3  # us per layer call
+            return a.elapsed_time(b) / (reps * L) * 1e3
 
-        y2 = torch.empty_like(ybuf)
-        t_ffn = timed(lambda: [sg.sfnn_sparse_ffn(ffn, xs, B, ids[l], counts[l], masks[l] if B > 1 else None, y2, ws)
+        gate = (lambda l: masks[l]) if B > 1 else (lambda l: None)
+        t_ffn = timed(lambda: [sg.sfnn_sparse_ffn(ffn, xcap[l], B, ids[l], counts[l:l + 1], gate(l), y2, ws)
                                for l, (_, ffn) in enumerate(layers)])
-        t_pred = timed(lambda: [sg.sfnn_predict(pred, xs, B, masks[l], None, ws) for l, (pred, _) in enumerate(layers)])
-        t_comp = timed(lambda: [sg.sfnn_compact(masks[l], B, f, ids[l], counts[l]) for l in range(L)])
-        t_dense = timed(lambda: [sg.sfnn_dense_ffn(ffn, xs, B, y2, ws) for _, ffn in layers])
-        t_layer = timed(lambda: [sg.sfnn_layer(pred, ffn, xs, B, y2, masks[l], ids[l], counts[l], ws)
+        t_pred = timed(lambda: [sg.sfnn_predict(pred, xcap[l], B, masks[l], None, ws)
+                                for l, (pred, _) in enumerate(layers)])
+        t_comp = timed(lambda: [sg.sfnn_compact(masks[l], B, f, ids[l], counts[l:l + 1]) for l in range(L)])
+        t_dense = timed(lambda: [sg.sfnn_dense_ffn(ffn, xcap[l], B, y2, ws) for l, (_, ffn) in enumerate(layers)])
+        t_layer = timed(lambda: [sg.sfnn_layer(pred, ffn, xcap[l], B, y2, masks[l], ids[l], counts[l:l + 1], ws)
                                  for l, (pred, ffn) in enumerate(layers)])
         dense_bytes = f * nmat * row_bytes + f * (nmat - 1) * xb
         extra.update({
+            "us_per_layer_stack": round(ms_per_step * 1e3 / L, 2),
             "us_sparse_ffn": round(t_ffn, 2), "us_predict": round(t_pred, 2), "us_compact": round(t_comp, 2),
-            "us_layer_eager": round(t_layer, 2), "us_dense_ffn": round(t_dense, 2),
+            "us_layer": round(t_layer, 2), "us_dense_ffn": round(t_dense, 2),
             "GBps_ffn_active": round(ffn_bytes / t_ffn / 1e3, 1),
             "GBps_predict": round(pred_bytes / t_pred / 1e3, 1),
+            "GBps_layer": round((ffn_bytes + pred_bytes) / t_layer / 1e3, 1),
             "GBps_dense_ffn": round(dense_bytes / t_dense / 1e3, 1),
             "speedup_sparse_vs_dense_ffn": round(t_dense / t_ffn, 2),
             "tokens_s_dense_ffn_stack_only": round(B / (L * t_dense * 1e-6), 1),
@@ -213,7 +226,7 @@ def main():
         out["roofline"] = {
             "bound": "hbm", "achieved": round(ffn_bytes / t_ffn / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ffn_bytes / t_ffn / 1e3 / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "sfnn_sparse_ffn (k_up + k_down)",
+            "kernel": "sfnn_sparse_ffn (k_up + k_down + k_reduce)",
             "bytes_per_launch": int(ffn_bytes), "us_per_launch": round(t_ffn, 2),
         }
 

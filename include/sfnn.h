@@ -26,7 +26,7 @@
  *    caller's next synchronisation.
  *  - Shapes: d_ff % 64 == 0, d_model % 128 == 0, rank % 8 == 0,
  *    8 <= rank <= 2048, 1 <= batch <= 64, d_ff <= 65536, d_model <= 16384.  Every pointer must be
- *    16-byte aligned (SFNN_E_ALIGN).
+ *    16-byte aligned (SFNN_E_ALIGN), except count pointers (int32, 4-byte aligned).
  *  - Weight layout is neuron-major: W_up, W_gate and W_down^T are
  *    [d_ff][d_model] row-major, so neuron i owns one contiguous row of each
  *    (row i of W_down^T is column i of the conventional W_down[d_model][d_ff]).
@@ -129,12 +129,36 @@ sfnn_status sfnn_sparse_ffn(const sfnn_ffn* ffn, const void* x, int32_t batch,
 sfnn_status sfnn_dense_ffn(const sfnn_ffn* ffn, const void* x, int32_t batch, float* y,
                            void* ws, size_t ws_bytes, void* stream);
 
-/* predict -> compact -> sparse_ffn for one layer.  mask/ids/count are outputs
- * the caller may inspect; any of them may be NULL, then they live in ws.
+/* predict -> compact -> sparse_ffn for one layer (same results as the three
+ * calls in sequence; the compaction runs inside the FFN's first kernel).
+ * mask/ids/count are outputs the caller may inspect; any of them may be NULL,
+ * then they live in ws.  With batch > 1 every token is gated by its own mask.
  * pred and ffn must agree on d_model, d_ff and the activation type. */
 sfnn_status sfnn_layer(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x,
                        int32_t batch, float* y, uint64_t* mask, int32_t* ids,
                        int32_t* count, void* ws, size_t ws_bytes, void* stream);
+
+/* One decode step through a stack of n_layers FFN layers joined by the
+ * pre-norm residual chain without gain (the pages give no stack recipe; this
+ * is the plain reading of "RMS-normalised inputs"):
+ *     r_0 = r_in;  for l = 0..n_layers-1:
+ *         x_l = r_l / sqrt(mean(r_l^2) + eps)   (rounded to x's type)
+ *         y_l = the layer's output for x_l, exactly as sfnn_layer computes it
+ *         r_{l+1} = r_l + y_l
+ *     r_out = r_{n_layers}.
+ * preds / ffns are HOST arrays of n_layers descriptors that share one shape
+ * and type (d_model, d_ff, rank, wtype, act); their device pointers may differ.
+ * r_in, r_out: [batch][d_model] fp32 (r_out may alias r_in).  Optional
+ * per-layer captures (NULL to skip): x_cap [n_layers][batch][d_model] in x's
+ * type, y_cap [n_layers][batch][d_model] fp32, mask_cap
+ * [n_layers][batch][d_ff/64], ids_cap [n_layers][d_ff] (first count valid),
+ * count_cap [n_layers].  The workspace is sfnn_workspace_bytes(&preds[0],
+ * &ffns[0], batch).  Same execution rules as every call: asynchronous on
+ * `stream`, no allocation, no host synchronisation (capturable in a graph). */
+sfnn_status sfnn_stack_decode(int32_t n_layers, const sfnn_pred* preds, const sfnn_ffn* ffns, int32_t batch,
+                              const float* r_in, float* r_out, float eps, void* x_cap, float* y_cap,
+                              uint64_t* mask_cap, int32_t* ids_cap, int32_t* count_cap, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /* Stack step between layers (pre-norm residual chain, no gain):
  * r_out = r_in + y (y may be NULL: r_out = r_in; r_out may alias r_in);

@@ -97,3 +97,24 @@ def band_check(gpu_words, gpu_logits, ora_logits, band, tau, f):
     assert not bad.any(), f"{int(bad.sum())} mask bits differ outside the rounding band"
     assert (np.abs(gpu_logits - ora_logits) <= band + 1e-30).all(), "logit error above the bound"
     return int(((gb != ob) & ~outside).sum())
+
+
+def gpu_stack(layers_dev, r_in: np.ndarray, eps: float = 1e-6, xdtype=torch.float16):
+    """sfnn_stack_decode over uploaded layers with every per-layer capture on."""
+    L = len(layers_dev)
+    B, d = r_in.shape
+    pred0, ffn0 = layers_dev[0]
+    f = ffn0.d_ff
+    st = sg.Stack(layers_dev)
+    rin = to_dev(r_in.astype(np.float32))
+    rout = torch.full((B, d), float("nan"), dtype=torch.float32, device=DEV)
+    xc = torch.full((L, B, d), float("nan"), dtype=xdtype, device=DEV)
+    yc = torch.full((L, B, d), float("nan"), dtype=torch.float32, device=DEV)
+    mc = torch.zeros((L, B, f // 64), dtype=torch.uint64, device=DEV)
+    ic = torch.full((L, f), -7, dtype=torch.int32, device=DEV)
+    cc = torch.full((L + 3,), -1, dtype=torch.int32, device=DEV)
+    ws = workspace(pred0, ffn0, B)
+    sg.sfnn_stack_decode(st, B, rin, rout, eps, ws, x_cap=xc, y_cap=yc, mask_cap=mc, ids_cap=ic, count_cap=cc)
+    torch.cuda.synchronize()
+    return dict(r_out=rout.cpu().numpy(), x=xc.float().cpu().numpy(), y=yc.cpu().numpy(), mask=mc.cpu().numpy(),
+                ids=ic.cpu().numpy(), count=cc.cpu().numpy()[:L])

@@ -1,0 +1,96 @@
+"""Parity of the residual-stack entry point (sfnn_stack_decode) with the
+oracle, layer by layer, on the inputs the GPU captured for each layer.
+
+For every layer l: the captured input x_l is the RMS-normalised residual
+r_l = r_in + y_0 + ... + y_{l-1} (fp32 adds in that order); its mask is the
+predictor's threshold outside the rounding band; ids/count are the compaction
+of that mask, bit-exact; y_l matches the oracle's masked FFN of x_l within
+2e-3; and y_l is bitwise what sfnn_layer returns for the same x_l.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import gpu_layer, gpu_stack, rel_err, upload_layer
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _stack_case(spec, L, B, seed=0):
+    lays = [synth.make_layer(spec, layer=l, seed=seed) for l in range(L)]
+    dev = [upload_layer(lay) for lay in lays]
+    r_in = synth.make_tokens(spec, B, stream=200 + B, dtype=np.float32) * np.float32(3.0)
+    xdt = torch.float32 if spec.wtype == "f32" else torch.float16
+    out = gpu_stack(dev, r_in, 1e-6, xdt)
+    f = spec.d_ff
+    r = r_in.astype(np.float32).copy()
+    for l, lay in enumerate(lays):
+        x = out["x"][l]
+        # the layer input is the RMS-normalised running residual
+        _, x_ref = oracle.residual_rmsnorm(r, np.zeros_like(r), 1e-6)
+        assert rel_err(x, x_ref) <= (1e-6 if spec.wtype == "f32" else 1e-3), l
+        xs = x.astype(spec.x_dtype)
+        assert np.array_equal(xs.astype(np.float32), x)
+        # mask: threshold of the predictor on x_l, outside the fp32 rounding band
+        ol, ob = oracle.predict(lay.w1_t, lay.w2_t, lay.tau, xs)
+        band = oracle.guard_band(lay.w1_t, lay.w2_t, xs)
+        gb = oracle.unpack_mask(out["mask"][l], f)
+        outside = np.abs(ol - lay.tau[None, :].astype(np.float64)) > band
+        assert not ((gb != ob) & outside).any(), l
+        # ids / count: compaction of the GPU's own mask, bit-exact
+        rid, rc, _ = oracle.compact(out["mask"][l], B, f)
+        assert out["count"][l] == rc and np.array_equal(out["ids"][l][:rc], rid), l
+        # y: the oracle's masked FFN on the same input and mask
+        ref = oracle.masked_ffn(lay, xs, out["mask"][l])
+        for b in range(B):
+            assert rel_err(out["y"][l][b], ref[b]) <= TOL, (l, b)
+        # and bitwise the single-layer entry point on the captured input
+        one = gpu_layer(dev[l][0], dev[l][1], xs)
+        assert np.array_equal(one["y"], out["y"][l]), l
+        assert np.array_equal(one["mask"], out["mask"][l]), l
+        r = (r + out["y"][l]).astype(np.float32)
+    assert np.array_equal(out["r_out"], r)
+
+
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_stack_fp16_relu(B):
+    _stack_case(synth.config("c2", d_model=1024, d_ff=4096, rank=128, n_layers=3), 3, B)
+
+
+@pytest.mark.parametrize("B", [1, 4])
+def test_stack_fp16_reglu_zipf(B):
+    _stack_case(synth.config("c4", d_model=768, d_ff=2048, rank=64, n_layers=3), 3, B)
+
+
+@pytest.mark.parametrize("B", [1, 2, 9])
+def test_stack_int4(B):
+    _stack_case(synth.config("c5", d_model=1536, d_ff=3072, rank=128, n_layers=2), 2, B)
+
+
+def test_stack_fp32_opt125m_shape():
+    _stack_case(synth.config("c1", n_layers=2), 2, 1)
+
+
+def test_stack_opt6_7b_full_width_two_layers():
+    """Full OPT-6.7B layer shape (d_model 4096, d_ff 16384, rank 1024), 2 layers, batch 1."""
+    _stack_case(synth.config("c2"), 2, 1)
+
+
+def test_stack_single_layer_and_aliasing():
+    spec = synth.config("c2", d_model=512, d_ff=1024, rank=64, n_layers=1)
+    lay = synth.make_layer(spec, layer=0)
+    pred, ffn = upload_layer(lay)
+    import activation_sparse_gemv_amd as sg
+    from activation_sparse_gemv_amd.device import to_dev, workspace
+    r_in = synth.make_tokens(spec, 2, stream=9, dtype=np.float32)
+    out = gpu_stack([(pred, ffn)], r_in)
+    # r_out may alias r_in
+    r = to_dev(r_in)
+    ws = workspace(pred, ffn, 2)
+    sg.sfnn_stack_decode(sg.Stack([(pred, ffn)]), 2, r, r, 1e-6, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(r.cpu().numpy(), out["r_out"])
