@@ -20,13 +20,13 @@ bool al16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 bool al4(const void* p) { return p == nullptr || ((uintptr_t)p & 3u) == 0; }
 
 struct Layout {
-  size_t z = 0, h = 0, partial = 0, mask = 0, uni = 0, ids = 0, count = 0, rbuf = 0, xbuf = 0, total = 0;
-  int R = 0;
+  size_t z = 0, partial = 0, mask = 0, uni = 0, ids = 0, count = 0, rbuf = 0, xbuf = 0, total = 0;
+  int G = 0;
 };
 
-// Workspace: predictor stage-1 output z, the up projection's h, the down
-// projection's row-block partials, masks, union mask, ids, count, and the
-// residual chain's two fp32 rows and layer input.
+// Workspace: predictor stage-1 output z, the FFN workgroups' partial rows,
+// masks, union mask, ids, count, and the residual chain's two fp32 rows and
+// layer input.
 Layout layout(const sfnn_pred* p, const sfnn_ffn* f, int batch) {
   Layout L;
   size_t off = 0;
@@ -37,12 +37,9 @@ Layout layout(const sfnn_pred* p, const sfnn_ffn* f, int batch) {
     off += up((size_t)batch * p->rank * 4);
   }
   if (f) {
-    L.R = ffn_row_blocks(f->wtype == SFNN_F32 ? WT_F32 : (f->wtype == SFNN_F16 ? WT_F16 : WT_I4), f->d_model,
-                         f->d_ff);
-    L.h = off;
-    off += up((size_t)batch * f->d_ff * 4);
+    L.G = ffn_groups(f->d_model, f->d_ff);
     L.partial = off;
-    off += up((size_t)L.R * batch * f->d_model * 4);
+    off += up((size_t)L.G * batch * f->d_model * 4);
   }
   L.mask = off;
   off += up((size_t)batch * (ff / 64) * 8);
@@ -144,9 +141,10 @@ FfnLaunch ffn_launch(const sfnn_ffn* f, const void* x, int batch, const uint64_t
   L.count_out = nullptr;
   L.mask = mask;
   L.y = y;
-  L.h = reinterpret_cast<float*>(ws + Lw.h);
+  L.r_in = nullptr;
+  L.r_out = nullptr;
   L.partial = reinterpret_cast<float*>(ws + Lw.partial);
-  L.row_blocks = Lw.R;
+  L.groups = Lw.G;
   return L;
 }
 
@@ -272,51 +270,35 @@ sfnn_status sfnn_stack_decode(int32_t n_layers, const sfnn_pred* preds, const sf
   hipStream_t s = as_stream(stream);
   const int d = preds[0].d_model, f = preds[0].d_ff, W = f / 64;
   const int xb = preds[0].wtype == SFNN_F32 ? 4 : 2;
-  const int xt = preds[0].wtype == SFNN_F32 ? WT_F32 : WT_F16;
   float* rbuf[2] = {reinterpret_cast<float*>(w + Lw.rbuf),
                     reinterpret_cast<float*>(w + Lw.rbuf) + (size_t)batch * d};
-  float* partial = reinterpret_cast<float*>(w + Lw.partial);
-  // the previous layer's partials are summed inside the next predictor when
-  // few enough; otherwise by a separate reduce launch
-  const bool fuse = Lw.R <= kChainFuseMaxR;
+  const float* rl = r_in;  // r_l, the residual entering layer l
   for (int l = 0; l < n_layers; ++l) {
     void* xl = x_cap ? (char*)x_cap + (size_t)l * batch * d * xb : (void*)(w + Lw.xbuf);
     uint64_t* ml = mask_cap ? mask_cap + (size_t)l * batch * W : reinterpret_cast<uint64_t*>(w + Lw.mask);
     int32_t* il = ids_cap ? ids_cap + (size_t)l * f : reinterpret_cast<int32_t*>(w + Lw.ids);
     int32_t* cl = count_cap ? count_cap + l : reinterpret_cast<int32_t*>(w + Lw.count);
     uint64_t* uni = reinterpret_cast<uint64_t*>(w + Lw.uni);
+    // x_l = RMSNorm(r_l), built inside the predictor's first kernel
     PredLaunch P = pred_launch(&preds[l], nullptr, batch, ml, uni, nullptr, reinterpret_cast<float*>(w + Lw.z));
-    P.norm.eps = eps;
+    P.norm.r_in = rl;
     P.norm.x_out = xl;
-    float* yprev = (l > 0 && y_cap) ? y_cap + (size_t)(l - 1) * batch * d : nullptr;
-    if (l == 0) {
-      P.norm.r_in = r_in;
-      P.norm.r_out = rbuf[0];
-    } else if (fuse) {
-      P.norm.r_in = rbuf[(l - 1) & 1];
-      P.norm.partial = partial;
-      P.norm.R = Lw.R;
-      P.norm.b_down = ffns[l - 1].b_down;
-      P.norm.r_out = rbuf[l & 1];
-      P.norm.y_out = yprev;
-    } else {
-      hipError_t e = launch_reduce(partial, Lw.R, batch, d, ffns[l - 1].b_down, xt, yprev, rbuf[(l - 1) & 1],
-                                   rbuf[l & 1], s);
-      if (e != hipSuccess) return SFNN_E_HIP;
-      P.norm.r_in = rbuf[l & 1];
-      P.norm.r_out = nullptr;
-    }
+    P.norm.eps = eps;
     if (launch_predict(P, s) != hipSuccess) return SFNN_E_HIP;
-    FfnLaunch F = ffn_launch(&ffns[l], xl, batch, batch > 1 ? ml : nullptr, nullptr, w, Lw);
+    // y_l and r_{l+1} = r_l + y_l (the last layer writes the caller's r_out)
+    float* rnext = (l == n_layers - 1) ? r_out : rbuf[l & 1];
+    FfnLaunch F = ffn_launch(&ffns[l], xl, batch, batch > 1 ? ml : nullptr,
+                             y_cap ? y_cap + (size_t)l * batch * d : nullptr, w, Lw);
     F.src = SRC_UNION;
     F.union_mask = uni;
     F.ids_out = il;
     F.count_out = cl;
+    F.r_in = rl;
+    F.r_out = rnext;
     if (launch_ffn(F, s) != hipSuccess) return SFNN_E_HIP;
+    rl = rnext;
   }
-  float* ylast = y_cap ? y_cap + (size_t)(n_layers - 1) * batch * d : nullptr;
-  return hip_status(launch_reduce(partial, Lw.R, batch, d, ffns[n_layers - 1].b_down, xt, ylast,
-                                  rbuf[(n_layers - 1) & 1], r_out, s));
+  return SFNN_OK;
 }
 
 sfnn_status sfnn_residual_rmsnorm(const float* r_in, const float* y, float* r_out, int32_t batch,

@@ -90,6 +90,56 @@ __device__ __forceinline__ void stage_rows(XT* xs, const XT* __restrict__ x, int
   }
 }
 
+// stage_rows in two parts, so that loads issued later (weight rows) can be
+// in flight while the activations arrive: issue() starts the loads of the
+// first SP * blockDim vectors into registers, commit() writes them to LDS and
+// stages any remainder with stage-as-you-go loads.  Vector loads return in
+// order, so waiting for these (issued first) does not wait for later loads.
+template <typename XT, bool PERM8, int SP>
+struct StageSplit {
+  u32x4 v[SP];
+
+  __device__ __forceinline__ void issue(const XT* __restrict__ x, int K, int tok0, int nt, int NT) {
+    const int vpr = K * (int)sizeof(XT) / 16;
+    const int total = NT * vpr;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x);
+#pragma unroll
+    for (int j = 0; j < SP; ++j) {
+      const int e = threadIdx.x + j * blockDim.x;
+      const int t = e / vpr;
+      const bool ok = e < total && t < nt;
+      v[j] = ok ? src[(size_t)(tok0 + t) * vpr + (e - t * vpr)] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  __device__ __forceinline__ void commit(XT* xs, const XT* __restrict__ x, int K, int tok0, int nt, int NT) {
+    const int vpr = K * (int)sizeof(XT) / 16;
+    const int total = NT * vpr;
+    u32x4* dst = reinterpret_cast<u32x4*>(xs);
+#pragma unroll
+    for (int j = 0; j < SP; ++j) {
+      const int e = threadIdx.x + j * blockDim.x;
+      if (e < total) dst[e] = PERM8 ? perm8(v[j]) : v[j];
+    }
+    const u32x4* src = reinterpret_cast<const u32x4*>(x);
+    for (int e = threadIdx.x + SP * blockDim.x; e < total; e += blockDim.x) {
+      const int t = e / vpr;
+      const u32x4 w = (t < nt) ? src[(size_t)(tok0 + t) * vpr + (e - t * vpr)] : u32x4{0u, 0u, 0u, 0u};
+      dst[e] = PERM8 ? perm8(w) : w;
+    }
+  }
+
+  // (x0x1, x2x3, x4x5, x6x7) -> (x0x4, x1x5, x2x6, x3x7): the INT4 pairing order
+  static __device__ __forceinline__ u32x4 perm8(const u32x4 a) {
+    u32x4 o;
+    o.x = (a.x & 0xFFFFu) | (a.z << 16);
+    o.y = (a.x >> 16) | (a.z & 0xFFFF0000u);
+    o.z = (a.y & 0xFFFFu) | (a.w << 16);
+    o.w = (a.y >> 16) | (a.w & 0xFFFF0000u);
+    return o;
+  }
+};
+
 // ---- one 16-byte weight vector against NT token rows of staged x ----------
 // xs points at element (vector start) of token 0; xstride is the LDS row
 // stride in elements.

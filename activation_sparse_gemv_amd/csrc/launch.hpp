@@ -11,29 +11,15 @@ namespace sfnn {
 constexpr int kMaxNT = 8;
 // LDS budget for staged activations per workgroup.
 constexpr int kStageBytes = 64 * 1024;
-// A residual stack sums the previous layer's down-projection partials inside
-// the next predictor launch when there are at most this many row blocks.
-#ifndef SFNN_CHAIN_FUSE_MAXR
-#define SFNN_CHAIN_FUSE_MAXR 8
-#endif
-constexpr int kChainFuseMaxR = SFNN_CHAIN_FUSE_MAXR;
-
 // ---- predictor ------------------------------------------------------------
 
 // Input of the predictor's first stage.  Plain: x [B][d] as given.  Residual
-// chain (r_in != null): the layer input is made in the kernel's prologue from
-// the previous layer's down-projection partials,
-//     y = b_down_prev + sum_q partial[q][t][:]   (q = 0..R-1 in order; R may be 0)
-//     r = r_in + y,   x = r / sqrt(mean(r^2) + eps)  (rounded to x's type),
-// and workgroup 0 writes r_out, y_out (if not null) and x_out.
+// chain (r_in != null): the layer input is made in the kernel's prologue,
+//     x = r_in / sqrt(mean(r_in^2) + eps)  (rounded to x's type),
+// and workgroup 0 also writes it to x_out.
 struct NormIn {
-  const float* r_in = nullptr;     // [B][d]
-  const float* partial = nullptr;  // [R][B][d]
-  int R = 0;
-  const void* b_down = nullptr;    // [d] in x's type, or null
-  float* r_out = nullptr;          // [B][d]
-  float* y_out = nullptr;          // [B][d] or null
-  void* x_out = nullptr;           // [B][d]
+  const float* r_in = nullptr;  // [B][d]
+  void* x_out = nullptr;        // [B][d]
   float eps = 1e-6f;
 };
 
@@ -67,24 +53,21 @@ struct FfnLaunch {
   const void *b_up, *b_gate, *b_down;
   const void* x;          // [B][d]
   int batch;
-  int src;                // SRC_IDS: ids/count given; SRC_UNION: compact union_mask in the up kernel; SRC_DENSE
+  int src;                // SRC_IDS: ids/count given; SRC_UNION: compact union_mask in the FFN kernel; SRC_DENSE
   const int32_t* ids;     // SRC_IDS
   const int32_t* count;   // SRC_IDS
   const uint64_t* union_mask;  // SRC_UNION: [f/64]
   int32_t* ids_out;       // SRC_UNION: compacted ids are written here ([f], first count valid)
   int32_t* count_out;     // SRC_UNION
   const uint64_t* mask;   // per-token gate [B][f/64] or null
-  float* y;               // [B][d]; null: leave the sum in `partial` (residual chain)
-  float* h;               // [B][f] workspace
-  float* partial;         // [R][B][d] workspace
-  int row_blocks;         // R
+  float* partial;         // [groups][B][d] workspace
+  int groups;             // FFN workgroups (= partial rows per token)
+  float* y;               // [B][d] or null
+  const float* r_in;      // residual add: r_out = r_in + y (both null to skip)
+  float* r_out;
 };
 hipError_t launch_ffn(const FfnLaunch& p, hipStream_t s);
-int ffn_row_blocks(int wt, int d, int f);
-
-// y = b_down + sum_q partial[q] (q in order); if r_in: r_out = r_in + y.
-hipError_t launch_reduce(const float* partial, int R, int batch, int d, const void* b_down, int xtype, float* y,
-                         const float* r_in, float* r_out, hipStream_t s);
+int ffn_groups(int d, int f);
 
 hipError_t launch_compact(const uint64_t* mask, int batch, int f, int32_t* ids, int32_t* count,
                           uint64_t* union_mask, hipStream_t s);
