@@ -70,7 +70,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sfnn_sparse_ffn": (i32, [F, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
         "sfnn_dense_ffn": (i32, [F, vp, i32, vp, vp, sz, vp]),
         "sfnn_layer": (i32, [P, F, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
-        "sfnn_stack_decode": (i32, [i32, P, F, i32, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "sfnn_stack_decode": (i32, [i32, P, F, i32, vp, vp, ctypes.c_float, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "sfnn_residual_rmsnorm": (i32, [vp, vp, vp, i32, i32, ctypes.c_float, vp, i32, vp]),
         "sfnn_fire_counts": (i32, [vp, i32, i32, vp, vp]),
         "sfnn_hot_first_perm": (i32, [vp, i32, vp]),
@@ -207,10 +207,13 @@ class Stack:
         return len(self.layers)
 
 
-def sfnn_stack_decode(stack: Stack, batch: int, r_in, r_out, eps: float, ws, x_cap=None, y_cap=None, mask_cap=None,
-                      ids_cap=None, count_cap=None, stream=None):
+SFNN_STACK_LOOKAHEAD = 1
+
+
+def sfnn_stack_decode(stack: Stack, batch: int, r_in, r_out, eps: float, ws, flags: int = 0, x_cap=None, y_cap=None,
+                      mask_cap=None, ids_cap=None, count_cap=None, stream=None):
     _check("sfnn_stack_decode", load().sfnn_stack_decode(
-        len(stack), stack.preds, stack.ffns, batch, _p(r_in), _p(r_out), eps, _p(x_cap), _p(y_cap),
+        len(stack), stack.preds, stack.ffns, batch, _p(r_in), _p(r_out), eps, flags, _p(x_cap), _p(y_cap),
         _p(mask_cap), _p(ids_cap), _p(count_cap), _p(ws), ws.numel() * ws.element_size(), _s(stream)))
 
 

@@ -20,7 +20,7 @@ bool al16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 bool al4(const void* p) { return p == nullptr || ((uintptr_t)p & 3u) == 0; }
 
 struct Layout {
-  size_t z = 0, partial = 0, mask = 0, uni = 0, ids = 0, count = 0, rbuf = 0, xbuf = 0, total = 0;
+  size_t z = 0, partial = 0, mask = 0, uni = 0, ids = 0, count = 0, rbuf = 0, xbuf = 0, rtmp = 0, total = 0;
   int G = 0;
 };
 
@@ -52,6 +52,8 @@ Layout layout(const sfnn_pred* p, const sfnn_ffn* f, int batch) {
   L.rbuf = off;
   off += up((size_t)2 * batch * dm * 4);
   L.xbuf = off;
+  off += up((size_t)batch * dm * 4);
+  L.rtmp = off;
   off += up((size_t)batch * dm * 4);
   L.total = off;
   return L;
@@ -248,11 +250,12 @@ sfnn_status sfnn_layer(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x
 }
 
 sfnn_status sfnn_stack_decode(int32_t n_layers, const sfnn_pred* preds, const sfnn_ffn* ffns, int32_t batch,
-                              const float* r_in, float* r_out, float eps, void* x_cap, float* y_cap,
+                              const float* r_in, float* r_out, float eps, int32_t flags, void* x_cap, float* y_cap,
                               uint64_t* mask_cap, int32_t* ids_cap, int32_t* count_cap, void* ws, size_t ws_bytes,
                               void* stream) {
   if (!preds || !ffns || !r_in || !r_out || !ws) return SFNN_E_NULL;
   if (n_layers < 1 || !batch_ok(batch)) return SFNN_E_SHAPE;
+  if (flags & ~SFNN_STACK_LOOKAHEAD) return SFNN_E_SHAPE;
   for (int l = 0; l < n_layers; ++l) {
     const sfnn_status st = check_pair(&preds[l], &ffns[l]);
     if (st != SFNN_OK) return st;
@@ -272,31 +275,54 @@ sfnn_status sfnn_stack_decode(int32_t n_layers, const sfnn_pred* preds, const sf
   const int xb = preds[0].wtype == SFNN_F32 ? 4 : 2;
   float* rbuf[2] = {reinterpret_cast<float*>(w + Lw.rbuf),
                     reinterpret_cast<float*>(w + Lw.rbuf) + (size_t)batch * d};
-  const float* rl = r_in;  // r_l, the residual entering layer l
+  uint64_t* uni = reinterpret_cast<uint64_t*>(w + Lw.uni);
+  float* z = reinterpret_cast<float*>(w + Lw.z);
+  // per-layer buffers: captures when given, else shared workspace
+  auto x_of = [&](int l) -> void* { return x_cap ? (char*)x_cap + (size_t)l * batch * d * xb : (void*)(w + Lw.xbuf); };
+  auto m_of = [&](int l) { return mask_cap ? mask_cap + (size_t)l * batch * W : reinterpret_cast<uint64_t*>(w + Lw.mask); };
+  auto i_of = [&](int l) { return ids_cap ? ids_cap + (size_t)l * f : reinterpret_cast<int32_t*>(w + Lw.ids); };
+  auto c_of = [&](int l) { return count_cap ? count_cap + l : reinterpret_cast<int32_t*>(w + Lw.count); };
+  auto y_of = [&](int l) { return y_cap ? y_cap + (size_t)l * batch * d : nullptr; };
+  // r_l, the residual entering layer l: r_0 = r_in, r_L = r_out, ping-pong between
+  auto r_of = [&](int l) -> float* {
+    if (l == 0) return const_cast<float*>(r_in);
+    if (l == n_layers) return r_out;
+    return rbuf[(l - 1) & 1];
+  };
+  auto ffn_of = [&](int l) {
+    FfnLaunch F = ffn_launch(&ffns[l], x_of(l), batch, batch > 1 ? m_of(l) : nullptr, y_of(l), w, Lw);
+    F.src = SRC_UNION;
+    F.union_mask = uni;
+    F.ids_out = i_of(l);
+    F.count_out = c_of(l);
+    return F;
+  };
+
+  if (flags & SFNN_STACK_LOOKAHEAD) {
+    std::vector<PredLaunch> P((size_t)n_layers);
+    std::vector<FfnLaunch> F((size_t)n_layers);
+    std::vector<const float*> R((size_t)n_layers + 1);
+    for (int l = 0; l < n_layers; ++l) {
+      P[l] = pred_launch(&preds[l], nullptr, batch, m_of(l), uni, nullptr, z);
+      F[l] = ffn_of(l);
+    }
+    for (int l = 0; l <= n_layers; ++l) R[l] = r_of(l);
+    return hip_status(launch_stack_lookahead(P.data(), F.data(), R.data(), n_layers, eps,
+                                             reinterpret_cast<float*>(w + Lw.rtmp), s));
+  }
+
   for (int l = 0; l < n_layers; ++l) {
-    void* xl = x_cap ? (char*)x_cap + (size_t)l * batch * d * xb : (void*)(w + Lw.xbuf);
-    uint64_t* ml = mask_cap ? mask_cap + (size_t)l * batch * W : reinterpret_cast<uint64_t*>(w + Lw.mask);
-    int32_t* il = ids_cap ? ids_cap + (size_t)l * f : reinterpret_cast<int32_t*>(w + Lw.ids);
-    int32_t* cl = count_cap ? count_cap + l : reinterpret_cast<int32_t*>(w + Lw.count);
-    uint64_t* uni = reinterpret_cast<uint64_t*>(w + Lw.uni);
     // x_l = RMSNorm(r_l), built inside the predictor's first kernel
-    PredLaunch P = pred_launch(&preds[l], nullptr, batch, ml, uni, nullptr, reinterpret_cast<float*>(w + Lw.z));
-    P.norm.r_in = rl;
-    P.norm.x_out = xl;
+    PredLaunch P = pred_launch(&preds[l], nullptr, batch, m_of(l), uni, nullptr, z);
+    P.norm.r_in = r_of(l);
+    P.norm.x_out = x_of(l);
     P.norm.eps = eps;
     if (launch_predict(P, s) != hipSuccess) return SFNN_E_HIP;
     // y_l and r_{l+1} = r_l + y_l (the last layer writes the caller's r_out)
-    float* rnext = (l == n_layers - 1) ? r_out : rbuf[l & 1];
-    FfnLaunch F = ffn_launch(&ffns[l], xl, batch, batch > 1 ? ml : nullptr,
-                             y_cap ? y_cap + (size_t)l * batch * d : nullptr, w, Lw);
-    F.src = SRC_UNION;
-    F.union_mask = uni;
-    F.ids_out = il;
-    F.count_out = cl;
-    F.r_in = rl;
-    F.r_out = rnext;
+    FfnLaunch F = ffn_of(l);
+    F.r_in = r_of(l);
+    F.r_out = r_of(l + 1);
     if (launch_ffn(F, s) != hipSuccess) return SFNN_E_HIP;
-    rl = rnext;
   }
   return SFNN_OK;
 }

@@ -32,12 +32,75 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(bitcast<f16x2>(a), bitcast<f16x2>(b), c, false);
 }
 
-// Sum over aligned groups of G consecutive lanes (G a power of two <= 64).
+// ---- cross-lane sums on the DPP path --------------------------------------
+// Data-parallel-primitive modifiers move values between lanes inside a VALU
+// instruction, with no LDS round trip (a shuffle through ds_bpermute costs an
+// LDS latency per step).  Controls used (CDNA): row_shr:n = 0x110 + n and
+// row_ror:n = 0x120 + n act within rows of 16 lanes; row_bcast:15 = 0x142
+// feeds lane 15 of each row to the next row, row_bcast:31 = 0x143 feeds lane
+// 31 to rows 2 and 3.  Lanes with no source, and rows left out by the row
+// mask, read 0.  All 64 lanes must be active.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL, ROWS>(__builtin_bit_cast(int, v)));
+}
+
+// Inclusive prefix sum over the 64 lanes (Hillis-Steele within rows, then
+// the row totals carried across rows).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_i<0x111>(x);
+  x += dpp_i<0x112>(x);
+  x += dpp_i<0x114>(x);
+  x += dpp_i<0x118>(x);
+  x += dpp_i<0x142, 0xa>(x);
+  x += dpp_i<0x143, 0xc>(x);
+  return x;
+}
+
+// Sum over the 64 lanes, returned in every lane (the scan's last lane).
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0x111>(v);
+  v += dpp_f<0x112>(v);
+  v += dpp_f<0x114>(v);
+  v += dpp_f<0x118>(v);
+  v += dpp_f<0x142, 0xa>(v);
+  v += dpp_f<0x143, 0xc>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
+}
+
+// Sum over each row of 16 lanes, in every lane of the row (rotations).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0x128>(v);
+  v += dpp_f<0x124>(v);
+  v += dpp_f<0x122>(v);
+  v += dpp_f<0x121>(v);
+  return v;
+}
+
+// Sum over aligned groups of G consecutive lanes (G = 16 or 64), in every
+// lane of the group.  Called with all lanes active.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = G / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+  static_assert(G == 16 || G == kWave, "group_sum: 16 or 64 lanes");
+  if constexpr (G == kWave)
+    return wave_sum(v);
+  else
+    return row16_sum(v);
+}
+
+// Number of set bits of m below this lane (m is wave-uniform).
+__device__ __forceinline__ int bits_below_lane(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // INT4 nibbles of one dword as four fp16 pairs (e0,e4) (e1,e5) (e2,e6) (e3,e7).
@@ -99,6 +162,18 @@ template <typename XT, bool PERM8, int SP>
 struct StageSplit {
   u32x4 v[SP];
 
+  // Nothing looks at the values before commit(), so the loads stay in flight
+  // while the caller issues more.  Slots past the rows load nothing (zeros):
+  // redundant loads of one shared address would serialise in the cache.
+  // Token of flat vector e < NT * vpr without a division (NT <= 8 is a
+  // compile-time constant at every call site).
+  static __device__ __forceinline__ int tok_of(int e, int vpr, int NT) {
+    int t = 0;
+#pragma unroll
+    for (int m = 1; m < 8; ++m) t += (m < NT && e >= m * vpr) ? 1 : 0;
+    return t;
+  }
+
   __device__ __forceinline__ void issue(const XT* __restrict__ x, int K, int tok0, int nt, int NT) {
     const int vpr = K * (int)sizeof(XT) / 16;
     const int total = NT * vpr;
@@ -106,9 +181,9 @@ struct StageSplit {
 #pragma unroll
     for (int j = 0; j < SP; ++j) {
       const int e = threadIdx.x + j * blockDim.x;
-      const int t = e / vpr;
-      const bool ok = e < total && t < nt;
-      v[j] = ok ? src[(size_t)(tok0 + t) * vpr + (e - t * vpr)] : u32x4{0u, 0u, 0u, 0u};
+      const int t = tok_of(e, vpr, NT);
+      v[j] = u32x4{0u, 0u, 0u, 0u};
+      if (e < total && t < nt) v[j] = src[(size_t)(tok0 + t) * vpr + (e - t * vpr)];
     }
   }
 
@@ -119,11 +194,11 @@ struct StageSplit {
 #pragma unroll
     for (int j = 0; j < SP; ++j) {
       const int e = threadIdx.x + j * blockDim.x;
-      if (e < total) dst[e] = PERM8 ? perm8(v[j]) : v[j];
+      if (e < total) dst[e] = PERM8 ? perm8(v[j]) : v[j];  // tokens >= nt stage zeros
     }
     const u32x4* src = reinterpret_cast<const u32x4*>(x);
     for (int e = threadIdx.x + SP * blockDim.x; e < total; e += blockDim.x) {
-      const int t = e / vpr;
+      const int t = tok_of(e, vpr, NT);
       const u32x4 w = (t < nt) ? src[(size_t)(tok0 + t) * vpr + (e - t * vpr)] : u32x4{0u, 0u, 0u, 0u};
       dst[e] = PERM8 ? perm8(w) : w;
     }

@@ -1,0 +1,76 @@
+// Look-ahead stack: DejaVu's asynchronous predictor, which predicts the next
+// layer's sparsity one step ahead so that prediction leaves the critical path
+// (53ai.com sparsity survey, DejaVu section 如何充分利用结构化稀疏进行加速).
+// Layer l+1's predictor reads layer l's input x_l, so its two stages share
+// launches with layer l's FFN and sum:
+//   launch A(l): FFN_l workgroups (x_l = RMSNorm(r_l) built in their
+//                prologue) + predictor stage 1 of layer l+1 on the same x_l;
+//   launch B(l): sum of FFN_l's partials (y_l, r_{l+1} = r_l + y_l)
+//                + predictor stage 2 of layer l+1 (mask, union).
+// Two launches per layer instead of four, and the predictor's weight stream
+// overlaps the FFN's.  Layer 0's mask comes from its own input.
+#include "la_launch.hpp"
+
+namespace sfnn {
+
+// The fused path handles token groups of 1 or 2 (decode batches 1 and 2);
+// larger batches run the same schedule as separate launches.
+static int la_group(const FfnLaunch& F, const PredLaunch& P) {
+  const FfnShape sh = ffn_shape(F.wt, F.d, F.batch);
+  if (F.batch > 2) return 0;
+  int nt = F.batch;
+  if (sh.nt < nt) nt = sh.nt;
+  const int pwt = F.wt == WT_F32 ? WT_F32 : WT_F16;
+  if (pred2_group(pwt, P.r, F.batch) < F.batch || pred2_vpl(pwt, P.r) > 4) return 0;
+  if (!chain_fits(F.d, nt, sh.nth, sh.cpt)) return 0;  // residual rows must fit the prologue's registers
+  return nt;
+}
+
+hipError_t launch_stack_lookahead(const PredLaunch* P, const FfnLaunch* F, const float* const* R, int L, float eps,
+                                  float* rtmp, hipStream_t s) {
+  // layer 0 predicts from its own input
+  PredLaunch P0 = P[0];
+  P0.norm.r_in = R[0];
+  P0.norm.x_out = const_cast<void*>(F[0].x);
+  P0.norm.eps = eps;
+  hipError_t e = launch_predict(P0, s);
+  if (e != hipSuccess) return e;
+  const int NT = la_group(F[0], P[0]);
+  if (NT > 0) {
+    if (F[0].wt == WT_F32)
+      stack_fused_f32(P, F, R, L, eps, NT, s);
+    else if (F[0].wt == WT_F16)
+      stack_fused_f16(P, F, R, L, eps, NT, s);
+    else
+      stack_fused_i4(P, F, R, L, eps, NT, s);
+    return hipGetLastError();
+  }
+  // larger batches: the same schedule, one launch per stage
+  for (int l = 0; l < L; ++l) {
+    if (l + 1 < L) {
+      PredLaunch Pn = P[l + 1];  // stage 1 of the next layer also writes x_l for this layer's FFN
+      Pn.norm.r_in = R[l];
+      Pn.norm.x_out = const_cast<void*>(F[l].x);
+      Pn.norm.eps = eps;
+      e = launch_predict_stage1(Pn, s);
+    } else {
+      // the last layer's input: RMSNorm of its residual row (the row copy goes to rtmp)
+      e = launch_residual_rmsnorm(R[l], nullptr, rtmp, F[l].batch, F[l].d, eps, const_cast<void*>(F[l].x),
+                              F[l].wt == WT_F32 ? WT_F32 : WT_F16, s);
+    }
+    FfnLaunch Fl = F[l];
+    Fl.y = nullptr;
+    Fl.r_in = nullptr;
+    Fl.r_out = nullptr;
+    if (e == hipSuccess) e = launch_ffn(Fl, s);
+    FfnLaunch Fs = F[l];
+    Fs.r_in = R[l];
+    Fs.r_out = const_cast<float*>(R[l + 1]);
+    if (e == hipSuccess) e = launch_sum(Fs, s);
+    if (e == hipSuccess && l + 1 < L) e = launch_predict_stage2(P[l + 1], s);
+    if (e != hipSuccess) return e;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sfnn

@@ -22,22 +22,12 @@ __global__ __launch_bounds__(1024) void k_compact(const uint64_t* __restrict__ m
   if (w < words)
     for (int b = 0; b < batch; ++b) u |= mask[(size_t)b * words + w];
   const int local = __popcll(u);
-  int v = local;  // inclusive scan inside the wave
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int n = __shfl_up(v, o, kWave);
-    if (lane >= o) v += n;
-  }
+  const int v = wave_incl_scan(local);  // inclusive scan inside the wave
   if (lane == kWave - 1) wsum[wave] = v;
   __syncthreads();
   if (wave == 0) {
     const int nw = blockDim.x / kWave;
-    int s = lane < nw ? wsum[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int n = __shfl_up(s, o, kWave);
-      if (lane >= o) s += n;
-    }
+    const int s = wave_incl_scan(lane < nw ? wsum[lane] : 0);
     if (lane < nw) wsum[lane] = s;
   }
   __syncthreads();

@@ -68,6 +68,20 @@ struct FfnLaunch {
 };
 hipError_t launch_ffn(const FfnLaunch& p, hipStream_t s);
 int ffn_groups(int d, int f);
+// The fixed-order sum of an FFN's partials alone (y and / or the residual add).
+hipError_t launch_sum(const FfnLaunch& p, hipStream_t s);
+// Predictor stages on their own (the look-ahead stack runs them apart).
+hipError_t launch_predict_stage1(const PredLaunch& p, hipStream_t s);
+hipError_t launch_predict_stage2(const PredLaunch& p, hipStream_t s);
+
+// One decode step through a stack with the look-ahead predictor: layer l's
+// FFN uses the mask that layer l's predictor made from the previous layer's
+// input (layer 0 from its own).  pred / ffn: per-layer launch descriptors
+// whose mask, union, ids, count, z, x, y and partial pointers are set; r:
+// n_layers + 1 residual rows (r[0] the input, r[n_layers] the output);
+// rtmp: one scratch residual row set [B][d].
+hipError_t launch_stack_lookahead(const PredLaunch* pred, const FfnLaunch* ffn, const float* const* r,
+                                  int n_layers, float eps, float* rtmp, hipStream_t s);
 
 hipError_t launch_compact(const uint64_t* mask, int batch, int f, int32_t* ids, int32_t* count,
                           uint64_t* union_mask, hipStream_t s);

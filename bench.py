@@ -31,6 +31,8 @@ def _parse():
     ap.add_argument("--config", default="c2", help="workload: c2 (default) | c3 | c4 | c5")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--rho", type=float, default=None, help="override the mean fire probability")
+    ap.add_argument("--lookahead", action="store_true",
+                    help="time the look-ahead predictor schedule (layer l+1 predicted from layer l's input)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-extra", action="store_true", help="skip per-kernel, dense and probe timings")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -89,41 +91,53 @@ def main():
     ws = workspace(layers[0][0], layers[0][1], B)
     stack = sg.Stack(layers)
 
-    def step():
+    flags = sg.SFNN_STACK_LOOKAHEAD if args.lookahead else 0
+
+    def make_step(fl):
         # one decode step: every layer's predict -> compact -> sparse FFN, joined
         # by the residual chain (r += y; x = RMSNorm(r)), all inside the library
-        sg.sfnn_stack_decode(stack, B, stage, rbuf, 1e-6, ws, count_cap=counts)
+        return lambda: sg.sfnn_stack_decode(stack, B, stage, rbuf, 1e-6, ws, flags=fl, count_cap=counts)
 
-    # eager warm-up on a side stream, then capture one step
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        stage.copy_(tokens[0])
-        step()
-        step()
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        step()
-    torch.cuda.synchronize()
+    def capture(fn):
+        # eager warm-up on a side stream, then capture one step
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            stage.copy_(tokens[0])
+            fn()
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
 
-    for t in range(args.warmup):
-        stage.copy_(tokens[t])
-        graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for t in range(args.steps):
-        stage.copy_(tokens[args.warmup + t])
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    elapsed_ms = e0.elapsed_time(e1)
+    def run(g, n, first):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(n):
+            stage.copy_(tokens[first + t])
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    graph = capture(make_step(flags))
+    run(graph, args.warmup, 0)
+    elapsed_ms = run(graph, args.steps, args.warmup)
     ms_per_step = elapsed_ms / args.steps
     tok_s = B * args.steps / (elapsed_ms / 1e3)
     cnt = counts[:L].cpu().numpy().astype(np.float64)
     mean_u = float(cnt.mean())
+    # the other schedule, timed the same way (reported beside the main figure)
+    other = capture(make_step(0 if args.lookahead else sg.SFNN_STACK_LOOKAHEAD))
+    run(other, min(args.warmup, 8), 0)
+    n_other = min(args.steps, 64)
+    other_ms = run(other, n_other, args.warmup) / n_other
+    del other
+
     # the layer inputs of the last step, for the per-call timings below
     xcap = torch.empty((L, B, d), dtype=xdt, device=dev)
     masks = torch.zeros((L, B, f // 64), dtype=torch.uint64, device=dev)
@@ -157,14 +171,18 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights, calibrated biases/thresholds, x~N(0,1))",
         "config": {"workload": f"{spec.name} FFN stack: {L} layers, d_model {d}, d_ff {f}, "
                                f"rank-{r} predictor, {spec.act}, {spec.wtype}, "
-                               f"{'zipf phi=%.2f ' % spec.phi if spec.profile == 'zipf' else ''}rho={spec.rho}",
-                   "global_batch": B, "decode_steps": args.steps, "layers": L},
+                               f"{'zipf phi=%.2f ' % spec.phi if spec.profile == 'zipf' else ''}rho={spec.rho}"
+                               f"{', look-ahead predictor' if args.lookahead else ''}",
+                   "global_batch": B, "decode_steps": args.steps, "layers": L,
+                   "predictor": "look-ahead (layer l+1 from x_l)" if args.lookahead else "per layer (layer l from x_l)"},
     }
 
     extra = {"mean_active_neurons": round(mean_u, 1), "active_fraction": round(mean_u / f, 4),
              "ffn_active_bytes_per_layer": int(ffn_bytes), "predictor_bytes_per_layer": int(pred_bytes),
              "setup_s": round(t_setup, 1)}
     extra["layer_GBps_stack"] = round(L * (ffn_bytes + pred_bytes) / (ms_per_step / 1e3) / 1e9, 1)
+    key = "tokens_s_per_layer_predictor" if args.lookahead else "tokens_s_lookahead_predictor"
+    extra[key] = round(B / (other_ms / 1e3), 2)
 
     # ---- per-call timings: each call captured for all layers in one graph ----
     if not args.no_extra:

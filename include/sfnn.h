@@ -143,20 +143,30 @@ sfnn_status sfnn_layer(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x
  * is the plain reading of "RMS-normalised inputs"):
  *     r_0 = r_in;  for l = 0..n_layers-1:
  *         x_l = r_l / sqrt(mean(r_l^2) + eps)   (rounded to x's type)
- *         y_l = the layer's output for x_l, exactly as sfnn_layer computes it
+ *         m_l = layer l's predicted mask (see flags)
+ *         y_l = layer l's FFN over the union of m_l, each token gated by its
+ *               own mask, exactly as sfnn_sparse_ffn computes it
  *         r_{l+1} = r_l + y_l
  *     r_out = r_{n_layers}.
+ * flags = 0: m_l = predictor_l(x_l), i.e. each layer exactly as sfnn_layer.
+ * flags = SFNN_STACK_LOOKAHEAD: m_l = predictor_l(x_{l-1}) for l >= 1 (and
+ *     predictor_0(x_0)): DejaVu's asynchronous look-ahead, where the next
+ *     layer's sparsity is predicted one step ahead so the predictor runs
+ *     beside the current layer's FFN (53ai.com sparsity survey, DejaVu
+ *     section 如何充分利用结构化稀疏进行加速).
  * preds / ffns are HOST arrays of n_layers descriptors that share one shape
  * and type (d_model, d_ff, rank, wtype, act); their device pointers may differ.
  * r_in, r_out: [batch][d_model] fp32 (r_out may alias r_in).  Optional
  * per-layer captures (NULL to skip): x_cap [n_layers][batch][d_model] in x's
  * type, y_cap [n_layers][batch][d_model] fp32, mask_cap
- * [n_layers][batch][d_ff/64], ids_cap [n_layers][d_ff] (first count valid),
- * count_cap [n_layers].  The workspace is sfnn_workspace_bytes(&preds[0],
- * &ffns[0], batch).  Same execution rules as every call: asynchronous on
- * `stream`, no allocation, no host synchronisation (capturable in a graph). */
+ * [n_layers][batch][d_ff/64] (the mask layer l used), ids_cap [n_layers][d_ff]
+ * (first count valid), count_cap [n_layers].  The workspace is
+ * sfnn_workspace_bytes(&preds[0], &ffns[0], batch).  Same execution rules as
+ * every call: asynchronous on `stream`, no device allocation, no host
+ * synchronisation (capturable in a graph). */
+#define SFNN_STACK_LOOKAHEAD 1
 sfnn_status sfnn_stack_decode(int32_t n_layers, const sfnn_pred* preds, const sfnn_ffn* ffns, int32_t batch,
-                              const float* r_in, float* r_out, float eps, void* x_cap, float* y_cap,
+                              const float* r_in, float* r_out, float eps, int32_t flags, void* x_cap, float* y_cap,
                               uint64_t* mask_cap, int32_t* ids_cap, int32_t* count_cap, void* ws, size_t ws_bytes,
                               void* stream);
 

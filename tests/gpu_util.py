@@ -99,7 +99,7 @@ def band_check(gpu_words, gpu_logits, ora_logits, band, tau, f):
     return int(((gb != ob) & ~outside).sum())
 
 
-def gpu_stack(layers_dev, r_in: np.ndarray, eps: float = 1e-6, xdtype=torch.float16):
+def gpu_stack(layers_dev, r_in: np.ndarray, eps: float = 1e-6, xdtype=torch.float16, flags: int = 0):
     """sfnn_stack_decode over uploaded layers with every per-layer capture on."""
     L = len(layers_dev)
     B, d = r_in.shape
@@ -114,7 +114,8 @@ def gpu_stack(layers_dev, r_in: np.ndarray, eps: float = 1e-6, xdtype=torch.floa
     ic = torch.full((L, f), -7, dtype=torch.int32, device=DEV)
     cc = torch.full((L + 3,), -1, dtype=torch.int32, device=DEV)
     ws = workspace(pred0, ffn0, B)
-    sg.sfnn_stack_decode(st, B, rin, rout, eps, ws, x_cap=xc, y_cap=yc, mask_cap=mc, ids_cap=ic, count_cap=cc)
+    sg.sfnn_stack_decode(st, B, rin, rout, eps, ws, flags=flags, x_cap=xc, y_cap=yc, mask_cap=mc, ids_cap=ic,
+                         count_cap=cc)
     torch.cuda.synchronize()
     return dict(r_out=rout.cpu().numpy(), x=xc.float().cpu().numpy(), y=yc.cpu().numpy(), mask=mc.cpu().numpy(),
                 ids=ic.cpu().numpy(), count=cc.cpu().numpy()[:L])

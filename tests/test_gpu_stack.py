@@ -3,9 +3,10 @@ oracle, layer by layer, on the inputs the GPU captured for each layer.
 
 For every layer l: the captured input x_l is the RMS-normalised residual
 r_l = r_in + y_0 + ... + y_{l-1} (fp32 adds in that order); its mask is the
-predictor's threshold outside the rounding band; ids/count are the compaction
-of that mask, bit-exact; y_l matches the oracle's masked FFN of x_l within
-2e-3; and y_l is bitwise what sfnn_layer returns for the same x_l.
+predictor's threshold outside the rounding band (of x_l, or with the
+look-ahead flag of x_{l-1} for l >= 1); ids/count are the compaction of that
+mask, bit-exact; y_l matches the oracle's masked FFN of x_l within 2e-3; and
+without look-ahead y_l is bitwise what sfnn_layer returns for the same x_l.
 """
 import numpy as np
 import pytest
@@ -20,12 +21,12 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3
 
 
-def _stack_case(spec, L, B, seed=0):
+def _stack_case(spec, L, B, seed=0, lookahead=False):
     lays = [synth.make_layer(spec, layer=l, seed=seed) for l in range(L)]
     dev = [upload_layer(lay) for lay in lays]
     r_in = synth.make_tokens(spec, B, stream=200 + B, dtype=np.float32) * np.float32(3.0)
     xdt = torch.float32 if spec.wtype == "f32" else torch.float16
-    out = gpu_stack(dev, r_in, 1e-6, xdt)
+    out = gpu_stack(dev, r_in, 1e-6, xdt, flags=1 if lookahead else 0)
     f = spec.d_ff
     r = r_in.astype(np.float32).copy()
     for l, lay in enumerate(lays):
@@ -35,9 +36,11 @@ def _stack_case(spec, L, B, seed=0):
         assert rel_err(x, x_ref) <= (1e-6 if spec.wtype == "f32" else 1e-3), l
         xs = x.astype(spec.x_dtype)
         assert np.array_equal(xs.astype(np.float32), x)
-        # mask: threshold of the predictor on x_l, outside the fp32 rounding band
-        ol, ob = oracle.predict(lay.w1_t, lay.w2_t, lay.tau, xs)
-        band = oracle.guard_band(lay.w1_t, lay.w2_t, xs)
+        # mask: threshold of the predictor on its input (x_l, or x_{l-1} when
+        # looking ahead), outside the fp32 rounding band
+        xp = xs if (not lookahead or l == 0) else out["x"][l - 1].astype(spec.x_dtype)
+        ol, ob = oracle.predict(lay.w1_t, lay.w2_t, lay.tau, xp)
+        band = oracle.guard_band(lay.w1_t, lay.w2_t, xp)
         gb = oracle.unpack_mask(out["mask"][l], f)
         outside = np.abs(ol - lay.tau[None, :].astype(np.float64)) > band
         assert not ((gb != ob) & outside).any(), l
@@ -49,9 +52,10 @@ def _stack_case(spec, L, B, seed=0):
         for b in range(B):
             assert rel_err(out["y"][l][b], ref[b]) <= TOL, (l, b)
         # and bitwise the single-layer entry point on the captured input
-        one = gpu_layer(dev[l][0], dev[l][1], xs)
-        assert np.array_equal(one["y"], out["y"][l]), l
-        assert np.array_equal(one["mask"], out["mask"][l]), l
+        if not lookahead:
+            one = gpu_layer(dev[l][0], dev[l][1], xs)
+            assert np.array_equal(one["y"], out["y"][l]), l
+            assert np.array_equal(one["mask"], out["mask"][l]), l
         r = (r + out["y"][l]).astype(np.float32)
     assert np.array_equal(out["r_out"], r)
 
@@ -94,3 +98,52 @@ def test_stack_single_layer_and_aliasing():
     sg.sfnn_stack_decode(sg.Stack([(pred, ffn)]), 2, r, r, 1e-6, ws)
     torch.cuda.synchronize()
     assert np.array_equal(r.cpu().numpy(), out["r_out"])
+
+
+# ---------------------------------------------------------------------------
+# look-ahead predictor: batches 1 and 2 run the fused two-launch schedule,
+# larger batches the same schedule as separate launches
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B", [1, 2, 3])
+def test_stack_lookahead_fp16_relu(B):
+    _stack_case(synth.config("c2", d_model=1024, d_ff=4096, rank=128, n_layers=3), 3, B, lookahead=True)
+
+
+@pytest.mark.parametrize("B", [1, 2, 5])
+def test_stack_lookahead_fp16_reglu_zipf(B):
+    _stack_case(synth.config("c4", d_model=768, d_ff=2048, rank=64, n_layers=3), 3, B, lookahead=True)
+
+
+@pytest.mark.parametrize("B", [1, 2, 4])
+def test_stack_lookahead_int4(B):
+    _stack_case(synth.config("c5", d_model=1536, d_ff=3072, rank=128, n_layers=3), 3, B, lookahead=True)
+
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_stack_lookahead_fp32(B):
+    _stack_case(synth.config("c1", n_layers=2), 2, B, lookahead=True)
+
+
+def test_stack_lookahead_single_layer():
+    _stack_case(synth.config("c2", d_model=512, d_ff=1024, rank=64, n_layers=1), 1, 1, lookahead=True)
+
+
+def test_stack_lookahead_opt6_7b_full_width():
+    """Full OPT-6.7B layer shape, 3 layers, batch 1 (the fused schedule at bench shape)."""
+    _stack_case(synth.config("c2"), 3, 1, lookahead=True)
+
+
+def test_stack_lookahead_int4_wide():
+    """d_model 12288 INT4 (32 columns per thread in the down projection), 2 layers."""
+    _stack_case(synth.config("c5", d_ff=4096, rank=256, n_layers=2), 2, 1, lookahead=True)
+
+
+def test_stack_bad_flags_rejected():
+    import activation_sparse_gemv_amd as sg
+    from activation_sparse_gemv_amd.device import workspace
+    spec = synth.config("c2", d_model=512, d_ff=1024, rank=64, n_layers=1)
+    pred, ffn = upload_layer(synth.make_layer(spec, layer=0))
+    r = torch.zeros((1, 512), dtype=torch.float32, device="cuda")
+    with pytest.raises(sg.SfnnError):
+        sg.sfnn_stack_decode(sg.Stack([(pred, ffn)]), 1, r, r, 1e-6, workspace(pred, ffn, 1), flags=6)
