@@ -448,30 +448,40 @@ struct SumArgs {
 };
 
 // y[e] = b_down[c] + sum over workgroups g = 0..G-1 of partial[g][e], e = t*d + c.
-// A workgroup of 16*EPW threads covers EPW elements: thread (q, c) adds the
-// g's of group q (of 16) in order, then the 16 group sums are added in order.
-// Split in two so that a fused launch can issue these loads, do other work,
-// and finish the sum afterwards.  Requires G <= 16 * kSumBat.
-constexpr int kSumBat = 32;
+// A 512-thread workgroup covers kSumEPW elements: thread (q, c) adds the
+// partials of g-group q (of kSumNQ, kSumBat consecutive g's) in order, then
+// the group sums are added in order.  Split in two so that a fused launch can
+// issue these loads, do other work, and finish the sum afterwards.  Requires
+// G <= kSumNQ * kSumBat.
+constexpr int kSumEPW = 16;
+constexpr int kSumNQ = 512 / kSumEPW;
+constexpr int kSumBat = 16;
+
+// Element block of sum workgroup vb: workgroups are dealt to the 8 XCDs in
+// turn (vb % 8), so blocks 2m and 2m+1, which share each 128-byte line of
+// the partials, go to workgroups vb and vb + 8 of one XCD and the line is
+// fetched into that XCD's L2 once.
+__device__ __forceinline__ int sum_block(int vb, int gs) {
+  if (vb >= (gs & ~15)) return vb;
+  return (vb & ~15) + 2 * (vb & 7) + ((vb >> 3) & 1);
+}
 
 struct SumLoads {
   float p[kSumBat];
   float bias, rin;  // this element's b_down and residual, fetched with the partials
 };
 
-__device__ __forceinline__ void sum_issue(const SumArgs& a, int vb, SumLoads& L) {
-  constexpr int NQ = 16;
-  const int EPW = blockDim.x / NQ;  // <= 32
-  const int c16 = threadIdx.x % EPW, q = threadIdx.x / EPW;
+__device__ __forceinline__ void sum_issue(const SumArgs& a, int vb, int gs, SumLoads& L) {
+  const int c16 = threadIdx.x % kSumEPW, q = threadIdx.x / kSumEPW;
   const int n = a.B * a.d;
-  const int e = vb * EPW + c16;
+  const int e = sum_block(vb, gs) * kSumEPW + c16;
   const int ec = e < n ? e : 0;
-  const int per = (a.G + NQ - 1) / NQ;
+  const int per = (a.G + kSumNQ - 1) / kSumNQ;
   const int g0 = q * per;
 #pragma unroll
   for (int j = 0; j < kSumBat; ++j) {
-    const int gg = (j < per && g0 + j < a.G) ? g0 + j : 0;
-    L.p[j] = (j < per) ? a.partial[(size_t)gg * n + ec] : 0.0f;
+    L.p[j] = 0.0f;
+    if (j < per && g0 + j < a.G) L.p[j] = a.partial[(size_t)(g0 + j) * n + ec];
   }
   L.bias = 0.0f;
   L.rin = 0.0f;
@@ -482,35 +492,30 @@ __device__ __forceinline__ void sum_issue(const SumArgs& a, int vb, SumLoads& L)
   }
 }
 
-__device__ __forceinline__ void sum_finish(const SumArgs& a, int vb, const SumLoads& L) {
-  constexpr int NQ = 16;
-  __shared__ float part[NQ][32];
-  const int EPW = blockDim.x / NQ;
-  const int c16 = threadIdx.x % EPW, q = threadIdx.x / EPW;
+__device__ __forceinline__ void sum_finish(const SumArgs& a, int vb, int gs, const SumLoads& L) {
+  __shared__ float part[kSumNQ][kSumEPW];
+  const int c16 = threadIdx.x % kSumEPW, q = threadIdx.x / kSumEPW;
   const int n = a.B * a.d;
-  const int e = vb * EPW + c16;
-  const int per = (a.G + NQ - 1) / NQ;
-  const int g0 = q * per;
+  const int e = sum_block(vb, gs) * kSumEPW + c16;
   float s = 0.0f;
 #pragma unroll
-  for (int j = 0; j < kSumBat; ++j)
-    if (j < per && g0 + j < a.G) s += L.p[j];
+  for (int j = 0; j < kSumBat; ++j) s += L.p[j];  // slots past the group hold zeros
   part[q][c16] = s;
   __syncthreads();
   if (q == 0 && e < n) {
     float tot = 0.0f;
 #pragma unroll
-    for (int k = 0; k < NQ; ++k) tot += part[k][c16];
+    for (int k = 0; k < kSumNQ; ++k) tot += part[k][c16];
     const float v = L.bias + tot;
     if (a.y) a.y[e] = v;
     if (a.r_in) a.r_out[e] = L.rin + v;
   }
 }
 
-__device__ __forceinline__ void sum_body(const SumArgs& a, int vb) {
+__device__ __forceinline__ void sum_body(const SumArgs& a, int vb, int gs) {
   SumLoads L;
-  sum_issue(a, vb, L);
-  sum_finish(a, vb, L);
+  sum_issue(a, vb, gs, L);
+  sum_finish(a, vb, gs, L);
 }
 
 // Shape choices and argument builders shared by the launchers.

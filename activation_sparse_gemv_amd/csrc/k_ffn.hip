@@ -9,7 +9,7 @@
 
 namespace sfnn {
 
-__global__ __launch_bounds__(512) void k_sum(SumArgs a) { sum_body(a, blockIdx.x); }
+__global__ __launch_bounds__(512) void k_sum(SumArgs a) { sum_body(a, blockIdx.x, gridDim.x); }
 
 // Threads own CPT columns each for the down projection (at most 512
 // threads); the token group is bounded by the staged activations (LDS) and by
@@ -88,7 +88,7 @@ SumArgs sum_args(const FfnLaunch& p) {
   return a;
 }
 
-int sum_groups(int batch, int d) { return (batch * d + 31) / 32; }  // 512-thread workgroups, 32 elements each
+int sum_groups(int batch, int d) { return (batch * d + kSumEPW - 1) / kSumEPW; }  // 512-thread workgroups
 
 hipError_t launch_sum(const FfnLaunch& p, hipStream_t s) {
   hipLaunchKernelGGL(k_sum, dim3(sum_groups(p.batch, p.d)), dim3(512), 0, s, sum_args(p));

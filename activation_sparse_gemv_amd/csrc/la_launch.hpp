@@ -23,9 +23,9 @@ __global__ __launch_bounds__(512) void k_la_sum_pred2(SumArgs sa, int gs, Pred2A
   constexpr int RB = VPL <= 2 ? 8 : (VPL == 4 ? 4 : 2);
   const int vb = blockIdx.x;
   SumLoads L;
-  if (vb < gs) sum_issue(sa, vb, L);
+  if (vb < gs) sum_issue(sa, vb, gs, L);
   if (vb < gp) pred2_body<PWT, NT2, VPL, RB>(pa, vb);
-  if (vb < gs) sum_finish(sa, vb, L);
+  if (vb < gs) sum_finish(sa, vb, gs, L);
 }
 
 // Launch A for one token group.  next == null: the last layer (FFN only).
