@@ -117,46 +117,13 @@ __device__ __forceinline__ void int4_pairs(uint32_t u, uint32_t out[4]) {
   }
 }
 
-// Stage tokens [tok0, tok0+nt) of x [*, K] into LDS xs [NT][K]; rows of
-// tokens >= nt are zero.  16-byte vectors, four loads in flight per thread
-// before any store.  PERM8 applies the INT4 pairing order inside every
-// 8-element (16-byte fp16) vector.  K * sizeof(XT) must be a multiple of 16.
-template <typename XT, bool PERM8>
-__device__ __forceinline__ void stage_rows(XT* xs, const XT* __restrict__ x, int K, int tok0, int nt,
-                                           int NT) {
-  const int vpr = K * (int)sizeof(XT) / 16;  // vectors per token row
-  const int total = NT * vpr;
-  const u32x4* src = reinterpret_cast<const u32x4*>(x);
-  u32x4* dst = reinterpret_cast<u32x4*>(xs);
-  for (int base = threadIdx.x; base < total; base += 4 * blockDim.x) {
-    u32x4 v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = base + j * blockDim.x;
-      const int t = e / vpr;
-      v[j] = (e < total && t < nt) ? src[(size_t)(tok0 + t) * vpr + (e - t * vpr)] : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = base + j * blockDim.x;
-      if (e < total) {
-        u32x4 o = v[j];
-        if (PERM8) {  // (x0x1, x2x3, x4x5, x6x7) -> (x0x4, x1x5, x2x6, x3x7)
-          o.x = (v[j].x & 0xFFFFu) | (v[j].z << 16);
-          o.y = (v[j].x >> 16) | (v[j].z & 0xFFFF0000u);
-          o.z = (v[j].y & 0xFFFFu) | (v[j].w << 16);
-          o.w = (v[j].y >> 16) | (v[j].w & 0xFFFF0000u);
-        }
-        dst[e] = o;
-      }
-    }
-  }
-}
-
-// stage_rows in two parts, so that loads issued later (weight rows) can be
-// in flight while the activations arrive: issue() starts the loads of the
-// first SP * blockDim vectors into registers, commit() writes them to LDS and
-// stages any remainder with stage-as-you-go loads.  Vector loads return in
+// Stage tokens [tok0, tok0+nt) of x [*, K] into LDS xs [NT][K] (rows of
+// tokens >= nt are zero) in two parts, so that loads issued later (weight
+// rows) can be in flight while the activations arrive: issue() starts the
+// loads of the first SP * blockDim 16-byte vectors into registers, commit()
+// writes them to LDS and stages any remainder with stage-as-you-go loads.
+// PERM8 applies the INT4 pairing order inside every 8-element vector.
+// K * sizeof(XT) must be a multiple of 16.  Vector loads return in
 // order, so waiting for these (issued first) does not wait for later loads.
 template <typename XT, bool PERM8, int SP>
 struct StageSplit {

@@ -5,12 +5,18 @@ d_ff 16384, fp16 weights N(0, 0.02), ReLU at ~90% per-token sparsity, rank-1024
 fp16 predictor per layer), batch 1, 256 decode steps of fresh x ~ N(0, I)
 through the RMS-normalised residual chain.  One step = one sfnn_stack_decode
 call: for every layer, predict -> compact -> sparse FFN, joined by the
-residual + RMSNorm chain.  Weights are drawn on the host from seeded streams
-and copied to HBM before timing; a step is captured once in a HIP graph and
-replayed, the next token copied in between.
+residual + RMSNorm chain.  The default schedule is the look-ahead one (layer
+l+1's predictor runs on layer l's input, two launches per layer);
+--per-layer-predictor times the schedule that predicts each layer from its
+own input (four launches per layer).  Weights are drawn on the host from
+seeded streams and copied to HBM before timing; a step is captured once in a
+HIP graph and replayed, the next token copied in between.
 
-Prints one JSON line (metric/value/unit, ms_per_step, roofline of the sparse
-FFN kernel pair, CPU-oracle baseline, and a breakdown under "extra").
+Prints one JSON line (metric/value/unit, ms_per_step, roofline of one stack
+layer, CPU-oracle baseline, and a breakdown under "extra").
+
+--copy-probe only runs the 16-byte copy kernel over a known number of bytes
+(the calibration run for the HBM traffic counters) and prints its size.
 """
 from __future__ import annotations
 
@@ -31,8 +37,11 @@ def _parse():
     ap.add_argument("--config", default="c2", help="workload: c2 (default) | c3 | c4 | c5")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--rho", type=float, default=None, help="override the mean fire probability")
-    ap.add_argument("--lookahead", action="store_true",
-                    help="time the look-ahead predictor schedule (layer l+1 predicted from layer l's input)")
+    ap.add_argument("--per-layer-predictor", action="store_true",
+                    help="time the schedule that predicts every layer from its own input "
+                         "(default: the look-ahead schedule, layer l+1 predicted from layer l's input)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run the copy kernel over 1 GiB, 4 times (traffic-counter calibration)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-extra", action="store_true", help="skip per-kernel, dense and probe timings")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -40,6 +49,36 @@ def _parse():
 
 
 HBM_PEAK_GBS = 8000.0
+COPY_PROBE_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "stack_layer_opt6.7b_b1_hbm_traffic.md")
+
+
+def _kernel_source_digest():
+    """Digest of the kernel sources, to tell whether stored counter figures still apply."""
+    import hashlib
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "activation_sparse_gemv_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as fh:
+                h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _stored_traffic(workload):
+    """HBM bytes per stack layer from the committed counter summary, if it was taken
+    on this workload with the current kernel sources (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if line.startswith("traffic-json: "):
+                    rec = json.loads(line[len("traffic-json: "):])
+                    if rec.get("source_digest") == _kernel_source_digest() and rec.get("workload") == workload:
+                        return rec
+    except OSError:
+        pass
+    return None
 
 
 def main():
@@ -55,6 +94,15 @@ def main():
     import synth
     import activation_sparse_gemv_amd as sg
     from activation_sparse_gemv_amd.device import to_dev, upload_layer, workspace
+
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            sg.sfnn_probe_copy(src, dst, COPY_PROBE_BYTES)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": COPY_PROBE_BYTES, "launches": 4}), flush=True)
+        return
 
     dev = "cuda"
     over = {}
@@ -91,7 +139,8 @@ def main():
     ws = workspace(layers[0][0], layers[0][1], B)
     stack = sg.Stack(layers)
 
-    flags = sg.SFNN_STACK_LOOKAHEAD if args.lookahead else 0
+    lookahead = not args.per_layer_predictor
+    flags = sg.SFNN_STACK_LOOKAHEAD if lookahead else 0
 
     def make_step(fl):
         # one decode step: every layer's predict -> compact -> sparse FFN, joined
@@ -132,7 +181,7 @@ def main():
     cnt = counts[:L].cpu().numpy().astype(np.float64)
     mean_u = float(cnt.mean())
     # the other schedule, timed the same way (reported beside the main figure)
-    other = capture(make_step(0 if args.lookahead else sg.SFNN_STACK_LOOKAHEAD))
+    other = capture(make_step(0 if lookahead else sg.SFNN_STACK_LOOKAHEAD))
     run(other, min(args.warmup, 8), 0)
     n_other = min(args.steps, 64)
     other_ms = run(other, n_other, args.warmup) / n_other
@@ -172,16 +221,16 @@ def main():
         "config": {"workload": f"{spec.name} FFN stack: {L} layers, d_model {d}, d_ff {f}, "
                                f"rank-{r} predictor, {spec.act}, {spec.wtype}, "
                                f"{'zipf phi=%.2f ' % spec.phi if spec.profile == 'zipf' else ''}rho={spec.rho}"
-                               f"{', look-ahead predictor' if args.lookahead else ''}",
+                               f"{', look-ahead predictor' if lookahead else ', per-layer predictor'}",
                    "global_batch": B, "decode_steps": args.steps, "layers": L,
-                   "predictor": "look-ahead (layer l+1 from x_l)" if args.lookahead else "per layer (layer l from x_l)"},
+                   "predictor": "look-ahead (layer l+1 from x_l)" if lookahead else "per layer (layer l from x_l)"},
     }
 
     extra = {"mean_active_neurons": round(mean_u, 1), "active_fraction": round(mean_u / f, 4),
              "ffn_active_bytes_per_layer": int(ffn_bytes), "predictor_bytes_per_layer": int(pred_bytes),
              "setup_s": round(t_setup, 1)}
     extra["layer_GBps_stack"] = round(L * (ffn_bytes + pred_bytes) / (ms_per_step / 1e3) / 1e9, 1)
-    key = "tokens_s_per_layer_predictor" if args.lookahead else "tokens_s_lookahead_predictor"
+    key = "tokens_s_per_layer_predictor" if lookahead else "tokens_s_lookahead_predictor"
     extra[key] = round(B / (other_ms / 1e3), 2)
 
     # ---- per-call timings: each call captured for all layers in one graph ----
@@ -217,7 +266,6 @@ def main():
                                  for l, (pred, ffn) in enumerate(layers)])
         dense_bytes = f * nmat * row_bytes + f * (nmat - 1) * xb
         extra.update({
-            "us_per_layer_stack": round(ms_per_step * 1e3 / L, 2),
             "us_sparse_ffn": round(t_ffn, 2), "us_predict": round(t_pred, 2), "us_compact": round(t_comp, 2),
             "us_layer": round(t_layer, 2), "us_dense_ffn": round(t_dense, 2),
             "GBps_ffn_active": round(ffn_bytes / t_ffn / 1e3, 1),
@@ -241,12 +289,30 @@ def main():
         probe = 5 * buf.numel() / (a.elapsed_time(b) / 1e3) / 1e9
         extra["probe_read_GBps"] = round(probe, 1)
         del buf
-        out["roofline"] = {
-            "bound": "hbm", "achieved": round(ffn_bytes / t_ffn / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(ffn_bytes / t_ffn / 1e3 / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "sfnn_sparse_ffn (k_up + k_down + k_reduce)",
-            "bytes_per_launch": int(ffn_bytes), "us_per_launch": round(t_ffn, 2),
-        }
+        extra["sparse_ffn_call_roofline"] = {
+            "kernels": "sfnn_sparse_ffn: k_ffn (ids from a list) + k_sum",
+            "bytes_per_call": int(ffn_bytes), "us_per_call": round(t_ffn, 2),
+            "achieved_GBps": round(ffn_bytes / t_ffn / 1e3, 1),
+            "frac": round(ffn_bytes / t_ffn / 1e3 / HBM_PEAK_GBS, 4)}
+
+    # ---- roofline of one stack layer (the timed step / layers) ---------------
+    # algorithmic bytes of a layer: the active rows of the FFN plus the whole
+    # predictor; its time: the step's HIP-event time divided by the layers
+    us_layer_stack = ms_per_step * 1e3 / L
+    layer_bytes = ffn_bytes + pred_bytes
+    workload_key = f"{spec.name}/b{B}/{'lookahead' if lookahead else 'per-layer'}"
+    tr = _stored_traffic(workload_key)
+    out["roofline"] = {
+        "bound": "hbm", "achieved": round(layer_bytes / us_layer_stack / 1e3, 1), "peak": HBM_PEAK_GBS,
+        "unit": "GB/s", "frac": round(layer_bytes / us_layer_stack / 1e3 / HBM_PEAK_GBS, 4),
+        "traffic": (int(tr["fetch_bytes_per_layer"] + tr["write_bytes_per_layer"]) if tr else None),
+        "kernel": ("stack layer, look-ahead: k_la_ffn_pred1 (FFN_l + predictor stage 1 of l+1) "
+                   "+ k_la_sum_pred2 (partial sum + predictor stage 2 of l+1)") if lookahead else
+                  ("stack layer, per-layer predictor: k_pred1 + k_pred2 + k_ffn + k_sum"),
+        "bytes_per_launch": int(layer_bytes), "us_per_launch": round(us_layer_stack, 3),
+        "launch": "one stack layer (two kernels in the look-ahead schedule)",
+    }
+    extra["us_per_layer_stack"] = round(us_layer_stack, 3)
 
     # ---- CPU oracle baseline (bounded sample) ---------------------------------
     if not args.no_cpu:
@@ -294,9 +360,10 @@ def _cpu_baseline(lay, spec, B, L, budget_s):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
-    xs = synth.make_tokens(spec, 64 * B, stream=123)
+    nmax = 512
+    xs = synth.make_tokens(spec, nmax * B, stream=123)
     n, t_total = 0, 0.0
-    while n < 64 and (t_total < budget_s or n < 2):
+    while n < nmax and (t_total < budget_s or n < 2):
         x = xs[n * B:(n + 1) * B]
         t = time.perf_counter()
         _, m = oracle.predict(lay.w1_t, lay.w2_t, lay.tau, x)
