@@ -45,6 +45,12 @@ def _parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--no-extra", action="store_true", help="skip per-kernel, dense and probe timings")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--distinct-layers", type=int, default=0,
+                    help="draw this many distinct layers and cycle them through the stack (0: all distinct)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the stack: sparse vs dense FFN per layer over batch sizes and fire rates")
+    ap.add_argument("--sweep-batches", default="1,2,4,8,16,32")
+    ap.add_argument("--sweep-rhos", default="0.05,0.1,0.2")
     return ap.parse_args()
 
 
@@ -109,26 +115,32 @@ def main():
     if args.rho is not None:
         over["rho"] = args.rho
     spec = synth.config(args.config, **over)
+    if args.sweep:
+        _sweep(args, spec)
+        return
     B, L = args.batch, spec.n_layers
     d, f, r = spec.d_model, spec.d_ff, spec.rank
     t0 = time.time()
 
     # ---- weights: drawn per layer on the host, resident in HBM -------------
-    layers = []
+    nd = L if args.distinct_layers <= 0 else min(args.distinct_layers, L)
+    distinct = []
     host0 = None
-    for l in range(L):
+    for l in range(nd):
         lay = synth.make_layer(spec, layer=l)
-        layers.append(upload_layer(lay, device=dev))
+        distinct.append(upload_layer(lay, device=dev))
         if l == 0:
             host0 = lay
         del lay
+    layers = [distinct[l % nd] for l in range(L)]
     torch.cuda.synchronize()
     t_setup = time.time() - t0
-    print(f"# {L} layers of {spec.name} resident in HBM after {t_setup:.1f}s", file=sys.stderr, flush=True)
+    print(f"# {L} layers of {spec.name} ({nd} distinct) resident in HBM after {t_setup:.1f}s",
+          file=sys.stderr, flush=True)
 
     # ---- hot-first relayout for power-law workloads -------------------------
     if spec.profile == "zipf":
-        _hot_first(sg, layers, spec, B, dev)
+        _hot_first(sg, distinct, spec, B, dev)
 
     xdt = torch.float32 if spec.wtype == "f32" else torch.float16
     ntok = args.steps + args.warmup
@@ -218,7 +230,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f16" if spec.wtype == "f16" else ("f32" if spec.wtype == "f32" else "i4g128+f16"),
         "data": "synthetic (seeded N(0,0.02) weights, calibrated biases/thresholds, x~N(0,1))",
-        "config": {"workload": f"{spec.name} FFN stack: {L} layers, d_model {d}, d_ff {f}, "
+        "config": {"workload": f"{spec.name} FFN stack: {L} layers"
+                               f"{'' if nd == L else f' (weights of {nd} distinct layers cycled)'}, d_model {d}, d_ff {f}, "
                                f"rank-{r} predictor, {spec.act}, {spec.wtype}, "
                                f"{'zipf phi=%.2f ' % spec.phi if spec.profile == 'zipf' else ''}rho={spec.rho}"
                                f"{', look-ahead predictor' if lookahead else ', per-layer predictor'}",
@@ -320,6 +333,76 @@ def main():
 
     out["extra"] = extra
     print(json.dumps(out), flush=True)
+
+
+def _sweep(args, spec):
+    """Sparse vs dense FFN per layer over batch sizes and fire rates.  Each point
+    cycles over enough distinct layers (>= 1 GB of weights) that the 256 MB
+    Infinity Cache cannot serve them; each call is timed with HIP events around
+    a graph of calls over those layers."""
+    import torch
+    import synth
+    import activation_sparse_gemv_amd as sg
+    from activation_sparse_gemv_amd.device import to_dev, upload_layer, workspace
+    dev = "cuda"
+    d, f, r = spec.d_model, spec.d_ff, spec.rank
+    wb = {"f32": 4.0, "f16": 2.0, "i4g128": 0.5 + 2.0 / 128}[spec.wtype]
+    nmat = spec.n_mat
+    layer_bytes = f * nmat * d * wb + (d * r + r * f) * (4 if spec.pred_dtype == "f32" else 2)
+    nl = max(2, int(np.ceil(1.0e9 / layer_bytes)))
+    batches = [int(b) for b in args.sweep_batches.split(",") if b]
+    rhos = [float(x) for x in args.sweep_rhos.split(",") if x] if spec.profile == "uniform" else [spec.rho]
+    xdt = np.float32 if spec.wtype == "f32" else np.float16
+    points = []
+    for rho in rhos:
+        sp = synth.config(args.config, rho=rho)
+        layers = [upload_layer(synth.make_layer(sp, layer=l), device=dev) for l in range(nl)]
+        if sp.profile == "zipf":
+            _hot_first(sg, layers, sp, 8, dev)
+        for B in batches:
+            ws = workspace(layers[0][0], layers[0][1], B)
+            x = [to_dev(synth.make_tokens(sp, B, stream=500 + l).astype(xdt)) for l in range(nl)]
+            y = torch.empty((B, d), dtype=torch.float32, device=dev)
+            masks = torch.zeros((nl, B, f // 64), dtype=torch.uint64, device=dev)
+            ids = torch.zeros((nl, f), dtype=torch.int32, device=dev)
+            cnt = torch.zeros((nl,), dtype=torch.int32, device=dev)
+            for l, (pred, ffn) in enumerate(layers):
+                sg.sfnn_layer(pred, ffn, x[l], B, y, masks[l], ids[l], cnt[l:l + 1], ws)
+            torch.cuda.synchronize()
+            u = float(cnt.float().mean().item())
+            gate = (lambda l: masks[l]) if B > 1 else (lambda l: None)
+
+            def timed(fn, reps=8):
+                fn()
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    fn()
+                g.replay()
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(reps):
+                    g.replay()
+                b.record()
+                torch.cuda.synchronize()
+                return a.elapsed_time(b) / (reps * nl) * 1e3
+
+            t_sp = timed(lambda: [sg.sfnn_sparse_ffn(ffn, x[l], B, ids[l], cnt[l:l + 1], gate(l), y, ws)
+                                  for l, (_, ffn) in enumerate(layers)])
+            t_ly = timed(lambda: [sg.sfnn_layer(pred, ffn, x[l], B, y, masks[l], ids[l], cnt[l:l + 1], ws)
+                                  for l, (pred, ffn) in enumerate(layers)])
+            t_de = timed(lambda: [sg.sfnn_dense_ffn(ffn, x[l], B, y, ws) for l, (_, ffn) in enumerate(layers)])
+            act_bytes = u * nmat * d * wb
+            points.append({"rho": rho, "batch": B, "union_frac": round(u / f, 4),
+                           "us_sparse_ffn": round(t_sp, 2), "us_layer": round(t_ly, 2), "us_dense_ffn": round(t_de, 2),
+                           "speedup_ffn": round(t_de / t_sp, 2), "speedup_layer_vs_dense_ffn": round(t_de / t_ly, 2),
+                           "GBps_sparse_ffn": round(act_bytes / t_sp / 1e3, 1),
+                           "GBps_dense_ffn": round(f * nmat * d * wb / t_de / 1e3, 1)})
+            print(json.dumps(points[-1]), file=sys.stderr, flush=True)
+        del layers
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": spec.name, "distinct_layers": nl, "points": points}), flush=True)
 
 
 def _hot_first(sg, layers, spec, B, dev):
