@@ -311,7 +311,10 @@ struct RowLoads {
     for (int u = 0; u < UB; ++u) {
       const int v = v0 + u * LPR;
       const bool ok = v < nvec;
-      const int vc = ok ? v : v0;
+      // a slot past the row uses vector 0 of the staged rows (finite values)
+      // and zero weights / a zero scale, so it adds exactly zero; v0 itself
+      // can lie past a short row
+      const int vc = ok ? v : 0;
       const u32x4 z = {0u, 0u, 0u, 0u};
       const u32x4 wv = ok ? w[u] : z;
       if constexpr (WT == WT_F32) {
@@ -322,7 +325,7 @@ struct RowLoads {
         else
           vec_f16<NT>(wv, reinterpret_cast<const f16*>(xs) + E * vc, xstride, acc);
       } else {
-        vec_i4<NT>(w[u], ok ? sc[u] : 0.0f, reinterpret_cast<const f16*>(xs) + E * vc, xstride, acc);
+        vec_i4<NT>(wv, ok ? sc[u] : 0.0f, reinterpret_cast<const f16*>(xs) + E * vc, xstride, acc);
       }
     }
   }

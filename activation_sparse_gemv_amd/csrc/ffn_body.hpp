@@ -149,7 +149,10 @@ __device__ __forceinline__ void ffn_body(const FfnArgs& a, int vb, int vg) {
   constexpr int kDB1 = (NT * CPT >= 64 && kDB0 > 2) ? kDB0 / 4 : ((NT * CPT >= 32 && kDB0 > 2) ? kDB0 / 2 : kDB0);
   constexpr int kDB = kDB1 * CPT > 128 ? 128 / CPT : kDB1;
   constexpr int UB = 8;                  // predictor-row vectors per lane per batch
-  constexpr int UBU = WT == WT_I4 ? 4 : 8;  // up-row vectors per lane per batch (INT4 rows are short)
+  // up-row vectors per lane per batch, two batches in flight: 8 (4 for the
+  // short INT4 rows), halved for ReGLU's second row and for 4+ tokens
+  constexpr int UBU0 = (WT == WT_I4 ? 4 : 8) / (ACT == ACT_REGLU ? 2 : 1) / (NT >= 4 ? 2 : 1);
+  constexpr int UBU = UBU0 < 2 ? 2 : UBU0;
   constexpr int SP = NT == 2 ? 8 : 4;    // staged x vectors per thread held in registers
   extern __shared__ __align__(16) unsigned char smem[];
   XT* xs = reinterpret_cast<XT*>(smem);
@@ -196,7 +199,7 @@ __device__ __forceinline__ void ffn_body(const FfnArgs& a, int vb, int vg) {
   constexpr int CV = CHAIN ? ffn_chain_vecs(NT, CPT) : 1;
   f32x4 rv[CV];
   if constexpr (CHAIN)
-    chain_issue<NT, CV>(a.r_in, rv, d, a.tok0, a.nt);
+    chain_issue<NT, CV, true>(a.r_in, rv, d, a.tok0, a.nt);  // CV is sized to the shape
   else
     stage.issue(reinterpret_cast<const XT*>(a.x), d, a.tok0, a.nt, NT);
 
@@ -298,50 +301,84 @@ __device__ __forceinline__ void ffn_body(const FfnArgs& a, int vb, int vg) {
   __syncthreads();
 
   // ---- 5. up (+ gate) rows: one wavefront per slot -------------------------
-  for (int j = wave; j < cnt; j += NW) {  // wave-uniform loop over this workgroup's slots
-    const int i = ids_w[j];
-    const bool ok = i >= 0;
-    const int ic = ok ? i : 0;
+  // The wavefront's rows (slots wave, wave + NW, ...) are walked as one
+  // sequence of batches of UBU vectors per lane, two buffers deep: batch q+1
+  // (of this row or the next) is requested before batch q is used, so a
+  // wavefront with many rows keeps a row in flight while it computes.
+  {
+    const int bstep = UBU * kWave;
+    const int nb = (nvec + bstep - 1) / bstep;                    // batches per row
+    const int nrow = wave < cnt ? (cnt - 1 - wave) / NW + 1 : 0;  // this wavefront's rows
+    const int nq = nrow * nb;
+    RowLoads<WT, kWave, UBU> Lu2, Lg2;  // Lu / Lg hold batch 0 (step 3)
+    int pk = 0, pb = 0;                 // row and batch of the last request
+    int ck = 0, cb = 0;                 // row and batch being used
     float au[NT], ag[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) au[t] = ag[t] = 0.0f;
-    const uint8_t* ru = a.w_up + (size_t)ic * row_bytes;
-    const f16* su = a.s_up ? a.s_up + (size_t)ic * ngroups : nullptr;
-    const uint8_t* rg = (ACT == ACT_REGLU) ? a.w_gate + (size_t)ic * row_bytes : nullptr;
-    const f16* sg = (ACT == ACT_REGLU && a.s_gate) ? a.s_gate + (size_t)ic * ngroups : nullptr;
-    for (int v0 = lane; v0 < nvec; v0 += UBU * kWave) {
-      if (!(j == wave && v0 == lane)) {  // the first batch was issued in step 3
-        Lu.issue(ru, su, nvec, v0);
-        if constexpr (ACT == ACT_REGLU) Lg.issue(rg, sg, nvec, v0);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // every load above is issued before any math
-      Lu.template consume<NT>(nvec, v0, xs, d, au);
-      if constexpr (ACT == ACT_REGLU) Lg.template consume<NT>(nvec, v0, xs, d, ag);
-    }
+    for (int q = 0; q < nq; q += 2) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      au[t] = group_sum<kWave>(au[t]);
-      if (ACT == ACT_REGLU) ag[t] = group_sum<kWave>(ag[t]);
-    }
-    // lane t finishes token t
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (lane == t) {
-        float hv = 0.0f;
-        if (ok && t < a.nt) {
-          const float up = au[t] + (a.b_up ? load_as_float<XT>(a.b_up, i) : 0.0f);
-          if (ACT == ACT_RELU) {
-            hv = up > 0.0f ? up : 0.0f;
-          } else {
-            const float gt = ag[t] + (a.b_gate ? load_as_float<XT>(a.b_gate, i) : 0.0f);
-            hv = (gt > 0.0f ? gt : 0.0f) * up;
+      for (int hb = 0; hb < 2; ++hb) {
+        if (q + hb < nq) {  // wave-uniform
+          RowLoads<WT, kWave, UBU>& Lc = hb ? Lu2 : Lu;
+          RowLoads<WT, kWave, UBU>& Ln = hb ? Lu : Lu2;
+          RowLoads<WT, kWave, UBU>& Gc = hb ? Lg2 : Lg;
+          RowLoads<WT, kWave, UBU>& Gn = hb ? Lg : Lg2;
+          if (q + hb + 1 < nq) {  // request the next batch into the other buffer
+            if (++pb == nb) {
+              pb = 0;
+              ++pk;
+            }
+            const int in = ids_w[wave + pk * NW];
+            const int inc = in >= 0 ? in : 0;
+            const int v0 = lane + pb * bstep;
+            const int v0c = v0 < nvec ? v0 : 0;  // lanes past a short row read its first vector
+            Ln.issue(a.w_up + (size_t)inc * row_bytes, a.s_up ? a.s_up + (size_t)inc * ngroups : nullptr, nvec,
+                     v0c);
+            if constexpr (ACT == ACT_REGLU)
+              Gn.issue(a.w_gate + (size_t)inc * row_bytes, a.s_gate ? a.s_gate + (size_t)inc * ngroups : nullptr,
+                       nvec, v0c);
           }
-          if (a.mask) {
-            const uint64_t wv = a.mask[(size_t)(a.tok0 + t) * words + (i >> 6)];
-            if (!((wv >> (i & 63)) & 1ull)) hv = 0.0f;  // select: gated-off neurons add nothing
+          __builtin_amdgcn_sched_barrier(0);  // the next batch is requested before this one is used
+          const int v0 = lane + cb * bstep;
+          Lc.template consume<NT>(nvec, v0, xs, d, au);
+          if constexpr (ACT == ACT_REGLU) Gc.template consume<NT>(nvec, v0, xs, d, ag);
+          if (++cb == nb) {  // the row is done: h for its slot
+            const int j = wave + ck * NW;
+            const int i = ids_w[j];
+            const bool ok = i >= 0;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              au[t] = group_sum<kWave>(au[t]);
+              if (ACT == ACT_REGLU) ag[t] = group_sum<kWave>(ag[t]);
+            }
+            // lane t finishes token t
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              if (lane == t) {
+                float hv = 0.0f;
+                if (ok && t < a.nt) {
+                  const float up = au[t] + (a.b_up ? load_as_float<XT>(a.b_up, i) : 0.0f);
+                  if (ACT == ACT_RELU) {
+                    hv = up > 0.0f ? up : 0.0f;
+                  } else {
+                    const float gt = ag[t] + (a.b_gate ? load_as_float<XT>(a.b_gate, i) : 0.0f);
+                    hv = (gt > 0.0f ? gt : 0.0f) * up;
+                  }
+                  if (a.mask) {
+                    const uint64_t wv = a.mask[(size_t)(a.tok0 + t) * words + (i >> 6)];
+                    if (!((wv >> (i & 63)) & 1ull)) hv = 0.0f;  // select: gated-off neurons add nothing
+                  }
+                }
+                s_h[t][j] = hv;
+              }
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) au[t] = ag[t] = 0.0f;
+            cb = 0;
+            ++ck;
           }
         }
-        s_h[t][j] = hv;
       }
     }
   }
@@ -360,7 +397,7 @@ __device__ __forceinline__ void ffn_body(const FfnArgs& a, int vb, int vg) {
         for (int u = 0; u < UB; ++u) {
           const int v = v0 + u * kWave;
           const bool ok = v < pnvec;
-          const int vc = ok ? v : v0;
+          const int vc = ok ? v : 0;
           u32x4 wv = ok ? Lp.w[u] : u32x4{0u, 0u, 0u, 0u};
           if constexpr (WT == WT_F32) {
             vec_f32<NT>(wv, reinterpret_cast<const float*>(xs) + 4 * vc, d, acc);
@@ -382,11 +419,17 @@ __device__ __forceinline__ void ffn_body(const FfnArgs& a, int vb, int vg) {
   __syncthreads();
 
   // ---- 6. down: acc[t][k] += h[t][j] * W_down^T[id_j][col + k], slots in order
+  // INT4: acc[t][k] += (h[t][j] * s_j) * (q_jk + 8) with q + 8 read straight
+  // from the offset-binary nibble as a byte; the 8 * sum_j h s_j that this adds
+  // to every column is taken off at the end (sb).
   float acc[NT][CPT];
+  float sb[WT == WT_I4 ? NT : 1];
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int t = 0; t < NT; ++t) {
 #pragma unroll
     for (int k = 0; k < CPT; ++k) acc[t][k] = 0.0f;
+    if constexpr (WT == WT_I4) sb[t] = 0.0f;
+  }
 
   for (int j0 = 0; j0 < cnt; j0 += 2 * kDB) {
 #pragma unroll
@@ -408,19 +451,49 @@ __device__ __forceinline__ void ffn_body(const FfnArgs& a, int vb, int vg) {
           const int jj = jb + u;
           const int jc = jj < cnt ? jj : jb;
           const bool ok = jj < cnt && ids_w[jc] >= 0 && colok;
-          float wf[CPT];
-          wd[half][u].unpack(wf);
+          if constexpr (WT == WT_I4) {
+            float hs[NT];
 #pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const float hv = ok ? s_h[t][jc] : 0.0f;
+            for (int t = 0; t < NT; ++t) {
+              hs[t] = ok ? s_h[t][jc] * wd[half][u].s : 0.0f;  // a select: a poisoned scale never enters
+              sb[t] += hs[t];
+            }
 #pragma unroll
-            for (int k = 0; k < CPT; ++k) acc[t][k] = __builtin_fmaf(hv, ok ? wf[k] : 0.0f, acc[t][k]);
+            for (int m = 0; m < CPT / 8; ++m) {
+              const uint32_t v = wd[half][u].q[m] ^ 0x88888888u;  // nibbles as q + 8
+              const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
+              float n[8];
+#pragma unroll
+              for (int b = 0; b < 4; ++b) {
+                n[2 * b] = (float)((lo >> (8 * b)) & 0xFFu);
+                n[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu);
+              }
+#pragma unroll
+              for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int k = 0; k < 8; ++k) acc[t][8 * m + k] = __builtin_fmaf(hs[t], n[k], acc[t][8 * m + k]);
+            }
+          } else {
+            float wf[CPT];
+            wd[half][u].unpack(wf);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              const float hv = ok ? s_h[t][jc] : 0.0f;
+#pragma unroll
+              for (int k = 0; k < CPT; ++k) acc[t][k] = __builtin_fmaf(hv, ok ? wf[k] : 0.0f, acc[t][k]);
+            }
           }
         }
       }
     }
   }
 
+  if constexpr (WT == WT_I4) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) acc[t][k] = __builtin_fmaf(-8.0f, sb[t], acc[t][k]);
+  }
   if (colok) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {

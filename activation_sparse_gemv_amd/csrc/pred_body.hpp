@@ -40,12 +40,16 @@ constexpr bool chain_fits(int d, int nt, int nth, int cpt) {
 
 // Residual-chain prologue, issue half: this thread's float4 vectors of the
 // nt residual rows.  Slot (t, k) holds vector threadIdx.x + k * blockDim.x of
-// token t's row, k < CV / NT; slots past the row load nothing and hold zeros
-// (redundant loads of one shared address would serialise in the cache).
-// Callers issue their weight loads unconditionally after this, so the waits
-// in chain_finish stop short of those.  Requires d / 4 <= (CV / NT) *
-// blockDim.x (chain_fits on the host).
-template <int NT, int CV>
+// token t's row, k < CV / NT.  Requires d / 4 <= (CV / NT) * blockDim.x
+// (chain_fits on the host).
+// UNCOND = false: slots past the row load nothing and hold zeros; use it where
+// many slots are spare (redundant loads of one shared address serialise in
+// the cache).  The loads sit in branches, so a later wait for anything
+// issued before them also waits for them.
+// UNCOND = true (slot count sized to the shape): every slot loads, spare ones
+// re-read the row's last vector or token tok0's row, and chain_finish masks
+// them; with no branch, waits for earlier loads stop short of these.
+template <int NT, int CV, bool UNCOND = false>
 __device__ __forceinline__ void chain_issue(const float* __restrict__ r_in, f32x4 (&v)[CV], int d, int tok0,
                                             int nt) {
   constexpr int KPT = CV / NT;
@@ -55,8 +59,15 @@ __device__ __forceinline__ void chain_issue(const float* __restrict__ r_in, f32x
 #pragma unroll
     for (int k = 0; k < KPT; ++k) {
       const int c4 = threadIdx.x + k * blockDim.x;
-      v[t * KPT + k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (t < nt && c4 < nv) v[t * KPT + k] = *reinterpret_cast<const f32x4*>(r_in + (size_t)(tok0 + t) * d + 4 * c4);
+      if constexpr (UNCOND) {
+        const int tc = t < nt ? t : 0;
+        const int cc = c4 < nv ? c4 : nv - 1;
+        v[t * KPT + k] = *reinterpret_cast<const f32x4*>(r_in + (size_t)(tok0 + tc) * d + 4 * cc);
+      } else {
+        v[t * KPT + k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (t < nt && c4 < nv)
+          v[t * KPT + k] = *reinterpret_cast<const f32x4*>(r_in + (size_t)(tok0 + t) * d + 4 * c4);
+      }
     }
   }
 }
@@ -76,10 +87,11 @@ __device__ __forceinline__ void chain_finish(const f32x4 (&v)[CV], XT* xs, float
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    float ss = 0.0f;  // empty slots hold zeros
+    float ss = 0.0f;
 #pragma unroll
     for (int k = 0; k < KPT; ++k) {
-      const f32x4 q = v[t * KPT + k];
+      const bool ok = t < nt && (int)threadIdx.x + k * (int)blockDim.x < nv;  // spare slots add nothing
+      const f32x4 q = ok ? v[t * KPT + k] : f32x4{0.f, 0.f, 0.f, 0.f};
       ss = __builtin_fmaf(q.x, q.x, ss);
       ss = __builtin_fmaf(q.y, q.y, ss);
       ss = __builtin_fmaf(q.z, q.z, ss);
@@ -98,7 +110,7 @@ __device__ __forceinline__ void chain_finish(const f32x4 (&v)[CV], XT* xs, float
     for (int k = 0; k < KPT; ++k) {
       const int c4 = threadIdx.x + k * blockDim.x;
       if (c4 < nv) {
-        const f32x4 o = v[t * KPT + k] * sc;
+        const f32x4 o = t < nt ? v[t * KPT + k] * sc : f32x4{0.f, 0.f, 0.f, 0.f};  // tokens >= nt stage zeros
         const XT o0 = (XT)o.x, o1 = (XT)o.y, o2 = (XT)o.z, o3 = (XT)o.w;
         if constexpr (PERM8) {
           // elements 4h..4h+3 of an 8-vector go to positions h, h+2, h+4, h+6
