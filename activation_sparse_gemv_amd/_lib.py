@@ -26,6 +26,7 @@ EXPORTS = [
     "sfnn_workspace_bytes", "sfnn_predict", "sfnn_compact", "sfnn_sparse_ffn", "sfnn_dense_ffn",
     "sfnn_layer", "sfnn_stack_decode", "sfnn_residual_rmsnorm", "sfnn_fire_counts", "sfnn_hot_first_perm",
     "sfnn_gather_rows", "sfnn_probe_read", "sfnn_probe_copy", "sfnn_status_str", "sfnn_version",
+    "sfnn_set_mfma_min_batch",
 ]
 
 
@@ -79,6 +80,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sfnn_probe_copy": (i32, [vp, vp, sz, vp]),
         "sfnn_status_str": (ctypes.c_char_p, [i32]),
         "sfnn_version": (i32, []),
+        "sfnn_set_mfma_min_batch": (i32, [i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -252,3 +254,9 @@ def sfnn_status_str(code: int) -> str:
 
 def sfnn_version() -> int:
     return int(load().sfnn_version())
+
+
+def sfnn_set_mfma_min_batch(min_batch: int) -> int:
+    """Batch size from which fp16 FFNs run on the matrix cores (<= 0: never);
+    returns the previous value."""
+    return int(load().sfnn_set_mfma_min_batch(int(min_batch)))

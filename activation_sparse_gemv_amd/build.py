@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsfnn.so")
 SOURCES = ["api.hip", "k_predict.hip", "k_ffn.hip", "k_ffn_f32.hip", "k_ffn_f16.hip", "k_ffn_i4.hip",
-           "k_lookahead.hip", "k_la_f32.hip", "k_la_f16.hip", "k_la_i4.hip", "k_misc.hip"]
+           "k_lookahead.hip", "k_la_f32.hip", "k_la_f16.hip", "k_la_i4.hip", "k_misc.hip",
+           "k_mfma.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -20,13 +20,14 @@ bool al16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 bool al4(const void* p) { return p == nullptr || ((uintptr_t)p & 3u) == 0; }
 
 struct Layout {
-  size_t z = 0, partial = 0, mask = 0, uni = 0, ids = 0, count = 0, rbuf = 0, xbuf = 0, rtmp = 0, total = 0;
+  size_t z = 0, partial = 0, mask = 0, uni = 0, ids = 0, count = 0, rbuf = 0, xbuf = 0, rtmp = 0, hbuf = 0,
+         sid = 0, total = 0;
   int G = 0;
 };
 
 // Workspace: predictor stage-1 output z, the FFN workgroups' partial rows,
-// masks, union mask, ids, count, and the residual chain's two fp32 rows and
-// layer input.
+// masks, union mask, ids, count, the residual chain's two fp32 rows and
+// layer input, and the matrix-core FFN's h (one 32-token pass) and slot ids.
 Layout layout(const sfnn_pred* p, const sfnn_ffn* f, int batch) {
   Layout L;
   size_t off = 0;
@@ -55,6 +56,13 @@ Layout layout(const sfnn_pred* p, const sfnn_ffn* f, int batch) {
   off += up((size_t)batch * dm * 4);
   L.rtmp = off;
   off += up((size_t)batch * dm * 4);
+  if (f) {
+    // matrix-core FFN: h of one 32-token pass (two fp16 planes) and the slot ids
+    L.hbuf = off;
+    off += up((size_t)2 * 32 * f->d_ff * 2);
+    L.sid = off;
+    off += up((size_t)f->d_ff * 4);
+  }
   L.total = off;
   return L;
 }
@@ -147,12 +155,16 @@ FfnLaunch ffn_launch(const sfnn_ffn* f, const void* x, int batch, const uint64_t
   L.r_out = nullptr;
   L.partial = reinterpret_cast<float*>(ws + Lw.partial);
   L.groups = Lw.G;
+  L.hbuf = ws + Lw.hbuf;
+  L.sidbuf = reinterpret_cast<int32_t*>(ws + Lw.sid);
   return L;
 }
 
 }  // namespace
 
 extern "C" {
+
+int32_t sfnn_set_mfma_min_batch(int32_t min_batch) { return mfma_min_batch(min_batch < 0 ? 0 : min_batch); }
 
 size_t sfnn_workspace_bytes(const sfnn_pred* pred, const sfnn_ffn* ffn, int32_t batch) {
   if (!batch_ok(batch) || (!pred && !ffn)) return 0;

@@ -77,7 +77,7 @@ FfnArgs ffn_args(const FfnLaunch& p, int tok0, int nt, bool first) {
 SumArgs sum_args(const FfnLaunch& p) {
   SumArgs a;
   a.partial = p.partial;
-  a.G = p.groups;
+  a.G = ffn_uses_mfma(p) ? mfma_groups(p.d, p.groups) : p.groups;
   a.B = p.batch;
   a.d = p.d;
   a.xtype = p.wt == WT_F32 ? WT_F32 : WT_F16;
@@ -96,6 +96,7 @@ hipError_t launch_sum(const FfnLaunch& p, hipStream_t s) {
 }
 
 hipError_t launch_ffn(const FfnLaunch& p, hipStream_t s) {
+  if (ffn_uses_mfma(p)) return launch_ffn_mfma(p, s);
   if (p.wt == WT_F32)
     ffn_run_f32(p, s);
   else if (p.wt == WT_F16)

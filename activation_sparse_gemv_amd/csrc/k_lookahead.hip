@@ -17,7 +17,7 @@ namespace sfnn {
 // larger batches run the same schedule as separate launches.
 static int la_group(const FfnLaunch& F, const PredLaunch& P) {
   const FfnShape sh = ffn_shape(F.wt, F.d, F.batch);
-  if (F.batch > 2) return 0;
+  if (F.batch > 2 || ffn_uses_mfma(F)) return 0;
   int nt = F.batch;
   if (sh.nt < nt) nt = sh.nt;
   const int pwt = F.wt == WT_F32 ? WT_F32 : WT_F16;

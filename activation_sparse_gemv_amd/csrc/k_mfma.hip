@@ -1,0 +1,467 @@
+// Larger batches of the gathered FFN on the matrix cores (fp16 weights).
+//
+// Once a batch has a dozen tokens the FFN over its union of active neurons is
+// a dense contraction: h = act(W_up[U] x^T) over |U| gathered rows and
+// y = W_down^T[U]^T h over the same rows (PowerInfer's neuron-aware operators,
+// [53ai] GPU-CPU混合执行; the per-row work of the pages, batched).  The VALU
+// kernels re-read the weights once per token group at such batches; here one
+// pass covers up to 32 tokens with v_mfma_f32_16x16x32_f16, fp32 accumulation.
+//
+//  k_up_mfma   workgroup = 32 gathered rows (two 16-row tiles); its 8
+//              wavefronts split d_model into 64-column pairs (wavefront w
+//              takes pairs w, w+8, ...), each holding a 16x16 fp32 block per
+//              (tile, 16 tokens); the blocks are added in wavefront order in
+//              LDS, then bias, activation and the per-token select give
+//              h [token][slot], kept as two fp16 planes hi + lo (hi = fp16(h),
+//              lo = fp16(h - hi): 22 of fp32's 24 significant bits, exact for
+//              integers below 2^22; |h| must stay within fp16's range).
+//  k_down_mfma workgroup = 128 (one token tile) or 64 (two) output columns
+//              x one group of slots; its 8
+//              wavefronts split the group's 32-slot steps and multiply both
+//              h planes; one fp32 partial row per group and token, added in a
+//              fixed order by k_sum.
+//
+// MFMA operands (16x16x32): lane l holds 8 consecutive K values of row
+// l % 16 of A and of column l % 16 of B, K block l / 16; D row 4*(l/16) + q,
+// column l % 16 in register q.  Up: A = 16 weight rows (contiguous in K),
+// B = 16 tokens of x.  Down: A = 16 tokens of h (contiguous in slots),
+// B = 16 columns of 32 W_down^T rows: each lane reads CPL consecutive
+// columns of each of its 8 rows and regroups them with byte permutes, so one
+// set of loads feeds CPL products whose columns are CPL apart.
+#include "ffn_body.hpp"
+#include "launch.hpp"
+
+namespace sfnn {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
+}
+
+struct MfmaUpArgs {
+  const f16 *w_up, *w_gate;    // [f][d]
+  const f16 *b_up, *b_gate;    // [f] or null
+  const f16* x;                // [B][d]
+  const int32_t* ids;          // compacted ids, or null: slot s is neuron s
+  const int32_t* count;        // |U|, or null: f
+  const uint64_t* mask;        // per-token gate [B][f/64] or null
+  f16* h;                      // [2][32][f] this pass's h (hi, lo planes), token-major, slot-contiguous
+  int32_t* sid;                // [f] the row each slot reads (dropped slots: the last listed row)
+  int d, f, tok0, nt;          // tokens tok0 .. tok0 + nt - 1, nt <= 16 * NB
+};
+
+struct MfmaDownArgs {
+  const f16* w_down_t;         // [f][d]
+  const int32_t* sid;          // as written by k_up_mfma
+  const int32_t* count;
+  const f16* h;                // as written by k_up_mfma ([2][32][f])
+  float* partial;              // [KG][B][d]
+  int d, f, B, tok0, nt, KG;
+};
+
+constexpr int kUpSlots = 32;
+
+// |U| as the sparse FFN takes it: clamped to [0, f]; null: every neuron.
+__device__ __forceinline__ int slot_count(const int32_t* count, int f) {
+  if (!count) return f;
+  const int c = *count;
+  return c < 0 ? 0 : (c > f ? f : c);
+}
+
+// One 64-column pair of this wavefront's rows and tokens: 2 K blocks.
+template <int NM, int NB>
+struct UpFrag {
+  u32x4 w[NM][2][2];  // [matrix][tile][K block]
+  u32x4 x[NB][2];     // [token tile][K block]
+};
+
+template <int NM, int NB>
+__device__ __forceinline__ void up_issue(UpFrag<NM, NB>& F, const f16* (&wr)[NM][2], const f16* (&xr)[NB],
+                                         int pair) {
+  const int k = pair * 64;
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) F.w[m][t][s] = ld16_stream(wr[m][t] + k + 32 * s);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) F.x[nb][s] = ld16(xr[nb] + k + 32 * s);
+}
+
+template <int NM, int NB>
+__device__ __forceinline__ void up_mul(const UpFrag<NM, NB>& F, const bool (&xok)[NB], f32x4 (&acc)[NM][2][NB]) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const u32x4 xv = xok[nb] ? F.x[nb][s] : z;  // tokens past the pass add nothing
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) acc[m][t][nb] = mfma_16x16x32(F.w[m][t][s], xv, acc[m][t][nb]);
+    }
+}
+
+template <int ACT, int NB>
+__global__ __launch_bounds__(512) void k_up_mfma(MfmaUpArgs a) {
+  constexpr int NM = ACT == ACT_REGLU ? 2 : 1;
+  __shared__ f32x4 red[8][2][NB][kWave];  // one matrix's blocks at a time
+  __shared__ int s_id[kUpSlots];
+  const int cnt = slot_count(a.count, a.f);
+  const int s0 = blockIdx.x * kUpSlots;
+  if (s0 >= cnt) return;  // the whole workgroup
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int r = lane & 15, g = lane >> 4;
+  const int d = a.d;
+  // Slots past |U| and ids outside [0, f) are dropped (h = 0); they re-read
+  // the last listed row, so no row outside the list is touched.
+  int pad = 0;
+  if (a.ids) {
+    const int v = a.ids[cnt - 1];
+    pad = v >= 0 && v < a.f ? v : 0;
+  }
+  const f16* wr[NM][2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int s = s0 + t * 16 + r;
+    int id = s < cnt ? (a.ids ? a.ids[s] : s) : -1;
+    if (id >= a.f) id = -1;
+    const int idc = id < 0 ? pad : id;
+    if (wave == 0 && g == 0) {
+      s_id[t * 16 + r] = id;
+      a.sid[s] = idc;
+    }
+    wr[0][t] = a.w_up + (size_t)idc * d + 8 * g;
+    if constexpr (NM == 2) wr[1][t] = a.w_gate + (size_t)idc * d + 8 * g;
+  }
+  const f16* xr[NB];
+  bool xok[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int tk = nb * 16 + r;
+    xok[nb] = tk < a.nt;
+    xr[nb] = a.x + (size_t)(a.tok0 + (xok[nb] ? tk : 0)) * d + 8 * g;
+  }
+  f32x4 acc[NM][2][NB];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[m][t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // pairs wave, wave + 8, ...; two fragment sets in flight.  Every request is
+  // unconditional (the last one re-reads the current pair) so the waits count
+  // exactly the loads issued after the set being used.
+  const int npair = d >> 6;
+  const int iters = wave < npair ? (npair - wave + 7) >> 3 : 0;
+  if (iters > 0) {
+    UpFrag<NM, NB> A, Bf;
+    up_issue(A, wr, xr, wave);
+    for (int it = 0; it < iters; it += 2) {
+      const int pa = wave + 8 * it;
+      const int pb = it + 1 < iters ? pa + 8 : pa;
+      up_issue(Bf, wr, xr, pb);
+      __builtin_amdgcn_sched_barrier(0);
+      up_mul(A, xok, acc);
+      if (it + 1 >= iters) break;
+      const int pc = it + 2 < iters ? pa + 16 : pb;
+      up_issue(A, wr, xr, pc);
+      __builtin_amdgcn_sched_barrier(0);
+      up_mul(Bf, xok, acc);
+    }
+  }
+
+  // the 8 wavefronts' blocks added in wavefront order; thread e-slots
+  // e = threadIdx.x + 512 k, k < NB, cover 32 slots x 16 NB tokens
+  constexpr int E = 2 * NB * kWave * 4;
+  const float* rf = reinterpret_cast<const float*>(&red[0][0][0][0]);
+  float su[NB], sg[NB];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    if (m) __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) red[wave][t][nb][lane] = acc[m][t][nb];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int e = threadIdx.x + 512 * k;
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) v += rf[w * E + e];
+      if (m == 0) su[k] = v; else sg[k] = v;
+    }
+  }
+  const int words = a.f >> 6;
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const int e = threadIdx.x + 512 * k;
+    const int q = e & 3, ln = (e >> 2) & (kWave - 1), nb = (e >> 8) % NB, t = e / (256 * NB);
+    const int row = t * 16 + 4 * (ln >> 4) + q;
+    const int tk = nb * 16 + (ln & 15);  // tokens past the pass get h = 0 (k_down_mfma reads them)
+    const int id = tk < a.nt ? s_id[row] : -1;
+    float hv = 0.0f;
+    if (id >= 0) {
+      const float up = su[k] + (a.b_up ? (float)a.b_up[id] : 0.0f);
+      if constexpr (ACT == ACT_RELU) {
+        hv = up > 0.0f ? up : 0.0f;
+      } else {
+        const float gt = sg[k] + (a.b_gate ? (float)a.b_gate[id] : 0.0f);
+        hv = (gt > 0.0f ? gt : 0.0f) * up;
+      }
+      if (a.mask) {
+        const uint64_t wv = a.mask[(size_t)(a.tok0 + tk) * words + (id >> 6)];
+        if (!((wv >> (id & 63)) & 1ull)) hv = 0.0f;  // select: gated-off neurons add nothing
+      }
+    }
+    const f16 hi = (f16)hv;
+    a.h[(size_t)tk * a.f + s0 + row] = hi;
+    a.h[(size_t)(32 + tk) * a.f + s0 + row] = (f16)(hv - (float)hi);
+  }
+}
+
+// One 32-slot step of the down projection for this lane: 8 rows (its K
+// block), CPL consecutive columns of each, and both h planes of its tokens.
+template <int NB, int CPL>
+struct DownFrag {
+  uint32_t w[8][CPL / 2];
+  u32x4 h[2][NB];  // [plane][token tile]
+};
+
+__device__ __forceinline__ void down_ids(const MfmaDownArgs& a, int st, int g, int (&id)[8]) {
+  // sid holds every slot below |U| rounded up to 32 (d_ff is a multiple of 64)
+  const int base = st * 32 + 8 * g;
+  const u32x4 v0 = ld16(a.sid + base), v1 = ld16(a.sid + base + 4);
+  id[0] = (int)v0.x; id[1] = (int)v0.y; id[2] = (int)v0.z; id[3] = (int)v0.w;
+  id[4] = (int)v1.x; id[5] = (int)v1.y; id[6] = (int)v1.z; id[7] = (int)v1.w;
+}
+
+template <int NB, int CPL>
+__device__ __forceinline__ void down_issue(DownFrag<NB, CPL>& F, const MfmaDownArgs& a, const int (&id)[8], int col0,
+                                           const f16* (&hr)[NB], int st) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const f16* src = a.w_down_t + (size_t)id[e] * a.d + col0;
+    if constexpr (CPL == 8) {
+      const u32x4 v = ld16_stream(src);
+      F.w[e][0] = v.x; F.w[e][1] = v.y; F.w[e][2] = v.z; F.w[e][3] = v.w;
+    } else {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
+      F.w[e][0] = v.x; F.w[e][1] = v.y;
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    F.h[0][nb] = ld16(hr[nb] + st * 32);
+    F.h[1][nb] = ld16(hr[nb] + (size_t)32 * a.f + st * 32);
+  }
+}
+
+__device__ __forceinline__ uint32_t pick16(uint32_t lo, uint32_t hi, int odd) {
+  return odd ? ((hi & 0xffff0000u) | (lo >> 16)) : ((hi << 16) | (lo & 0xffffu));
+}
+
+template <int NB, int CPL>
+__device__ __forceinline__ void down_mul(const DownFrag<NB, CPL>& F, f32x4 (&acc)[CPL][NB]) {
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    // column i of this lane's CPL columns, over its 8 rows (K)
+    u32x4 b;
+    b.x = pick16(F.w[0][i >> 1], F.w[1][i >> 1], i & 1);
+    b.y = pick16(F.w[2][i >> 1], F.w[3][i >> 1], i & 1);
+    b.z = pick16(F.w[4][i >> 1], F.w[5][i >> 1], i & 1);
+    b.w = pick16(F.w[6][i >> 1], F.w[7][i >> 1], i & 1);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      acc[i][nb] = mfma_16x16x32(F.h[0][nb], b, acc[i][nb]);
+      acc[i][nb] = mfma_16x16x32(F.h[1][nb], b, acc[i][nb]);
+    }
+  }
+}
+
+// Columns per lane: 8 (one 16-byte load per row) for one token tile, 4 for
+// two, so the accumulators and row fragments fit 256 registers.
+template <int NB>
+constexpr int down_cpl() { return NB == 1 ? 8 : 4; }
+
+template <int NB>
+__global__ __launch_bounds__(512) void k_down_mfma(MfmaDownArgs a) {
+  constexpr int CPL = down_cpl<NB>();
+  constexpr int WC = 16 * CPL;  // columns per workgroup
+  __shared__ f32x4 red[8][2][NB][kWave];
+  const int cnt = slot_count(a.count, a.f);
+  const int CS = a.d / WC;
+  const int cs = blockIdx.x % CS, kg = blockIdx.x / CS;
+  const int nsteps = (cnt + 31) >> 5;
+  const int spg = (nsteps + a.KG - 1) / a.KG;
+  const int st0 = kg * spg;
+  const int st1 = st0 + spg < nsteps ? st0 + spg : nsteps;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int n = lane & 15, g = lane >> 4;
+  const int col0 = cs * WC + CPL * n;
+  const f16* hr[NB];  // rows of tokens past the pass hold zeros
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) hr[nb] = a.h + (size_t)(nb * 16 + n) * a.f + 8 * g;
+  f32x4 acc[CPL][NB];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[i][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // steps st0 + wave, + 8, ...: ids two steps ahead, rows one step ahead; every
+  // request unconditional (the last ones re-read the current step)
+  const int first = st0 + wave;
+  const int iters = first < st1 ? (st1 - first + 7) >> 3 : 0;
+  if (iters > 0) {
+    int idA[8], idB[8];
+    DownFrag<NB, CPL> A, Bf;
+    down_ids(a, first, g, idA);
+    const int s1 = iters > 1 ? first + 8 : first;
+    down_ids(a, s1, g, idB);
+    down_issue(A, a, idA, col0, hr, first);
+    for (int it = 0; it < iters; it += 2) {
+      const int sa = first + 8 * it;
+      const int sb = it + 1 < iters ? sa + 8 : sa;
+      const int sc = it + 2 < iters ? sa + 16 : sb;
+      down_ids(a, sc, g, idA);
+      down_issue(Bf, a, idB, col0, hr, sb);
+      __builtin_amdgcn_sched_barrier(0);
+      down_mul(A, acc);
+      if (it + 1 >= iters) break;
+      const int sd = it + 3 < iters ? sa + 24 : sc;
+      down_ids(a, sd, g, idB);
+      down_issue(A, a, idA, col0, hr, sc);
+      __builtin_amdgcn_sched_barrier(0);
+      down_mul(Bf, acc);
+    }
+  }
+
+  // add the 8 wavefronts' blocks in order, two column indices at a time;
+  // every workgroup writes its rows (zeros when its group is empty)
+  const float* rf = reinterpret_cast<const float*>(&red[0][0][0][0]);
+  constexpr int E = 2 * NB * kWave * 4;
+#pragma unroll
+  for (int qt = 0; qt < CPL / 2; ++qt) {
+    if (qt) __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) red[wave][i][nb][lane] = acc[qt * 2 + i][nb];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int e = threadIdx.x + 512 * k;
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) s += rf[w * E + e];
+      const int q = e & 3, ln = (e >> 2) & (kWave - 1), nb = (e >> 8) % NB, i = e / (256 * NB);
+      const int tk = nb * 16 + 4 * (ln >> 4) + q;
+      if (tk >= a.nt) continue;
+      const int col = cs * WC + CPL * (ln & 15) + qt * 2 + i;
+      a.partial[((size_t)kg * a.B + a.tok0 + tk) * a.d + col] = s;
+    }
+  }
+}
+
+// ---- host side ---------------------------------------------------------------
+
+static int g_mfma_min_batch = kMfmaMinBatchDefault;
+
+int mfma_min_batch(int b) {
+  const int old = g_mfma_min_batch;
+  g_mfma_min_batch = b;
+  return old;
+}
+
+bool ffn_uses_mfma(const FfnLaunch& p) {
+  return g_mfma_min_batch > 0 && p.batch >= g_mfma_min_batch && p.wt == WT_F16 && p.hbuf != nullptr && p.sidbuf != nullptr;
+}
+
+// Slot groups of the down projection: enough workgroups of 128 columns x
+// group to cover the chip once (two token tiles use 64-column workgroups,
+// twice as many).  One count for every pass of a call, as k_sum adds them.
+int mfma_groups(int d, int max_groups) {
+  const int cs = d / 128;
+  int kg = (256 + cs - 1) / cs;
+  if (kg > max_groups) kg = max_groups;  // the partial buffer holds max_groups rows per token
+  if (kg < 1) kg = 1;
+  return kg;
+}
+
+template <int ACT, int NB>
+static void mfma_pass(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int tok0, int nt, int kg,
+                      hipStream_t s) {
+  MfmaUpArgs u;
+  u.w_up = (const f16*)p.w_up;
+  u.w_gate = (const f16*)p.w_gate;
+  u.b_up = (const f16*)p.b_up;
+  u.b_gate = (const f16*)p.b_gate;
+  u.x = (const f16*)p.x;
+  u.ids = ids;
+  u.count = count;
+  u.mask = p.mask;
+  u.h = (f16*)p.hbuf;
+  u.sid = p.sidbuf;
+  u.d = p.d;
+  u.f = p.f;
+  u.tok0 = tok0;
+  u.nt = nt;
+  hipLaunchKernelGGL((k_up_mfma<ACT, NB>), dim3(p.f / kUpSlots), dim3(512), 0, s, u);
+  MfmaDownArgs dn;
+  dn.w_down_t = (const f16*)p.w_down_t;
+  dn.sid = p.sidbuf;
+  dn.count = count;
+  dn.h = (const f16*)p.hbuf;
+  dn.partial = p.partial;
+  dn.d = p.d;
+  dn.f = p.f;
+  dn.B = p.batch;
+  dn.tok0 = tok0;
+  dn.nt = nt;
+  dn.KG = kg;
+  hipLaunchKernelGGL((k_down_mfma<NB>), dim3((p.d / (16 * down_cpl<NB>())) * kg), dim3(512), 0, s, dn);
+}
+
+template <int ACT>
+static void mfma_all(const FfnLaunch& p, const int32_t* ids, const int32_t* count, hipStream_t s) {
+  const int kg = mfma_groups(p.d, p.groups);
+  for (int tok0 = 0; tok0 < p.batch; tok0 += 32) {
+    const int nt = p.batch - tok0 < 32 ? p.batch - tok0 : 32;
+    if (nt > 16)
+      mfma_pass<ACT, 2>(p, ids, count, tok0, nt, kg, s);
+    else
+      mfma_pass<ACT, 1>(p, ids, count, tok0, nt, kg, s);
+  }
+}
+
+hipError_t launch_ffn_mfma(const FfnLaunch& p, hipStream_t s) {
+  const int32_t* ids = nullptr;
+  const int32_t* count = nullptr;
+  if (p.src == SRC_UNION) {
+    // the union's ids in ascending order (and |U|), as the FFN kernels write them
+    const hipError_t e = launch_compact(p.union_mask, 1, p.f, p.ids_out, p.count_out, nullptr, s);
+    if (e != hipSuccess) return e;
+    ids = p.ids_out;
+    count = p.count_out;
+  } else if (p.src == SRC_IDS) {
+    ids = p.ids;
+    count = p.count;
+  }
+  if (p.act == ACT_RELU)
+    mfma_all<ACT_RELU>(p, ids, count, s);
+  else
+    mfma_all<ACT_REGLU>(p, ids, count, s);
+  if (p.y || p.r_out) return launch_sum(p, s);
+  return hipGetLastError();
+}
+
+}  // namespace sfnn

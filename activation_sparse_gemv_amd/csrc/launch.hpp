@@ -65,8 +65,18 @@ struct FfnLaunch {
   float* y;               // [B][d] or null
   const float* r_in;      // residual add: r_out = r_in + y (both null to skip)
   float* r_out;
+  void* hbuf = nullptr;   // matrix-core path: h workspace [2][32][f] fp16 (null: path off)
+  int32_t* sidbuf = nullptr;  // matrix-core path: slot ids [f]
 };
 hipError_t launch_ffn(const FfnLaunch& p, hipStream_t s);
+
+// Batches at or above this size run the fp16 FFN on the matrix cores
+// (k_up_mfma + k_down_mfma + k_sum); 0 turns that path off.
+constexpr int kMfmaMinBatchDefault = 8;
+int mfma_min_batch(int b);  // sets the threshold, returns the previous one
+bool ffn_uses_mfma(const FfnLaunch& p);
+int mfma_groups(int d, int max_groups);  // partial rows per token on that path
+hipError_t launch_ffn_mfma(const FfnLaunch& p, hipStream_t s);
 int ffn_groups(int d, int f);
 // The fixed-order sum of an FFN's partials alone (y and / or the residual add).
 hipError_t launch_sum(const FfnLaunch& p, hipStream_t s);

@@ -388,17 +388,33 @@ def _sweep(args, spec):
                 torch.cuda.synchronize()
                 return a.elapsed_time(b) / (reps * nl) * 1e3
 
-            t_sp = timed(lambda: [sg.sfnn_sparse_ffn(ffn, x[l], B, ids[l], cnt[l:l + 1], gate(l), y, ws)
-                                  for l, (_, ffn) in enumerate(layers)])
+            def t_sparse():
+                return timed(lambda: [sg.sfnn_sparse_ffn(ffn, x[l], B, ids[l], cnt[l:l + 1], gate(l), y, ws)
+                                      for l, (_, ffn) in enumerate(layers)])
+
+            def t_dense():
+                return timed(lambda: [sg.sfnn_dense_ffn(ffn, x[l], B, y, ws) for l, (_, ffn) in enumerate(layers)])
+
+            # the default batch-aware dispatch
+            t_sp, t_de = t_sparse(), t_dense()
             t_ly = timed(lambda: [sg.sfnn_layer(pred, ffn, x[l], B, y, masks[l], ids[l], cnt[l:l + 1], ws)
                                   for l, (pred, ffn) in enumerate(layers)])
-            t_de = timed(lambda: [sg.sfnn_dense_ffn(ffn, x[l], B, y, ws) for l, (_, ffn) in enumerate(layers)])
             act_bytes = u * nmat * d * wb
-            points.append({"rho": rho, "batch": B, "union_frac": round(u / f, 4),
-                           "us_sparse_ffn": round(t_sp, 2), "us_layer": round(t_ly, 2), "us_dense_ffn": round(t_de, 2),
-                           "speedup_ffn": round(t_de / t_sp, 2), "speedup_layer_vs_dense_ffn": round(t_de / t_ly, 2),
-                           "GBps_sparse_ffn": round(act_bytes / t_sp / 1e3, 1),
-                           "GBps_dense_ffn": round(f * nmat * d * wb / t_de / 1e3, 1)})
+            pt = {"rho": rho, "batch": B, "union_frac": round(u / f, 4),
+                  "us_sparse_ffn": round(t_sp, 2), "us_layer": round(t_ly, 2), "us_dense_ffn": round(t_de, 2),
+                  "speedup_ffn": round(t_de / t_sp, 2), "speedup_layer_vs_dense_ffn": round(t_de / t_ly, 2),
+                  "GBps_sparse_ffn": round(act_bytes / t_sp / 1e3, 1),
+                  "GBps_dense_ffn": round(f * nmat * d * wb / t_de / 1e3, 1)}
+            if spec.wtype == "f16":
+                # both FFN paths at every batch size: per-row kernels and matrix cores
+                for name, thr in (("rows", 0), ("mfma", 1)):
+                    old = sg.sfnn_set_mfma_min_batch(thr)
+                    try:
+                        pt[f"us_sparse_ffn_{name}"] = round(t_sparse(), 2)
+                        pt[f"us_dense_ffn_{name}"] = round(t_dense(), 2)
+                    finally:
+                        sg.sfnn_set_mfma_min_batch(old)
+            points.append(pt)
             print(json.dumps(points[-1]), file=sys.stderr, flush=True)
         del layers
         torch.cuda.empty_cache()

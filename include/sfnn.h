@@ -129,6 +129,20 @@ sfnn_status sfnn_sparse_ffn(const sfnn_ffn* ffn, const void* x, int32_t batch,
 sfnn_status sfnn_dense_ffn(const sfnn_ffn* ffn, const void* x, int32_t batch, float* y,
                            void* ws, size_t ws_bytes, void* stream);
 
+/* Batch-aware dispatch of the FFN (sparse, dense, layer and stack calls).
+ * Gathering rows is the pages' per-row kernel (PowerInfer's neuron-aware
+ * operators, [53ai] GPU-CPU混合执行); once a batch has many tokens the work over
+ * the union of active rows is a dense contraction.  fp16 FFNs with batch >=
+ * min_batch run it on the matrix cores: the up projection over the gathered
+ * rows and the down projection over column slices, fp32 accumulation, h
+ * carried between them as two fp16 parts (22 significant bits; |h| must lie
+ * within fp16's range), partial rows added in a fixed order
+ * (deterministic run to run, no atomics).  Smaller batches, fp32 and INT4
+ * weights keep the per-row kernels.  min_batch <= 0 turns the matrix-core
+ * path off.  Process-wide; not synchronised with calls in flight: set it
+ * between calls.  Returns the previous threshold (the default is 8). */
+int32_t sfnn_set_mfma_min_batch(int32_t min_batch);
+
 /* predict -> compact -> sparse_ffn for one layer (same results as the three
  * calls in sequence; the compaction runs inside the FFN's first kernel).
  * mask/ids/count are outputs the caller may inspect; any of them may be NULL,
