@@ -10,5 +10,5 @@ from ._lib import (  # noqa: F401
     EXPORTS, FFN, LIB_PATH, Pred, SFNN_F16, SFNN_F32, SFNN_I4G128, SFNN_RELU, SFNN_REGLU, SfnnError, load,
     sfnn_compact, sfnn_dense_ffn, sfnn_fire_counts, sfnn_gather_rows, sfnn_hot_first_perm, sfnn_layer,
     sfnn_predict, sfnn_probe_copy, sfnn_stack_decode, Stack, SFNN_STACK_LOOKAHEAD, sfnn_probe_read, sfnn_residual_rmsnorm, sfnn_sparse_ffn, sfnn_status_str,
-    sfnn_set_mfma_min_batch, sfnn_version, sfnn_workspace_bytes,
+    sfnn_version, sfnn_workspace_bytes,
 )

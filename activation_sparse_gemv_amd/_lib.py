@@ -26,7 +26,6 @@ EXPORTS = [
     "sfnn_workspace_bytes", "sfnn_predict", "sfnn_compact", "sfnn_sparse_ffn", "sfnn_dense_ffn",
     "sfnn_layer", "sfnn_stack_decode", "sfnn_residual_rmsnorm", "sfnn_fire_counts", "sfnn_hot_first_perm",
     "sfnn_gather_rows", "sfnn_probe_read", "sfnn_probe_copy", "sfnn_status_str", "sfnn_version",
-    "sfnn_set_mfma_min_batch",
 ]
 
 
@@ -47,7 +46,8 @@ class sfnn_ffn(ctypes.Structure):
                 ("act", ctypes.c_int32),
                 ("w_up", ctypes.c_void_p), ("w_gate", ctypes.c_void_p), ("w_down_t", ctypes.c_void_p),
                 ("s_up", ctypes.c_void_p), ("s_gate", ctypes.c_void_p), ("s_down_t", ctypes.c_void_p),
-                ("b_up", ctypes.c_void_p), ("b_gate", ctypes.c_void_p), ("b_down", ctypes.c_void_p)]
+                ("b_up", ctypes.c_void_p), ("b_gate", ctypes.c_void_p), ("b_down", ctypes.c_void_p),
+                ("mfma_min_batch", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -80,7 +80,6 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sfnn_probe_copy": (i32, [vp, vp, sz, vp]),
         "sfnn_status_str": (ctypes.c_char_p, [i32]),
         "sfnn_version": (i32, []),
-        "sfnn_set_mfma_min_batch": (i32, [i32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -143,7 +142,7 @@ class FFN:
     """Device FFN descriptor (keeps its tensors alive)."""
 
     def __init__(self, w_up, w_down_t, act: int = SFNN_RELU, w_gate=None, s_up=None, s_gate=None,
-                 s_down_t=None, b_up=None, b_gate=None, b_down=None):
+                 s_down_t=None, b_up=None, b_gate=None, b_down=None, mfma_min_batch: int = 0):
         self.t = dict(w_up=w_up, w_gate=w_gate, w_down_t=w_down_t, s_up=s_up, s_gate=s_gate,
                       s_down_t=s_down_t, b_up=b_up, b_gate=b_gate, b_down=b_down)
         wt = _wtype_of(w_up)
@@ -152,7 +151,17 @@ class FFN:
         self.d_model, self.d_ff, self.wtype, self.act = d, f, wt, act
         self.c = sfnn_ffn(d, f, wt, act, *[_p(self.t[k]) for k in
                                            ("w_up", "w_gate", "w_down_t", "s_up", "s_gate", "s_down_t",
-                                            "b_up", "b_gate", "b_down")])
+                                            "b_up", "b_gate", "b_down")], mfma_min_batch)
+
+    @property
+    def mfma_min_batch(self) -> int:
+        """Batch size from which an fp16 FFN runs on the matrix cores (0: the
+        library default, negative: never); read by every call."""
+        return int(self.c.mfma_min_batch)
+
+    @mfma_min_batch.setter
+    def mfma_min_batch(self, v: int):
+        self.c.mfma_min_batch = int(v)
 
     @property
     def ref(self):
@@ -254,9 +263,3 @@ def sfnn_status_str(code: int) -> str:
 
 def sfnn_version() -> int:
     return int(load().sfnn_version())
-
-
-def sfnn_set_mfma_min_batch(min_batch: int) -> int:
-    """Batch size from which fp16 FFNs run on the matrix cores (<= 0: never);
-    returns the previous value."""
-    return int(load().sfnn_set_mfma_min_batch(int(min_batch)))

@@ -157,14 +157,13 @@ FfnLaunch ffn_launch(const sfnn_ffn* f, const void* x, int batch, const uint64_t
   L.groups = Lw.G;
   L.hbuf = ws + Lw.hbuf;
   L.sidbuf = reinterpret_cast<int32_t*>(ws + Lw.sid);
+  L.mfma_min_batch = f->mfma_min_batch;
   return L;
 }
 
 }  // namespace
 
 extern "C" {
-
-int32_t sfnn_set_mfma_min_batch(int32_t min_batch) { return mfma_min_batch(min_batch < 0 ? 0 : min_batch); }
 
 size_t sfnn_workspace_bytes(const sfnn_pred* pred, const sfnn_ffn* ffn, int32_t batch) {
   if (!batch_ok(batch) || (!pred && !ffn)) return 0;
@@ -402,6 +401,6 @@ const char* sfnn_status_str(sfnn_status s) {
   return "unknown status";
 }
 
-int32_t sfnn_version(void) { return 200; }
+int32_t sfnn_version(void) { return 300; }  // 300: sfnn_ffn.mfma_min_batch
 
 }  // extern "C"

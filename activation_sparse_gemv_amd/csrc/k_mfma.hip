@@ -161,17 +161,18 @@ __global__ __launch_bounds__(512) void k_up_mfma(MfmaUpArgs a) {
   // exactly the loads issued after the set being used.
   const int npair = d >> 6;
   const int iters = wave < npair ? (npair - wave + 7) >> 3 : 0;
+  auto P = [&](int it) { return wave + 8 * it; };
   if (iters > 0) {
     UpFrag<NM, NB> A, Bf;
-    up_issue(A, wr, xr, wave);
+    up_issue(A, wr, xr, P(0));
     for (int it = 0; it < iters; it += 2) {
-      const int pa = wave + 8 * it;
-      const int pb = it + 1 < iters ? pa + 8 : pa;
+      const int pa = P(it);
+      const int pb = it + 1 < iters ? P(it + 1) : pa;
       up_issue(Bf, wr, xr, pb);
       __builtin_amdgcn_sched_barrier(0);
       up_mul(A, xok, acc);
       if (it + 1 >= iters) break;
-      const int pc = it + 2 < iters ? pa + 16 : pb;
+      const int pc = it + 2 < iters ? P(it + 2) : pb;
       up_issue(A, wr, xr, pc);
       __builtin_amdgcn_sched_barrier(0);
       up_mul(Bf, xok, acc);
@@ -321,23 +322,24 @@ __global__ __launch_bounds__(512) void k_down_mfma(MfmaDownArgs a) {
   // request unconditional (the last ones re-read the current step)
   const int first = st0 + wave;
   const int iters = first < st1 ? (st1 - first + 7) >> 3 : 0;
+  auto S = [&](int it) { return first + 8 * it; };
   if (iters > 0) {
     int idA[8], idB[8];
     DownFrag<NB, CPL> A, Bf;
     down_ids(a, first, g, idA);
-    const int s1 = iters > 1 ? first + 8 : first;
+    const int s1 = iters > 1 ? S(1) : first;
     down_ids(a, s1, g, idB);
     down_issue(A, a, idA, col0, hr, first);
     for (int it = 0; it < iters; it += 2) {
-      const int sa = first + 8 * it;
-      const int sb = it + 1 < iters ? sa + 8 : sa;
-      const int sc = it + 2 < iters ? sa + 16 : sb;
+      const int sa = S(it);
+      const int sb = it + 1 < iters ? S(it + 1) : sa;
+      const int sc = it + 2 < iters ? S(it + 2) : sb;
       down_ids(a, sc, g, idA);
       down_issue(Bf, a, idB, col0, hr, sb);
       __builtin_amdgcn_sched_barrier(0);
       down_mul(A, acc);
       if (it + 1 >= iters) break;
-      const int sd = it + 3 < iters ? sa + 24 : sc;
+      const int sd = it + 3 < iters ? S(it + 3) : sc;
       down_ids(a, sd, g, idB);
       down_issue(A, a, idA, col0, hr, sc);
       __builtin_amdgcn_sched_barrier(0);
@@ -374,16 +376,9 @@ __global__ __launch_bounds__(512) void k_down_mfma(MfmaDownArgs a) {
 
 // ---- host side ---------------------------------------------------------------
 
-static int g_mfma_min_batch = kMfmaMinBatchDefault;
-
-int mfma_min_batch(int b) {
-  const int old = g_mfma_min_batch;
-  g_mfma_min_batch = b;
-  return old;
-}
-
 bool ffn_uses_mfma(const FfnLaunch& p) {
-  return g_mfma_min_batch > 0 && p.batch >= g_mfma_min_batch && p.wt == WT_F16 && p.hbuf != nullptr && p.sidbuf != nullptr;
+  const int thr = p.mfma_min_batch == 0 ? kMfmaMinBatchDefault : p.mfma_min_batch;
+  return thr > 0 && p.batch >= thr && p.wt == WT_F16 && p.hbuf != nullptr && p.sidbuf != nullptr;
 }
 
 // Slot groups of the down projection: enough workgroups of 128 columns x

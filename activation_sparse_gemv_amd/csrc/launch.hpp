@@ -67,13 +67,13 @@ struct FfnLaunch {
   float* r_out;
   void* hbuf = nullptr;   // matrix-core path: h workspace [2][32][f] fp16 (null: path off)
   int32_t* sidbuf = nullptr;  // matrix-core path: slot ids [f]
+  int mfma_min_batch = 0;     // matrix-core path from this batch on (0: default, < 0: never)
 };
 hipError_t launch_ffn(const FfnLaunch& p, hipStream_t s);
 
 // Batches at or above this size run the fp16 FFN on the matrix cores
-// (k_up_mfma + k_down_mfma + k_sum); 0 turns that path off.
+// (k_up_mfma + k_down_mfma + k_sum) unless the descriptor says otherwise.
 constexpr int kMfmaMinBatchDefault = 8;
-int mfma_min_batch(int b);  // sets the threshold, returns the previous one
 bool ffn_uses_mfma(const FfnLaunch& p);
 int mfma_groups(int d, int max_groups);  // partial rows per token on that path
 hipError_t launch_ffn_mfma(const FfnLaunch& p, hipStream_t s);

@@ -407,13 +407,13 @@ def _sweep(args, spec):
                   "GBps_dense_ffn": round(f * nmat * d * wb / t_de / 1e3, 1)}
             if spec.wtype == "f16":
                 # both FFN paths at every batch size: per-row kernels and matrix cores
-                for name, thr in (("rows", 0), ("mfma", 1)):
-                    old = sg.sfnn_set_mfma_min_batch(thr)
-                    try:
-                        pt[f"us_sparse_ffn_{name}"] = round(t_sparse(), 2)
-                        pt[f"us_dense_ffn_{name}"] = round(t_dense(), 2)
-                    finally:
-                        sg.sfnn_set_mfma_min_batch(old)
+                for name, thr in (("rows", -1), ("mfma", 1)):
+                    for _, ffn in layers:
+                        ffn.mfma_min_batch = thr
+                    pt[f"us_sparse_ffn_{name}"] = round(t_sparse(), 2)
+                    pt[f"us_dense_ffn_{name}"] = round(t_dense(), 2)
+                for _, ffn in layers:
+                    ffn.mfma_min_batch = 0
             points.append(pt)
             print(json.dumps(points[-1]), file=sys.stderr, flush=True)
         del layers

@@ -77,7 +77,19 @@ typedef struct sfnn_pred {
 /* One FFN layer.  ReLU:  y = b_down + sum_i relu(W_up[i].x + b_up[i]) W_down[:, i]
  *                ReGLU: y = b_down + sum_i relu(W_gate[i].x + b_gate[i])
  *                                         * (W_up[i].x + b_up[i]) W_down[:, i]
- * Biases have x's type (fp32 for F32 weights, else fp16); NULL means zero. */
+ * Biases have x's type (fp32 for F32 weights, else fp16); NULL means zero.
+ *
+ * Batch-aware dispatch (sparse, dense, layer and stack calls).  Gathering
+ * rows is the pages' per-row kernel (PowerInfer's neuron-aware operators,
+ * [53ai] GPU-CPU混合执行); once a batch has many tokens the work over the union
+ * of active rows is a dense contraction.  An F16 FFN called with batch >=
+ * mfma_min_batch (0 selects the default, 8; a negative value never) runs it on
+ * the matrix cores: the up projection over the gathered rows and the down
+ * projection over column slices, fp32 accumulation, h carried between them as
+ * two fp16 parts (22 significant bits; |h| must lie within fp16's range), the
+ * partial rows added in a fixed order (deterministic, no atomics).  Smaller
+ * batches, F32 and I4G128 weights take the per-row kernels.  The field is
+ * read per call, like the rest of the descriptor. */
 typedef struct sfnn_ffn {
   int32_t d_model, d_ff;
   int32_t wtype;       /* sfnn_wtype                                     */
@@ -91,6 +103,7 @@ typedef struct sfnn_ffn {
   const void* b_up;    /* [d_ff]     or NULL                             */
   const void* b_gate;  /* [d_ff]     or NULL                             */
   const void* b_down;  /* [d_model]  or NULL                             */
+  int32_t mfma_min_batch; /* batch-aware dispatch, see below; 0: default */
 } sfnn_ffn;
 
 /* Bytes of device workspace needed by sfnn_predict / sfnn_sparse_ffn /
@@ -128,20 +141,6 @@ sfnn_status sfnn_sparse_ffn(const sfnn_ffn* ffn, const void* x, int32_t batch,
 /* The same FFN over all d_ff neurons with no gather: the dense baseline. */
 sfnn_status sfnn_dense_ffn(const sfnn_ffn* ffn, const void* x, int32_t batch, float* y,
                            void* ws, size_t ws_bytes, void* stream);
-
-/* Batch-aware dispatch of the FFN (sparse, dense, layer and stack calls).
- * Gathering rows is the pages' per-row kernel (PowerInfer's neuron-aware
- * operators, [53ai] GPU-CPU混合执行); once a batch has many tokens the work over
- * the union of active rows is a dense contraction.  fp16 FFNs with batch >=
- * min_batch run it on the matrix cores: the up projection over the gathered
- * rows and the down projection over column slices, fp32 accumulation, h
- * carried between them as two fp16 parts (22 significant bits; |h| must lie
- * within fp16's range), partial rows added in a fixed order
- * (deterministic run to run, no atomics).  Smaller batches, fp32 and INT4
- * weights keep the per-row kernels.  min_batch <= 0 turns the matrix-core
- * path off.  Process-wide; not synchronised with calls in flight: set it
- * between calls.  Returns the previous threshold (the default is 8). */
-int32_t sfnn_set_mfma_min_batch(int32_t min_batch);
 
 /* predict -> compact -> sparse_ffn for one layer (same results as the three
  * calls in sequence; the compaction runs inside the FFN's first kernel).
@@ -213,7 +212,7 @@ sfnn_status sfnn_probe_read(const void* buf, size_t bytes, float* sink, void* st
 sfnn_status sfnn_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 const char* sfnn_status_str(sfnn_status s);
-int32_t sfnn_version(void);
+int32_t sfnn_version(void);  /* 300 and up: sfnn_ffn has mfma_min_batch */
 
 #ifdef __cplusplus
 }

@@ -1,8 +1,8 @@
 """Parity of the matrix-core FFN path (k_up_mfma + k_down_mfma + k_sum) with the
 float64 oracle, through the C ABI.
 
-The path is selected per call by batch size (sfnn_set_mfma_min_batch); these
-tests force it on (threshold 1) or off (0) and restore the default afterwards.
+The path is selected per call by batch size (the FFN descriptor's
+mfma_min_batch); these tests force it on (threshold 1) or off (-1).
 Bars as for the per-row kernels: 2e-3 normwise relative error per token on
 random layers, bit-exact on integer-grid layers (every intermediate an integer
 below 2^22, so fp32 accumulation in any order and the two-part fp16 h are
@@ -19,40 +19,32 @@ from test_gpu_parity import TOL, _ffn_layer, _layer_case, full_layer
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture
-def mfma():
-    """Force the matrix-core path for every batch size during the test."""
-    import activation_sparse_gemv_amd as sg
-    old = sg.sfnn_set_mfma_min_batch(1)
-    yield
-    sg.sfnn_set_mfma_min_batch(old)
+ON, OFF = 1, -1  # mfma_min_batch: matrix cores for every batch / never
 
 
-@pytest.fixture
-def rows():
-    """Force the per-row kernels for every batch size during the test."""
-    import activation_sparse_gemv_amd as sg
-    old = sg.sfnn_set_mfma_min_batch(0)
-    yield
-    sg.sfnn_set_mfma_min_batch(old)
+def _up(lay, thr):
+    _, ffn = upload_layer(lay, predictor=False)
+    ffn.mfma_min_batch = thr
+    return ffn
 
 
-def test_threshold_setter_round_trips():
-    import activation_sparse_gemv_amd as sg
-    old = sg.sfnn_set_mfma_min_batch(5)
-    assert sg.sfnn_set_mfma_min_batch(old) == 5
-    assert sg.sfnn_set_mfma_min_batch(old) == old
+def test_descriptor_threshold_round_trips():
+    lay = _ffn_layer("f16", "relu", d=128, f=64)
+    ffn = _up(lay, 0)
+    assert ffn.mfma_min_batch == 0 and ffn.c.mfma_min_batch == 0
+    ffn.mfma_min_batch = 5
+    assert ffn.c.mfma_min_batch == 5
 
 
 @pytest.mark.parametrize("act", ["relu", "reglu"])
 @pytest.mark.parametrize("B", [1, 5, 16, 17, 32, 33, 64])
-def test_mfma_sparse_ffn_random_masks(mfma, act, B):
+def test_mfma_sparse_ffn_random_masks(act, B):
     # d 640: 10 column pairs over 8 wavefronts; d_ff 1088: 34 row workgroups,
     # |U| ragged against the 32-slot steps
     lay = _ffn_layer("f16", act)
     x = synth.make_tokens(lay.spec, B, stream=140 + B)
     words = synth.random_masks(B, lay.spec.d_ff, 0.1, seed=100 + B)
-    _, ffn = upload_layer(lay, predictor=False)
+    ffn = _up(lay, ON)
     y = gpu_sparse_ffn(ffn, x, words)
     ref = oracle.masked_ffn(lay, x, words)
     for b in range(B):
@@ -62,20 +54,15 @@ def test_mfma_sparse_ffn_random_masks(mfma, act, B):
 @pytest.mark.parametrize("act", ["relu", "reglu"])
 def test_mfma_matches_rows_path(act):
     """Both paths on the same call, each within the bar of the oracle."""
-    import activation_sparse_gemv_amd as sg
     lay = _ffn_layer("f16", act, d=1024, f=4096, seed=4)
     B = 16
     x = synth.make_tokens(lay.spec, B, stream=150)
     words = synth.random_masks(B, 4096, 0.2, seed=150)
-    _, ffn = upload_layer(lay, predictor=False)
+    ffn = _up(lay, OFF)
     ref = oracle.masked_ffn(lay, x, words)
-    old = sg.sfnn_set_mfma_min_batch(0)
-    try:
-        y_rows = gpu_sparse_ffn(ffn, x, words)
-        sg.sfnn_set_mfma_min_batch(1)
-        y_mfma = gpu_sparse_ffn(ffn, x, words)
-    finally:
-        sg.sfnn_set_mfma_min_batch(old)
+    y_rows = gpu_sparse_ffn(ffn, x, words)
+    ffn.mfma_min_batch = ON
+    y_mfma = gpu_sparse_ffn(ffn, x, words)
     for b in range(B):
         assert rel_err(y_rows[b], ref[b]) <= TOL, b
         assert rel_err(y_mfma[b], ref[b]) <= TOL, b
@@ -83,10 +70,10 @@ def test_mfma_matches_rows_path(act):
 
 @pytest.mark.parametrize("act", ["relu", "reglu"])
 @pytest.mark.parametrize("B", [8, 32])
-def test_mfma_dense_ffn(mfma, act, B):
+def test_mfma_dense_ffn(act, B):
     lay = _ffn_layer("f16", act, d=1024, f=2048, seed=2)
     x = synth.make_tokens(lay.spec, B, stream=160 + B)
-    _, ffn = upload_layer(lay, predictor=False)
+    ffn = _up(lay, ON)
     y = gpu_dense_ffn(ffn, x)
     ref = oracle.dense_ffn(lay, x)
     for b in range(B):
@@ -96,35 +83,30 @@ def test_mfma_dense_ffn(mfma, act, B):
 @pytest.mark.parametrize("act", ["relu", "reglu"])
 @pytest.mark.parametrize("B", [6, 17, 40])
 def test_mfma_integer_grid_bitwise(act, B):
-    import activation_sparse_gemv_amd as sg
     d, f = (256, 1088) if act == "relu" else (128, 576)
     lay = synth.make_grid_layer(d, f, 32, act=act, wtype="f16", seed=20 + B)
     x = synth.make_grid_tokens(d, B, seed=20 + B, dtype=np.float16)
     words = synth.random_masks(B, f, 0.3, seed=20 + B)
-    _, ffn = upload_layer(lay, predictor=False)
+    ffn = _up(lay, ON)
     ref = oracle.masked_ffn(lay, x, words, return_f64=True)
     assert np.abs(ref).max() < 2 ** 22
-    old = sg.sfnn_set_mfma_min_batch(1)
-    try:
-        y = gpu_sparse_ffn(ffn, x, words)
-        yd = gpu_dense_ffn(ffn, x)
-        sg.sfnn_set_mfma_min_batch(0)
-        y_rows = gpu_sparse_ffn(ffn, x, words)
-    finally:
-        sg.sfnn_set_mfma_min_batch(old)
+    y = gpu_sparse_ffn(ffn, x, words)
+    yd = gpu_dense_ffn(ffn, x)
+    ffn.mfma_min_batch = OFF
+    y_rows = gpu_sparse_ffn(ffn, x, words)
     assert np.array_equal(y.astype(np.float64), ref)
     assert np.array_equal(yd.astype(np.float64), oracle.dense_ffn(lay, x, return_f64=True))
     assert np.array_equal(y, y_rows)  # the two paths agree bitwise on the grid
 
 
-def test_mfma_rows_outside_union_never_read(mfma):
+def test_mfma_rows_outside_union_never_read():
     """NaN in every row and bias outside the union changes nothing, bitwise."""
     lay = _ffn_layer("f16", "reglu")
     B, f = 9, lay.spec.d_ff
     x = synth.make_tokens(lay.spec, B, stream=170)
     words = synth.random_masks(B, f, 0.05, seed=170)
     words[:, 0] &= ~np.uint64(1)  # keep row 0 out of the union
-    _, ffn = upload_layer(lay, predictor=False)
+    ffn = _up(lay, ON)
     y_clean = gpu_sparse_ffn(ffn, x, words)
     _, _, uni = oracle.compact(words, B, f)
     off = ~oracle.unpack_mask(uni[None], f)[0]
@@ -133,31 +115,31 @@ def test_mfma_rows_outside_union_never_read(mfma):
         a = getattr(lay, name).copy()
         a[off] = np.float16(np.nan)
         setattr(lay, name, a)
-    _, ffn2 = upload_layer(lay, predictor=False)
+    ffn2 = _up(lay, ON)
     y_poison = gpu_sparse_ffn(ffn2, x, words)
     assert np.isfinite(y_poison).all()
     assert np.array_equal(y_clean, y_poison)
 
 
-def test_mfma_empty_set_gives_bias_bitwise(mfma):
+def test_mfma_empty_set_gives_bias_bitwise():
     lay = _ffn_layer("f16", "relu")
     lay.b_down = (np.arange(lay.spec.d_model) % 7 - 3).astype(np.float16) * np.float16(0.25)
     B = 12
     x = synth.make_tokens(lay.spec, B, stream=180)
     words = np.zeros((B, lay.spec.d_ff // 64), dtype=np.uint64)
-    _, ffn = upload_layer(lay, predictor=False)
+    ffn = _up(lay, ON)
     y = gpu_sparse_ffn(ffn, x, words)
     assert np.array_equal(y, np.tile(lay.b_down.astype(np.float32), (B, 1)))
 
 
-def test_mfma_out_of_range_ids_skipped_and_count_clamped(mfma):
+def test_mfma_out_of_range_ids_skipped_and_count_clamped():
     import torch
     import activation_sparse_gemv_amd as sg
     from activation_sparse_gemv_amd.device import workspace
     lay = _ffn_layer("f16", "relu", d=256, f=1024)
     B = 3
     x = synth.make_tokens(lay.spec, B, stream=185)
-    _, ffn = upload_layer(lay, predictor=False)
+    ffn = _up(lay, ON)
     ws = workspace(None, ffn, B)
     xd = to_dev(x)
     # ids 5, 1<<20 (out of range), -3 (out of range), 9: only 5 and 9 contribute
@@ -178,44 +160,44 @@ def test_mfma_out_of_range_ids_skipped_and_count_clamped(mfma):
         assert rel_err(y.cpu().numpy()[b], ref[b]) <= TOL
 
 
-def test_mfma_deterministic_run_to_run(mfma):
+def test_mfma_deterministic_run_to_run():
     lay = _ffn_layer("f16", "reglu", d=1024, f=4096)
     B = 24
     x = synth.make_tokens(lay.spec, B, stream=190)
     words = synth.random_masks(B, 4096, 0.2, seed=190)
-    _, ffn = upload_layer(lay, predictor=False)
+    ffn = _up(lay, ON)
     a = gpu_sparse_ffn(ffn, x, words)
     b = gpu_sparse_ffn(ffn, x, words)
     assert np.array_equal(a, b)
 
 
-def test_mfma_layer_opt6_7b_full_size_b32(mfma):
+def test_mfma_layer_opt6_7b_full_size_b32():
     spec = synth.config("c2")
     lay = full_layer("c2")
     x = synth.make_tokens(spec, 32, stream=5)
-    _layer_case(lay, x, check_tokens=[0, 13, 31])
+    _layer_case(lay, x, check_tokens=[0, 13, 31], mfma_min_batch=ON)
 
 
-def test_mfma_layer_llama_reglu70b_full_size_b16(mfma):
+def test_mfma_layer_llama_reglu70b_full_size_b16():
     spec = synth.config("c4")
     lay = full_layer("c4")
     x = synth.make_tokens(spec, 16, stream=6)
-    _layer_case(lay, x, check_tokens=[0, 15])
+    _layer_case(lay, x, check_tokens=[0, 15], mfma_min_batch=ON)
 
 
 @pytest.mark.parametrize("lookahead", [False, True])
-def test_mfma_stack_fp16_relu_b9(mfma, lookahead):
+def test_mfma_stack_fp16_relu_b9(lookahead):
     from test_gpu_stack import _stack_case
     spec = synth.config("c2", d_model=512, d_ff=2048, rank=64, n_layers=3)
-    _stack_case(spec, 3, 9, seed=11, lookahead=lookahead)
+    _stack_case(spec, 3, 9, seed=11, lookahead=lookahead, mfma_min_batch=ON)
 
 
-def test_rows_path_still_covers_large_batches(rows):
+def test_rows_path_still_covers_large_batches():
     lay = _ffn_layer("f16", "relu")
     B = 17
     x = synth.make_tokens(lay.spec, B, stream=195)
     words = synth.random_masks(B, lay.spec.d_ff, 0.1, seed=195)
-    _, ffn = upload_layer(lay, predictor=False)
+    ffn = _up(lay, OFF)
     y = gpu_sparse_ffn(ffn, x, words)
     ref = oracle.masked_ffn(lay, x, words)
     for b in range(B):

@@ -264,10 +264,11 @@ def test_deterministic_run_to_run():
 # whole layer: predict -> compact -> sparse FFN
 # ---------------------------------------------------------------------------
 
-def _layer_case(lay, x, check_tokens=None, max_flip_frac=1e-4):
+def _layer_case(lay, x, check_tokens=None, max_flip_frac=1e-4, mfma_min_batch=0):
     spec = lay.spec
     f = spec.d_ff
     pred, ffn = upload_layer(lay)
+    ffn.mfma_min_batch = mfma_min_batch
     out = gpu_layer(pred, ffn, x)
     ol, ob = oracle.predict(lay.w1_t, lay.w2_t, lay.tau, x)
     band = oracle.guard_band(lay.w1_t, lay.w2_t, x)

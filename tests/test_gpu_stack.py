@@ -21,9 +21,11 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3
 
 
-def _stack_case(spec, L, B, seed=0, lookahead=False):
+def _stack_case(spec, L, B, seed=0, lookahead=False, mfma_min_batch=0):
     lays = [synth.make_layer(spec, layer=l, seed=seed) for l in range(L)]
     dev = [upload_layer(lay) for lay in lays]
+    for _, ffn in dev:
+        ffn.mfma_min_batch = mfma_min_batch
     r_in = synth.make_tokens(spec, B, stream=200 + B, dtype=np.float32) * np.float32(3.0)
     xdt = torch.float32 if spec.wtype == "f32" else torch.float16
     out = gpu_stack(dev, r_in, 1e-6, xdt, flags=1 if lookahead else 0)
