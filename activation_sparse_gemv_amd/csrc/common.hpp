@@ -32,6 +32,34 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(bitcast<f16x2>(a), bitcast<f16x2>(b), c, false);
 }
 
+// ---- matrix cores -----------------------------------------------------------
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// D = A B + C on one 16x16x32 fp16 tile, fp32 accumulation.  Lane l holds 8
+// consecutive K values of row l % 16 of A and of column l % 16 of B (K block
+// l / 16); D row 4 (l / 16) + q, column l % 16 sits in register q.
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
+}
+
+// Eight fp32 values as two fp16 planes, hi = fp16(v) and lo = fp16(v - hi):
+// 22 of fp32's 24 significant bits, exact for integers below 2^22 (|v| must
+// stay within fp16's range).
+__device__ __forceinline__ void split_hi_lo(const f32x4 a, const f32x4 b, u32x4& hi, u32x4& lo) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f16 h0 = (f16)v[2 * k], h1 = (f16)v[2 * k + 1];
+    const f16 l0 = (f16)(v[2 * k] - (float)h0), l1 = (f16)(v[2 * k + 1] - (float)h1);
+    h[k] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    l[k] = (uint32_t)__builtin_bit_cast(uint16_t, l0) | ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+  }
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
+}
+
 // ---- cross-lane sums on the DPP path --------------------------------------
 // Data-parallel-primitive modifiers move values between lanes inside a VALU
 // instruction, with no LDS round trip (a shuffle through ds_bpermute costs an

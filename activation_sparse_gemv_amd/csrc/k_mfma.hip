@@ -33,13 +33,6 @@
 
 namespace sfnn {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
-                                                0, 0);
-}
-
 struct MfmaUpArgs {
   const f16 *w_up, *w_gate;    // [f][d]
   const f16 *b_up, *b_gate;    // [f] or null
@@ -378,7 +371,8 @@ __global__ __launch_bounds__(512) void k_down_mfma(MfmaDownArgs a) {
 
 bool ffn_uses_mfma(const FfnLaunch& p) {
   const int thr = p.mfma_min_batch == 0 ? kMfmaMinBatchDefault : p.mfma_min_batch;
-  return thr > 0 && p.batch >= thr && p.wt == WT_F16 && p.hbuf != nullptr && p.sidbuf != nullptr;
+  return thr > 0 && p.batch >= thr && (p.wt == WT_F16 || p.wt == WT_I4) && p.hbuf != nullptr &&
+         p.sidbuf != nullptr;
 }
 
 // Slot groups of the down projection: enough workgroups of 128 columns x
@@ -451,7 +445,9 @@ hipError_t launch_ffn_mfma(const FfnLaunch& p, hipStream_t s) {
     ids = p.ids;
     count = p.count;
   }
-  if (p.act == ACT_RELU)
+  if (p.wt == WT_I4)
+    mfma_all_i4(p, ids, count, mfma_groups(p.d, p.groups), s);
+  else if (p.act == ACT_RELU)
     mfma_all<ACT_RELU>(p, ids, count, s);
   else
     mfma_all<ACT_REGLU>(p, ids, count, s);

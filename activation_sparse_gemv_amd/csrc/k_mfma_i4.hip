@@ -1,0 +1,491 @@
+// Larger batches of the gathered FFN on the matrix cores, INT4-g128 weights
+// (weight-only quantisation dequantised inside the kernel, [ciyun] 2.2 量化;
+// INT4 support of PowerInfer, [news]).
+//
+// Each 128-element group of a weight row holds signed nibbles q with one fp16
+// scale s; w = q s.  The nibbles enter the matrix cores exactly (as fp16
+// integers), and the scale is applied in fp32, so no weight is rounded:
+//
+//  k_up_mfma_i4   workgroup = 16 RT gathered rows (RT row tiles) x the
+//                 pass's tokens; its 8 wavefronts split d_model into the
+//                 128-wide scale groups (group w, w + 8, ...).  Per group and
+//                 16x16 block: four v_mfma_f32_16x16x32_f16 on the group's
+//                 nibbles (lane l takes the 32 nibbles 32 (l / 16) .. + 31 of
+//                 row l % 16, one 16-byte load) and the token values in the
+//                 same pairing order, then acc += s_row * (that sum), with the
+//                 workgroup's scales staged in LDS.  Blocks added in wavefront
+//                 order; bias, activation and per-token select give h [token]
+//                 [slot] in fp32.
+//  k_down_mfma_i4 workgroup = one 128-column scale group x one group of
+//                 slots.  In that column group row k has a single scale s_k,
+//                 so y = sum_k h_k s_k q_k: each step of 32 slots scales h by
+//                 its rows' scales (fp32), splits the product into two fp16
+//                 planes (22 bits), and multiplies them with the nibbles of 8
+//                 consecutive columns per lane (4 bytes per row), regrouped
+//                 per column with byte permutes.  One fp32 partial row per
+//                 slot group and token, added in a fixed order by k_sum.
+//
+// Workgroups of neighbouring column groups read the two 64-byte halves of the
+// same 128-byte lines; they are paired onto one XCD (blocks b and b + 8 of a
+// 16-block run share an XCD), so a line's second half meets it in that L2.
+#include "ffn_body.hpp"
+#include "launch.hpp"
+
+namespace sfnn {
+
+struct MfmaUpI4Args {
+  const uint8_t *q_up, *q_gate;  // [f][d/2] nibbles
+  const f16 *s_up, *s_gate;      // [f][d/128] scales
+  const f16 *b_up, *b_gate;      // [f] or null
+  const f16* x;                  // [B][d]
+  const int32_t* ids;            // compacted ids, or null: slot s is neuron s
+  const int32_t* count;          // |U|, or null: f
+  const uint64_t* mask;          // per-token gate [B][f/64] or null
+  float* h;                      // [32][f] this pass's h, token-major, slot-contiguous
+  int32_t* sid;                  // [f] the row each slot reads (dropped slots: the last listed row)
+  int d, f, tok0, nt;
+};
+
+struct MfmaDownI4Args {
+  const uint8_t* q_down_t;  // [f][d/2]
+  const f16* s_down_t;      // [f][d/128]
+  const int32_t* sid;
+  const int32_t* count;
+  const float* h;           // [32][f]
+  float* partial;           // [KG][B][d]
+  int d, f, B, tok0, nt, KG;
+};
+
+__device__ __forceinline__ int slot_count_i4(const int32_t* count, int f) {
+  if (!count) return f;
+  const int c = *count;
+  return c < 0 ? 0 : (c > f ? f : c);
+}
+
+// (x0x1, x2x3, x4x5, x6x7) -> (x0x4, x1x5, x2x6, x3x7): the order int4_pairs
+// gives a dword's nibbles in
+__device__ __forceinline__ u32x4 pair_order(const u32x4 a) {
+  u32x4 o;
+  o.x = __builtin_amdgcn_perm(a.z, a.x, 0x05040100u);
+  o.y = __builtin_amdgcn_perm(a.z, a.x, 0x07060302u);
+  o.z = __builtin_amdgcn_perm(a.w, a.y, 0x05040100u);
+  o.w = __builtin_amdgcn_perm(a.w, a.y, 0x07060302u);
+  return o;
+}
+
+__device__ __forceinline__ u32x4 nib8(uint32_t u) {
+  uint32_t p[4];
+  int4_pairs(u, p);
+  return u32x4{p[0], p[1], p[2], p[3]};
+}
+
+template <int NM, int RT, int NB>
+struct UpI4Frag {
+  u32x4 w[NM][RT];     // one 16-byte load per row tile: 32 nibbles of the group
+  u32x4 x[NB][4];      // 4 x 8 token values, natural order
+};
+
+template <int ACT, int RT, int NB>
+__global__ __launch_bounds__(512) void k_up_mfma_i4(MfmaUpI4Args a) {
+  constexpr int NM = ACT == ACT_REGLU ? 2 : 1;
+  constexpr int ROWS = 16 * RT;
+  constexpr int kMaxGroups = 128;                    // d_model <= 16384
+  __shared__ f32x4 red[8][2][NB][kWave];             // two row tiles at a time
+  __shared__ f16 ssc[NM][kMaxGroups][ROWS];          // scales, group-major
+  __shared__ int s_id[ROWS];
+  const int cnt = slot_count_i4(a.count, a.f);
+  const int s0 = blockIdx.x * ROWS;
+  if (s0 >= cnt) return;  // the whole workgroup
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int r = lane & 15, g = lane >> 4;
+  const int d = a.d, G = d >> 7;
+  int pad = 0;
+  if (a.ids) {
+    const int v = a.ids[cnt - 1];
+    pad = v >= 0 && v < a.f ? v : 0;
+  }
+  // this lane's rows (one per tile); slots past |U| and ids outside [0, f)
+  // are dropped (h = 0) and re-read the last listed row
+  const uint8_t* wr[NM][RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int s = s0 + t * 16 + r;
+    int id = s < cnt ? (a.ids ? a.ids[s] : s) : -1;
+    if (id >= a.f) id = -1;
+    const int idc = id < 0 ? pad : id;
+    if (wave == 0 && g == 0) {
+      s_id[t * 16 + r] = id;
+      a.sid[s] = idc;
+    }
+    wr[0][t] = a.q_up + (size_t)idc * (d >> 1) + 16 * g;
+    if constexpr (NM == 2) wr[1][t] = a.q_gate + (size_t)idc * (d >> 1) + 16 * g;
+  }
+  const f16* xr[NB];
+  bool xok[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int tk = nb * 16 + r;
+    xok[nb] = tk < a.nt;
+    xr[nb] = a.x + (size_t)(a.tok0 + (xok[nb] ? tk : 0)) * d + 32 * g;
+  }
+  auto issue = [&](UpI4Frag<NM, RT, NB>& F, int grp) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int t = 0; t < RT; ++t) F.w[m][t] = ld16_stream(wr[m][t] + grp * 64);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) F.x[nb][s] = ld16(xr[nb] + grp * 128 + 8 * s);
+  };
+
+  // the first groups' loads go out before the scales are staged
+  const int iters = wave < G ? (G - wave + 7) >> 3 : 0;
+  UpI4Frag<NM, RT, NB> A, Bf;
+  if (iters > 0) issue(A, wave);
+  {
+    const int n = NM * ROWS * G;
+    for (int i = threadIdx.x; i < n; i += 512) {
+      const int m = i / (ROWS * G), rem = i - m * ROWS * G;
+      const int row = rem / G, grp = rem - row * G;
+      const int s = s0 + row;
+      int id = s < cnt ? (a.ids ? a.ids[s] : s) : pad;
+      if (id < 0 || id >= a.f) id = pad;
+      const f16* sp = m == 0 ? a.s_up : a.s_gate;
+      ssc[m][grp][row] = sp[(size_t)id * G + grp];
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc[NM][RT][NB];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[m][t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto mul = [&](const UpI4Frag<NM, RT, NB>& F, int grp) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    u32x4 xv[NB][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xv[nb][s] = xok[nb] ? pair_order(F.x[nb][s]) : zero;
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const u32x4 q = F.w[m][t];
+        const u32x4 qa[4] = {nib8(q.x), nib8(q.y), nib8(q.z), nib8(q.w)};
+        // scales of this lane's D rows 4g .. 4g + 3 of tile t
+        const f16* sc = &ssc[m][grp][t * 16 + 4 * g];
+        const f32x4 sv = {(float)sc[0], (float)sc[1], (float)sc[2], (float)sc[3]};
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) p = mfma_16x16x32(qa[s], xv[nb][s], p);
+          acc[m][t][nb].x = __builtin_fmaf(sv.x, p.x, acc[m][t][nb].x);
+          acc[m][t][nb].y = __builtin_fmaf(sv.y, p.y, acc[m][t][nb].y);
+          acc[m][t][nb].z = __builtin_fmaf(sv.z, p.z, acc[m][t][nb].z);
+          acc[m][t][nb].w = __builtin_fmaf(sv.w, p.w, acc[m][t][nb].w);
+        }
+      }
+  };
+
+  // groups wave, wave + 8, ...; two fragment sets in flight; every request is
+  // unconditional (the last one re-reads the current group)
+  if (iters > 0) {
+    for (int it = 0; it < iters; it += 2) {
+      const int ga = wave + 8 * it;
+      const int gb = it + 1 < iters ? ga + 8 : ga;
+      issue(Bf, gb);
+      __builtin_amdgcn_sched_barrier(0);
+      mul(A, ga);
+      if (it + 1 >= iters) break;
+      issue(A, it + 2 < iters ? gb + 8 : gb);
+      __builtin_amdgcn_sched_barrier(0);
+      mul(Bf, gb);
+    }
+  }
+
+  // the 8 wavefronts' blocks added in wavefront order, two tiles at a time;
+  // thread e-slots e = threadIdx.x + 512 k (k < NB) cover 2 tiles x 16 NB tokens
+  constexpr int E = 2 * NB * kWave * 4;
+  const float* rf = reinterpret_cast<const float*>(&red[0][0][0][0]);
+  const int words = a.f >> 6;
+#pragma unroll
+  for (int tp = 0; tp < RT / 2; ++tp) {
+    float su[NB], sg[NB];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) red[wave][i][nb][lane] = acc[m][2 * tp + i][nb];
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int e = threadIdx.x + 512 * k;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) v += rf[w * E + e];
+        if (m == 0) su[k] = v; else sg[k] = v;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int e = threadIdx.x + 512 * k;
+      const int q = e & 3, ln = (e >> 2) & (kWave - 1), nb = (e >> 8) % NB, i = e / (256 * NB);
+      const int row = (2 * tp + i) * 16 + 4 * (ln >> 4) + q;
+      const int tk = nb * 16 + (ln & 15);  // tokens past the pass get h = 0 (k_down_mfma_i4 reads them)
+      const int id = tk < a.nt ? s_id[row] : -1;
+      float hv = 0.0f;
+      if (id >= 0) {
+        const float up = su[k] + (a.b_up ? (float)a.b_up[id] : 0.0f);
+        if constexpr (ACT == ACT_RELU) {
+          hv = up > 0.0f ? up : 0.0f;
+        } else {
+          const float gt = sg[k] + (a.b_gate ? (float)a.b_gate[id] : 0.0f);
+          hv = (gt > 0.0f ? gt : 0.0f) * up;
+        }
+        if (a.mask) {
+          const uint64_t wv = a.mask[(size_t)(a.tok0 + tk) * words + (id >> 6)];
+          if (!((wv >> (id & 63)) & 1ull)) hv = 0.0f;  // select: gated-off neurons add nothing
+        }
+      }
+      a.h[(size_t)tk * a.f + s0 + row] = hv;
+    }
+  }
+}
+
+// One 32-slot step of the down projection for this lane: its 8 rows (K
+// block), 8 consecutive columns of each (one dword of nibbles), the rows'
+// scales of this column group, and h of its tokens over the 8 slots.
+template <int NB>
+struct DownI4Frag {
+  uint32_t w[8];
+  f16 s[8];
+  f32x4 h[NB][2];
+};
+
+__device__ __forceinline__ void down_ids_i4(const MfmaDownI4Args& a, int st, int g, int (&id)[8]) {
+  const int base = st * 32 + 8 * g;  // sid holds every slot below |U| rounded up to 32
+  const u32x4 v0 = ld16(a.sid + base), v1 = ld16(a.sid + base + 4);
+  id[0] = (int)v0.x; id[1] = (int)v0.y; id[2] = (int)v0.z; id[3] = (int)v0.w;
+  id[4] = (int)v1.x; id[5] = (int)v1.y; id[6] = (int)v1.z; id[7] = (int)v1.w;
+}
+
+template <int NB>
+__device__ __forceinline__ void down_issue_i4(DownI4Frag<NB>& F, const MfmaDownI4Args& a, const int (&id)[8],
+                                              int cs, int boff, const float* (&hr)[NB], int st) {
+  const int G = a.d >> 7;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    F.w[e] = *reinterpret_cast<const uint32_t*>(a.q_down_t + (size_t)id[e] * (a.d >> 1) + boff);
+    F.s[e] = a.s_down_t[(size_t)id[e] * G + cs];
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    F.h[nb][0] = *reinterpret_cast<const f32x4*>(hr[nb] + st * 32);
+    F.h[nb][1] = *reinterpret_cast<const f32x4*>(hr[nb] + st * 32 + 4);
+  }
+}
+
+template <int NB>
+__device__ __forceinline__ void down_mul_i4(const DownI4Frag<NB>& F, f32x4 (&acc)[8][NB]) {
+  // A operands: h of each token tile times its rows' scales, as two fp16 planes
+  u32x4 ah[NB], al[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const f32x4 p0 = {F.h[nb][0].x * (float)F.s[0], F.h[nb][0].y * (float)F.s[1], F.h[nb][0].z * (float)F.s[2],
+                      F.h[nb][0].w * (float)F.s[3]};
+    const f32x4 p1 = {F.h[nb][1].x * (float)F.s[4], F.h[nb][1].y * (float)F.s[5], F.h[nb][1].z * (float)F.s[6],
+                      F.h[nb][1].w * (float)F.s[7]};
+    split_hi_lo(p0, p1, ah[nb], al[nb]);
+  }
+  // B operands: column i over the 8 rows, nibbles as fp16 integers.  Offset
+  // binary first (t ^ 8 = t + 8); a row pair's byte k sits in the low bytes of
+  // each half of perm's result, its low nibble is column 2k, its high one 2k+1.
+  uint32_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = F.w[e] ^ 0x88888888u;
+  const f16x2 bias = {(f16)1032.0f, (f16)1032.0f};
+  u32x4 b[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int rp = 0; rp < 4; ++rp) {
+      const uint32_t sel = 0x0c000c00u | (uint32_t)k | ((uint32_t)(4 + k) << 16);
+      const uint32_t t = __builtin_amdgcn_perm(v[2 * rp + 1], v[2 * rp], sel);
+      const f16x2 ql = bitcast<f16x2>((t & 0x000F000Fu) | 0x64006400u) - bias;
+      const f16x2 qh = bitcast<f16x2>(((t >> 4) & 0x000F000Fu) | 0x64006400u) - bias;
+      lo[rp] = __builtin_bit_cast(uint32_t, ql);
+      hi[rp] = __builtin_bit_cast(uint32_t, qh);
+    }
+    b[2 * k] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    b[2 * k + 1] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      acc[i][nb] = mfma_16x16x32(ah[nb], b[i], acc[i][nb]);
+      acc[i][nb] = mfma_16x16x32(al[nb], b[i], acc[i][nb]);
+    }
+}
+
+// Column group and slot group of workgroup b: within every full run of 16
+// blocks, blocks j and j + 8 (one XCD) take the column groups 2j' and 2j' + 1.
+__device__ __forceinline__ void down_block_i4(int b, int total, int CS, int& cs, int& kg) {
+  int bb = b;
+  if ((b | 15) < total) bb = (b & ~15) | ((b & 7) << 1) | ((b >> 3) & 1);
+  cs = bb % CS;
+  kg = bb / CS;
+}
+
+template <int NB>
+__global__ __launch_bounds__(512) void k_down_mfma_i4(MfmaDownI4Args a) {
+  __shared__ f32x4 red[8][2][NB][kWave];
+  const int cnt = slot_count_i4(a.count, a.f);
+  const int CS = a.d >> 7;
+  int cs, kg;
+  down_block_i4(blockIdx.x, gridDim.x, CS, cs, kg);
+  const int nsteps = (cnt + 31) >> 5;
+  const int spg = (nsteps + a.KG - 1) / a.KG;
+  const int st0 = kg * spg;
+  const int st1 = st0 + spg < nsteps ? st0 + spg : nsteps;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int n = lane & 15, g = lane >> 4;
+  const int boff = cs * 64 + 4 * n;  // this lane's 8 columns cs*128 + 8n .. + 7, in bytes
+  const float* hr[NB];  // rows of tokens past the pass hold zeros
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) hr[nb] = a.h + (size_t)(nb * 16 + n) * a.f + 8 * g;
+  f32x4 acc[8][NB];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[i][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // steps st0 + wave, + 8, ...: ids two steps ahead, rows one step ahead;
+  // every request unconditional (the last ones re-read the current step)
+  const int first = st0 + wave;
+  const int iters = first < st1 ? (st1 - first + 7) >> 3 : 0;
+  auto S = [&](int it) { return first + 8 * it; };
+  if (iters > 0) {
+    int idA[8], idB[8];
+    DownI4Frag<NB> A, Bf;
+    down_ids_i4(a, first, g, idA);
+    down_ids_i4(a, iters > 1 ? S(1) : first, g, idB);
+    down_issue_i4(A, a, idA, cs, boff, hr, first);
+    for (int it = 0; it < iters; it += 2) {
+      const int sa = S(it);
+      const int sb = it + 1 < iters ? S(it + 1) : sa;
+      const int sc = it + 2 < iters ? S(it + 2) : sb;
+      down_ids_i4(a, sc, g, idA);
+      down_issue_i4(Bf, a, idB, cs, boff, hr, sb);
+      __builtin_amdgcn_sched_barrier(0);
+      down_mul_i4(A, acc);
+      if (it + 1 >= iters) break;
+      const int sd = it + 3 < iters ? S(it + 3) : sc;
+      down_ids_i4(a, sd, g, idB);
+      down_issue_i4(A, a, idA, cs, boff, hr, sc);
+      __builtin_amdgcn_sched_barrier(0);
+      down_mul_i4(Bf, acc);
+    }
+  }
+
+  // add the 8 wavefronts' blocks in order, two columns at a time; every
+  // workgroup writes its rows (zeros when its slot group is empty)
+  const float* rf = reinterpret_cast<const float*>(&red[0][0][0][0]);
+  constexpr int E = 2 * NB * kWave * 4;
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    if (qt) __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) red[wave][i][nb][lane] = acc[qt * 2 + i][nb];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int e = threadIdx.x + 512 * k;
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) s += rf[w * E + e];
+      const int q = e & 3, ln = (e >> 2) & (kWave - 1), nb = (e >> 8) % NB, i = e / (256 * NB);
+      const int tk = nb * 16 + 4 * (ln >> 4) + q;
+      if (tk >= a.nt) continue;
+      const int col = cs * 128 + 8 * (ln & 15) + qt * 2 + i;
+      a.partial[((size_t)kg * a.B + a.tok0 + tk) * a.d + col] = s;
+    }
+  }
+}
+
+// ---- host side ---------------------------------------------------------------
+
+// Row tiles per up workgroup: 64 rows for ReLU, 32 for ReGLU (two matrices),
+// so each workgroup's token reads stay at most twice its weight bytes.
+template <int ACT>
+constexpr int up_rt_i4() { return ACT == ACT_REGLU ? 2 : 4; }
+
+template <int ACT, int NB>
+static void mfma_pass_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int tok0, int nt, int kg,
+                         hipStream_t s) {
+  constexpr int RT = up_rt_i4<ACT>();
+  MfmaUpI4Args u;
+  u.q_up = (const uint8_t*)p.w_up;
+  u.q_gate = (const uint8_t*)p.w_gate;
+  u.s_up = (const f16*)p.s_up;
+  u.s_gate = (const f16*)p.s_gate;
+  u.b_up = (const f16*)p.b_up;
+  u.b_gate = (const f16*)p.b_gate;
+  u.x = (const f16*)p.x;
+  u.ids = ids;
+  u.count = count;
+  u.mask = p.mask;
+  u.h = (float*)p.hbuf;
+  u.sid = p.sidbuf;
+  u.d = p.d;
+  u.f = p.f;
+  u.tok0 = tok0;
+  u.nt = nt;
+  hipLaunchKernelGGL((k_up_mfma_i4<ACT, RT, NB>), dim3((p.f + 16 * RT - 1) / (16 * RT)), dim3(512), 0, s, u);
+  MfmaDownI4Args dn;
+  dn.q_down_t = (const uint8_t*)p.w_down_t;
+  dn.s_down_t = (const f16*)p.s_down_t;
+  dn.sid = p.sidbuf;
+  dn.count = count;
+  dn.h = (const float*)p.hbuf;
+  dn.partial = p.partial;
+  dn.d = p.d;
+  dn.f = p.f;
+  dn.B = p.batch;
+  dn.tok0 = tok0;
+  dn.nt = nt;
+  dn.KG = kg;
+  hipLaunchKernelGGL((k_down_mfma_i4<NB>), dim3((p.d / 128) * kg), dim3(512), 0, s, dn);
+}
+
+template <int ACT>
+static void mfma_all_i4_act(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int kg, hipStream_t s) {
+  for (int tok0 = 0; tok0 < p.batch; tok0 += 32) {
+    const int nt = p.batch - tok0 < 32 ? p.batch - tok0 : 32;
+    if (nt > 16)
+      mfma_pass_i4<ACT, 2>(p, ids, count, tok0, nt, kg, s);
+    else
+      mfma_pass_i4<ACT, 1>(p, ids, count, tok0, nt, kg, s);
+  }
+}
+
+void mfma_all_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int kg, hipStream_t s) {
+  if (p.act == ACT_RELU)
+    mfma_all_i4_act<ACT_RELU>(p, ids, count, kg, s);
+  else
+    mfma_all_i4_act<ACT_REGLU>(p, ids, count, kg, s);
+}
+
+}  // namespace sfnn

@@ -83,7 +83,7 @@ __device__ __forceinline__ float block_sum256(float v, float* sh) {
   return t;
 }
 
-// r_out = r_in + y (y optional); x = r_out / sqrt(mean(r_out^2) + eps).
+// r_out = r_in + y (y and r_out optional); x = (r_in + y) / sqrt(mean((r_in + y)^2) + eps).
 // One workgroup per token; each thread keeps up to 64 values in registers
 // (d_model <= 16384), loaded as 16-byte vectors.
 __global__ __launch_bounds__(256) void k_residual_rmsnorm(const float* r_in, const float* y, float* r_out, int d,
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void k_residual_rmsnorm(const float* r_in, con
   for (int j = 0; j < kMaxV; ++j) {
     const int e = threadIdx.x + j * blockDim.x;
     if (e < nv) {
-      ro[e] = v[j];
+      if (r_out) ro[e] = v[j];
       ss = __builtin_fmaf(v[j].x, v[j].x, ss);
       ss = __builtin_fmaf(v[j].y, v[j].y, ss);
       ss = __builtin_fmaf(v[j].z, v[j].z, ss);

@@ -1,0 +1,312 @@
+// The low-rank predictor of larger batches on the matrix cores (fp16
+// predictor weights).
+//
+// The predictor is a dense chain over every neuron ([53ai] 自适应稀疏预测器:
+// a small network in front of each FFN that guesses the active neurons):
+// z = W1^T x, logits = W2^T z, active iff logit > tau.  The VALU kernels hold
+// at most a few tokens per pass and re-read W1 and W2 once per token group;
+// here one pass covers up to 32 tokens with v_mfma_f32_16x16x32_f16, fp32
+// accumulation.
+//
+//  k_pred1_mfma  workgroup = 16 rows of W1^T; its 8 wavefronts split d_model
+//                into 64-column pairs (pair w, w + 8, ...), each holding a
+//                16x16 fp32 block per 16 tokens; the blocks are added in
+//                wavefront order in LDS and written as z [B][r] fp32.
+//  k_pred2_mfma  workgroup = 64 neurons (one mask word, four 16-row tiles) x
+//                every token of the pass; its 8 wavefronts split the rank
+//                into 32-wide steps (step w, w + 8, ...).  z enters the
+//                matrix cores as two fp16 planes (hi = fp16(z), lo =
+//                fp16(z - hi)), so the logits keep 22 bits of z, far inside
+//                the predictor's fp32 error band.  Blocks added in wavefront
+//                order, then threshold, one ballot per token and mask word,
+//                union OR.
+//
+// Every sum is taken in a fixed order, so the results are run-to-run
+// bitwise deterministic, and on integer inputs below 2^22 they are exact.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace sfnn {
+
+struct Pred1MfmaArgs {
+  const f16* w1_t;  // [r][d]
+  const f16* x;     // [B][d]
+  float* z;         // [B][r]
+  int d, r, tok0, nt;
+};
+
+struct Pred2MfmaArgs {
+  const f16* w2_t;        // [f][r]
+  const float* z;         // [B][r]
+  const float* tau;       // [f]
+  uint64_t* mask;         // [B][f/64]
+  uint64_t* union_mask;   // [f/64]
+  float* logits;          // [B][f] or null
+  int f, r, tok0, nt, first_pass;
+};
+
+template <int NB>
+struct P1Frag {
+  u32x4 w[2];      // [K block of the pair]
+  u32x4 x[NB][2];  // [token tile][K block]
+};
+
+template <int NB>
+__global__ __launch_bounds__(512) void k_pred1_mfma(Pred1MfmaArgs a) {
+  __shared__ f32x4 red[8][NB][kWave];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int rr = lane & 15, g = lane >> 4;
+  const int d = a.d;
+  const int row = blockIdx.x * 16 + rr;
+  const f16* wr = a.w1_t + (size_t)(row < a.r ? row : a.r - 1) * d + 8 * g;  // rows past r: dropped below
+  const f16* xr[NB];
+  bool xok[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int tk = nb * 16 + rr;
+    xok[nb] = tk < a.nt;
+    xr[nb] = a.x + (size_t)(a.tok0 + (xok[nb] ? tk : 0)) * d + 8 * g;
+  }
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto issue = [&](P1Frag<NB>& F, int pair) {
+    const int k = pair * 64;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) F.w[s] = ld16_stream(wr + k + 32 * s);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) F.x[nb][s] = ld16(xr[nb] + k + 32 * s);
+  };
+  auto mul = [&](const P1Frag<NB>& F) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_16x16x32(F.w[s], xok[nb] ? F.x[nb][s] : zero, acc[nb]);
+  };
+
+  // pairs wave, wave + 8, ...; two fragment sets in flight; every request is
+  // unconditional (the last one re-reads the current pair)
+  const int npair = d >> 6;
+  const int iters = wave < npair ? (npair - wave + 7) >> 3 : 0;
+  if (iters > 0) {
+    P1Frag<NB> A, Bf;
+    issue(A, wave);
+    for (int it = 0; it < iters; it += 2) {
+      const int pa = wave + 8 * it;
+      const int pb = it + 1 < iters ? pa + 8 : pa;
+      issue(Bf, pb);
+      __builtin_amdgcn_sched_barrier(0);
+      mul(A);
+      if (it + 1 >= iters) break;
+      issue(A, it + 2 < iters ? pb + 8 : pb);
+      __builtin_amdgcn_sched_barrier(0);
+      mul(Bf);
+    }
+  }
+
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) red[wave][nb][lane] = acc[nb];
+  __syncthreads();
+  constexpr int E = NB * kWave * 4;  // floats per wavefront's blocks
+  const int e = threadIdx.x;
+  if (e < E) {
+    const float* rf = reinterpret_cast<const float*>(&red[0][0][0]);
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) s += rf[w * E + e];
+    const int q = e & 3, ln = (e >> 2) & (kWave - 1), nb = e >> 8;
+    const int orow = blockIdx.x * 16 + 4 * (ln >> 4) + q;
+    const int tk = nb * 16 + (ln & 15);
+    if (orow < a.r && tk < a.nt) a.z[(size_t)(a.tok0 + tk) * a.r + orow] = s;
+  }
+}
+
+template <int NB>
+__global__ __launch_bounds__(512) void k_pred2_mfma(Pred2MfmaArgs a) {
+  __shared__ f32x4 red[8][2][NB][kWave];  // two row tiles at a time
+  __shared__ unsigned char bits[32][64];  // [token][neuron of the word]
+  __shared__ unsigned long long wsh[32];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int rr = lane & 15, g = lane >> 4;
+  const int r = a.r;
+  const int n0 = blockIdx.x * 64;
+  const f16* wr[4];  // row starts
+#pragma unroll
+  for (int t = 0; t < 4; ++t) wr[t] = a.w2_t + (size_t)(n0 + t * 16 + rr) * r;
+  const float* zr[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int tk = nb * 16 + rr;
+    zr[nb] = a.z + (size_t)(a.tok0 + (tk < a.nt ? tk : 0)) * r;
+  }
+  bool zok[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) zok[nb] = nb * 16 + rr < a.nt;
+  f32x4 acc[4][NB];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // K block of step ks for this lane: 32 ks + 8 g; the rank is a multiple of
+  // 8, so a block is either whole or past the row (then the row's first block
+  // is read and zeroed: every load is unconditional and in bounds)
+  struct Raw {
+    u32x4 w[4];
+    f32x4 z[NB][2];
+  };
+  auto issue = [&](Raw& R, int ks) {
+    const int kb = 32 * ks + 8 * g;
+    const int kc = kb < r ? kb : 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) R.w[t] = ld16_stream(wr[t] + kc);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      R.z[nb][0] = *reinterpret_cast<const f32x4*>(zr[nb] + kc);
+      R.z[nb][1] = *reinterpret_cast<const f32x4*>(zr[nb] + kc + 4);
+    }
+  };
+  auto mul = [&](const Raw& R, int ks) {
+    const bool ok = 32 * ks + 8 * g < r;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      u32x4 hi, lo;
+      split_hi_lo(R.z[nb][0], R.z[nb][1], hi, lo);
+      if (!ok || !zok[nb]) {
+        hi = zero;
+        lo = zero;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const u32x4 wv = ok ? R.w[t] : zero;
+        acc[t][nb] = mfma_16x16x32(wv, hi, acc[t][nb]);
+        acc[t][nb] = mfma_16x16x32(wv, lo, acc[t][nb]);
+      }
+    }
+  };
+
+  const int nks = (r + 31) >> 5;
+  const int iters = wave < nks ? (nks - wave + 7) >> 3 : 0;
+  if (iters > 0) {
+    Raw A, Bf;
+    issue(A, wave);
+    for (int it = 0; it < iters; it += 2) {
+      const int ka = wave + 8 * it;
+      const int kb = it + 1 < iters ? ka + 8 : ka;
+      issue(Bf, kb);
+      __builtin_amdgcn_sched_barrier(0);
+      mul(A, ka);
+      if (it + 1 >= iters) break;
+      const int kc = it + 2 < iters ? kb + 8 : kb;
+      issue(A, kc);
+      __builtin_amdgcn_sched_barrier(0);
+      mul(Bf, kb);
+    }
+  }
+
+  // add the 8 wavefronts' blocks in order, two row tiles at a time; thread
+  // e-slots e = threadIdx.x + 512 k (k < NB) cover 2 tiles x 16 NB tokens
+  constexpr int E = 2 * NB * kWave * 4;
+  const float* rf = reinterpret_cast<const float*>(&red[0][0][0][0]);
+#pragma unroll
+  for (int tp = 0; tp < 2; ++tp) {
+    if (tp) __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) red[wave][i][nb][lane] = acc[2 * tp + i][nb];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int e = threadIdx.x + 512 * k;
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 8; ++w) s += rf[w * E + e];
+      const int q = e & 3, ln = (e >> 2) & (kWave - 1), nb = (e >> 8) % NB, i = e / (256 * NB);
+      const int nrow = (2 * tp + i) * 16 + 4 * (ln >> 4) + q;  // neuron within the word
+      const int tk = nb * 16 + (ln & 15);
+      if (tk < a.nt) {
+        const int n = n0 + nrow;
+        bits[tk][nrow] = s > a.tau[n] ? 1 : 0;
+        if (a.logits) a.logits[(size_t)(a.tok0 + tk) * a.f + n] = s;
+      }
+    }
+  }
+  __syncthreads();
+  const int words = a.f >> 6;
+  for (int tk = wave; tk < a.nt; tk += 8) {
+    const unsigned long long word = __ballot(bits[tk][lane] != 0);
+    if (lane == 0) {
+      a.mask[(size_t)(a.tok0 + tk) * words + blockIdx.x] = (uint64_t)word;
+      wsh[tk] = word;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t u = a.first_pass ? 0ull : a.union_mask[blockIdx.x];
+    for (int t = 0; t < a.nt; ++t) u |= wsh[t];
+    a.union_mask[blockIdx.x] = u;
+  }
+}
+
+// ---- host side ---------------------------------------------------------------
+
+bool pred_uses_mfma(const PredLaunch& p) { return p.wt == WT_F16 && p.batch >= kPredMfmaMinBatch; }
+
+// The residual chain's layer input first (x = r / rms(r), written to x_out),
+// then stage 1 on it.
+hipError_t launch_pred1_mfma(const PredLaunch& p, hipStream_t s) {
+  const void* x = p.x;
+  if (p.norm.r_in) {
+    const hipError_t e = launch_residual_rmsnorm(p.norm.r_in, nullptr, nullptr, p.batch, p.d, p.norm.eps,
+                                                 p.norm.x_out, WT_F16, s);
+    if (e != hipSuccess) return e;
+    x = p.norm.x_out;
+  }
+  Pred1MfmaArgs a;
+  a.w1_t = (const f16*)p.w1_t;
+  a.x = (const f16*)x;
+  a.z = p.z;
+  a.d = p.d;
+  a.r = p.r;
+  const dim3 grid((p.r + 15) / 16);
+  for (int tok0 = 0; tok0 < p.batch; tok0 += 32) {
+    a.tok0 = tok0;
+    a.nt = p.batch - tok0 < 32 ? p.batch - tok0 : 32;
+    if (a.nt > 16)
+      hipLaunchKernelGGL(k_pred1_mfma<2>, grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_pred1_mfma<1>, grid, dim3(512), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pred2_mfma(const PredLaunch& p, hipStream_t s) {
+  Pred2MfmaArgs a;
+  a.w2_t = (const f16*)p.w2_t;
+  a.z = p.z;
+  a.tau = p.tau;
+  a.mask = p.mask;
+  a.union_mask = p.union_mask;
+  a.logits = p.logits;
+  a.f = p.f;
+  a.r = p.r;
+  const dim3 grid(p.f / 64);
+  for (int tok0 = 0; tok0 < p.batch; tok0 += 32) {
+    a.tok0 = tok0;
+    a.nt = p.batch - tok0 < 32 ? p.batch - tok0 : 32;
+    a.first_pass = tok0 == 0 ? 1 : 0;
+    if (a.nt > 16)
+      hipLaunchKernelGGL(k_pred2_mfma<2>, grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL(k_pred2_mfma<1>, grid, dim3(512), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sfnn

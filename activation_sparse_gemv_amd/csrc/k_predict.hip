@@ -159,6 +159,10 @@ static void pred2_dispatch(const PredLaunch& p, hipStream_t s) {
 }
 
 hipError_t launch_predict(const PredLaunch& p, hipStream_t s) {
+  if (pred_uses_mfma(p)) {
+    const hipError_t e = launch_pred1_mfma(p, s);
+    return e != hipSuccess ? e : launch_pred2_mfma(p, s);
+  }
   if (p.wt == WT_F32) {
     pred1_dispatch<WT_F32>(p, s);
     pred2_dispatch<WT_F32>(p, s);
@@ -170,6 +174,7 @@ hipError_t launch_predict(const PredLaunch& p, hipStream_t s) {
 }
 
 hipError_t launch_predict_stage1(const PredLaunch& p, hipStream_t s) {
+  if (pred_uses_mfma(p)) return launch_pred1_mfma(p, s);
   if (p.wt == WT_F32)
     pred1_dispatch<WT_F32>(p, s);
   else
@@ -178,6 +183,7 @@ hipError_t launch_predict_stage1(const PredLaunch& p, hipStream_t s) {
 }
 
 hipError_t launch_predict_stage2(const PredLaunch& p, hipStream_t s) {
+  if (pred_uses_mfma(p)) return launch_pred2_mfma(p, s);
   if (p.wt == WT_F32)
     pred2_dispatch<WT_F32>(p, s);
   else

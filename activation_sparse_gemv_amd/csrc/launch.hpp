@@ -65,21 +65,31 @@ struct FfnLaunch {
   float* y;               // [B][d] or null
   const float* r_in;      // residual add: r_out = r_in + y (both null to skip)
   float* r_out;
-  void* hbuf = nullptr;   // matrix-core path: h workspace [2][32][f] fp16 (null: path off)
+  void* hbuf = nullptr;   // matrix-core path: h of one 32-token pass, 128 f bytes: fp16 [2][32][f]
+                          // (hi, lo planes), fp32 [32][f] for INT4 (null: path off)
   int32_t* sidbuf = nullptr;  // matrix-core path: slot ids [f]
   int mfma_min_batch = 0;     // matrix-core path from this batch on (0: default, < 0: never)
 };
 hipError_t launch_ffn(const FfnLaunch& p, hipStream_t s);
 
-// Batches at or above this size run the fp16 FFN on the matrix cores
-// (k_up_mfma + k_down_mfma + k_sum) unless the descriptor says otherwise.
+// Batches at or above this size run the fp16 and INT4 FFNs on the matrix
+// cores (k_up_mfma + k_down_mfma, or their INT4 forms, + k_sum) unless the
+// descriptor says otherwise.
 constexpr int kMfmaMinBatchDefault = 8;
 bool ffn_uses_mfma(const FfnLaunch& p);
 int mfma_groups(int d, int max_groups);  // partial rows per token on that path
 hipError_t launch_ffn_mfma(const FfnLaunch& p, hipStream_t s);
+// INT4 passes of that path (h in the workspace as fp32 [32][f]).
+void mfma_all_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int kg, hipStream_t s);
 int ffn_groups(int d, int f);
 // The fixed-order sum of an FFN's partials alone (y and / or the residual add).
 hipError_t launch_sum(const FfnLaunch& p, hipStream_t s);
+// Batches at or above this size run the fp16 predictor on the matrix cores
+// (k_pred1_mfma + k_pred2_mfma, up to 32 tokens per pass).
+constexpr int kPredMfmaMinBatch = 8;
+bool pred_uses_mfma(const PredLaunch& p);
+hipError_t launch_pred1_mfma(const PredLaunch& p, hipStream_t s);  // residual chain: RMSNorm launch first
+hipError_t launch_pred2_mfma(const PredLaunch& p, hipStream_t s);
 // Predictor stages on their own (the look-ahead stack runs them apart).
 hipError_t launch_predict_stage1(const PredLaunch& p, hipStream_t s);
 hipError_t launch_predict_stage2(const PredLaunch& p, hipStream_t s);

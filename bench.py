@@ -399,9 +399,13 @@ def _sweep(args, spec):
             t_sp, t_de = t_sparse(), t_dense()
             t_ly = timed(lambda: [sg.sfnn_layer(pred, ffn, x[l], B, y, masks[l], ids[l], cnt[l:l + 1], ws)
                                   for l, (pred, ffn) in enumerate(layers)])
+            t_pr = timed(lambda: [sg.sfnn_predict(pred, x[l], B, masks[l], None, ws)
+                                  for l, (pred, _) in enumerate(layers)])
+            pbytes = (d * r + r * f) * (4 if spec.pred_dtype == "f32" else 2) + 4 * f
             act_bytes = u * nmat * d * wb
             pt = {"rho": rho, "batch": B, "union_frac": round(u / f, 4),
                   "us_sparse_ffn": round(t_sp, 2), "us_layer": round(t_ly, 2), "us_dense_ffn": round(t_de, 2),
+                  "us_predict": round(t_pr, 2), "GBps_predict": round(pbytes / t_pr / 1e3, 1),
                   "speedup_ffn": round(t_de / t_sp, 2), "speedup_layer_vs_dense_ffn": round(t_de / t_ly, 2),
                   "GBps_sparse_ffn": round(act_bytes / t_sp / 1e3, 1),
                   "GBps_dense_ffn": round(f * nmat * d * wb / t_de / 1e3, 1)}
