@@ -9,13 +9,16 @@ namespace sfnn {
 // (53ai.com sparsity survey, PowerInfer one-layer example 单层计算优化: only the
 // predicted set {3, 4, 5} is computed).  One workgroup: every thread owns one
 // mask word, a popcount + workgroup prefix sum gives each word its output
-// offset, and bits are emitted lowest first, so ids come out in ascending
-// order with no sort.
+// offset; then each wavefront emits whole words, one bit per lane at the
+// word's offset plus the number of set bits below the lane, so every word's
+// ids go out as one coalesced store, in ascending order with no sort.
 __global__ __launch_bounds__(1024) void k_compact(const uint64_t* __restrict__ mask, int batch, int words,
                                                   int32_t* __restrict__ ids, int32_t* __restrict__ count,
                                                   uint64_t* __restrict__ union_mask) {
   // words <= 1024 (d_ff <= 65536): thread w owns mask word w
   __shared__ int wsum[16];
+  __shared__ uint64_t su[1024];
+  __shared__ int so[1024];
   const int w = threadIdx.x;
   const int lane = w & (kWave - 1), wave = w / kWave;
   uint64_t u = 0;
@@ -31,16 +34,17 @@ __global__ __launch_bounds__(1024) void k_compact(const uint64_t* __restrict__ m
     if (lane < nw) wsum[lane] = s;
   }
   __syncthreads();
-  int off = v - local + (wave > 0 ? wsum[wave - 1] : 0);
-  if (w < words) {
-    if (union_mask) union_mask[w] = u;
-    while (u) {
-      const int bit = __builtin_ctzll(u);
-      ids[off++] = w * 64 + bit;
-      u &= u - 1;
-    }
+  const int off = v - local + (wave > 0 ? wsum[wave - 1] : 0);
+  su[w] = u;
+  so[w] = off;
+  if (w < words && union_mask) union_mask[w] = u;
+  if (w == blockDim.x - 1) *count = off + local;
+  __syncthreads();
+  const int nwaves = blockDim.x / kWave;
+  for (int j = wave; j < words; j += nwaves) {
+    const uint64_t m = su[j];
+    if ((m >> lane) & 1ull) ids[so[j] + bits_below_lane(m)] = j * 64 + lane;
   }
-  if (w == blockDim.x - 1) *count = off;
 }
 
 // counts[i] += number of masks with bit i set (offline hot/cold profiling).
