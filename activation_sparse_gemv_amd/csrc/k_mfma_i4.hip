@@ -11,8 +11,8 @@
 //                 128-wide scale groups (group w, w + 8, ...).  Per group and
 //                 16x16 block: four v_mfma_f32_16x16x32_f16 on the group's
 //                 nibbles (lane l takes the 32 nibbles 32 (l / 16) .. + 31 of
-//                 row l % 16, one 16-byte load) and the token values in the
-//                 same pairing order, then acc += s_row * (that sum), with the
+//                 row l % 16, one 16-byte load) and the token values, then
+//                 acc += s_row * (that sum), with the
 //                 workgroup's scales staged in LDS.  Blocks added in wavefront
 //                 order; bias, activation and per-token select give h [token]
 //                 [slot] in fp32.
@@ -62,20 +62,18 @@ __device__ __forceinline__ int slot_count_i4(const int32_t* count, int f) {
   return c < 0 ? 0 : (c > f ? f : c);
 }
 
-// (x0x1, x2x3, x4x5, x6x7) -> (x0x4, x1x5, x2x6, x3x7): the order int4_pairs
-// gives a dword's nibbles in
-__device__ __forceinline__ u32x4 pair_order(const u32x4 a) {
-  u32x4 o;
-  o.x = __builtin_amdgcn_perm(a.z, a.x, 0x05040100u);
-  o.y = __builtin_amdgcn_perm(a.z, a.x, 0x07060302u);
-  o.z = __builtin_amdgcn_perm(a.w, a.y, 0x05040100u);
-  o.w = __builtin_amdgcn_perm(a.w, a.y, 0x07060302u);
-  return o;
-}
-
+// The 8 nibbles of a dword (element j in bits 4j .. 4j + 3, two's
+// complement) as fp16 integers in element order, two per dword: (t ^ 8) is t
+// + 8 in offset binary, fp16 0x6400 | n is 1024 + n, and 1032 is taken off.
 __device__ __forceinline__ u32x4 nib8(uint32_t u) {
+  const uint32_t v = u ^ 0x88888888u;
+  const f16x2 bias = {(f16)1032.0f, (f16)1032.0f};
   uint32_t p[4];
-  int4_pairs(u, p);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t lo = (v >> (8 * k)) & 0xFu, hi = (v >> (8 * k + 4)) & 0xFu;
+    p[k] = __builtin_bit_cast(uint32_t, bitcast<f16x2>(lo | (hi << 16) | 0x64006400u) - bias);
+  }
   return u32x4{p[0], p[1], p[2], p[3]};
 }
 
@@ -92,41 +90,45 @@ __global__ __launch_bounds__(512) void k_up_mfma_i4(MfmaUpI4Args a) {
   constexpr int kMaxGroups = 128;                    // d_model <= 16384
   __shared__ f32x4 red[8][2][NB][kWave];             // two row tiles at a time
   __shared__ f16 ssc[NM][kMaxGroups][ROWS];          // scales, group-major
-  __shared__ int s_id[ROWS];
+  __shared__ int s_id[ROWS];   // neuron of each row, -1 for a dropped slot
+  __shared__ int s_idc[ROWS];  // the row actually read (dropped slots: the pad row)
   const int cnt = slot_count_i4(a.count, a.f);
   const int s0 = blockIdx.x * ROWS;
   if (s0 >= cnt) return;  // the whole workgroup
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int r = lane & 15, g = lane >> 4;
   const int d = a.d, G = d >> 7;
-  int pad = 0;
-  if (a.ids) {
-    const int v = a.ids[cnt - 1];
-    pad = v >= 0 && v < a.f ? v : 0;
-  }
   // this lane's rows (one per tile); slots past |U| and ids outside [0, f)
-  // are dropped (h = 0) and re-read the last listed row
+  // are dropped (h = 0) and re-read the last listed row.  All id loads go
+  // out together (slots past |U| re-read the last one).
+  int raw[RT + 1];
+#pragma unroll
+  for (int t = 0; t <= RT; ++t) {
+    const int s = t < RT ? s0 + t * 16 + r : cnt - 1;
+    const int sc = s < cnt ? s : cnt - 1;
+    raw[t] = a.ids ? a.ids[sc] : sc;
+  }
+  const int pad = raw[RT] >= 0 && raw[RT] < a.f ? raw[RT] : 0;
   const uint8_t* wr[NM][RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const int s = s0 + t * 16 + r;
-    int id = s < cnt ? (a.ids ? a.ids[s] : s) : -1;
+    int id = s < cnt ? raw[t] : -1;
     if (id >= a.f) id = -1;
     const int idc = id < 0 ? pad : id;
     if (wave == 0 && g == 0) {
       s_id[t * 16 + r] = id;
+      s_idc[t * 16 + r] = idc;
       a.sid[s] = idc;
     }
     wr[0][t] = a.q_up + (size_t)idc * (d >> 1) + 16 * g;
     if constexpr (NM == 2) wr[1][t] = a.q_gate + (size_t)idc * (d >> 1) + 16 * g;
   }
   const f16* xr[NB];
-  bool xok[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int tk = nb * 16 + r;
-    xok[nb] = tk < a.nt;
-    xr[nb] = a.x + (size_t)(a.tok0 + (xok[nb] ? tk : 0)) * d + 32 * g;
+    xr[nb] = a.x + (size_t)(a.tok0 + (tk < a.nt ? tk : 0)) * d + 32 * g;
   }
   auto issue = [&](UpI4Frag<NM, RT, NB>& F, int grp) {
 #pragma unroll
@@ -143,16 +145,31 @@ __global__ __launch_bounds__(512) void k_up_mfma_i4(MfmaUpI4Args a) {
   const int iters = wave < G ? (G - wave + 7) >> 3 : 0;
   UpI4Frag<NM, RT, NB> A, Bf;
   if (iters > 0) issue(A, wave);
+  __syncthreads();  // s_idc
   {
+    // every scale load goes out before the first LDS store (one round trip):
+    // NM * ROWS * G <= 8192 values, at most 16 per thread; indices past the
+    // end re-read the last value
+    constexpr int kPer = NM * ROWS * kMaxGroups / 512;
     const int n = NM * ROWS * G;
-    for (int i = threadIdx.x; i < n; i += 512) {
+    f16 sv[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i0 = threadIdx.x + 512 * j;
+      const int i = i0 < n ? i0 : n - 1;
       const int m = i / (ROWS * G), rem = i - m * ROWS * G;
       const int row = rem / G, grp = rem - row * G;
-      const int s = s0 + row;
-      int id = s < cnt ? (a.ids ? a.ids[s] : s) : pad;
-      if (id < 0 || id >= a.f) id = pad;
       const f16* sp = m == 0 ? a.s_up : a.s_gate;
-      ssc[m][grp][row] = sp[(size_t)id * G + grp];
+      sv[j] = sp[(size_t)s_idc[row] * G + grp];
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = threadIdx.x + 512 * j;
+      if (i < n) {
+        const int m = i / (ROWS * G), rem = i - m * ROWS * G;
+        const int row = rem / G, grp = rem - row * G;
+        ssc[m][grp][row] = sv[j];
+      }
     }
   }
   __syncthreads();
@@ -165,13 +182,8 @@ __global__ __launch_bounds__(512) void k_up_mfma_i4(MfmaUpI4Args a) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[m][t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // tokens past the pass multiply token 0's values; their h is set to zero
   auto mul = [&](const UpI4Frag<NM, RT, NB>& F, int grp) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 xv[NB][4];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) xv[nb][s] = xok[nb] ? pair_order(F.x[nb][s]) : zero;
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -185,7 +197,7 @@ __global__ __launch_bounds__(512) void k_up_mfma_i4(MfmaUpI4Args a) {
         for (int nb = 0; nb < NB; ++nb) {
           f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < 4; ++s) p = mfma_16x16x32(qa[s], xv[nb][s], p);
+          for (int s = 0; s < 4; ++s) p = mfma_16x16x32(qa[s], F.x[nb][s], p);
           acc[m][t][nb].x = __builtin_fmaf(sv.x, p.x, acc[m][t][nb].x);
           acc[m][t][nb].y = __builtin_fmaf(sv.y, p.y, acc[m][t][nb].y);
           acc[m][t][nb].z = __builtin_fmaf(sv.z, p.z, acc[m][t][nb].z);

@@ -8,8 +8,8 @@
 // here one pass covers up to 32 tokens with v_mfma_f32_16x16x32_f16, fp32
 // accumulation.
 //
-//  k_pred1_mfma  workgroup = 16 rows of W1^T; its 8 wavefronts split d_model
-//                into 64-column pairs (pair w, w + 8, ...), each holding a
+//  k_pred1_mfma  workgroup = 16 rows of W1^T; its 16 wavefronts split d_model
+//                into 64-column pairs (pair w, w + 16, ...), each holding a
 //                16x16 fp32 block per 16 tokens; the blocks are added in
 //                wavefront order in LDS and written as z [B][r] fp32.
 //  k_pred2_mfma  workgroup = 64 neurons (one mask word, four 16-row tiles) x
@@ -27,6 +27,11 @@
 #include "launch.hpp"
 
 namespace sfnn {
+
+// Stage 1 has only r / 16 workgroups, so each runs 16 wavefronts; both stages
+// keep kPredBatch iterations of loads in flight per wavefront.
+constexpr int kPred1Waves = 16;
+constexpr int kPredBatch = 4;
 
 struct Pred1MfmaArgs {
   const f16* w1_t;  // [r][d]
@@ -52,8 +57,8 @@ struct P1Frag {
 };
 
 template <int NB>
-__global__ __launch_bounds__(512) void k_pred1_mfma(Pred1MfmaArgs a) {
-  __shared__ f32x4 red[8][NB][kWave];
+__global__ __launch_bounds__(1024) void k_pred1_mfma(Pred1MfmaArgs a) {
+  __shared__ f32x4 red[kPred1Waves][NB][kWave];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int rr = lane & 15, g = lane >> 4;
   const int d = a.d;
@@ -88,24 +93,19 @@ __global__ __launch_bounds__(512) void k_pred1_mfma(Pred1MfmaArgs a) {
       for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_16x16x32(F.w[s], xok[nb] ? F.x[nb][s] : zero, acc[nb]);
   };
 
-  // pairs wave, wave + 8, ...; two fragment sets in flight; every request is
-  // unconditional (the last one re-reads the current pair)
+  // pairs wave, wave + W, ... in batches of kPredBatch: every batch's loads
+  // go out before any of its products (a pair past the last re-reads the last)
+  constexpr int W = kPred1Waves;
   const int npair = d >> 6;
-  const int iters = wave < npair ? (npair - wave + 7) >> 3 : 0;
-  if (iters > 0) {
-    P1Frag<NB> A, Bf;
-    issue(A, wave);
-    for (int it = 0; it < iters; it += 2) {
-      const int pa = wave + 8 * it;
-      const int pb = it + 1 < iters ? pa + 8 : pa;
-      issue(Bf, pb);
-      __builtin_amdgcn_sched_barrier(0);
-      mul(A);
-      if (it + 1 >= iters) break;
-      issue(A, it + 2 < iters ? pb + 8 : pb);
-      __builtin_amdgcn_sched_barrier(0);
-      mul(Bf);
-    }
+  const int iters = wave < npair ? (npair - wave + W - 1) / W : 0;
+  for (int b0 = 0; b0 < iters; b0 += kPredBatch) {
+    P1Frag<NB> F[kPredBatch];
+#pragma unroll
+    for (int j = 0; j < kPredBatch; ++j) issue(F[j], wave + W * (b0 + j < iters ? b0 + j : iters - 1));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kPredBatch; ++j)
+      if (b0 + j < iters) mul(F[j]);
   }
 
 #pragma unroll
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(512) void k_pred1_mfma(Pred1MfmaArgs a) {
     const float* rf = reinterpret_cast<const float*>(&red[0][0][0]);
     float s = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) s += rf[w * E + e];
+    for (int w = 0; w < kPred1Waves; ++w) s += rf[w * E + e];
     const int q = e & 3, ln = (e >> 2) & (kWave - 1), nb = e >> 8;
     const int orow = blockIdx.x * 16 + 4 * (ln >> 4) + q;
     const int tk = nb * 16 + (ln & 15);
@@ -146,6 +146,17 @@ __global__ __launch_bounds__(512) void k_pred2_mfma(Pred2MfmaArgs a) {
   bool zok[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) zok[nb] = nb * 16 + rr < a.nt;
+  // thresholds of the logits this thread sums after the reduction (tile pair
+  // tp, e-slot k), fetched now so that no load waits at the end
+  float tv[2][NB];
+#pragma unroll
+  for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int e = threadIdx.x + 512 * k;
+      const int q = e & 3, ln = (e >> 2) & (kWave - 1), i = e / (256 * NB);
+      tv[tp][k] = a.tau[n0 + (2 * tp + i) * 16 + 4 * (ln >> 4) + q];
+    }
   f32x4 acc[4][NB];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -190,23 +201,18 @@ __global__ __launch_bounds__(512) void k_pred2_mfma(Pred2MfmaArgs a) {
     }
   };
 
+  // steps wave, wave + 8, ... in batches of kPredBatch: every batch's loads go
+  // out before any of its products (a step past the last re-reads the last)
   const int nks = (r + 31) >> 5;
   const int iters = wave < nks ? (nks - wave + 7) >> 3 : 0;
-  if (iters > 0) {
-    Raw A, Bf;
-    issue(A, wave);
-    for (int it = 0; it < iters; it += 2) {
-      const int ka = wave + 8 * it;
-      const int kb = it + 1 < iters ? ka + 8 : ka;
-      issue(Bf, kb);
-      __builtin_amdgcn_sched_barrier(0);
-      mul(A, ka);
-      if (it + 1 >= iters) break;
-      const int kc = it + 2 < iters ? kb + 8 : kb;
-      issue(A, kc);
-      __builtin_amdgcn_sched_barrier(0);
-      mul(Bf, kb);
-    }
+  for (int b0 = 0; b0 < iters; b0 += kPredBatch) {
+    Raw R[kPredBatch];
+#pragma unroll
+    for (int j = 0; j < kPredBatch; ++j) issue(R[j], wave + 8 * (b0 + j < iters ? b0 + j : iters - 1));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kPredBatch; ++j)
+      if (b0 + j < iters) mul(R[j], wave + 8 * (b0 + j));
   }
 
   // add the 8 wavefronts' blocks in order, two row tiles at a time; thread
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(512) void k_pred2_mfma(Pred2MfmaArgs a) {
       const int tk = nb * 16 + (ln & 15);
       if (tk < a.nt) {
         const int n = n0 + nrow;
-        bits[tk][nrow] = s > a.tau[n] ? 1 : 0;
+        bits[tk][nrow] = s > tv[tp][k] ? 1 : 0;
         if (a.logits) a.logits[(size_t)(a.tok0 + tk) * a.f + n] = s;
       }
     }
@@ -279,9 +285,9 @@ hipError_t launch_pred1_mfma(const PredLaunch& p, hipStream_t s) {
     a.tok0 = tok0;
     a.nt = p.batch - tok0 < 32 ? p.batch - tok0 : 32;
     if (a.nt > 16)
-      hipLaunchKernelGGL(k_pred1_mfma<2>, grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL(k_pred1_mfma<2>, grid, dim3(64 * kPred1Waves), 0, s, a);
     else
-      hipLaunchKernelGGL(k_pred1_mfma<1>, grid, dim3(512), 0, s, a);
+      hipLaunchKernelGGL(k_pred1_mfma<1>, grid, dim3(64 * kPred1Waves), 0, s, a);
   }
   return hipGetLastError();
 }
