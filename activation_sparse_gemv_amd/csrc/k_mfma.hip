@@ -293,8 +293,7 @@ __global__ __launch_bounds__(512) void k_down_mfma(MfmaDownArgs a) {
   constexpr int WC = 16 * CPL;  // columns per workgroup
   __shared__ f32x4 red[8][2][NB][kWave];
   const int cnt = slot_count(a.count, a.f);
-  const int CS = a.d / WC;
-  const int cs = blockIdx.x % CS, kg = blockIdx.x / CS;
+  const int cs = blockIdx.x / a.KG, kg = blockIdx.x % a.KG;  // slot group b % KG: one XCD's slots, see mfma_groups
   const int nsteps = (cnt + 31) >> 5;
   const int spg = (nsteps + a.KG - 1) / a.KG;
   const int st0 = kg * spg;
@@ -370,17 +369,22 @@ __global__ __launch_bounds__(512) void k_down_mfma(MfmaDownArgs a) {
 // ---- host side ---------------------------------------------------------------
 
 bool ffn_uses_mfma(const FfnLaunch& p) {
-  const int thr = p.mfma_min_batch == 0 ? kMfmaMinBatchDefault : p.mfma_min_batch;
+  const int def = p.wt == WT_I4 ? kMfmaMinBatchI4Default : kMfmaMinBatchDefault;
+  const int thr = p.mfma_min_batch == 0 ? def : p.mfma_min_batch;
   return thr > 0 && p.batch >= thr && (p.wt == WT_F16 || p.wt == WT_I4) && p.hbuf != nullptr &&
          p.sidbuf != nullptr;
 }
 
-// Slot groups of the down projection: enough workgroups of 128 columns x
-// group to cover the chip once (two token tiles use 64-column workgroups,
-// twice as many).  One count for every pass of a call, as k_sum adds them.
+// Slot groups of the down projection.  Every column workgroup re-reads h of
+// its slot group, and workgroup b runs on XCD b % 8, so the count is a
+// multiple of 8 and block b takes slot group b % KG: each XCD then works on
+// its own eighth (or sixteenth ...) of the slots, whose h stays in that XCD's
+// L2 instead of streaming the whole h from the Infinity Cache once per column
+// workgroup.  About 256 workgroups of 128 columns; one count for every pass
+// of a call, as k_sum adds them.
 int mfma_groups(int d, int max_groups) {
   const int cs = d / 128;
-  int kg = (256 + cs - 1) / cs;
+  int kg = 8 * ((32 + cs - 1) / cs);
   if (kg > max_groups) kg = max_groups;  // the partial buffer holds max_groups rows per token
   if (kg < 1) kg = 1;
   return kg;

@@ -22,12 +22,16 @@
 //                 its rows' scales (fp32), splits the product into two fp16
 //                 planes (22 bits), and multiplies them with the nibbles of 8
 //                 consecutive columns per lane (4 bytes per row), regrouped
-//                 per column with byte permutes.  One fp32 partial row per
-//                 slot group and token, added in a fixed order by k_sum.
+//                 per column with byte permutes.  The row ids and this column
+//                 group's scales of up to 8192 slots at a time are staged in
+//                 LDS, so a wavefront issues the row loads of several steps
+//                 back to back.  One fp32 partial row per slot group and
+//                 token, added in a fixed order by k_sum.
 //
 // Workgroups of neighbouring column groups read the two 64-byte halves of the
-// same 128-byte lines; they are paired onto one XCD (blocks b and b + 8 of a
-// 16-block run share an XCD), so a line's second half meets it in that L2.
+// same 128-byte lines; with the slot group as the fast block index they run
+// on one XCD (blocks b and b + KG), so a line's second half meets it in that
+// L2.
 #include "ffn_body.hpp"
 #include "launch.hpp"
 
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(512) void k_up_mfma_i4(MfmaUpI4Args a) {
     if (wave == 0 && g == 0) {
       s_id[t * 16 + r] = id;
       s_idc[t * 16 + r] = idc;
-      a.sid[s] = idc;
+      if (s < a.f) a.sid[s] = idc;  // the last workgroup's rows may run past d_ff
     }
     wr[0][t] = a.q_up + (size_t)idc * (d >> 1) + 16 * g;
     if constexpr (NM == 2) wr[1][t] = a.q_gate + (size_t)idc * (d >> 1) + 16 * g;
@@ -268,37 +272,40 @@ __global__ __launch_bounds__(512) void k_up_mfma_i4(MfmaUpI4Args a) {
           if (!((wv >> (id & 63)) & 1ull)) hv = 0.0f;  // select: gated-off neurons add nothing
         }
       }
-      a.h[(size_t)tk * a.f + s0 + row] = hv;
+      if (s0 + row < a.f) a.h[(size_t)tk * a.f + s0 + row] = hv;
     }
   }
 }
 
+// Slots per LDS chunk of the down projection: their row ids and this column
+// group's scales (48 KB).
+constexpr int kDownChunk = 8192;
+
+// Steps of loads a wavefront issues before multiplying (registers allow four
+// with one token tile, three with two).
+template <int NB>
+constexpr int down_i4_batch() { return NB == 1 ? 4 : 3; }
+
 // One 32-slot step of the down projection for this lane: its 8 rows (K
-// block), 8 consecutive columns of each (one dword of nibbles), the rows'
-// scales of this column group, and h of its tokens over the 8 slots.
+// block), 8 consecutive columns of each (one dword of nibbles), and h of its
+// tokens over the 8 slots.
 template <int NB>
 struct DownI4Frag {
   uint32_t w[8];
-  f16 s[8];
   f32x4 h[NB][2];
 };
 
-__device__ __forceinline__ void down_ids_i4(const MfmaDownI4Args& a, int st, int g, int (&id)[8]) {
-  const int base = st * 32 + 8 * g;  // sid holds every slot below |U| rounded up to 32
-  const u32x4 v0 = ld16(a.sid + base), v1 = ld16(a.sid + base + 4);
-  id[0] = (int)v0.x; id[1] = (int)v0.y; id[2] = (int)v0.z; id[3] = (int)v0.w;
-  id[4] = (int)v1.x; id[5] = (int)v1.y; id[6] = (int)v1.z; id[7] = (int)v1.w;
-}
-
+// Loads of step st; lid holds the chunk's row ids (slot c0 * 32 onwards).
 template <int NB>
-__device__ __forceinline__ void down_issue_i4(DownI4Frag<NB>& F, const MfmaDownI4Args& a, const int (&id)[8],
-                                              int cs, int boff, const float* (&hr)[NB], int st) {
-  const int G = a.d >> 7;
+__device__ __forceinline__ void down_issue_i4(DownI4Frag<NB>& F, const MfmaDownI4Args& a, const int* lid, int c0,
+                                              int boff, const float* (&hr)[NB], int st, int g) {
+  const int* ip = lid + (st - c0) * 32 + 8 * g;
+  const int4 i0 = *reinterpret_cast<const int4*>(ip);
+  const int4 i1 = *reinterpret_cast<const int4*>(ip + 4);
+  const int id[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+  for (int e = 0; e < 8; ++e)
     F.w[e] = *reinterpret_cast<const uint32_t*>(a.q_down_t + (size_t)id[e] * (a.d >> 1) + boff);
-    F.s[e] = a.s_down_t[(size_t)id[e] * G + cs];
-  }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     F.h[nb][0] = *reinterpret_cast<const f32x4*>(hr[nb] + st * 32);
@@ -306,16 +313,20 @@ __device__ __forceinline__ void down_issue_i4(DownI4Frag<NB>& F, const MfmaDownI
   }
 }
 
+// sc: the 8 rows' scales of this column group (LDS).
 template <int NB>
-__device__ __forceinline__ void down_mul_i4(const DownI4Frag<NB>& F, f32x4 (&acc)[8][NB]) {
+__device__ __forceinline__ void down_mul_i4(const DownI4Frag<NB>& F, const f16* sc, f32x4 (&acc)[8][NB]) {
+  const u32x4 sraw = *reinterpret_cast<const u32x4*>(sc);
+  const f16x2 s01 = bitcast<f16x2>(sraw.x), s23 = bitcast<f16x2>(sraw.y);
+  const f16x2 s45 = bitcast<f16x2>(sraw.z), s67 = bitcast<f16x2>(sraw.w);
   // A operands: h of each token tile times its rows' scales, as two fp16 planes
   u32x4 ah[NB], al[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const f32x4 p0 = {F.h[nb][0].x * (float)F.s[0], F.h[nb][0].y * (float)F.s[1], F.h[nb][0].z * (float)F.s[2],
-                      F.h[nb][0].w * (float)F.s[3]};
-    const f32x4 p1 = {F.h[nb][1].x * (float)F.s[4], F.h[nb][1].y * (float)F.s[5], F.h[nb][1].z * (float)F.s[6],
-                      F.h[nb][1].w * (float)F.s[7]};
+    const f32x4 p0 = {F.h[nb][0].x * (float)s01.x, F.h[nb][0].y * (float)s01.y, F.h[nb][0].z * (float)s23.x,
+                      F.h[nb][0].w * (float)s23.y};
+    const f32x4 p1 = {F.h[nb][1].x * (float)s45.x, F.h[nb][1].y * (float)s45.y, F.h[nb][1].z * (float)s67.x,
+                      F.h[nb][1].w * (float)s67.y};
     split_hi_lo(p0, p1, ah[nb], al[nb]);
   }
   // B operands: column i over the 8 rows, nibbles as fp16 integers.  Offset
@@ -325,7 +336,6 @@ __device__ __forceinline__ void down_mul_i4(const DownI4Frag<NB>& F, f32x4 (&acc
 #pragma unroll
   for (int e = 0; e < 8; ++e) v[e] = F.w[e] ^ 0x88888888u;
   const f16x2 bias = {(f16)1032.0f, (f16)1032.0f};
-  u32x4 b[8];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     uint32_t lo[4], hi[4];
@@ -338,34 +348,27 @@ __device__ __forceinline__ void down_mul_i4(const DownI4Frag<NB>& F, f32x4 (&acc
       lo[rp] = __builtin_bit_cast(uint32_t, ql);
       hi[rp] = __builtin_bit_cast(uint32_t, qh);
     }
-    b[2 * k] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    b[2 * k + 1] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
+    const u32x4 b0 = {lo[0], lo[1], lo[2], lo[3]};
+    const u32x4 b1 = {hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      acc[i][nb] = mfma_16x16x32(ah[nb], b[i], acc[i][nb]);
-      acc[i][nb] = mfma_16x16x32(al[nb], b[i], acc[i][nb]);
+      acc[2 * k][nb] = mfma_16x16x32(ah[nb], b0, acc[2 * k][nb]);
+      acc[2 * k][nb] = mfma_16x16x32(al[nb], b0, acc[2 * k][nb]);
+      acc[2 * k + 1][nb] = mfma_16x16x32(ah[nb], b1, acc[2 * k + 1][nb]);
+      acc[2 * k + 1][nb] = mfma_16x16x32(al[nb], b1, acc[2 * k + 1][nb]);
     }
-}
-
-// Column group and slot group of workgroup b: within every full run of 16
-// blocks, blocks j and j + 8 (one XCD) take the column groups 2j' and 2j' + 1.
-__device__ __forceinline__ void down_block_i4(int b, int total, int CS, int& cs, int& kg) {
-  int bb = b;
-  if ((b | 15) < total) bb = (b & ~15) | ((b & 7) << 1) | ((b >> 3) & 1);
-  cs = bb % CS;
-  kg = bb / CS;
+  }
 }
 
 template <int NB>
 __global__ __launch_bounds__(512) void k_down_mfma_i4(MfmaDownI4Args a) {
   __shared__ f32x4 red[8][2][NB][kWave];
+  __shared__ __align__(16) int lid[kDownChunk];  // the chunk's row ids
+  __shared__ __align__(16) f16 lsc[kDownChunk];  // their scales in this column group
   const int cnt = slot_count_i4(a.count, a.f);
-  const int CS = a.d >> 7;
-  int cs, kg;
-  down_block_i4(blockIdx.x, gridDim.x, CS, cs, kg);
+  // slot group b % KG (one XCD's slots, see mfma_groups); neighbouring column
+  // groups b and b + KG share an XCD and the halves of 128-byte lines
+  const int cs = blockIdx.x / a.KG, kg = blockIdx.x % a.KG;
   const int nsteps = (cnt + 31) >> 5;
   const int spg = (nsteps + a.KG - 1) / a.KG;
   const int st0 = kg * spg;
@@ -382,31 +385,48 @@ __global__ __launch_bounds__(512) void k_down_mfma_i4(MfmaDownI4Args a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[i][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // steps st0 + wave, + 8, ...: ids two steps ahead, rows one step ahead;
-  // every request unconditional (the last ones re-read the current step)
-  const int first = st0 + wave;
-  const int iters = first < st1 ? (st1 - first + 7) >> 3 : 0;
-  auto S = [&](int it) { return first + 8 * it; };
-  if (iters > 0) {
-    int idA[8], idB[8];
-    DownI4Frag<NB> A, Bf;
-    down_ids_i4(a, first, g, idA);
-    down_ids_i4(a, iters > 1 ? S(1) : first, g, idB);
-    down_issue_i4(A, a, idA, cs, boff, hr, first);
-    for (int it = 0; it < iters; it += 2) {
-      const int sa = S(it);
-      const int sb = it + 1 < iters ? S(it + 1) : sa;
-      const int sc = it + 2 < iters ? S(it + 2) : sb;
-      down_ids_i4(a, sc, g, idA);
-      down_issue_i4(Bf, a, idB, cs, boff, hr, sb);
+  constexpr int CST = kDownChunk / 32;  // steps per chunk
+  constexpr int PER = kDownChunk / 512;
+  constexpr int NBT = down_i4_batch<NB>();
+  const int G = a.d >> 7;
+  for (int c0 = st0; c0 < st1; c0 += CST) {
+    const int c1 = c0 + CST < st1 ? c0 + CST : st1;
+    const int ns = (c1 - c0) * 32;  // slots of this chunk (sid holds them all)
+    __syncthreads();                // the previous chunk's LDS reads are done
+    {
+      // ids, then their scales: every load of a kind goes out before any use
+      int idv[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = threadIdx.x + 512 * j;
+        idv[j] = a.sid[c0 * 32 + (i < ns ? i : ns - 1)];
+      }
+      f16 sv[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) sv[j] = a.s_down_t[(size_t)idv[j] * G + cs];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = threadIdx.x + 512 * j;
+        if (i < ns) {
+          lid[i] = idv[j];
+          lsc[i] = sv[j];
+        }
+      }
+    }
+    __syncthreads();
+    // steps c0 + wave, + 8, ... in batches of NBT: every batch's loads go out
+    // before any of its products (a step past the last re-reads the last)
+    const int first = c0 + wave;
+    const int iters = first < c1 ? (c1 - first + 7) >> 3 : 0;
+    for (int b0 = 0; b0 < iters; b0 += NBT) {
+      DownI4Frag<NB> F[NBT];
+#pragma unroll
+      for (int j = 0; j < NBT; ++j)
+        down_issue_i4(F[j], a, lid, c0, boff, hr, first + 8 * (b0 + j < iters ? b0 + j : iters - 1), g);
       __builtin_amdgcn_sched_barrier(0);
-      down_mul_i4(A, acc);
-      if (it + 1 >= iters) break;
-      const int sd = it + 3 < iters ? S(it + 3) : sc;
-      down_ids_i4(a, sd, g, idB);
-      down_issue_i4(A, a, idA, cs, boff, hr, sc);
-      __builtin_amdgcn_sched_barrier(0);
-      down_mul_i4(Bf, acc);
+#pragma unroll
+      for (int j = 0; j < NBT; ++j)
+        if (b0 + j < iters) down_mul_i4(F[j], lsc + (first + 8 * (b0 + j) - c0) * 32 + 8 * g, acc);
     }
   }
 
@@ -439,15 +459,17 @@ __global__ __launch_bounds__(512) void k_down_mfma_i4(MfmaDownI4Args a) {
 
 // ---- host side ---------------------------------------------------------------
 
-// Row tiles per up workgroup: 64 rows for ReLU, 32 for ReGLU (two matrices),
-// so each workgroup's token reads stay at most twice its weight bytes.
-template <int ACT>
-constexpr int up_rt_i4() { return ACT == ACT_REGLU ? 2 : 4; }
+// Row tiles per up workgroup.  Every workgroup reads all of the pass's x, so
+// the more rows it takes the less x traffic per weight byte: 128 rows for
+// ReLU and 64 for ReGLU (two matrices) with one token tile, half that with two
+// (registers).
+template <int ACT, int NB>
+constexpr int up_rt_i4() { return (ACT == ACT_REGLU ? 4 : 8) / NB; }
 
 template <int ACT, int NB>
 static void mfma_pass_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int tok0, int nt, int kg,
                          hipStream_t s) {
-  constexpr int RT = up_rt_i4<ACT>();
+  constexpr int RT = up_rt_i4<ACT, NB>();
   MfmaUpI4Args u;
   u.q_up = (const uint8_t*)p.w_up;
   u.q_gate = (const uint8_t*)p.w_gate;

@@ -9,9 +9,11 @@ namespace sfnn {
 // (53ai.com sparsity survey, PowerInfer one-layer example 单层计算优化: only the
 // predicted set {3, 4, 5} is computed).  One workgroup: every thread owns one
 // mask word, a popcount + workgroup prefix sum gives each word its output
-// offset; then each wavefront emits whole words, one bit per lane at the
-// word's offset plus the number of set bits below the lane, so every word's
-// ids go out as one coalesced store, in ascending order with no sort.
+// offset, and ids come out in ascending order with no sort.  Sparse unions
+// (at most 8 set bits per word on average) are emitted by each thread for its
+// own word, lowest bit first; denser ones by whole words per wavefront, one
+// bit per lane at the word's offset plus the set bits below the lane, so each
+// word's ids go out as one coalesced store.
 __global__ __launch_bounds__(1024) void k_compact(const uint64_t* __restrict__ mask, int batch, int words,
                                                   int32_t* __restrict__ ids, int32_t* __restrict__ count,
                                                   uint64_t* __restrict__ union_mask) {
@@ -34,13 +36,24 @@ __global__ __launch_bounds__(1024) void k_compact(const uint64_t* __restrict__ m
     if (lane < nw) wsum[lane] = s;
   }
   __syncthreads();
-  const int off = v - local + (wave > 0 ? wsum[wave - 1] : 0);
+  int off = v - local + (wave > 0 ? wsum[wave - 1] : 0);
+  const int nwaves = blockDim.x / kWave;
+  const int total = wsum[nwaves - 1];
+  if (w < words && union_mask) union_mask[w] = u;
+  if (w == blockDim.x - 1) *count = total;
+  if (total <= 8 * words) {  // uniform over the workgroup
+    if (w < words) {
+      while (u) {
+        ids[off++] = w * 64 + __builtin_ctzll(u);
+        u &= u - 1;
+      }
+    }
+    return;
+  }
   su[w] = u;
   so[w] = off;
-  if (w < words && union_mask) union_mask[w] = u;
-  if (w == blockDim.x - 1) *count = off + local;
   __syncthreads();
-  const int nwaves = blockDim.x / kWave;
+#pragma unroll 4
   for (int j = wave; j < words; j += nwaves) {
     const uint64_t m = su[j];
     if ((m >> lane) & 1ull) ids[so[j] + bits_below_lane(m)] = j * 64 + lane;

@@ -72,10 +72,14 @@ struct FfnLaunch {
 };
 hipError_t launch_ffn(const FfnLaunch& p, hipStream_t s);
 
-// Batches at or above this size run the fp16 and INT4 FFNs on the matrix
+// Batches at or above these sizes run the fp16 and INT4 FFNs on the matrix
 // cores (k_up_mfma + k_down_mfma, or their INT4 forms, + k_sum) unless the
-// descriptor says otherwise.
+// descriptor says otherwise.  The per-row INT4 kernels hold only two tokens
+// per pass at d_model 12288, so from three tokens the matrix cores take half
+// the time (up to two, the stack's fused look-ahead launches keep the per-row
+// kernels); for fp16 the two paths cross near eight.
 constexpr int kMfmaMinBatchDefault = 8;
+constexpr int kMfmaMinBatchI4Default = 3;
 bool ffn_uses_mfma(const FfnLaunch& p);
 int mfma_groups(int d, int max_groups);  // partial rows per token on that path
 hipError_t launch_ffn_mfma(const FfnLaunch& p, hipStream_t s);

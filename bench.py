@@ -409,7 +409,7 @@ def _sweep(args, spec):
                   "speedup_ffn": round(t_de / t_sp, 2), "speedup_layer_vs_dense_ffn": round(t_de / t_ly, 2),
                   "GBps_sparse_ffn": round(act_bytes / t_sp / 1e3, 1),
                   "GBps_dense_ffn": round(f * nmat * d * wb / t_de / 1e3, 1)}
-            if spec.wtype == "f16":
+            if spec.wtype in ("f16", "i4g128"):
                 # both FFN paths at every batch size: per-row kernels and matrix cores
                 for name, thr in (("rows", -1), ("mfma", 1)):
                     for _, ffn in layers:

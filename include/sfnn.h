@@ -65,7 +65,10 @@ typedef enum { SFNN_RELU = 0, SFNN_REGLU = 1 } sfnn_act;
 
 /* Per-layer low-rank predictor.  logit = W2^T (W1^T x); neuron i is predicted
  * active iff logit_i > tau_i (strict).  wtype is SFNN_F32 or SFNN_F16 and
- * must match the activation type of x. */
+ * must match the activation type of x.  An F16 predictor called with 8 or
+ * more tokens runs on the matrix cores (fp32 accumulation, z carried as two
+ * fp16 parts: 22 significant bits, |z| within fp16's range); smaller batches
+ * and F32 predictors take the per-row kernels. */
 typedef struct sfnn_pred {
   int32_t d_model, d_ff, rank;
   int32_t wtype;       /* sfnn_wtype: F32 or F16                         */
@@ -82,14 +85,17 @@ typedef struct sfnn_pred {
  * Batch-aware dispatch (sparse, dense, layer and stack calls).  Gathering
  * rows is the pages' per-row kernel (PowerInfer's neuron-aware operators,
  * [53ai] GPU-CPU混合执行); once a batch has many tokens the work over the union
- * of active rows is a dense contraction.  An F16 FFN called with batch >=
- * mfma_min_batch (0 selects the default, 8; a negative value never) runs it on
- * the matrix cores: the up projection over the gathered rows and the down
- * projection over column slices, fp32 accumulation, h carried between them as
- * two fp16 parts (22 significant bits; |h| must lie within fp16's range), the
- * partial rows added in a fixed order (deterministic, no atomics).  Smaller
- * batches, F32 and I4G128 weights take the per-row kernels.  The field is
- * read per call, like the rest of the descriptor. */
+ * of active rows is a dense contraction.  An F16 or I4G128 FFN called with
+ * batch >= mfma_min_batch (0 selects the default: 8 for F16, 3 for I4G128,
+ * whose per-row kernels hold only a few tokens per pass; a negative value
+ * never) runs it on the matrix cores: the up projection over the gathered
+ * rows and the down projection over column slices, fp32 accumulation, h
+ * carried between them as two fp16 parts (22 significant bits; |h| must lie
+ * within fp16's range), the partial rows added in a fixed order
+ * (deterministic, no atomics).  I4G128 nibbles enter as exact fp16 integers
+ * and the group scales are applied in fp32, so no weight is rounded.  Smaller
+ * batches and F32 weights take the per-row kernels.  The field is read per
+ * call, like the rest of the descriptor. */
 typedef struct sfnn_ffn {
   int32_t d_model, d_ff;
   int32_t wtype;       /* sfnn_wtype                                     */
