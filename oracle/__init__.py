@@ -20,4 +20,5 @@ from .ffn import (  # noqa: F401
     hot_first_perm,
     permute_layer_ids,
     residual_rmsnorm,
+    input_sparse_gemv,
 )

@@ -16,6 +16,9 @@ Pages cited (by title and section):
   example, INT4 paragraph.
 * [ciyun] the ciyundata.com survey "LLM inference optimisation techniques",
   section 2.2 量化 (weight-only quantisation dequantised inside the kernel).
+* [53ai] section "第二阶段——插入新的ReLU" (relufication stage 2: a ReLU after
+  the normalisation layer makes the inputs of the up and QKV projections
+  sparse).
 
 Readings of points the pages leave open (each also listed in the design notes):
 
@@ -39,7 +42,7 @@ import numpy as np
 __all__ = [
     "unpack_mask", "pack_mask", "predict", "guard_band", "compact", "dequant_int4",
     "rows_f64", "masked_ffn", "dense_ffn", "true_active", "fire_counts",
-    "hot_first_perm", "permute_layer_ids", "residual_rmsnorm",
+    "hot_first_perm", "permute_layer_ids", "residual_rmsnorm", "input_sparse_gemv",
 ]
 
 _U24 = 2.0 ** -24
@@ -256,3 +259,33 @@ def residual_rmsnorm(r, y, eps: float = 1e-6):
     r2 = np.atleast_2d(np.asarray(r, dtype=np.float64)) + np.atleast_2d(np.asarray(y, dtype=np.float64))
     ms = np.mean(r2 * r2, axis=1, keepdims=True)
     return r2, r2 / np.sqrt(ms + eps)
+
+
+# ---------------------------------------------------------------------------
+# input-sparse GEMV ([53ai] 第二阶段——插入新的ReLU)
+# ---------------------------------------------------------------------------
+
+def input_sparse_gemv(w_t, x, bias=None, return_f64: bool = False):
+    """y = bias + W x for a batch of inputs with many zero entries, reading only
+    the columns of W whose input is nonzero for some token of the batch.
+
+    The relufication page's stage 2 puts a ReLU after the normalisation layer,
+    so the inputs of the following projections (FFN up projection, attention
+    QKV) are sparse and their zero entries select columns that contribute
+    nothing.  W is stored input-major: w_t [n_in][n_out], row j is the column of
+    W that input j multiplies.  J = the ascending indices j with x_b[j] != 0 for
+    some token b (a -0.0 counts as zero, a NaN as nonzero); every token sums over
+    J in ascending order:  y_b = bias + sum_{j in J} x_b[j] * w_t[j, :].
+    A token's own zero entries in J add exact zeros, so y_b equals the dense
+    product.  Returns (y [B][n_out] fp32, or fp64, and J as int64)."""
+    x = np.asarray(x)
+    w_t = np.asarray(w_t)
+    J = np.flatnonzero(np.any(x != 0, axis=0))
+    xb = x.astype(np.float64)
+    y = np.zeros((x.shape[0], w_t.shape[1]), dtype=np.float64)
+    if bias is not None:
+        y += np.asarray(bias, dtype=np.float64)[None, :]
+    for j in J:  # only the listed rows of w_t are read
+        y += xb[:, j:j + 1] * w_t[j].astype(np.float64)[None, :]
+    return (y if return_f64 else y.astype(np.float32)), J
+

@@ -20,4 +20,6 @@ from .workload import (  # noqa: F401
     quant_int4_g128,
     random_masks,
     pack_bits,
+    make_isg_weights,
+    make_relu_inputs,
 )

@@ -442,3 +442,38 @@ def random_masks(batch: int, f: int, density: float, seed: int = 0, probs=None) 
     p = np.full(f, density) if probs is None else np.asarray(probs)
     bits = g.random((batch, f)) < p[None, :]
     return pack_bits(bits)
+
+
+# ---------------------------------------------------------------------------
+# input-sparse GEMV inputs (relufication stage 2: a ReLU inserted after the
+# normalisation layer, [53ai] 第二阶段——插入新的ReLU)
+# ---------------------------------------------------------------------------
+
+_T_ISG_W, _T_ISG_B, _T_ISG_X = 200, 201, 202
+
+
+def make_isg_weights(n_in: int, n_out: int, wtype: str = "f16", seed: int = 0, key: int = 0,
+                     bias: bool = True):
+    """A projection stored input-major: w_t [n_in][n_out] ~ N(0, 0.02^2) (row j is
+    the column of W that input j multiplies), and a bias [n_out] ~ N(0, 0.02^2)
+    (or None).  Storage dtype fp16 or fp32."""
+    dt = np.float32 if wtype == "f32" else np.float16
+    w_t = _normal((n_in, n_out), 0.02, dt, seed, (_T_ISG_W, key))
+    b = _normal((n_out,), 0.02, dt, seed, (_T_ISG_B, key)) if bias else None
+    return w_t, b
+
+
+def make_relu_inputs(n_in: int, n: int, density: float, seed: int = 0, stream: int = 0,
+                     dtype=np.float16) -> np.ndarray:
+    """n input vectors as a ReLU after a normalisation layer would hand them on:
+    x = max(z - theta, 0) with z ~ N(0, 1) and theta = Phi^-1(1 - density), so
+    each entry is nonzero with probability ``density`` (theta = 0 at 0.5, the
+    plain ReLU of a normalised input)."""
+    theta = 0.0 if density >= 1.0 else float(ndtri(1.0 - density)) if density > 0.0 else np.inf
+    z = _stream(seed, (_T_ISG_X, n_in, n, stream)).standard_normal((n, n_in), dtype=np.float32)
+    if density >= 1.0:
+        x = z  # every entry kept: the dense input
+    else:
+        x = np.maximum(z - np.float32(theta), np.float32(0.0))
+    return x.astype(dtype)
+

@@ -395,3 +395,94 @@ def test_residual_rmsnorm_closed_form():
     g = np.random.default_rng(0).normal(0, 5, (3, 64))
     _, xg = oracle.residual_rmsnorm(g, np.zeros_like(g), eps=0.0)
     np.testing.assert_allclose((xg ** 2).mean(axis=1), 1.0, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# input-sparse GEMV (relufication stage 2, [53ai] 第二阶段——插入新的ReLU)
+# ---------------------------------------------------------------------------
+
+def _isg_case(n_in, n_out, B, density, seed):
+    g = np.random.default_rng(seed)
+    w_t = g.normal(0, 0.5, (n_in, n_out))
+    bias = g.normal(0, 0.5, n_out)
+    x = g.normal(0, 1, (B, n_in)) * (g.random((B, n_in)) < density)
+    return w_t, bias, x
+
+
+@pytest.mark.parametrize("B,density", [(1, 0.3), (3, 0.5), (2, 0.0), (4, 1.0)])
+def test_isg_brute_force(B, density):
+    """Literal loops over every input (zero or not) give the same y and J."""
+    w_t, bias, x = _isg_case(12, 7, B, density, seed=B)
+    y, J = oracle.input_sparse_gemv(w_t, x, bias, return_f64=True)
+    ref = np.zeros((B, 7))
+    for b in range(B):
+        for o in range(7):
+            acc = bias[o]
+            for j in range(12):
+                acc += x[b, j] * w_t[j, o]
+            ref[b, o] = acc
+    assert np.allclose(y, ref, rtol=0, atol=1e-12)
+    cols = [j for j in range(12) if any(x[b, j] != 0 for b in range(B))]
+    assert list(J) == cols
+
+
+def test_isg_equals_dense_matmul():
+    """The skipped columns carry exact zeros: y is the textbook product."""
+    w_t, bias, x = _isg_case(256, 96, 5, 0.2, seed=7)
+    y, J = oracle.input_sparse_gemv(w_t, x, bias, return_f64=True)
+    dense = x @ w_t + bias[None, :]
+    scale = np.abs(x) @ np.abs(w_t) + np.abs(bias)[None, :]
+    assert np.all(np.abs(y - dense) <= 1e-13 * scale)
+    assert len(J) < 256
+
+
+def test_isg_closed_forms():
+    w_t, bias, _ = _isg_case(32, 16, 1, 0.0, seed=3)
+    # no nonzero input: the bias alone, nothing read
+    y, J = oracle.input_sparse_gemv(w_t, np.zeros((2, 32)), bias, return_f64=True)
+    assert len(J) == 0 and np.array_equal(y, np.tile(bias, (2, 1)))
+    # one nonzero input: bias + x_j times row j of w_t
+    x = np.zeros((1, 32))
+    x[0, 9] = -1.75
+    y, J = oracle.input_sparse_gemv(w_t, x, bias, return_f64=True)
+    assert list(J) == [9] and np.array_equal(y[0], bias + (-1.75) * w_t[9])
+    # no bias: the product alone
+    y, _ = oracle.input_sparse_gemv(w_t, x, None, return_f64=True)
+    assert np.array_equal(y[0], (-1.75) * w_t[9])
+
+
+def test_isg_unused_rows_never_read():
+    """Rows of w_t outside J (no token has a nonzero input there) may hold NaN."""
+    w_t, bias, x = _isg_case(64, 24, 3, 0.25, seed=11)
+    y, J = oracle.input_sparse_gemv(w_t, x, bias)
+    poisoned = w_t.copy()
+    off = np.ones(64, dtype=bool)
+    off[J] = False
+    assert off.any()
+    poisoned[off] = np.nan
+    y2, J2 = oracle.input_sparse_gemv(poisoned, x, bias)
+    assert np.array_equal(J, J2) and np.array_equal(y, y2)
+
+
+def test_isg_signed_zero_and_nan_inputs():
+    w_t, bias, _ = _isg_case(8, 4, 1, 0.0, seed=5)
+    x = np.zeros((1, 8))
+    x[0, 2] = -0.0   # a negative zero is a zero input: its column is skipped
+    x[0, 5] = np.nan  # a NaN is not zero: its column is read
+    y, J = oracle.input_sparse_gemv(w_t, x, bias, return_f64=True)
+    assert list(J) == [5] and np.isnan(y).all()
+
+
+def test_relu_inputs_density():
+    """The generator's entries are nonzero with the requested probability
+    (99.9% binomial interval over 64 x 4096 draws) and never negative."""
+    for density in (0.5, 0.3, 0.1):
+        x = synth.make_relu_inputs(4096, 64, density, dtype=np.float32)
+        n = x.size
+        k = int((x != 0).sum())
+        sd = np.sqrt(n * density * (1 - density))
+        assert abs(k - n * density) <= 3.3 * sd, density
+        assert (x >= 0).all()
+    # density 1: the dense input, negative values kept
+    x = synth.make_relu_inputs(512, 4, 1.0, dtype=np.float32)
+    assert (x < 0).any() and (x != 0).all()
