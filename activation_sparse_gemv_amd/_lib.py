@@ -26,6 +26,7 @@ EXPORTS = [
     "sfnn_workspace_bytes", "sfnn_predict", "sfnn_compact", "sfnn_sparse_ffn", "sfnn_dense_ffn",
     "sfnn_layer", "sfnn_stack_decode", "sfnn_residual_rmsnorm", "sfnn_fire_counts", "sfnn_hot_first_perm",
     "sfnn_gather_rows", "sfnn_probe_read", "sfnn_probe_copy", "sfnn_status_str", "sfnn_version",
+    "sfnn_isg_workspace_bytes", "sfnn_input_sparse_gemv",
 ]
 
 
@@ -50,6 +51,11 @@ class sfnn_ffn(ctypes.Structure):
                 ("mfma_min_batch", ctypes.c_int32)]
 
 
+class sfnn_isg(ctypes.Structure):
+    _fields_ = [("n_in", ctypes.c_int32), ("n_out", ctypes.c_int32), ("wtype", ctypes.c_int32),
+                ("w_t", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -63,7 +69,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                           "`python -m activation_sparse_gemv_amd.build`")
     L = ctypes.CDLL(path)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
-    P, F = ctypes.POINTER(sfnn_pred), ctypes.POINTER(sfnn_ffn)
+    P, F, G = ctypes.POINTER(sfnn_pred), ctypes.POINTER(sfnn_ffn), ctypes.POINTER(sfnn_isg)
     sig = {
         "sfnn_workspace_bytes": (sz, [P, F, i32]),
         "sfnn_predict": (i32, [P, vp, i32, vp, vp, vp, sz, vp]),
@@ -79,6 +85,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sfnn_probe_read": (i32, [vp, sz, vp, vp]),
         "sfnn_probe_copy": (i32, [vp, vp, sz, vp]),
         "sfnn_status_str": (ctypes.c_char_p, [i32]),
+        "sfnn_isg_workspace_bytes": (sz, [G, i32]),
+        "sfnn_input_sparse_gemv": (i32, [G, vp, i32, vp, vp, vp, vp, sz, vp]),
         "sfnn_version": (i32, []),
     }
     for name, (res, args) in sig.items():
@@ -162,6 +170,20 @@ class FFN:
     @mfma_min_batch.setter
     def mfma_min_batch(self, v: int):
         self.c.mfma_min_batch = int(v)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+class Isg:
+    """Device descriptor of an input-sparse GEMV (keeps its tensors alive):
+    w_t [n_in][n_out] fp16 or fp32, bias [n_out] or None."""
+
+    def __init__(self, w_t: torch.Tensor, bias: Optional[torch.Tensor] = None):
+        self.w_t, self.bias = w_t, bias
+        self.n_in, self.n_out = w_t.shape
+        self.c = sfnn_isg(self.n_in, self.n_out, _wtype_of(w_t), _p(w_t), _p(bias))
 
     @property
     def ref(self):
@@ -263,3 +285,14 @@ def sfnn_status_str(code: int) -> str:
 
 def sfnn_version() -> int:
     return int(load().sfnn_version())
+
+
+def sfnn_isg_workspace_bytes(op: Isg, batch: int) -> int:
+    return int(load().sfnn_isg_workspace_bytes(op.ref, batch))
+
+
+def sfnn_input_sparse_gemv(op: Isg, x, batch: int, y, ws, cols=None, count=None, stream=None):
+    _check("sfnn_input_sparse_gemv", load().sfnn_input_sparse_gemv(op.ref, _p(x), batch, _p(y), _p(cols), _p(count),
+                                                                    _p(ws), ws.numel() * ws.element_size(),
+                                                                    _s(stream)))
+

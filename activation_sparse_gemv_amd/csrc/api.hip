@@ -388,6 +388,85 @@ sfnn_status sfnn_probe_copy(const void* src, void* dst, size_t bytes, void* stre
   return hip_status(launch_probe_copy(src, dst, bytes, as_stream(stream)));
 }
 
+namespace {
+
+constexpr int kIsgMaxGroups = 512;
+
+struct IsgLayout {
+  size_t mask = 0, ids = 0, count = 0, partial = 0, hbuf = 0, sid = 0, total = 0;
+  int G = 0;
+};
+
+IsgLayout isg_layout(const sfnn_isg* op, int batch) {
+  IsgLayout L;
+  size_t off = 0;
+  L.G = isg_groups(op->n_out, kIsgMaxGroups);
+  L.mask = off;
+  off += up((size_t)(op->n_in / 64) * 8);
+  L.ids = off;
+  off += up((size_t)op->n_in * 4);
+  L.count = off;
+  off += up(4);
+  L.partial = off;
+  off += up((size_t)L.G * batch * op->n_out * 4);
+  if (op->wtype == SFNN_F16) {  // matrix-core path: one 32-token pass of h and the slot map
+    L.hbuf = off;
+    off += up((size_t)2 * 32 * op->n_in * 2);
+    L.sid = off;
+    off += up((size_t)op->n_in * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+sfnn_status check_isg(const sfnn_isg* op) {
+  if (!op || !op->w_t) return SFNN_E_NULL;
+  if (op->wtype != SFNN_F32 && op->wtype != SFNN_F16) return SFNN_E_DTYPE;
+  if (op->n_in < 64 || op->n_in > 65536 || op->n_in % 64 || op->n_out < 128 || op->n_out > 65536 ||
+      op->n_out % 128)
+    return SFNN_E_SHAPE;
+  if (!al16(op->w_t) || !al16(op->bias)) return SFNN_E_ALIGN;
+  return SFNN_OK;
+}
+
+}  // namespace
+
+size_t sfnn_isg_workspace_bytes(const sfnn_isg* op, int32_t batch) {
+  if (check_isg(op) == SFNN_E_SHAPE || !op || !batch_ok(batch)) return 0;
+  return isg_layout(op, batch).total;
+}
+
+sfnn_status sfnn_input_sparse_gemv(const sfnn_isg* op, const void* x, int32_t batch, float* y, int32_t* cols,
+                                   int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  sfnn_status st = check_isg(op);
+  if (st != SFNN_OK) return st;
+  if (!x || !y || !ws) return SFNN_E_NULL;
+  if (!batch_ok(batch)) return SFNN_E_SHAPE;
+  if (!al16(x) || !al16(y) || !al16(cols) || !al4(count) || !al16(ws)) return SFNN_E_ALIGN;
+  const IsgLayout Lw = isg_layout(op, batch);
+  if (ws_bytes < Lw.total) return SFNN_E_WORKSPACE;
+  char* w = (char*)ws;
+  IsgLaunch L;
+  L.wt = op->wtype == SFNN_F32 ? WT_F32 : WT_F16;
+  L.n_in = op->n_in;
+  L.n_out = op->n_out;
+  L.w_t = op->w_t;
+  L.bias = op->bias;
+  L.x = x;
+  L.batch = batch;
+  L.mask = reinterpret_cast<uint64_t*>(w + Lw.mask);
+  L.ids = cols ? cols : reinterpret_cast<int32_t*>(w + Lw.ids);
+  L.count = count ? count : reinterpret_cast<int32_t*>(w + Lw.count);
+  L.partial = reinterpret_cast<float*>(w + Lw.partial);
+  L.groups = Lw.G;
+  L.y = y;
+  if (op->wtype == SFNN_F16) {
+    L.hbuf = w + Lw.hbuf;
+    L.sidbuf = reinterpret_cast<int32_t*>(w + Lw.sid);
+  }
+  return hip_status(launch_isg(L, as_stream(stream)));
+}
+
 const char* sfnn_status_str(sfnn_status s) {
   switch (s) {
     case SFNN_OK: return "ok";
@@ -401,6 +480,6 @@ const char* sfnn_status_str(sfnn_status s) {
   return "unknown status";
 }
 
-int32_t sfnn_version(void) { return 300; }  // 300: sfnn_ffn.mfma_min_batch
+int32_t sfnn_version(void) { return 310; }  // 300: sfnn_ffn.mfma_min_batch; 310: sfnn_input_sparse_gemv
 
 }  // extern "C"

@@ -424,6 +424,26 @@ static void mfma_pass(const FfnLaunch& p, const int32_t* ids, const int32_t* cou
   hipLaunchKernelGGL((k_down_mfma<NB>), dim3((p.d / (16 * down_cpl<NB>())) * kg), dim3(512), 0, s, dn);
 }
 
+void launch_rows_mfma(const void* w_t, const int32_t* sid, const int32_t* count, const void* h, float* partial, int d,
+                      int f, int B, int tok0, int nt, int kg, hipStream_t s) {
+  MfmaDownArgs dn;
+  dn.w_down_t = (const f16*)w_t;
+  dn.sid = sid;
+  dn.count = count;
+  dn.h = (const f16*)h;
+  dn.partial = partial;
+  dn.d = d;
+  dn.f = f;
+  dn.B = B;
+  dn.tok0 = tok0;
+  dn.nt = nt;
+  dn.KG = kg;
+  if (nt > 16)
+    hipLaunchKernelGGL((k_down_mfma<2>), dim3((d / (16 * down_cpl<2>())) * kg), dim3(512), 0, s, dn);
+  else
+    hipLaunchKernelGGL((k_down_mfma<1>), dim3((d / (16 * down_cpl<1>())) * kg), dim3(512), 0, s, dn);
+}
+
 template <int ACT>
 static void mfma_all(const FfnLaunch& p, const int32_t* ids, const int32_t* count, hipStream_t s) {
   const int kg = mfma_groups(p.d, p.groups);

@@ -107,6 +107,35 @@ hipError_t launch_predict_stage2(const PredLaunch& p, hipStream_t s);
 hipError_t launch_stack_lookahead(const PredLaunch* pred, const FfnLaunch* ffn, const float* const* r,
                                   int n_layers, float eps, float* rtmp, hipStream_t s);
 
+// ---- input-sparse GEMV -------------------------------------------------------
+
+struct IsgLaunch {
+  int wt;                 // WT_F32 | WT_F16 (w_t, x and bias)
+  int n_in, n_out;
+  const void* w_t;        // [n_in][n_out]
+  const void* bias;       // [n_out] or null
+  const void* x;          // [B][n_in]
+  int batch;
+  uint64_t* mask;         // [n_in/64] workspace: inputs nonzero for some token
+  int32_t* ids;           // [n_in] the listed inputs
+  int32_t* count;         // [1]
+  float* partial;         // [groups][B][n_out] workspace
+  int groups;             // row groups (= partial rows per token)
+  float* y;               // [B][n_out]
+  void* hbuf = nullptr;   // matrix-core path: [2][32][n_in] fp16 (x at the listed inputs, zero low plane)
+  int32_t* sidbuf = nullptr;  // matrix-core path: [n_in] slot -> input
+};
+hipError_t launch_isg(const IsgLaunch& p, hipStream_t s);
+int isg_groups(int n_out, int max_groups);
+// fp16 inputs from this batch size on run on the matrix cores (the listed
+// rows' products through k_down_mfma); the IsgLaunch then needs hbuf / sidbuf.
+constexpr int kIsgMfmaMinBatch = 4;
+// partial[kg][B][d] over the rows sid[0 .. count) of the fp16 matrix w_t
+// [f][d], with h of one pass of up to 32 tokens as two fp16 planes [2][32][f]
+// (k_down_mfma; kg = mfma_groups(d, ...)).
+void launch_rows_mfma(const void* w_t, const int32_t* sid, const int32_t* count, const void* h, float* partial, int d,
+                      int f, int B, int tok0, int nt, int kg, hipStream_t s);
+
 hipError_t launch_compact(const uint64_t* mask, int batch, int f, int32_t* ids, int32_t* count,
                           uint64_t* union_mask, hipStream_t s);
 hipError_t launch_fire_counts(const uint64_t* masks, int n, int f, uint32_t* counts, hipStream_t s);

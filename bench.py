@@ -51,6 +51,8 @@ def _parse():
                     help="instead of the stack: sparse vs dense FFN per layer over batch sizes and fire rates")
     ap.add_argument("--sweep-batches", default="1,2,4,8,16,32")
     ap.add_argument("--sweep-rhos", default="0.05,0.1,0.2")
+    ap.add_argument("--isg", action="store_true",
+                    help="time the input-sparse GEMV (ReLU after the norm) over input densities and batches")
     return ap.parse_args()
 
 
@@ -115,6 +117,9 @@ def main():
     if args.rho is not None:
         over["rho"] = args.rho
     spec = synth.config(args.config, **over)
+    if args.isg:
+        _isg_sweep(args)
+        return
     if args.sweep:
         _sweep(args, spec)
         return
@@ -423,6 +428,64 @@ def _sweep(args, spec):
         del layers
         torch.cuda.empty_cache()
     print(json.dumps({"sweep": spec.name, "distinct_layers": nl, "points": points}), flush=True)
+
+
+def _isg_sweep(args):
+    """Input-sparse GEMV (relufication stage 2) at OPT-6.7B shapes: the up
+    projection (4096 -> 16384) and the fused QKV projection (4096 -> 12288),
+    over input densities (1.0 = every input nonzero: every row read) and
+    batches.  Each point cycles over distinct weight copies holding at least
+    1 GB; HIP events around replays of one graph of calls over the copies."""
+    import torch
+    import synth
+    import activation_sparse_gemv_amd as sg
+    from activation_sparse_gemv_amd.device import to_dev
+    points = []
+    for name, n_in, n_out in (("up 4096->16384", 4096, 16384), ("qkv 4096->12288", 4096, 12288)):
+        nc = max(2, int(np.ceil(1.0e9 / (n_in * n_out * 2))))
+        ops = []
+        for c in range(nc):
+            w_t, b = synth.make_isg_weights(n_in, n_out, "f16", seed=0, key=c)
+            ops.append(sg.Isg(to_dev(w_t), to_dev(b)))
+        for B in (1, 4, 16):
+            ws = torch.empty(sg.sfnn_isg_workspace_bytes(ops[0], B), dtype=torch.uint8, device="cuda")
+            y = torch.empty((B, n_out), dtype=torch.float32, device="cuda")
+            cols = torch.empty((nc, n_in), dtype=torch.int32, device="cuda")
+            cnt = torch.zeros((nc,), dtype=torch.int32, device="cuda")
+            for dens in (1.0, 0.5, 0.3, 0.1):
+                xs = [to_dev(synth.make_relu_inputs(n_in, B, dens, seed=0, stream=700 + c)) for c in range(nc)]
+
+                def calls():
+                    for c in range(nc):
+                        sg.sfnn_input_sparse_gemv(ops[c], xs[c], B, y, ws, cols[c], cnt[c:c + 1])
+
+                calls()
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    calls()
+                g.replay()
+                torch.cuda.synchronize()
+                a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = 8
+                a.record()
+                for _ in range(reps):
+                    g.replay()
+                e.record()
+                torch.cuda.synchronize()
+                us = a.elapsed_time(e) / (reps * nc) * 1e3
+                rows = float(cnt.float().mean().item())
+                pt = {"shape": name, "batch": B, "input_density": dens, "rows_read_frac": round(rows / n_in, 4),
+                      "us": round(us, 2), "GBps_rows_read": round(rows * n_out * 2 / us / 1e3, 1)}
+                points.append(pt)
+                print(json.dumps(pt), file=sys.stderr, flush=True)
+        del ops
+        torch.cuda.empty_cache()
+    for pt in points:
+        dense = next(q for q in points if q["shape"] == pt["shape"] and q["batch"] == pt["batch"]
+                     and q["input_density"] == 1.0)
+        pt["speedup_vs_all_rows"] = round(dense["us"] / pt["us"], 2)
+    print(json.dumps({"isg_sweep": points}), flush=True)
 
 
 def _hot_first(sg, layers, spec, B, dev):

@@ -217,8 +217,39 @@ sfnn_status sfnn_gather_rows(const void* src, const int32_t* perm, int32_t n_row
 sfnn_status sfnn_probe_read(const void* buf, size_t bytes, float* sink, void* stream);
 sfnn_status sfnn_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 
+/* Input-sparse GEMV: y = bias + W x for inputs with many zero entries.
+ * The relufication page's second stage ([53ai] 第二阶段——插入新的ReLU) puts a
+ * ReLU after the normalisation layer, so the inputs of the projections that
+ * follow it (FFN up projection, attention QKV) are sparse, and a zero input
+ * selects a column of W that contributes nothing.  W is stored input-major:
+ * w_t [n_in][n_out], row j the column of W that input j multiplies, so a
+ * skipped input skips one contiguous row.  wtype is SFNN_F32 or SFNN_F16;
+ * x [batch][n_in] and bias [n_out] (NULL: zero) have that type.
+ * Limits: n_in a multiple of 64 in [64, 65536], n_out a multiple of 128 in
+ * [128, 65536], 1 <= batch <= 64; pointers 16-byte aligned (count: 4). */
+typedef struct sfnn_isg {
+  int32_t n_in, n_out;
+  int32_t wtype;       /* SFNN_F32 or SFNN_F16                           */
+  const void* w_t;     /* [n_in][n_out]                                  */
+  const void* bias;    /* [n_out] or NULL                                */
+} sfnn_isg;
+
+/* Device workspace bytes for sfnn_input_sparse_gemv (0 on invalid input). */
+size_t sfnn_isg_workspace_bytes(const sfnn_isg* op, int32_t batch);
+
+/* J = the inputs j with x_b[j] != 0 for some token b (ascending; -0.0 is a
+ * zero, NaN is not); for every token y_b = bias + sum_{j in J} x_b[j] w_t[j, :]
+ * with fp32 accumulation, so only the rows of w_t listed in J are read.  A
+ * token's own zero inputs in J add exact zeros: y_b is the dense product up to
+ * rounding.  Writes y [batch][n_out] fp32 and, when not NULL, cols [n_in]
+ * (J, first *count entries) and count [1] on the device.  Asynchronous on the
+ * stream; the result is bitwise deterministic. */
+sfnn_status sfnn_input_sparse_gemv(const sfnn_isg* op, const void* x, int32_t batch, float* y,
+                                   int32_t* cols, int32_t* count, void* ws, size_t ws_bytes,
+                                   void* stream);
+
 const char* sfnn_status_str(sfnn_status s);
-int32_t sfnn_version(void);  /* 300 and up: sfnn_ffn has mfma_min_batch */
+int32_t sfnn_version(void);  /* 300 and up: sfnn_ffn has mfma_min_batch; 310 and up: sfnn_input_sparse_gemv */
 
 #ifdef __cplusplus
 }

@@ -94,3 +94,26 @@ def test_hot_first_perm_host_matches_oracle(L, seed):
     perm = np.empty(f, dtype=np.int32)
     m.sfnn_hot_first_perm(counts, f, perm)
     assert np.array_equal(perm, oracle.hot_first_perm(counts))
+
+
+def test_isg_validation_and_workspace(L):
+    import activation_sparse_gemv_amd as m
+    G = m._lib.sfnn_isg
+    fake = 1 << 20
+    ok = G(4096, 16384, 1, fake, None)
+    ws = L.sfnn_isg_workspace_bytes(ctypes.byref(ok), 1)
+    assert ws > 16384 * 4  # at least one partial row set
+    assert L.sfnn_isg_workspace_bytes(ctypes.byref(ok), 2) > ws
+    assert L.sfnn_isg_workspace_bytes(ctypes.byref(ok), 0) == 0
+    assert L.sfnn_input_sparse_gemv(None, fake, 1, fake, None, None, fake, 1 << 30, None) == 1
+    bad = G(4000, 16384, 1, fake, None)   # n_in % 64
+    assert L.sfnn_isg_workspace_bytes(ctypes.byref(bad), 1) == 0
+    assert L.sfnn_input_sparse_gemv(ctypes.byref(bad), fake, 1, fake, None, None, fake, 1 << 30, None) == 2
+    bad = G(4096, 1000, 1, fake, None)    # n_out % 128
+    assert L.sfnn_input_sparse_gemv(ctypes.byref(bad), fake, 1, fake, None, None, fake, 1 << 30, None) == 2
+    bad = G(4096, 16384, 2, fake, None)   # INT4 is not an input-sparse GEMV type
+    assert L.sfnn_input_sparse_gemv(ctypes.byref(bad), fake, 1, fake, None, None, fake, 1 << 30, None) == 4
+    assert L.sfnn_input_sparse_gemv(ctypes.byref(ok), fake, 65, fake, None, None, fake, 1 << 30, None) == 2
+    assert L.sfnn_input_sparse_gemv(ctypes.byref(ok), fake + 4, 1, fake, None, None, fake, 1 << 30, None) == 3
+    assert L.sfnn_input_sparse_gemv(ctypes.byref(ok), fake, 1, fake, None, fake + 2, fake, 1 << 30, None) == 3
+    assert L.sfnn_input_sparse_gemv(ctypes.byref(ok), fake, 1, fake, None, None, fake, 64, None) == 5
