@@ -34,8 +34,11 @@ Layout layout(const sfnn_pred* p, const sfnn_ffn* f, int batch) {
   const int ff = f ? f->d_ff : (p ? p->d_ff : 0);
   const int dm = f ? f->d_model : (p ? p->d_model : 0);
   if (p) {
+    // z [B][r], and for fp16 predictors the matrix-core stage 1's partial z
+    // of up to kPred1MaxSplits d_model slices right behind it
     L.z = off;
     off += up((size_t)batch * p->rank * 4);
+    if (p->wtype == SFNN_F16) off += up((size_t)kPred1MaxSplits * batch * p->rank * 4);
   }
   if (f) {
     L.G = ffn_groups(f->d_model, f->d_ff);
@@ -114,6 +117,7 @@ PredLaunch pred_launch(const sfnn_pred* p, const void* x, int batch, uint64_t* m
   L.x = x;
   L.batch = batch;
   L.z = z;
+  if (p->wtype == SFNN_F16) L.zpart = z + up((size_t)batch * p->rank * 4) / 4;  // see layout()
   L.mask = mask;
   L.union_mask = uni;
   L.logits = logits;

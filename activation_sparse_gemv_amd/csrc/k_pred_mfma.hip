@@ -8,10 +8,14 @@
 // here one pass covers up to 32 tokens with v_mfma_f32_16x16x32_f16, fp32
 // accumulation.
 //
-//  k_pred1_mfma  workgroup = 16 rows of W1^T; its 16 wavefronts split d_model
-//                into 64-column pairs (pair w, w + 16, ...), each holding a
-//                16x16 fp32 block per 16 tokens; the blocks are added in
-//                wavefront order in LDS and written as z [B][r] fp32.
+//  k_pred1_mfma  workgroup = 16 rows of W1^T x one of up to 8 d_model
+//                slices (enough for one batch of pairs per wavefront); its
+//                16 wavefronts split the
+//                slice into 64-column pairs (pair w, w + 16, ...), each
+//                holding a 16x16 fp32 block per 16 tokens; the blocks are
+//                added in wavefront order in LDS and written as the slice's
+//                partial z, which k_z_reduce adds in slice order into z
+//                [B][r] fp32.
 //  k_pred2_mfma  workgroup = 64 neurons (one mask word, four 16-row tiles) x
 //                every token of the pass; its 8 wavefronts split the rank
 //                into 32-wide steps (step w, w + 8, ...).  z enters the
@@ -36,8 +40,8 @@ constexpr int kPredBatch = 4;
 struct Pred1MfmaArgs {
   const f16* w1_t;  // [r][d]
   const f16* x;     // [B][d]
-  float* z;         // [B][r]
-  int d, r, tok0, nt;
+  float* z;         // [B][r] (one slice), or the slices' partial z [KS][B][r]
+  int d, r, B, tok0, nt, KS;
 };
 
 struct Pred2MfmaArgs {
@@ -62,7 +66,8 @@ __global__ __launch_bounds__(1024) void k_pred1_mfma(Pred1MfmaArgs a) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int rr = lane & 15, g = lane >> 4;
   const int d = a.d;
-  const int row = blockIdx.x * 16 + rr;
+  const int tile = blockIdx.x / a.KS, ks = blockIdx.x % a.KS;  // row tile, d_model slice
+  const int row = tile * 16 + rr;
   const f16* wr = a.w1_t + (size_t)(row < a.r ? row : a.r - 1) * d + 8 * g;  // rows past r: dropped below
   const f16* xr[NB];
   bool xok[NB];
@@ -93,15 +98,17 @@ __global__ __launch_bounds__(1024) void k_pred1_mfma(Pred1MfmaArgs a) {
       for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_16x16x32(F.w[s], xok[nb] ? F.x[nb][s] : zero, acc[nb]);
   };
 
-  // pairs wave, wave + W, ... in batches of kPredBatch: every batch's loads
-  // go out before any of its products (a pair past the last re-reads the last)
+  // this slice's pairs p0 + wave, + W, ... in batches of kPredBatch: every
+  // batch's loads go out before any of its products (a pair past the last
+  // re-reads the last)
   constexpr int W = kPred1Waves;
   const int npair = d >> 6;
-  const int iters = wave < npair ? (npair - wave + W - 1) / W : 0;
+  const int p0 = ks * npair / a.KS, p1 = (ks + 1) * npair / a.KS;
+  const int iters = p0 + wave < p1 ? (p1 - p0 - wave + W - 1) / W : 0;
   for (int b0 = 0; b0 < iters; b0 += kPredBatch) {
     P1Frag<NB> F[kPredBatch];
 #pragma unroll
-    for (int j = 0; j < kPredBatch; ++j) issue(F[j], wave + W * (b0 + j < iters ? b0 + j : iters - 1));
+    for (int j = 0; j < kPredBatch; ++j) issue(F[j], p0 + wave + W * (b0 + j < iters ? b0 + j : iters - 1));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < kPredBatch; ++j)
@@ -119,10 +126,21 @@ __global__ __launch_bounds__(1024) void k_pred1_mfma(Pred1MfmaArgs a) {
 #pragma unroll
     for (int w = 0; w < kPred1Waves; ++w) s += rf[w * E + e];
     const int q = e & 3, ln = (e >> 2) & (kWave - 1), nb = e >> 8;
-    const int orow = blockIdx.x * 16 + 4 * (ln >> 4) + q;
+    const int orow = tile * 16 + 4 * (ln >> 4) + q;
     const int tk = nb * 16 + (ln & 15);
-    if (orow < a.r && tk < a.nt) a.z[(size_t)(a.tok0 + tk) * a.r + orow] = s;
+    if (orow < a.r && tk < a.nt) a.z[((size_t)ks * a.B + a.tok0 + tk) * a.r + orow] = s;
   }
+}
+
+// z = the slices' partial z added in slice order, for elements [e0, e1) of
+// [B][r].
+__global__ __launch_bounds__(256) void k_z_reduce(const float* __restrict__ zpart, int KS, int n, int e0, int e1,
+                                                  float* __restrict__ z) {
+  const int e = e0 + blockIdx.x * 256 + threadIdx.x;
+  if (e >= e1) return;
+  float s = zpart[e];
+  for (int k = 1; k < KS; ++k) s += zpart[(size_t)k * n + e];
+  z[e] = s;
 }
 
 template <int NB>
@@ -274,13 +292,22 @@ hipError_t launch_pred1_mfma(const PredLaunch& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     x = p.norm.x_out;
   }
+  // d_model slices: just enough that every wavefront has one batch of pairs
+  // (a slice's extra reduce launch costs more than a second batch saves when
+  // d_model is small: one slice at 4096, three at 12288)
+  const int tiles = (p.r + 15) / 16, npair = p.d / 64;
+  int KS = (npair + kPred1Waves * kPredBatch - 1) / (kPred1Waves * kPredBatch);
+  if (KS > kPred1MaxSplits) KS = kPred1MaxSplits;
+  if (KS < 1 || !p.zpart) KS = 1;
   Pred1MfmaArgs a;
   a.w1_t = (const f16*)p.w1_t;
   a.x = (const f16*)x;
-  a.z = p.z;
+  a.z = KS > 1 ? p.zpart : p.z;
   a.d = p.d;
   a.r = p.r;
-  const dim3 grid((p.r + 15) / 16);
+  a.B = p.batch;
+  a.KS = KS;
+  const dim3 grid(tiles * KS);
   for (int tok0 = 0; tok0 < p.batch; tok0 += 32) {
     a.tok0 = tok0;
     a.nt = p.batch - tok0 < 32 ? p.batch - tok0 : 32;
@@ -288,6 +315,10 @@ hipError_t launch_pred1_mfma(const PredLaunch& p, hipStream_t s) {
       hipLaunchKernelGGL(k_pred1_mfma<2>, grid, dim3(64 * kPred1Waves), 0, s, a);
     else
       hipLaunchKernelGGL(k_pred1_mfma<1>, grid, dim3(64 * kPred1Waves), 0, s, a);
+  }
+  if (KS > 1) {
+    const int n = p.batch * p.r;
+    hipLaunchKernelGGL(k_z_reduce, dim3((n + 255) / 256), dim3(256), 0, s, p.zpart, KS, n, 0, n, p.z);
   }
   return hipGetLastError();
 }

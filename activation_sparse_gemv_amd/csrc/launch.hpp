@@ -33,6 +33,7 @@ struct PredLaunch {
   NormIn norm;       // residual-chain input when norm.r_in != null
   int batch;
   float* z;          // [B][r] workspace
+  float* zpart = nullptr;  // fp16: [kPred1MaxSplits][B][r] workspace for the matrix-core stage 1
   uint64_t* mask;    // [B][f/64]
   uint64_t* union_mask;  // [f/64] OR of the batch's masks (always written)
   float* logits;     // [B][f] or null
@@ -91,6 +92,9 @@ hipError_t launch_sum(const FfnLaunch& p, hipStream_t s);
 // Batches at or above this size run the fp16 predictor on the matrix cores
 // (k_pred1_mfma + k_pred2_mfma, up to 32 tokens per pass).
 constexpr int kPredMfmaMinBatch = 8;
+// Stage 1 on the matrix cores splits d_model into at most this many slices
+// (more workgroups than the r / 16 row tiles), added in a fixed order.
+constexpr int kPred1MaxSplits = 8;
 bool pred_uses_mfma(const PredLaunch& p);
 hipError_t launch_pred1_mfma(const PredLaunch& p, hipStream_t s);  // residual chain: RMSNorm launch first
 hipError_t launch_pred2_mfma(const PredLaunch& p, hipStream_t s);

@@ -85,3 +85,17 @@ def test_mfma_predict_stack_b20(lookahead):
     from test_gpu_stack import _stack_case
     spec = synth.config("c2", d_model=768, d_ff=3072, rank=96, n_layers=3)
     _stack_case(spec, 3, 20, seed=12, lookahead=lookahead)
+
+
+@pytest.mark.parametrize("B", [9, 20])
+def test_mfma_predict_split_stage1_integer_grid_bitwise(B):
+    # d_model 8192: stage 1 runs in two d_model slices whose partial z are
+    # added by the reduce launch; on the integer grid every sum is exact
+    lay = synth.make_grid_layer(8192, 1024, 64, wtype="f16", seed=9)
+    x = synth.make_grid_tokens(8192, B, seed=90 + B)
+    pred, _ = upload_layer(lay)
+    words, lg = gpu_predict(pred, x, 1024)
+    ol, ob = oracle.predict(lay.w1_t, lay.w2_t, lay.tau, x)
+    assert np.abs(ol).max() < 2 ** 24
+    assert np.array_equal(lg.astype(np.float64), ol)
+    assert np.array_equal(words, oracle.pack_mask(ob))
