@@ -11,6 +11,38 @@ namespace sfnn {
 
 __global__ __launch_bounds__(512) void k_sum(SumArgs a) { sum_body(a, blockIdx.x, gridDim.x); }
 
+// The same sum when there are few partial rows (the matrix-core paths write 8
+// or 16 per token): 4 consecutive elements per thread, the rows added one
+// after another from zero, then the bias, then the residual, exactly the
+// order k_sum takes with at most 32 rows, so both give the same bits.
+__global__ __launch_bounds__(256) void k_sum_wide(SumArgs a) {
+  const int n = a.B * a.d;
+  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;  // d is a multiple of 128: 4 elements never straddle
+  if (e >= n) return;
+  float t[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+  for (int g = 0; g < a.G; ++g) {
+    const f32x4 p = *reinterpret_cast<const f32x4*>(a.partial + (size_t)g * n + e);
+    t[0] += p.x;
+    t[1] += p.y;
+    t[2] += p.z;
+    t[3] += p.w;
+  }
+  const int c = e % a.d;
+  float v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float b = 0.0f;
+    if (a.b_down) b = (a.xtype == WT_F32) ? load_as_float<float>(a.b_down, c + k) : load_as_float<f16>(a.b_down, c + k);
+    v[k] = b + t[k];
+  }
+  if (a.y) *reinterpret_cast<f32x4*>(a.y + e) = f32x4{v[0], v[1], v[2], v[3]};
+  if (a.r_in) {
+    const f32x4 r = *reinterpret_cast<const f32x4*>(a.r_in + e);
+    *reinterpret_cast<f32x4*>(a.r_out + e) = f32x4{r.x + v[0], r.y + v[1], r.z + v[2], r.w + v[3]};
+  }
+}
+
 // Threads own CPT columns each for the down projection (at most 512
 // threads); the token group is bounded by the staged activations (LDS) and by
 // 64 accumulators per thread.
@@ -91,7 +123,13 @@ SumArgs sum_args(const FfnLaunch& p) {
 int sum_groups(int batch, int d) { return (batch * d + kSumEPW - 1) / kSumEPW; }  // 512-thread workgroups
 
 hipError_t launch_sum(const FfnLaunch& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_sum, dim3(sum_groups(p.batch, p.d)), dim3(512), 0, s, sum_args(p));
+  const SumArgs a = sum_args(p);
+  if (a.G <= 32) {
+    const int n4 = (p.batch * p.d) / 4;
+    hipLaunchKernelGGL(k_sum_wide, dim3((n4 + 255) / 256), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(k_sum, dim3(sum_groups(p.batch, p.d)), dim3(512), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -202,3 +202,12 @@ def test_rows_path_still_covers_large_batches():
     ref = oracle.masked_ffn(lay, x, words)
     for b in range(B):
         assert rel_err(y[b], ref[b]) <= TOL, b
+
+
+@pytest.mark.parametrize("lookahead", [False, True])
+def test_mfma_stack_few_partial_rows_b9(lookahead):
+    # d_model 1024: the matrix-core down projection writes 32 partial rows per
+    # token, which the wide sum adds (with the residual) instead of k_sum
+    from test_gpu_stack import _stack_case
+    spec = synth.config("c2", d_model=1024, d_ff=2048, rank=64, n_layers=2)
+    _stack_case(spec, 2, 9, seed=14, lookahead=lookahead, mfma_min_batch=ON)
