@@ -55,6 +55,7 @@ struct MfmaDownArgs {
 };
 
 constexpr int kUpSlots = 32;
+constexpr int kUpBatch = 4;  // column pairs of loads in flight per wavefront
 
 // |U| as the sparse FFN takes it: clamped to [0, f]; null: every neuron.
 __device__ __forceinline__ int slot_count(const int32_t* count, int f) {
@@ -149,27 +150,18 @@ __global__ __launch_bounds__(512) void k_up_mfma(MfmaUpArgs a) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[m][t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // pairs wave, wave + 8, ...; two fragment sets in flight.  Every request is
-  // unconditional (the last one re-reads the current pair) so the waits count
-  // exactly the loads issued after the set being used.
+  // pairs wave, wave + 8, ... in batches of kUpBatch: every batch's loads go
+  // out before any of its products (a pair past the last re-reads the last)
   const int npair = d >> 6;
   const int iters = wave < npair ? (npair - wave + 7) >> 3 : 0;
-  auto P = [&](int it) { return wave + 8 * it; };
-  if (iters > 0) {
-    UpFrag<NM, NB> A, Bf;
-    up_issue(A, wr, xr, P(0));
-    for (int it = 0; it < iters; it += 2) {
-      const int pa = P(it);
-      const int pb = it + 1 < iters ? P(it + 1) : pa;
-      up_issue(Bf, wr, xr, pb);
-      __builtin_amdgcn_sched_barrier(0);
-      up_mul(A, xok, acc);
-      if (it + 1 >= iters) break;
-      const int pc = it + 2 < iters ? P(it + 2) : pb;
-      up_issue(A, wr, xr, pc);
-      __builtin_amdgcn_sched_barrier(0);
-      up_mul(Bf, xok, acc);
-    }
+  for (int b0 = 0; b0 < iters; b0 += kUpBatch) {
+    UpFrag<NM, NB> F[kUpBatch];
+#pragma unroll
+    for (int j = 0; j < kUpBatch; ++j) up_issue(F[j], wr, xr, wave + 8 * (b0 + j < iters ? b0 + j : iters - 1));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kUpBatch; ++j)
+      if (b0 + j < iters) up_mul(F[j], xok, acc);
   }
 
   // the 8 wavefronts' blocks added in wavefront order; thread e-slots
