@@ -106,15 +106,21 @@ __global__ __launch_bounds__(256) void k_isg(IsgArgs a) {
     for (int c = 0; c < 8; ++c) acc[t][c] = 0.0f;
 
   constexpr int RB = isg_batch<NT>();
+  // a batch of rows: every load issued before any product (rows past the
+  // group re-read its last row and add nothing); the next batch's row ids are
+  // fetched while this batch's rows are in flight
+  int jn[RB];
+  auto fetch_ids = [&](int sb) {
+#pragma unroll
+    for (int k = 0; k < RB; ++k) jn[k] = a.ids[sb + k < s1 ? sb + k : (s1 > 0 ? s1 - 1 : 0)];
+  };
+  if (s0 < s1) fetch_ids(s0);
   for (int sb = s0; sb < s1; sb += RB) {
-    // a batch of rows: every load issued before any product (rows past the
-    // group re-read its last row and add nothing)
     u32x4 v[RB][sizeof(XT) / 2];
     float xv[RB][NT];
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
-      const int s = sb + k < s1 ? sb + k : s1 - 1;
-      int j = a.ids[s];
+      int j = jn[k];
       const bool ok = sb + k < s1 && j >= 0 && j < a.n_in;
       j = ok ? j : 0;
       isg_row<XT>(w + (size_t)j * a.n_out + colc, v[k]);
@@ -124,6 +130,7 @@ __global__ __launch_bounds__(256) void k_isg(IsgArgs a) {
         xv[k][t] = (ok && t < a.nt) ? xx : 0.0f;
       }
     }
+    if (sb + RB < s1) fetch_ids(sb + RB);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < RB; ++k) isg_fma<XT, NT>(v[k], xv[k], acc);
