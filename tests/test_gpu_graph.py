@@ -1,0 +1,100 @@
+"""Every entry point can be captured in a HIP graph (no host synchronisation,
+no allocation, no memset nodes): capture once, then replay several times with
+new inputs copied into the captured buffers between replays (eager work and a
+synchronisation in between), and check every replay bitwise against the eager
+call on the same input.  The calls are deterministic, so bitwise is the bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import activation_sparse_gemv_amd as sg
+import synth
+from activation_sparse_gemv_amd.device import to_dev, upload_layer, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+def _replays(run, set_input, inputs):
+    """Capture run() once; for each input: eager result, then graph result."""
+    set_input(inputs[0])
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = run()
+    torch.cuda.synchronize()
+    def raw(t):  # bit patterns, comparable for every dtype used here
+        return t.view(torch.int64) if t.dtype == torch.uint64 else (t.view(torch.uint8) if t.dtype.is_floating_point else t)
+
+    for inp in inputs:
+        set_input(inp)
+        eager = [raw(o).clone() for o in run()]
+        torch.cuda.synchronize()
+        for o in outs:  # poison the outputs, so a replay that writes nothing fails
+            if o.dtype.is_floating_point:
+                o.fill_(float("nan"))
+            else:
+                raw(o).fill_(123)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(eager, outs):
+            assert torch.equal(a, raw(b))
+
+
+@pytest.mark.parametrize("B", [1, 9])
+def test_graph_layer(B):
+    spec = synth.config("c2", d_model=1024, d_ff=4096, rank=128)
+    lay = synth.make_layer(spec, layer=0)
+    pred, ffn = upload_layer(lay)
+    f, d = spec.d_ff, spec.d_model
+    x = torch.empty((B, d), dtype=torch.float16, device="cuda")
+    y = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    mask = torch.zeros((B, f // 64), dtype=torch.uint64, device="cuda")
+    ids = torch.empty(f, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(4, dtype=torch.int32, device="cuda")
+    ws = workspace(pred, ffn, B)
+
+    def run():
+        sg.sfnn_layer(pred, ffn, x, B, y, mask, ids, cnt, ws)
+        return [y, mask, cnt[:1]]
+
+    inputs = [synth.make_tokens(spec, B, stream=300 + k) for k in range(3)]
+    _replays(run, lambda a: x.copy_(to_dev(a)), inputs)
+
+
+def test_graph_stack_lookahead():
+    spec = synth.config("c2", d_model=768, d_ff=3072, rank=96, n_layers=3)
+    lays = [synth.make_layer(spec, layer=l) for l in range(3)]
+    dev = [upload_layer(l) for l in lays]
+    st = sg.Stack(dev)
+    B = 1
+    r_in = torch.empty((B, 768), dtype=torch.float32, device="cuda")
+    r_out = torch.empty((B, 768), dtype=torch.float32, device="cuda")
+    ws = workspace(dev[0][0], dev[0][1], B)
+
+    def run():
+        sg.sfnn_stack_decode(st, B, r_in, r_out, 1e-6, ws, flags=sg.SFNN_STACK_LOOKAHEAD)
+        return [r_out]
+
+    inputs = [synth.make_tokens(spec, B, stream=310 + k, dtype=np.float32) * np.float32(3.0) for k in range(3)]
+    _replays(run, lambda a: r_in.copy_(to_dev(a)), inputs)
+
+
+@pytest.mark.parametrize("B", [1, 6])
+def test_graph_input_sparse_gemv(B):
+    w_t, b = synth.make_isg_weights(1024, 2048, "f16", seed=5, key=5)
+    op = sg.Isg(to_dev(w_t), to_dev(b))
+    x = torch.empty((B, 1024), dtype=torch.float16, device="cuda")
+    y = torch.empty((B, 2048), dtype=torch.float32, device="cuda")
+    cols = torch.empty(1024, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(4, dtype=torch.int32, device="cuda")
+    ws = torch.empty(sg.sfnn_isg_workspace_bytes(op, B), dtype=torch.uint8, device="cuda")
+
+    def run():
+        sg.sfnn_input_sparse_gemv(op, x, B, y, ws, cols, cnt)
+        return [y, cnt[:1]]
+
+    inputs = [synth.make_relu_inputs(1024, B, 0.3, seed=k, stream=B) for k in range(3)]
+    _replays(run, lambda a: x.copy_(to_dev(a)), inputs)
