@@ -329,7 +329,7 @@ def test_layer_opt6_7b_full_size_b1():
     _layer_case(lay, x)
 
 
-@pytest.mark.parametrize("B", [1, 16])
+@pytest.mark.parametrize("B", [1, 4, 16])
 def test_layer_opt30b_zipf_full_size(B):
     spec = synth.config("c3")
     lay = full_layer("c3")
@@ -337,14 +337,15 @@ def test_layer_opt30b_zipf_full_size(B):
     _layer_case(lay, x, check_tokens=[0, B - 1])
 
 
-def test_layer_llama_reglu70b_full_size_b8():
+@pytest.mark.parametrize("B", [1, 8])
+def test_layer_llama_reglu70b_full_size(B):
     spec = synth.config("c4")
     lay = full_layer("c4")
-    x = synth.make_tokens(spec, 8, stream=3)
-    _layer_case(lay, x, check_tokens=[0, 7])
+    x = synth.make_tokens(spec, B, stream=3)
+    _layer_case(lay, x, check_tokens=[0, B - 1])
 
 
-@pytest.mark.parametrize("B", [1, 32])
+@pytest.mark.parametrize("B", [1, 2, 4, 32])
 def test_layer_opt175b_int4_full_size(B):
     spec = synth.config("c5")
     lay = full_layer("c5")
