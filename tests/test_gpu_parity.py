@@ -351,3 +351,16 @@ def test_layer_opt175b_int4_full_size(B):
     lay = full_layer("c5")
     x = synth.make_tokens(spec, B, stream=4)
     _layer_case(lay, x, check_tokens=[0, B - 1])
+
+
+@pytest.mark.parametrize("wtype", ["f16", "i4g128"])
+@pytest.mark.parametrize("B", [1, 9])
+def test_layer_max_d_model(wtype, B):
+    """d_model 16384, the largest the ABI accepts: 128 INT4 scale groups per
+    row, 256 column pairs in the matrix-core kernels, four d_model slices in
+    predictor stage 1; per-row kernels at batch 1, matrix cores at 9."""
+    spec = synth.config("c2", d_model=16384, d_ff=2048, rank=256, wtype=wtype,
+                        pred_dtype="f16")
+    lay = synth.make_layer(spec, layer=0)
+    x = synth.make_tokens(spec, B, stream=17)
+    _layer_case(lay, x, check_tokens=[0, B - 1])
