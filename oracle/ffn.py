@@ -28,6 +28,8 @@ Readings of points the pages leave open (each also listed in the design notes):
 * Masks are packed uint64 words, bit i%64 of word i/64, LSB first.
 * A batch reads the union of the tokens' predicted sets; each token is gated
   by its own mask (a select: gated-off neurons contribute nothing at all).
+* Dense hot prefix (opt-in, for a hot-first layout): neurons i < H are taken
+  for every token without the predictor; their logits read +inf.
 * INT4: element 2k in the low nibble of byte k, two's complement, one fp16
   scale per row and 128 consecutive elements; w = q * s.
 
@@ -75,12 +77,18 @@ def pack_mask(bits) -> np.ndarray:
 # predictor  ([53ai] 自适应稀疏预测器; [news] per-layer predicting router)
 # ---------------------------------------------------------------------------
 
-def predict(w1_t, w2_t, tau, x):
+def predict(w1_t, w2_t, tau, x, hot_prefix: int = 0):
     """Low-rank predictor: logits [B][f] (float64) and the active mask [B][f].
 
     z_j = sum_k W1[k, j] x_k with W1^T stored as w1_t [r][d];
     logit_i = sum_j W2[j, i] z_j with W2^T stored as w2_t [f][r];
     active_i  <=>  logit_i > tau_i.
+
+    hot_prefix H: in a hot-first layout ([53ai] PowerInfer 概述 and 单层计算优化:
+    the hot neurons, found offline, carry most activations) neurons i < H are
+    taken for every token without asking the predictor, so the FFN runs them
+    as a dense block and their own ReLU decides what they contribute.  Their
+    mask bits are set whatever tau_i holds and their logits read +inf.
     """
     x = np.atleast_2d(np.asarray(x, dtype=np.float64))
     a = np.asarray(w1_t, dtype=np.float64)
@@ -88,7 +96,10 @@ def predict(w1_t, w2_t, tau, x):
     z = x @ a.T                      # [B][r]
     logits = z @ b.T                 # [B][f]
     t = np.asarray(tau, dtype=np.float64)
-    return logits, logits > t[None, :]
+    active = logits > t[None, :]
+    logits[:, :hot_prefix] = np.inf
+    active[:, :hot_prefix] = True
+    return logits, active
 
 
 def guard_band(w1_t, w2_t, x) -> np.ndarray:

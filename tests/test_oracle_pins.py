@@ -9,6 +9,7 @@ mathematics, never against the oracle itself re-typed.
 * permutation and batch invariance
 * INT4 nibble layout decoded by hand; quantise/dequantise round trip
 * predictor closed form; fp32 evaluation stays inside the guard band
+* dense hot prefix: the pages' example in hot-first order; prefix 0 and f
 """
 import json
 import os
@@ -363,6 +364,55 @@ def test_predictor_closed_form():
     expect = scale * x[0, sel]
     assert np.array_equal(logits[0], expect)
     assert np.array_equal(bits[0], expect > tau)
+
+
+def test_hot_prefix_toy_example(golden_dir):
+    """The pages' example in hot-first order with a dense hot prefix of the 3
+    hot neurons: the computed set is hot | predicted = {3, 4, 5, 7}, so hot
+    neuron 7, which the predictor skips for this input, is computed too."""
+    g = json.load(open(os.path.join(golden_dir, "powerinfer_toy_example.json")))
+    f = g["d_ff"]
+    counts = np.zeros(f, dtype=np.uint32)
+    counts[g["hot"]] = 10
+    perm = oracle.hot_first_perm(counts)          # position p holds neuron perm[p]
+    eye = np.eye(f)
+    x = np.zeros((1, f))
+    x[0, g["hot_first_positions_of_predicted"]] = 1.0   # logit = x, tau = 0.5
+    tau = np.full(f, 0.5)
+    _, plain = oracle.predict(eye, eye, tau, x)
+    assert sorted(perm[plain[0]]) == g["predicted"]
+    logits, bits = oracle.predict(eye, eye, tau, x, hot_prefix=len(g["hot"]))
+    assert sorted(perm[bits[0]]) == sorted(set(g["hot"]) | set(g["predicted"])) == [3, 4, 5, 7]
+    assert np.isposinf(logits[0, :3]).all() and np.array_equal(logits[0, 3:], x[0, 3:])
+
+
+@pytest.mark.parametrize("act", ["relu", "reglu"])
+def test_hot_prefix_bounds(act):
+    """Prefix 0 is the plain predictor; prefix f selects every neuron, so the
+    layer is the dense FFN (the matrix chain pinned above) whatever tau holds;
+    a partial prefix sets its bits even for tau = +inf or NaN and leaves the
+    rest of the logits and bits untouched."""
+    lay = tiny_layer(32, 256, 8, act=act, seed=11)
+    x = np.random.default_rng(12).normal(0, 1, (3, 32))
+    l0, b0 = oracle.predict(lay.w1_t, lay.w2_t, lay.tau, x)
+    lz, bz = oracle.predict(lay.w1_t, lay.w2_t, lay.tau, x, hot_prefix=0)
+    assert np.array_equal(l0, lz) and np.array_equal(b0, bz)
+    assert 0 < b0.sum() < b0.size
+    _, ball = oracle.predict(lay.w1_t, lay.w2_t, lay.tau, x, hot_prefix=256)
+    assert ball.all()
+    assert np.array_equal(oracle.masked_ffn(lay, x, ball), oracle.dense_ffn(lay, x))
+    tau = lay.tau.copy()
+    tau[:64] = np.inf
+    tau[64:128] = np.nan
+    lh, bh = oracle.predict(lay.w1_t, lay.w2_t, tau, x, hot_prefix=128)
+    assert bh[:, :128].all() and np.isposinf(lh[:, :128]).all()
+    assert np.array_equal(lh[:, 128:], l0[:, 128:]) and np.array_equal(bh[:, 128:], b0[:, 128:])
+    # ReLU: the prefix adds neurons whose exact output may be zero; over a
+    # superset of the true active set the layer stays the dense one
+    if act == "relu":
+        t = oracle.true_active(lay, x)
+        _, bp = oracle.predict(lay.w1_t, lay.w2_t, lay.tau, x, hot_prefix=64)
+        assert np.array_equal(oracle.masked_ffn(lay, x, bp | t), oracle.dense_ffn(lay, x))
 
 
 def test_guard_band_covers_fp32_evaluation():
