@@ -39,7 +39,7 @@ class SfnnError(RuntimeError):
 class sfnn_pred(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("wtype", ctypes.c_int32), ("w1_t", ctypes.c_void_p), ("w2_t", ctypes.c_void_p),
-                ("tau", ctypes.c_void_p)]
+                ("tau", ctypes.c_void_p), ("hot_prefix", ctypes.c_int32)]
 
 
 class sfnn_ffn(ctypes.Structure):
@@ -135,11 +135,19 @@ def _wtype_of(t: torch.Tensor) -> int:
 class Pred:
     """Device predictor descriptor (keeps its tensors alive)."""
 
-    def __init__(self, w1_t: torch.Tensor, w2_t: torch.Tensor, tau: torch.Tensor):
+    def __init__(self, w1_t: torch.Tensor, w2_t: torch.Tensor, tau: torch.Tensor, hot_prefix: int = 0):
         self.w1_t, self.w2_t, self.tau = w1_t, w2_t, tau
         r, d = w1_t.shape
         f = w2_t.shape[0]
-        self.c = sfnn_pred(d, f, r, _wtype_of(w1_t), _p(w1_t), _p(w2_t), _p(tau))
+        self.c = sfnn_pred(d, f, r, _wtype_of(w1_t), _p(w1_t), _p(w2_t), _p(tau), hot_prefix)
+
+    @property
+    def hot_prefix(self) -> int:
+        return self.c.hot_prefix
+
+    @hot_prefix.setter
+    def hot_prefix(self, h: int):
+        self.c.hot_prefix = h
 
     @property
     def ref(self):

@@ -79,6 +79,7 @@ sfnn_status check_pred(const sfnn_pred* p) {
   if (p->wtype != SFNN_F32 && p->wtype != SFNN_F16) return SFNN_E_DTYPE;
   if (!dmodel_ok(p->d_model) || !dff_ok(p->d_ff) || p->rank < 8 || p->rank > 2048 || p->rank % 8)
     return SFNN_E_SHAPE;
+  if (p->hot_prefix < 0 || p->hot_prefix > p->d_ff || p->hot_prefix % 64) return SFNN_E_SHAPE;
   if (!al16(p->w1_t) || !al16(p->w2_t) || !al16(p->tau)) return SFNN_E_ALIGN;
   return SFNN_OK;
 }
@@ -121,6 +122,7 @@ PredLaunch pred_launch(const sfnn_pred* p, const void* x, int batch, uint64_t* m
   L.mask = mask;
   L.union_mask = uni;
   L.logits = logits;
+  L.hot = p->hot_prefix / 64;
   return L;
 }
 
@@ -484,6 +486,6 @@ const char* sfnn_status_str(sfnn_status s) {
   return "unknown status";
 }
 
-int32_t sfnn_version(void) { return 310; }  // 300: sfnn_ffn.mfma_min_batch; 310: sfnn_input_sparse_gemv
+int32_t sfnn_version(void) { return 320; }  // 300: sfnn_ffn.mfma_min_batch; 310: sfnn_input_sparse_gemv; 320: sfnn_pred.hot_prefix
 
 }  // extern "C"

@@ -378,4 +378,18 @@ __device__ __forceinline__ float load_as_float(const void* p, int i) {
   return (float)reinterpret_cast<const XT*>(p)[i];
 }
 
+// Mask word vb of the dense hot prefix: its 64 neurons are taken for every
+// token without reading their predictor rows or thresholds; the logits read
+// +inf.  Any workgroup size that is a multiple of 64 threads.
+__device__ __forceinline__ void pred2_hot_word(uint64_t* mask, uint64_t* union_mask, float* logits, int f,
+                                               int tok0, int nt, int vb) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nw = blockDim.x / kWave;
+  for (int t = threadIdx.x / kWave; t < nt; t += nw) {
+    if (lane == 0) mask[(size_t)(tok0 + t) * (f / 64) + vb] = ~0ull;
+    if (logits) logits[(size_t)(tok0 + t) * f + vb * 64 + lane] = __builtin_inff();
+  }
+  if (threadIdx.x == 0) union_mask[vb] = ~0ull;
+}
+
 }  // namespace sfnn

@@ -52,6 +52,7 @@ struct Pred2MfmaArgs {
   uint64_t* union_mask;   // [f/64]
   float* logits;          // [B][f] or null
   int f, r, tok0, nt, first_pass;
+  int hot;                // mask words [0, hot) form the dense hot prefix
 };
 
 template <int NB>
@@ -148,6 +149,10 @@ __global__ __launch_bounds__(512) void k_pred2_mfma(Pred2MfmaArgs a) {
   __shared__ f32x4 red[8][2][NB][kWave];  // two row tiles at a time
   __shared__ unsigned char bits[32][64];  // [token][neuron of the word]
   __shared__ unsigned long long wsh[32];
+  if ((int)blockIdx.x < a.hot) {  // uniform over the workgroup
+    pred2_hot_word(a.mask, a.union_mask, a.logits, a.f, a.tok0, a.nt, blockIdx.x);
+    return;
+  }
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int rr = lane & 15, g = lane >> 4;
   const int r = a.r;
@@ -333,6 +338,7 @@ hipError_t launch_pred2_mfma(const PredLaunch& p, hipStream_t s) {
   a.logits = p.logits;
   a.f = p.f;
   a.r = p.r;
+  a.hot = p.hot;
   const dim3 grid(p.f / 64);
   for (int tok0 = 0; tok0 < p.batch; tok0 += 32) {
     a.tok0 = tok0;

@@ -87,6 +87,7 @@ Pred2Args pred2_args(const PredLaunch& p, int tok0, int nt) {
   a.tok0 = tok0;
   a.nt = nt;
   a.first_pass = tok0 == 0 ? 1 : 0;
+  a.hot = p.hot;
   return a;
 }
 

@@ -37,6 +37,7 @@ struct PredLaunch {
   uint64_t* mask;    // [B][f/64]
   uint64_t* union_mask;  // [f/64] OR of the batch's masks (always written)
   float* logits;     // [B][f] or null
+  int hot = 0;       // leading mask words taken for every token (dense hot prefix)
 };
 hipError_t launch_predict(const PredLaunch& p, hipStream_t s);
 // Token-group size the predictor uses for this shape (power of two <= kMaxNT).

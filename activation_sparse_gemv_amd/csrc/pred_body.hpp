@@ -242,6 +242,7 @@ struct Pred2Args {
   uint64_t* union_mask; // [f/64]
   float* logits;        // [B][f] or null
   int f, r, tok0, nt, first_pass;
+  int hot;              // mask words [0, hot) form the dense hot prefix
 };
 
 // Stage 2 for virtual workgroup vb (mask word vb): 8 waves (512 threads) of 8
@@ -251,6 +252,10 @@ __device__ __forceinline__ void pred2_body(const Pred2Args& a, int vb) {
   constexpr int E = vec_elems<WT>();  // 4 (fp32) or 8 (fp16) weights per vector
   __shared__ float lg[NT][64];
   __shared__ unsigned long long wsh[NT];
+  if (vb < a.hot) {  // uniform over the workgroup: no barrier below is reached
+    pred2_hot_word(a.mask, a.union_mask, a.logits, a.f, a.tok0, a.nt, vb);
+    return;
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int r = a.r, f = a.f;

@@ -51,6 +51,9 @@ def _parse():
                     help="instead of the stack: sparse vs dense FFN per layer over batch sizes and fire rates")
     ap.add_argument("--sweep-batches", default="1,2,4,8,16,32")
     ap.add_argument("--sweep-rhos", default="0.05,0.1,0.2")
+    ap.add_argument("--hot-prefix", default="0",
+                    help="dense hot prefix of power-law workloads: a neuron count (multiple of 64) or 'auto' "
+                         "(chosen per layer from the profiled fire rates of the batch's union)")
     ap.add_argument("--isg", action="store_true",
                     help="time the input-sparse GEMV (ReLU after the norm) over input densities and batches")
     return ap.parse_args()
@@ -144,8 +147,12 @@ def main():
           file=sys.stderr, flush=True)
 
     # ---- hot-first relayout for power-law workloads -------------------------
+    hots = [0] * nd
     if spec.profile == "zipf":
-        _hot_first(sg, distinct, spec, B, dev)
+        hots = _hot_first(sg, distinct, spec, B, dev, args.hot_prefix)
+    elif args.hot_prefix != "0":
+        sys.exit("a dense hot prefix needs the hot-first relayout of a power-law workload (c3, c4)")
+    hot_mean = float(np.mean([hots[l % nd] for l in range(L)]))
 
     xdt = torch.float32 if spec.wtype == "f32" else torch.float16
     ntok = args.steps + args.warmup
@@ -219,7 +226,7 @@ def main():
     pb = 4 if spec.pred_dtype == "f32" else 2
     nmat = spec.n_mat
     ffn_bytes_u = lambda u: u * nmat * row_bytes + u * (nmat - 1) * xb          # noqa: E731
-    pred_bytes = (d * r + r * f) * pb + 4 * f
+    pred_bytes = (d * r + r * (f - hot_mean)) * pb + 4 * (f - hot_mean)  # hot-prefix rows are not read
     ffn_bytes = ffn_bytes_u(mean_u)
 
     out = {
@@ -239,6 +246,7 @@ def main():
                                f"{'' if nd == L else f' (weights of {nd} distinct layers cycled)'}, d_model {d}, d_ff {f}, "
                                f"rank-{r} predictor, {spec.act}, {spec.wtype}, "
                                f"{'zipf phi=%.2f ' % spec.phi if spec.profile == 'zipf' else ''}rho={spec.rho}"
+                               f"{', dense hot prefix %s' % args.hot_prefix if hot_mean else ''}"
                                f"{', look-ahead predictor' if lookahead else ', per-layer predictor'}",
                    "global_batch": B, "decode_steps": args.steps, "layers": L,
                    "predictor": "look-ahead (layer l+1 from x_l)" if lookahead else "per layer (layer l from x_l)"},
@@ -247,6 +255,8 @@ def main():
     extra = {"mean_active_neurons": round(mean_u, 1), "active_fraction": round(mean_u / f, 4),
              "ffn_active_bytes_per_layer": int(ffn_bytes), "predictor_bytes_per_layer": int(pred_bytes),
              "setup_s": round(t_setup, 1)}
+    if hot_mean:
+        extra["hot_prefix_per_layer"] = hots
     extra["layer_GBps_stack"] = round(L * (ffn_bytes + pred_bytes) / (ms_per_step / 1e3) / 1e9, 1)
     key = "tokens_s_per_layer_predictor" if lookahead else "tokens_s_lookahead_predictor"
     extra[key] = round(B / (other_ms / 1e3), 2)
@@ -318,7 +328,8 @@ def main():
     # predictor; its time: the step's HIP-event time divided by the layers
     us_layer_stack = ms_per_step * 1e3 / L
     layer_bytes = ffn_bytes + pred_bytes
-    workload_key = f"{spec.name}/b{B}/{'lookahead' if lookahead else 'per-layer'}"
+    workload_key = (f"{spec.name}/b{B}/{'lookahead' if lookahead else 'per-layer'}"
+                    f"{'/hot%s' % args.hot_prefix if hot_mean else ''}")
     tr = _stored_traffic(workload_key)
     out["roofline"] = {
         "bound": "hbm", "achieved": round(layer_bytes / us_layer_stack / 1e3, 1), "peak": HBM_PEAK_GBS,
@@ -488,17 +499,23 @@ def _isg_sweep(args):
     print(json.dumps({"isg_sweep": points}), flush=True)
 
 
-def _hot_first(sg, layers, spec, B, dev):
-    """Profile fire counts on seeded tokens, then relayout each layer hot-first."""
+def _hot_first(sg, layers, spec, B, dev, hot_arg="0"):
+    """Offline profile: fire counts of seeded tokens give the hot-first
+    relayout of each distinct layer; then, for hot_arg 'auto', a few stack
+    steps on other seeded tokens give each neuron's fire rate in the batch's
+    union on the decode path itself, which sets the layer's dense hot prefix.
+    Returns the prefix per distinct layer (``layers`` is cycled through the
+    stack)."""
     import torch
     import synth
     from activation_sparse_gemv_amd.device import to_dev, workspace
-    f, d = spec.d_ff, spec.d_model
+    f, d, L, nd = spec.d_ff, spec.d_model, spec.n_layers, len(layers)
+    W = f // 64
     nprof = 256
     xs = to_dev(synth.make_tokens(spec, nprof, stream=99))
     for pred, ffn in layers:
         ws = workspace(pred, None, 8)
-        m = torch.zeros((nprof, f // 64), dtype=torch.uint64, device=dev)
+        m = torch.zeros((nprof, W), dtype=torch.uint64, device=dev)
         for i in range(0, nprof, 8):
             sg.sfnn_predict(pred, xs[i:i + 8], 8, m[i:i + 8], None, ws)
         counts = torch.zeros(f, dtype=torch.int32, device=dev)
@@ -515,6 +532,44 @@ def _hot_first(sg, layers, spec, B, dev):
             rb = t.numel() * t.element_size() // f
             sg.sfnn_gather_rows(src, pd, f, rb, t)
         torch.cuda.synchronize()
+    if hot_arg != "auto":
+        for pred, _ in layers:
+            pred.hot_prefix = int(hot_arg)
+        return [int(hot_arg)] * nd
+    steps = max(8, 256 // B)
+    st = sg.Stack([layers[l % nd] for l in range(L)])
+    xr = to_dev(synth.make_tokens(spec, steps * B, stream=98, dtype=np.float32)).view(steps, B, d)
+    rout = torch.empty((B, d), dtype=torch.float32, device=dev)
+    ws = workspace(layers[0][0], layers[0][1], B)
+    mc = torch.zeros((L, B, W), dtype=torch.uint64, device=dev)
+    hits = np.zeros((nd, f))
+    for t in range(steps):
+        sg.sfnn_stack_decode(st, B, xr[t], rout, 1e-6, ws, mask_cap=mc)
+        uw = np.bitwise_or.reduce(mc.cpu().numpy(), axis=1)                       # [L][W]
+        bits = np.unpackbits(uw.view(np.uint8), axis=1, bitorder="little")[:, :f]  # [L][f]
+        for l in range(L):
+            hits[l % nd] += bits[l]
+    n = np.array([steps * len(range(k, L, nd)) for k in range(nd)], dtype=np.float64)
+    hots = []
+    for k, (pred, _) in enumerate(layers):
+        pred.hot_prefix = _auto_hot_prefix(spec, hits[k] / n[k])
+        hots.append(pred.hot_prefix)
+    return hots
+
+
+def _auto_hot_prefix(spec, urate):
+    """Leading mask words (hot-first order) worth running as a dense block: a
+    word joins while computing its 64 neurons for every token reads fewer bytes
+    than predicting them, i.e. while sum(1 - u_i) FFN rows < 64 predictor rows,
+    where u_i is the neuron's fire rate in the batch's union."""
+    d, r = spec.d_model, spec.rank
+    wb = {"f32": 4.0, "f16": 2.0, "i4g128": 0.5 + 2.0 / 128}[spec.wtype]
+    ffn_row = spec.n_mat * d * wb
+    pred_row = r * (4 if spec.pred_dtype == "f32" else 2) + 4
+    w = 0
+    while w < spec.d_ff // 64 and (1.0 - urate[64 * w:64 * w + 64]).sum() * ffn_row < 64 * pred_row:
+        w += 1
+    return 64 * w
 
 
 def _cpu_baseline(lay, spec, B, L, budget_s):

@@ -68,13 +68,25 @@ typedef enum { SFNN_RELU = 0, SFNN_REGLU = 1 } sfnn_act;
  * must match the activation type of x.  An F16 predictor called with 8 or
  * more tokens runs on the matrix cores (fp32 accumulation, z carried as two
  * fp16 parts: 22 significant bits, |z| within fp16's range); smaller batches
- * and F32 predictors take the per-row kernels. */
+ * and F32 predictors take the per-row kernels.
+ *
+ * Dense hot prefix.  With the neurons in hot-first order (sfnn_fire_counts,
+ * sfnn_hot_first_perm, sfnn_gather_rows: [53ai] PowerInfer 概述 and
+ * 单层计算优化, hot neurons are found offline and carry most activations)
+ * the first hot_prefix neurons (a multiple of 64, at most d_ff; 0 turns it
+ * off) are taken for every token without reading their W2^T rows or tau:
+ * their mask bits are set, their logits (when asked for) read +inf, and the
+ * FFN computes them for every token, so their own ReLU / ReGLU decides their
+ * share exactly.  This saves their rank * element-size predictor bytes per
+ * neuron; it pays when the union of the batch fires them nearly always.
+ * Outside [0, d_ff] or not a multiple of 64: SFNN_E_SHAPE. */
 typedef struct sfnn_pred {
   int32_t d_model, d_ff, rank;
   int32_t wtype;       /* sfnn_wtype: F32 or F16                         */
   const void* w1_t;    /* [rank][d_model]                                */
-  const void* w2_t;    /* [d_ff][rank]                                   */
-  const float* tau;    /* [d_ff]                                         */
+  const void* w2_t;    /* [d_ff][rank] (rows below hot_prefix unread)    */
+  const float* tau;    /* [d_ff]       (entries below hot_prefix unread) */
+  int32_t hot_prefix;  /* dense hot prefix, see above; 0: none           */
 } sfnn_pred;
 
 /* One FFN layer.  ReLU:  y = b_down + sum_i relu(W_up[i].x + b_up[i]) W_down[:, i]
@@ -249,7 +261,7 @@ sfnn_status sfnn_input_sparse_gemv(const sfnn_isg* op, const void* x, int32_t ba
                                    void* stream);
 
 const char* sfnn_status_str(sfnn_status s);
-int32_t sfnn_version(void);  /* 300 and up: sfnn_ffn has mfma_min_batch; 310 and up: sfnn_input_sparse_gemv */
+int32_t sfnn_version(void);  /* 300 and up: sfnn_ffn has mfma_min_batch; 310 and up: sfnn_input_sparse_gemv; 320 and up: sfnn_pred has hot_prefix */
 
 #ifdef __cplusplus
 }

@@ -35,7 +35,7 @@ def test_exports_match_header(L):
 
 def test_version_and_status_strings(L):
     import activation_sparse_gemv_amd as m
-    assert m.sfnn_version() >= 100
+    assert m.sfnn_version() >= 320
     assert m.sfnn_status_str(0) == "ok"
     assert "workspace" in m.sfnn_status_str(5)
 
@@ -57,6 +57,12 @@ def test_validation_rejects_without_launching(L):
     assert L.sfnn_predict(ctypes.byref(p), fake, 1, fake, None, fake, 16, None) == 5          # workspace
     p.wtype = 2
     assert L.sfnn_predict(ctypes.byref(p), fake, 1, fake, None, fake, 1 << 30, None) == 4     # INT4 predictor
+    for hot in (32, -64, 3072 + 64):  # dense hot prefix: a multiple of 64 within [0, d_ff]
+        p = P(768, 3072, 128, 0, fake, fake, fake, hot)
+        assert L.sfnn_predict(ctypes.byref(p), fake, 1, fake, None, fake, 1 << 30, None) == 2
+        assert L.sfnn_workspace_bytes(ctypes.byref(p), None, 1) == 0
+    p = P(768, 3072, 128, 0, fake, fake, fake, 3072)
+    assert L.sfnn_workspace_bytes(ctypes.byref(p), None, 1) > 0
     f = F(768, 3072, 1, 1, fake, None, fake, None, None, None, None, None, None)         # ReGLU w/o gate
     assert L.sfnn_sparse_ffn(ctypes.byref(f), fake, 1, fake, fake, None, fake, fake, 1 << 30, None) == 1
     f = F(700, 3072, 1, 0, fake, None, fake, None, None, None, None, None, None)         # d_model % 128

@@ -21,11 +21,12 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3
 
 
-def _stack_case(spec, L, B, seed=0, lookahead=False, mfma_min_batch=0):
+def _stack_case(spec, L, B, seed=0, lookahead=False, mfma_min_batch=0, hot_prefix=0):
     lays = [synth.make_layer(spec, layer=l, seed=seed) for l in range(L)]
     dev = [upload_layer(lay) for lay in lays]
-    for _, ffn in dev:
+    for pred, ffn in dev:
         ffn.mfma_min_batch = mfma_min_batch
+        pred.hot_prefix = hot_prefix
     r_in = synth.make_tokens(spec, B, stream=200 + B, dtype=np.float32) * np.float32(3.0)
     xdt = torch.float32 if spec.wtype == "f32" else torch.float16
     out = gpu_stack(dev, r_in, 1e-6, xdt, flags=1 if lookahead else 0)
@@ -41,7 +42,7 @@ def _stack_case(spec, L, B, seed=0, lookahead=False, mfma_min_batch=0):
         # mask: threshold of the predictor on its input (x_l, or x_{l-1} when
         # looking ahead), outside the fp32 rounding band
         xp = xs if (not lookahead or l == 0) else out["x"][l - 1].astype(spec.x_dtype)
-        ol, ob = oracle.predict(lay.w1_t, lay.w2_t, lay.tau, xp)
+        ol, ob = oracle.predict(lay.w1_t, lay.w2_t, lay.tau, xp, hot_prefix=hot_prefix)
         band = oracle.guard_band(lay.w1_t, lay.w2_t, xp)
         gb = oracle.unpack_mask(out["mask"][l], f)
         outside = np.abs(ol - lay.tau[None, :].astype(np.float64)) > band
@@ -139,6 +140,19 @@ def test_stack_lookahead_opt6_7b_full_width():
 def test_stack_lookahead_int4_wide():
     """d_model 12288 INT4 (32 columns per thread in the down projection), 2 layers."""
     _stack_case(synth.config("c5", d_ff=4096, rank=256, n_layers=2), 2, 1, lookahead=True)
+
+
+# dense hot prefix (the first neurons taken for every token): per-layer and
+# look-ahead schedules, per-row and matrix-core batches
+@pytest.mark.parametrize("B", [1, 9])
+def test_stack_hot_prefix(B):
+    _stack_case(synth.config("c4", d_model=768, d_ff=2048, rank=64, n_layers=3), 3, B, hot_prefix=512)
+
+
+@pytest.mark.parametrize("B", [1, 2, 9])
+def test_stack_lookahead_hot_prefix(B):
+    _stack_case(synth.config("c2", d_model=1024, d_ff=4096, rank=128, n_layers=3), 3, B, lookahead=True,
+                hot_prefix=1024)
 
 
 def test_stack_bad_flags_rejected():
