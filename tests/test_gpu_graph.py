@@ -82,6 +82,28 @@ def test_graph_stack_lookahead():
     _replays(run, lambda a: r_in.copy_(to_dev(a)), inputs)
 
 
+@pytest.mark.parametrize("B", [1, 9])
+def test_graph_stack_lookahead_hot_prefix(B):
+    """Look-ahead stack with a dense hot prefix; batch 9 runs the matrix-core predictor."""
+    spec = synth.config("c2", d_model=768, d_ff=3072, rank=96, n_layers=3)
+    lays = [synth.make_layer(spec, layer=l) for l in range(3)]
+    dev = [upload_layer(l) for l in lays]
+    for pred, _ in dev:
+        pred.hot_prefix = 512
+    st = sg.Stack(dev)
+    r_in = torch.empty((B, 768), dtype=torch.float32, device="cuda")
+    r_out = torch.empty((B, 768), dtype=torch.float32, device="cuda")
+    mc = torch.zeros((3, B, 3072 // 64), dtype=torch.uint64, device="cuda")
+    ws = workspace(dev[0][0], dev[0][1], B)
+
+    def run():
+        sg.sfnn_stack_decode(st, B, r_in, r_out, 1e-6, ws, flags=sg.SFNN_STACK_LOOKAHEAD, mask_cap=mc)
+        return [r_out, mc]
+
+    inputs = [synth.make_tokens(spec, B, stream=320 + k, dtype=np.float32) * np.float32(3.0) for k in range(3)]
+    _replays(run, lambda a: r_in.copy_(to_dev(a)), inputs)
+
+
 @pytest.mark.parametrize("B", [1, 6])
 def test_graph_input_sparse_gemv(B):
     w_t, b = synth.make_isg_weights(1024, 2048, "f16", seed=5, key=5)
