@@ -40,6 +40,9 @@ def _parse():
     ap.add_argument("--per-layer-predictor", action="store_true",
                     help="time the schedule that predicts every layer from its own input "
                          "(default: the look-ahead schedule, layer l+1 predicted from layer l's input)")
+    ap.add_argument("--read-sizes", action="store_true",
+                    help="time one read-probe launch per size (4 MB .. 512 MB), each on a region not read "
+                         "for the last 32 launches, so neither L2 nor the memory-side cache serves it")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run the copy kernel over 1 GiB, 4 times (traffic-counter calibration)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
@@ -106,6 +109,9 @@ def main():
     import activation_sparse_gemv_amd as sg
     from activation_sparse_gemv_amd.device import to_dev, upload_layer, workspace
 
+    if args.read_sizes:
+        _read_sizes(sg)
+        return
     if args.copy_probe:
         src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -497,6 +503,39 @@ def _isg_sweep(args):
                      and q["input_density"] == 1.0)
         pt["speedup_vs_all_rows"] = round(dense["us"] / pt["us"], 2)
     print(json.dumps({"isg_sweep": points}), flush=True)
+
+
+def _read_sizes(sg):
+    """Single-launch read rate against size: the ceiling for a kernel that
+    streams S bytes in one launch (launch ramp and drain included)."""
+    import torch
+    total = 3 << 30
+    buf = torch.empty(total, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    rows = []
+    for mb in (4, 8, 16, 24, 34, 40, 64, 128, 512):
+        size, n = mb << 20, 32
+        views = [buf[o:o + size] for o in (((k * (size + (1 << 20))) % (total - size)) & ~0xFFF for k in range(n))]
+        for v in views[:2]:
+            sg.sfnn_probe_read(v, size, sink)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for v in views:
+                sg.sfnn_probe_read(v, size, sink)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(4):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (4 * n)
+        rows.append({"MB": mb, "us_per_launch": round(us, 2), "GBps": round(size / us / 1e3, 1)})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    print(json.dumps({"read_sizes": rows}), flush=True)
 
 
 def _hot_first(sg, layers, spec, B, dev, hot_arg="0"):
