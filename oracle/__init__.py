@@ -21,4 +21,6 @@ from .ffn import (  # noqa: F401
     permute_layer_ids,
     residual_rmsnorm,
     input_sparse_gemv,
+    head_qkv,
+    head_out,
 )

@@ -16,6 +16,9 @@ Pages cited (by title and section):
   example, INT4 paragraph.
 * [ciyun] the ciyundata.com survey "LLM inference optimisation techniques",
   section 2.2 量化 (weight-only quantisation dequantised inside the kernel).
+* [53ai] sections "如何充分利用结构化稀疏进行加速" and "验证上下文稀疏存在"
+  (contextual sparsity covers attention heads as well as MLP neurons: a
+  predictor picks the heads per input, up to 80% of heads are skipped).
 * [53ai] section "第二阶段——插入新的ReLU" (relufication stage 2: a ReLU after
   the normalisation layer makes the inputs of the up and QKV projections
   sparse).
@@ -45,6 +48,7 @@ __all__ = [
     "unpack_mask", "pack_mask", "predict", "guard_band", "compact", "dequant_int4",
     "rows_f64", "masked_ffn", "dense_ffn", "true_active", "fire_counts",
     "hot_first_perm", "permute_layer_ids", "residual_rmsnorm", "input_sparse_gemv",
+    "head_qkv", "head_out",
 ]
 
 _U24 = 2.0 ** -24
@@ -300,3 +304,50 @@ def input_sparse_gemv(w_t, x, bias=None, return_f64: bool = False):
         y += xb[:, j:j + 1] * w_t[j].astype(np.float64)[None, :]
     return (y if return_f64 else y.astype(np.float32)), J
 
+
+
+# ---------------------------------------------------------------------------
+# head-gated attention projections ([53ai] 如何充分利用结构化稀疏进行加速 and
+# 验证上下文稀疏存在: only the heads predicted for an input are computed)
+# ---------------------------------------------------------------------------
+
+def head_qkv(w_qkv, b_qkv, x, head_bits, head_dim: int, return_f64: bool = False):
+    """Q, K and V projections of the heads each token uses.
+
+    w_qkv [3 H hd][d]: the q rows of head h are h*hd .. h*hd + hd - 1, then the
+    k rows (offset H*hd) and the v rows (offset 2*H*hd).  out[t, r] is
+    w_qkv[r] . x_t + b_qkv[r] when the head of row r is on for token t, else 0
+    (a skipped head produces nothing).  head_bits [B][H] bool.
+    """
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    w = np.asarray(w_qkv, dtype=np.float64)
+    hb = np.atleast_2d(np.asarray(head_bits, dtype=bool))
+    n = w.shape[0]
+    H = n // (3 * head_dim)
+    b = np.zeros(n) if b_qkv is None else np.asarray(b_qkv, dtype=np.float64)
+    dense = x @ w.T + b[None, :]
+    head_of_row = (np.arange(n) % (H * head_dim)) // head_dim
+    out = np.where(hb[:, head_of_row], dense, 0.0)
+    return out if return_f64 else out.astype(np.float32)
+
+
+def head_out(w_o_t, b_o, attn, head_bits, head_dim: int, return_f64: bool = False):
+    """Output projection over the heads each token uses.
+
+    w_o_t [H hd][d] holds W_o's columns as rows (row j = column j); y_t =
+    b_o + sum over heads h on for token t of attn_t[h hd : (h+1) hd] @ w_o_t
+    [h hd : (h+1) hd].  Rows of heads that no token uses are never read.
+    """
+    a = np.atleast_2d(np.asarray(attn, dtype=np.float64))
+    hb = np.atleast_2d(np.asarray(head_bits, dtype=bool))
+    wt = np.asarray(w_o_t)
+    B, n_in = a.shape
+    d = wt.shape[1]
+    H = n_in // head_dim
+    y = np.zeros((B, d)) if b_o is None else np.tile(np.asarray(b_o, dtype=np.float64), (B, 1))
+    for t in range(B):
+        for h in range(H):
+            if hb[t, h]:
+                rows = slice(h * head_dim, (h + 1) * head_dim)
+                y[t] += a[t, rows] @ wt[rows].astype(np.float64)
+    return y if return_f64 else y.astype(np.float32)

@@ -536,3 +536,70 @@ def test_relu_inputs_density():
     # density 1: the dense input, negative values kept
     x = synth.make_relu_inputs(512, 4, 1.0, dtype=np.float32)
     assert (x < 0).any() and (x != 0).all()
+
+
+# ---------------------------------------------------------------------------
+# head-gated attention projections
+# ---------------------------------------------------------------------------
+
+def _heads(d, H, hd, seed):
+    g = np.random.default_rng(seed)
+    return (g.normal(0, 0.5, (3 * H * hd, d)), g.normal(0, 0.5, 3 * H * hd),
+            g.normal(0, 0.5, (H * hd, d)), g.normal(0, 0.5, d))
+
+
+def test_head_qkv_brute_force():
+    d, H, hd, B = 6, 3, 2, 2
+    w, b, _, _ = _heads(d, H, hd, 1)
+    x = np.random.default_rng(2).normal(0, 1, (B, d))
+    bits = np.array([[True, False, True], [False, False, True]])
+    out = oracle.head_qkv(w, b, x, bits, hd, return_f64=True)
+    for t in range(B):
+        for blk in range(3):                      # q, k, v blocks
+            for h in range(H):
+                for i in range(hd):
+                    r = blk * H * hd + h * hd + i
+                    ref = b[r]
+                    for k in range(d):
+                        ref += w[r, k] * x[t, k]
+                    assert out[t, r] == (pytest.approx(ref, rel=1e-12, abs=1e-12) if bits[t, h] else 0.0)
+
+
+def test_head_out_brute_force():
+    d, H, hd, B = 5, 3, 2, 2
+    _, _, wo, bo = _heads(d, H, hd, 3)
+    a = np.random.default_rng(4).normal(0, 1, (B, H * hd))
+    bits = np.array([[True, True, False], [False, True, False]])
+    y = oracle.head_out(wo, bo, a, bits, hd, return_f64=True)
+    for t in range(B):
+        for c in range(d):
+            ref = bo[c]
+            for h in range(H):
+                if bits[t, h]:
+                    for i in range(hd):
+                        ref += a[t, h * hd + i] * wo[h * hd + i, c]
+            assert y[t, c] == pytest.approx(ref, rel=1e-12, abs=1e-12)
+
+
+def test_head_projections_closed_forms():
+    """All heads: the dense projections (x W^T + b, attn W_o + b_o); no heads:
+    zeros and b_o exactly; rows of unused heads are never read (NaN-poisoned);
+    the output projection equals the input-sparse GEMV of the head-masked
+    attention output."""
+    d, H, hd, B = 16, 4, 8, 3
+    w, b, wo, bo = _heads(d, H, hd, 5)
+    x = np.random.default_rng(6).normal(0, 1, (B, d))
+    a = np.random.default_rng(7).normal(0, 1, (B, H * hd))
+    on = np.ones((B, H), dtype=bool)
+    off = np.zeros((B, H), dtype=bool)
+    assert np.allclose(oracle.head_qkv(w, b, x, on, hd, True), x @ w.T + b, rtol=1e-13, atol=1e-13)
+    assert np.allclose(oracle.head_out(wo, bo, a, on, hd, True), a @ wo + bo, rtol=1e-13, atol=1e-13)
+    assert not oracle.head_qkv(w, b, x, off, hd, True).any()
+    assert np.array_equal(oracle.head_out(wo, bo, a, off, hd, True), np.tile(bo, (B, 1)))
+    bits = np.array([[True, False, False, True], [False, False, False, True], [True, False, False, False]])
+    wo_p = wo.copy()
+    wo_p[hd:3 * hd] = np.nan                      # heads 1 and 2: used by no token
+    assert np.array_equal(oracle.head_out(wo_p, bo, a, bits, hd, True), oracle.head_out(wo, bo, a, bits, hd, True))
+    gated = a * np.repeat(bits, hd, axis=1)
+    y_isg, _ = oracle.input_sparse_gemv(wo, gated, bo, return_f64=True)
+    assert np.allclose(oracle.head_out(wo, bo, a, bits, hd, True), y_isg, rtol=1e-13, atol=1e-13)
