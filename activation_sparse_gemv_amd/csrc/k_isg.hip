@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void k_isg(IsgArgs a) {
     for (int k = 0; k < RB; ++k) {
       int j = jn[k];
       const bool ok = sb + k < s1 && j >= 0 && j < a.n_in;
-      j = ok ? j : 0;
+      j = (j >= 0 && j < a.n_in) ? j : 0;  // past the group: the group's last listed row, times 0
       isg_row<XT>(w + (size_t)j * a.n_out + colc, v[k]);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {

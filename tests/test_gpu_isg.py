@@ -98,6 +98,24 @@ def test_isg_unlisted_rows_never_read():
     assert np.array_equal(y, y2)
 
 
+@pytest.mark.parametrize("wt,B", [("f16", 1), ("f16", 2), ("f32", 3), ("f16", 5)])
+def test_isg_unlisted_rows_never_read_row0_off(wt, B):
+    """Per-row kernel (fp16 below 4 tokens, fp32) and matrix cores: input 0 is
+    zero for every token and its row is NaN; the slots past each workgroup's
+    share of the list must re-read a listed row, never row 0."""
+    w_t, b, x = _case(1024, 2048, B, 0.3, wt, seed=62 + B)
+    x[:, 0] = 0
+    y, cols, c = _run(w_t, b, x)
+    off = np.ones(1024, dtype=bool)
+    off[cols[:c]] = False
+    assert off[0]
+    w2 = w_t.copy()
+    w2[off] = np.nan
+    y2, _, c2 = _run(w2, b, x)
+    assert np.isfinite(y2).all() and c2 == c
+    assert np.array_equal(y, y2)
+
+
 @pytest.mark.parametrize("B", [3, 6])
 def test_isg_zero_input_gives_bias_bitwise(B):
     w_t, b, _ = _case(256, 512, 1, 0.5, "f16", seed=61)
