@@ -26,7 +26,8 @@ EXPORTS = [
     "sfnn_workspace_bytes", "sfnn_predict", "sfnn_compact", "sfnn_sparse_ffn", "sfnn_dense_ffn",
     "sfnn_layer", "sfnn_stack_decode", "sfnn_residual_rmsnorm", "sfnn_fire_counts", "sfnn_hot_first_perm",
     "sfnn_gather_rows", "sfnn_probe_read", "sfnn_probe_copy", "sfnn_status_str", "sfnn_version",
-    "sfnn_isg_workspace_bytes", "sfnn_input_sparse_gemv",
+    "sfnn_isg_workspace_bytes", "sfnn_input_sparse_gemv", "sfnn_heads_workspace_bytes", "sfnn_head_qkv",
+    "sfnn_head_out",
 ]
 
 
@@ -56,6 +57,12 @@ class sfnn_isg(ctypes.Structure):
                 ("w_t", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
 
 
+class sfnn_heads(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("wtype", ctypes.c_int32), ("w_qkv", ctypes.c_void_p), ("b_qkv", ctypes.c_void_p),
+                ("w_o_t", ctypes.c_void_p), ("b_o", ctypes.c_void_p)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -70,6 +77,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     L = ctypes.CDLL(path)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     P, F, G = ctypes.POINTER(sfnn_pred), ctypes.POINTER(sfnn_ffn), ctypes.POINTER(sfnn_isg)
+    Hd = ctypes.POINTER(sfnn_heads)
     sig = {
         "sfnn_workspace_bytes": (sz, [P, F, i32]),
         "sfnn_predict": (i32, [P, vp, i32, vp, vp, vp, sz, vp]),
@@ -87,6 +95,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sfnn_status_str": (ctypes.c_char_p, [i32]),
         "sfnn_isg_workspace_bytes": (sz, [G, i32]),
         "sfnn_input_sparse_gemv": (i32, [G, vp, i32, vp, vp, vp, vp, sz, vp]),
+        "sfnn_heads_workspace_bytes": (sz, [Hd, i32]),
+        "sfnn_head_qkv": (i32, [Hd, vp, i32, vp, vp, vp]),
+        "sfnn_head_out": (i32, [Hd, vp, i32, vp, vp, vp, sz, vp]),
         "sfnn_version": (i32, []),
     }
     for name, (res, args) in sig.items():
@@ -293,6 +304,34 @@ def sfnn_status_str(code: int) -> str:
 
 def sfnn_version() -> int:
     return int(load().sfnn_version())
+
+
+class Heads:
+    """Device descriptor of one attention block's projections (keeps its tensors
+    alive): w_qkv [3 H hd][d], w_o_t [H hd][d] fp16 or fp32, biases or None."""
+
+    def __init__(self, w_qkv: torch.Tensor, w_o_t: torch.Tensor, head_dim: int, b_qkv=None, b_o=None):
+        self.t = dict(w_qkv=w_qkv, w_o_t=w_o_t, b_qkv=b_qkv, b_o=b_o)
+        n, d = w_o_t.shape
+        self.d_model, self.head_dim, self.n_heads = d, head_dim, n // head_dim
+        self.c = sfnn_heads(d, self.n_heads, head_dim, _wtype_of(w_qkv), _p(w_qkv), _p(b_qkv), _p(w_o_t), _p(b_o))
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def sfnn_heads_workspace_bytes(op: Heads, batch: int) -> int:
+    return int(load().sfnn_heads_workspace_bytes(op.ref, batch))
+
+
+def sfnn_head_qkv(op: Heads, x, batch: int, head_mask, qkv, stream=None):
+    _check("sfnn_head_qkv", load().sfnn_head_qkv(op.ref, _p(x), batch, _p(head_mask), _p(qkv), _s(stream)))
+
+
+def sfnn_head_out(op: Heads, attn, batch: int, head_mask, y, ws, stream=None):
+    _check("sfnn_head_out", load().sfnn_head_out(op.ref, _p(attn), batch, _p(head_mask), _p(y), _p(ws),
+                                                 ws.numel() * ws.element_size(), _s(stream)))
 
 
 def sfnn_isg_workspace_bytes(op: Isg, batch: int) -> int:

@@ -17,7 +17,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsfnn.so")
 SOURCES = ["api.hip", "k_predict.hip", "k_ffn.hip", "k_ffn_f32.hip", "k_ffn_f16.hip", "k_ffn_i4.hip",
            "k_lookahead.hip", "k_la_f32.hip", "k_la_f16.hip", "k_la_i4.hip", "k_misc.hip",
-           "k_mfma.hip", "k_mfma_i4.hip", "k_pred_mfma.hip", "k_isg.hip"]
+           "k_mfma.hip", "k_mfma_i4.hip", "k_pred_mfma.hip", "k_isg.hip", "k_heads.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -442,16 +442,11 @@ size_t sfnn_isg_workspace_bytes(const sfnn_isg* op, int32_t batch) {
   return isg_layout(op, batch).total;
 }
 
-sfnn_status sfnn_input_sparse_gemv(const sfnn_isg* op, const void* x, int32_t batch, float* y, int32_t* cols,
-                                   int32_t* count, void* ws, size_t ws_bytes, void* stream) {
-  sfnn_status st = check_isg(op);
-  if (st != SFNN_OK) return st;
-  if (!x || !y || !ws) return SFNN_E_NULL;
-  if (!batch_ok(batch)) return SFNN_E_SHAPE;
-  if (!al16(x) || !al16(y) || !al16(cols) || !al4(count) || !al16(ws)) return SFNN_E_ALIGN;
-  const IsgLayout Lw = isg_layout(op, batch);
-  if (ws_bytes < Lw.total) return SFNN_E_WORKSPACE;
-  char* w = (char*)ws;
+namespace {
+
+// The input-sparse GEMV once the arguments are checked; w: its workspace.
+sfnn_status run_isg(const sfnn_isg* op, const void* x, int32_t batch, float* y, int32_t* cols, int32_t* count,
+                    char* w, const IsgLayout& Lw, hipStream_t s) {
   IsgLaunch L;
   L.wt = op->wtype == SFNN_F32 ? WT_F32 : WT_F16;
   L.n_in = op->n_in;
@@ -470,7 +465,89 @@ sfnn_status sfnn_input_sparse_gemv(const sfnn_isg* op, const void* x, int32_t ba
     L.hbuf = w + Lw.hbuf;
     L.sidbuf = reinterpret_cast<int32_t*>(w + Lw.sid);
   }
-  return hip_status(launch_isg(L, as_stream(stream)));
+  return hip_status(launch_isg(L, s));
+}
+
+// Head-gated projections: shapes the kernels and the input-sparse GEMV accept.
+sfnn_status check_heads(const sfnn_heads* op) {
+  if (!op || !op->w_qkv || !op->w_o_t) return SFNN_E_NULL;
+  if (op->wtype != SFNN_F32 && op->wtype != SFNN_F16) return SFNN_E_DTYPE;
+  const long n = (long)op->n_heads * op->head_dim;
+  if (!dmodel_ok(op->d_model) || op->n_heads < 1 || op->head_dim < 8 || op->head_dim > 512 ||
+      op->head_dim % 8 || n % 64 || n > 65536)
+    return SFNN_E_SHAPE;
+  if (!al16(op->w_qkv) || !al16(op->b_qkv) || !al16(op->w_o_t) || !al16(op->b_o)) return SFNN_E_ALIGN;
+  return SFNN_OK;
+}
+
+sfnn_isg isg_of(const sfnn_heads* op) {
+  sfnn_isg g;
+  g.n_in = op->n_heads * op->head_dim;
+  g.n_out = op->d_model;
+  g.wtype = op->wtype;
+  g.w_t = op->w_o_t;
+  g.bias = op->b_o;
+  return g;
+}
+
+}  // namespace
+
+sfnn_status sfnn_input_sparse_gemv(const sfnn_isg* op, const void* x, int32_t batch, float* y, int32_t* cols,
+                                   int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  sfnn_status st = check_isg(op);
+  if (st != SFNN_OK) return st;
+  if (!x || !y || !ws) return SFNN_E_NULL;
+  if (!batch_ok(batch)) return SFNN_E_SHAPE;
+  if (!al16(x) || !al16(y) || !al16(cols) || !al4(count) || !al16(ws)) return SFNN_E_ALIGN;
+  const IsgLayout Lw = isg_layout(op, batch);
+  if (ws_bytes < Lw.total) return SFNN_E_WORKSPACE;
+  return run_isg(op, x, batch, y, cols, count, (char*)ws, Lw, as_stream(stream));
+}
+
+size_t sfnn_heads_workspace_bytes(const sfnn_heads* op, int32_t batch) {
+  if (check_heads(op) == SFNN_E_SHAPE || !op || !batch_ok(batch)) return 0;
+  const sfnn_isg g = isg_of(op);
+  const size_t gated = up((size_t)batch * g.n_in * (op->wtype == SFNN_F32 ? 4 : 2));
+  return gated + isg_layout(&g, batch).total;
+}
+
+sfnn_status sfnn_head_qkv(const sfnn_heads* op, const void* x, int32_t batch, const uint64_t* head_mask, float* qkv,
+                          void* stream) {
+  sfnn_status st = check_heads(op);
+  if (st != SFNN_OK) return st;
+  if (!x || !head_mask || !qkv) return SFNN_E_NULL;
+  if (!batch_ok(batch)) return SFNN_E_SHAPE;
+  if (!al16(x) || !al16(head_mask) || !al16(qkv)) return SFNN_E_ALIGN;
+  HeadQkvLaunch L;
+  L.wt = op->wtype == SFNN_F32 ? WT_F32 : WT_F16;
+  L.d = op->d_model;
+  L.H = op->n_heads;
+  L.hd = op->head_dim;
+  L.w_qkv = op->w_qkv;
+  L.b_qkv = op->b_qkv;
+  L.x = x;
+  L.batch = batch;
+  L.head_mask = head_mask;
+  L.out = qkv;
+  return hip_status(launch_head_qkv(L, as_stream(stream)));
+}
+
+sfnn_status sfnn_head_out(const sfnn_heads* op, const void* attn, int32_t batch, const uint64_t* head_mask, float* y,
+                          void* ws, size_t ws_bytes, void* stream) {
+  sfnn_status st = check_heads(op);
+  if (st != SFNN_OK) return st;
+  if (!attn || !head_mask || !y || !ws) return SFNN_E_NULL;
+  if (!batch_ok(batch)) return SFNN_E_SHAPE;
+  if (!al16(attn) || !al16(head_mask) || !al16(y) || !al16(ws)) return SFNN_E_ALIGN;
+  if (ws_bytes < sfnn_heads_workspace_bytes(op, batch)) return SFNN_E_WORKSPACE;
+  const sfnn_isg g = isg_of(op);
+  const int wt = op->wtype == SFNN_F32 ? WT_F32 : WT_F16;
+  const size_t gated = up((size_t)batch * g.n_in * (wt == WT_F32 ? 4 : 2));
+  char* w = (char*)ws;
+  const hipStream_t s = as_stream(stream);
+  if (launch_head_gate(wt, attn, batch, op->n_heads, op->head_dim, head_mask, w, s) != hipSuccess)
+    return SFNN_E_HIP;
+  return run_isg(&g, w, batch, y, nullptr, nullptr, w + gated, isg_layout(&g, batch), s);
 }
 
 const char* sfnn_status_str(sfnn_status s) {
@@ -486,6 +563,6 @@ const char* sfnn_status_str(sfnn_status s) {
   return "unknown status";
 }
 
-int32_t sfnn_version(void) { return 320; }  // 300: sfnn_ffn.mfma_min_batch; 310: sfnn_input_sparse_gemv; 320: sfnn_pred.hot_prefix
+int32_t sfnn_version(void) { return 330; }  // 300: sfnn_ffn.mfma_min_batch; 310: sfnn_input_sparse_gemv; 320: sfnn_pred.hot_prefix; 330: head-gated projections
 
 }  // extern "C"

@@ -131,6 +131,23 @@ struct IsgLaunch {
   int32_t* sidbuf = nullptr;  // matrix-core path: [n_in] slot -> input
 };
 hipError_t launch_isg(const IsgLaunch& p, hipStream_t s);
+
+// ---- head-gated attention projections ----------------------------------------
+
+struct HeadQkvLaunch {
+  int wt;                      // WT_F32 | WT_F16 (weights, biases and x)
+  int d, H, hd;
+  const void* w_qkv;           // [3 H hd][d]
+  const void* b_qkv;           // [3 H hd] or null
+  const void* x;               // [B][d]
+  int batch;
+  const uint64_t* head_mask;   // [B][ceil(H/64)]
+  float* out;                  // [B][3 H hd]
+};
+hipError_t launch_head_qkv(const HeadQkvLaunch& p, hipStream_t s);
+// out[t][j] = attn[t][j] if head j / hd is on for token t, else 0 ([B][H hd], x's type)
+hipError_t launch_head_gate(int wt, const void* attn, int batch, int H, int hd, const uint64_t* head_mask,
+                            void* out, hipStream_t s);
 int isg_groups(int n_out, int max_groups);
 // fp16 inputs from this batch size on run on the matrix cores (the listed
 // rows' products through k_down_mfma); the IsgLaunch then needs hbuf / sidbuf.

@@ -261,7 +261,42 @@ sfnn_status sfnn_input_sparse_gemv(const sfnn_isg* op, const void* x, int32_t ba
                                    void* stream);
 
 const char* sfnn_status_str(sfnn_status s);
-int32_t sfnn_version(void);  /* 300 and up: sfnn_ffn has mfma_min_batch; 310 and up: sfnn_input_sparse_gemv; 320 and up: sfnn_pred has hot_prefix */
+/* Head-gated attention projections ([53ai] 如何充分利用结构化稀疏进行加速 and
+ * 验证上下文稀疏存在: contextual sparsity covers attention heads as well as
+ * MLP neurons; the heads each input uses are predicted and up to 80% of heads
+ * are skipped).  The attention between the two projections (scores, softmax,
+ * values) is the caller's.  Weights, biases, x and attn share one type (F32 or
+ * F16); outputs are fp32.  head_mask: [batch][ceil(n_heads/64)] packed uint64
+ * words, bit h%64 of word h/64 set when token t uses head h (the caller's
+ * head predictor).  Limits: d_model as elsewhere, head_dim a multiple of 8 in
+ * [8, 512], n_heads * head_dim a multiple of 64 and at most 65536. */
+typedef struct sfnn_heads {
+  int32_t d_model, n_heads, head_dim;
+  int32_t wtype;       /* SFNN_F32 or SFNN_F16                           */
+  const void* w_qkv;   /* [3 n_heads head_dim][d_model]: the q rows of all
+                          heads (head h: rows h*head_dim ..), then k, then v */
+  const void* b_qkv;   /* [3 n_heads head_dim] or NULL                   */
+  const void* w_o_t;   /* [n_heads head_dim][d_model]: row j = column j of W_o */
+  const void* b_o;     /* [d_model] or NULL                              */
+} sfnn_heads;
+
+/* qkv[t][r] = w_qkv[r] . x_t + b_qkv[r] for the rows r of heads on for token
+ * t, and 0 for the rest ([batch][3 n_heads head_dim] fp32, caller-owned).
+ * Rows of heads that no token of the batch uses are not read. */
+sfnn_status sfnn_head_qkv(const sfnn_heads* op, const void* x, int32_t batch, const uint64_t* head_mask,
+                          float* qkv, void* stream);
+
+/* y_t = b_o + sum over heads h on for token t of attn_t[h head_dim ..
+ * (h+1) head_dim) . w_o_t[the same rows] ([batch][d_model] fp32).  attn:
+ * [batch][n_heads head_dim]; the entries of heads off for a token are not
+ * used (may hold anything).  Runs as the input-sparse GEMV of the head-masked
+ * attn, so rows whose input is zero for every token, the unused heads among
+ * them, are not read.  ws: sfnn_heads_workspace_bytes(op, batch) bytes. */
+sfnn_status sfnn_head_out(const sfnn_heads* op, const void* attn, int32_t batch, const uint64_t* head_mask,
+                          float* y, void* ws, size_t ws_bytes, void* stream);
+size_t sfnn_heads_workspace_bytes(const sfnn_heads* op, int32_t batch);
+
+int32_t sfnn_version(void);  /* 300 and up: sfnn_ffn has mfma_min_batch; 310 and up: sfnn_input_sparse_gemv; 320 and up: sfnn_pred has hot_prefix; 330 and up: sfnn_head_qkv, sfnn_head_out */
 
 #ifdef __cplusplus
 }

@@ -22,4 +22,6 @@ from .workload import (  # noqa: F401
     pack_bits,
     make_isg_weights,
     make_relu_inputs,
+    make_head_weights,
+    make_head_masks,
 )

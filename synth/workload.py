@@ -477,3 +477,34 @@ def make_relu_inputs(n_in: int, n: int, density: float, seed: int = 0, stream: i
         x = np.maximum(z - np.float32(theta), np.float32(0.0))
     return x.astype(dtype)
 
+
+
+# ---- head-gated attention projections ----------------------------------------
+
+_T_HEAD_W, _T_HEAD_B, _T_HEAD_M = 210, 211, 212
+
+
+def make_head_weights(d: int, n_heads: int, head_dim: int, wtype: str = "f16", seed: int = 0,
+                      bias: bool = True):
+    """One attention block's projections in storage layout, N(0, 0.02^2):
+    w_qkv [3 H hd][d] (q rows of all heads, then k, then v), b_qkv [3 H hd],
+    w_o_t [H hd][d] (row j is column j of W_o), b_o [d] (biases None when
+    ``bias`` is False).  Storage dtype fp16 or fp32."""
+    dt = np.float32 if wtype == "f32" else np.float16
+    n = n_heads * head_dim
+    w_qkv = _normal((3 * n, d), 0.02, dt, seed, (_T_HEAD_W, 0))
+    w_o_t = _normal((n, d), 0.02, dt, seed, (_T_HEAD_W, 1))
+    b_qkv = _normal((3 * n,), 0.02, dt, seed, (_T_HEAD_B, 0)) if bias else None
+    b_o = _normal((d,), 0.02, dt, seed, (_T_HEAD_B, 1)) if bias else None
+    return w_qkv, b_qkv, w_o_t, b_o
+
+
+def make_head_masks(batch: int, n_heads: int, density: float, seed: int = 0):
+    """Per-token head sets: each head on with probability ``density`` (the
+    pages report up to 80% of heads skipped, i.e. density 0.2).  Returns the
+    bits [B][H] and the packed words [B][ceil(H/64)]."""
+    g = _stream(seed, (_T_HEAD_M, batch, n_heads))
+    bits = g.random((batch, n_heads)) < density
+    pad = np.zeros((batch, (n_heads + 63) // 64 * 64), dtype=bool)
+    pad[:, :n_heads] = bits
+    return bits, pack_bits(pad)

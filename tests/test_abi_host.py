@@ -123,3 +123,26 @@ def test_isg_validation_and_workspace(L):
     assert L.sfnn_input_sparse_gemv(ctypes.byref(ok), fake + 4, 1, fake, None, None, fake, 1 << 30, None) == 3
     assert L.sfnn_input_sparse_gemv(ctypes.byref(ok), fake, 1, fake, None, fake + 2, fake, 1 << 30, None) == 3
     assert L.sfnn_input_sparse_gemv(ctypes.byref(ok), fake, 1, fake, None, None, fake, 64, None) == 5
+
+
+def test_heads_validation_and_workspace(L):
+    import activation_sparse_gemv_amd as m
+    H = m._lib.sfnn_heads
+    fake = 1 << 20
+    ok = H(4096, 32, 128, 1, fake, None, fake, None)
+    ws = L.sfnn_heads_workspace_bytes(ctypes.byref(ok), 1)
+    assert ws >= 32 * 128 * 2 + 4096 * 4 and L.sfnn_heads_workspace_bytes(ctypes.byref(ok), 8) > ws
+    assert L.sfnn_heads_workspace_bytes(ctypes.byref(ok), 0) == 0
+    assert L.sfnn_head_qkv(None, fake, 1, fake, fake, None) == 1
+    assert L.sfnn_head_qkv(ctypes.byref(ok), fake, 1, None, fake, None) == 1          # no head mask
+    for bad in (H(4096, 32, 12, 1, fake, None, fake, None),    # head_dim % 8
+                H(4096, 3, 8, 1, fake, None, fake, None),      # n_heads * head_dim % 64
+                H(4000, 32, 128, 1, fake, None, fake, None),   # d_model % 128
+                H(4096, 1024, 128, 1, fake, None, fake, None)):  # n_heads * head_dim > 65536
+        assert L.sfnn_head_qkv(ctypes.byref(bad), fake, 1, fake, fake, None) == 2
+        assert L.sfnn_heads_workspace_bytes(ctypes.byref(bad), 1) == 0
+    assert L.sfnn_head_qkv(ctypes.byref(H(4096, 32, 128, 2, fake, None, fake, None)), fake, 1, fake, fake,
+                           None) == 4                                                 # INT4
+    assert L.sfnn_head_qkv(ctypes.byref(ok), fake, 65, fake, fake, None) == 2
+    assert L.sfnn_head_qkv(ctypes.byref(ok), fake + 4, 1, fake, fake, None) == 3
+    assert L.sfnn_head_out(ctypes.byref(ok), fake, 1, fake, fake, fake, 16, None) == 5
