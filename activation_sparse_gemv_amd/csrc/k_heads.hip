@@ -6,7 +6,9 @@
 //
 //   k_head_qkv   workgroup = 8 consecutive rows of W_qkv (4 wavefronts x 2
 //                rows; head_dim is a multiple of 8, so the 8 rows belong to
-//                one head) x a group of NT tokens.  A workgroup whose head is
+//                one head) x a group of NT tokens.  The token groups of one
+//                row block run on one XCD, next to each other in the grid, so
+//                the second group onwards finds the rows in that XCD's L2.  A workgroup whose head is
 //                off for all its tokens writes zeros and reads no weight.
 //                Otherwise x is staged in LDS and each wavefront streams its
 //                two rows with 16-byte loads, kHeadUB vectors per lane per row
@@ -43,8 +45,14 @@ __global__ __launch_bounds__(256) void k_head_qkv(HeadQkvArgs a) {
   using XT = typename std::conditional<WT == WT_F32, float, f16>::type;
   extern __shared__ __align__(16) unsigned char smem[];
   XT* xs = reinterpret_cast<XT*>(smem);
-  const int row0 = blockIdx.x * kHeadRows;
-  const int tok0 = blockIdx.y * NT;
+  // linear block b: XCD b % 8; row block = 8 (b / 8 / NG) + b % 8, token
+  // group (b / 8) % NG
+  const int NG = (a.B + NT - 1) / NT;
+  const int rest = blockIdx.x / 8;
+  const int rb = (rest / NG) * 8 + blockIdx.x % 8;
+  if (rb >= a.n / kHeadRows) return;  // padding of the last 8 row blocks
+  const int row0 = rb * kHeadRows;
+  const int tok0 = (rest % NG) * NT;
   const int nt = a.B - tok0 < NT ? a.B - tok0 : NT;
   const int head = (row0 % (a.H * a.hd)) / a.hd;
   bool on[NT];
@@ -131,10 +139,11 @@ __global__ __launch_bounds__(256) void k_head_gate(const u32x4* __restrict__ att
   out[i] = on ? attn[i] : u32x4{0u, 0u, 0u, 0u};
 }
 
-// Largest token group (4, 2 or 1) whose staged x fits 64 KB of LDS.
+// Largest token group (8, 4, 2 or 1) whose staged x fits 64 KB of LDS: each
+// group re-reads the rows, so fewer groups read fewer bytes.
 int head_group(int wt, int d, int batch) {
   const int bytes = d * (wt == WT_F32 ? 4 : 2);
-  int nt = 4;
+  int nt = 8;
   while (nt > 1 && (nt * bytes > 65536 || nt / 2 >= batch)) nt /= 2;
   return nt;
 }
@@ -142,13 +151,16 @@ int head_group(int wt, int d, int batch) {
 template <int WT, int NT>
 void qkv_launch(const HeadQkvArgs& a, hipStream_t s) {
   const size_t sh = (size_t)NT * a.d * (WT == WT_F32 ? 4 : 2);
-  const dim3 grid(a.n / kHeadRows, (a.B + NT - 1) / NT);
+  const int nrb8 = (a.n / kHeadRows + 7) / 8 * 8;  // row blocks, padded to whole XCD rounds
+  const dim3 grid(nrb8 * ((a.B + NT - 1) / NT));
   hipLaunchKernelGGL((k_head_qkv<WT, NT>), grid, dim3(256), sh, s, a);
 }
 
 template <int WT>
 void qkv_dispatch(const HeadQkvArgs& a, int nt, hipStream_t s) {
-  if (nt == 4)
+  if (nt == 8)
+    qkv_launch<WT, 8>(a, s);
+  else if (nt == 4)
     qkv_launch<WT, 4>(a, s);
   else if (nt == 2)
     qkv_launch<WT, 2>(a, s);

@@ -40,6 +40,9 @@ def _parse():
     ap.add_argument("--per-layer-predictor", action="store_true",
                     help="time the schedule that predicts every layer from its own input "
                          "(default: the look-ahead schedule, layer l+1 predicted from layer l's input)")
+    ap.add_argument("--heads", action="store_true",
+                    help="head-gated Q/K/V and output projections over head density and batch (OPT-6.7B and "
+                         "OPT-175B attention shapes)")
     ap.add_argument("--read-sizes", action="store_true",
                     help="time one read-probe launch per size (4 MB .. 512 MB), each on a region not read "
                          "for the last 32 launches, so neither L2 nor the memory-side cache serves it")
@@ -128,6 +131,9 @@ def main():
     spec = synth.config(args.config, **over)
     if args.isg:
         _isg_sweep(args)
+        return
+    if args.heads:
+        _heads_sweep()
         return
     if args.sweep:
         _sweep(args, spec)
@@ -503,6 +509,74 @@ def _isg_sweep(args):
                      and q["input_density"] == 1.0)
         pt["speedup_vs_all_rows"] = round(dense["us"] / pt["us"], 2)
     print(json.dumps({"isg_sweep": points}), flush=True)
+
+
+def _heads_sweep():
+    """Head-gated attention projections: sfnn_head_qkv and sfnn_head_out at the
+    OPT-6.7B (d 4096, 32 heads of 128) and OPT-175B (d 12288, 96 heads of 128)
+    attention shapes, over the fraction of heads each token uses (1.0 = every
+    head, the dense projections) and batches.  Each point cycles over distinct
+    weight copies holding at least 1 GB; HIP events around replays of one graph
+    of calls over the copies."""
+    import torch
+    import synth
+    import activation_sparse_gemv_amd as sg
+    from activation_sparse_gemv_amd.device import to_dev
+    points = []
+    for name, d, H, hd in (("opt6.7b", 4096, 32, 128), ("opt175b", 12288, 96, 128)):
+        n = H * hd
+        nc = max(2, int(np.ceil(1.0e9 / (4 * n * d * 2))))
+        ops = []
+        for c in range(nc):
+            w_qkv, b_qkv, w_o_t, b_o = synth.make_head_weights(d, H, hd, "f16", seed=c)
+            ops.append(sg.Heads(to_dev(w_qkv), to_dev(w_o_t), hd, to_dev(b_qkv), to_dev(b_o)))
+        for B in (1, 8):
+            ws = torch.empty(sg.sfnn_heads_workspace_bytes(ops[0], B), dtype=torch.uint8, device="cuda")
+            qkv = torch.empty((B, 3 * n), dtype=torch.float32, device="cuda")
+            y = torch.empty((B, d), dtype=torch.float32, device="cuda")
+            x = to_dev(synth.make_relu_inputs(d, B, 1.0, seed=1, stream=B))
+            attn = to_dev(synth.make_relu_inputs(n, B, 1.0, seed=2, stream=B))
+            for dens in (1.0, 0.5, 0.2):
+                masks = []
+                used = []
+                for c in range(nc):
+                    bits, words = synth.make_head_masks(B, H, dens, seed=800 + c)
+                    masks.append(to_dev(words))
+                    used.append(float(bits.any(axis=0).mean()))
+
+                def timed(fn):
+                    fn()
+                    torch.cuda.synchronize()
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        fn()
+                    g.replay()
+                    torch.cuda.synchronize()
+                    a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    for _ in range(8):
+                        g.replay()
+                    e.record()
+                    torch.cuda.synchronize()
+                    return a.elapsed_time(e) / (8 * nc) * 1e3
+
+                t_qkv = timed(lambda: [sg.sfnn_head_qkv(ops[c], x, B, masks[c], qkv) for c in range(nc)])
+                t_out = timed(lambda: [sg.sfnn_head_out(ops[c], attn, B, masks[c], y, ws) for c in range(nc)])
+                u = float(np.mean(used))
+                pt = {"shape": name, "batch": B, "head_density": dens, "heads_read_frac": round(u, 4),
+                      "us_qkv": round(t_qkv, 2), "us_out": round(t_out, 2),
+                      "GBps_qkv_rows_read": round(u * 3 * n * d * 2 / t_qkv / 1e3, 1),
+                      "GBps_out_rows_read": round(u * n * d * 2 / t_out / 1e3, 1)}
+                points.append(pt)
+                print(json.dumps(pt), file=sys.stderr, flush=True)
+        del ops
+        torch.cuda.empty_cache()
+    for pt in points:
+        dense = next(q for q in points if q["shape"] == pt["shape"] and q["batch"] == pt["batch"]
+                     and q["head_density"] == 1.0)
+        pt["speedup_qkv_vs_all_heads"] = round(dense["us_qkv"] / pt["us_qkv"], 2)
+        pt["speedup_out_vs_all_heads"] = round(dense["us_out"] / pt["us_out"], 2)
+    print(json.dumps({"heads_sweep": points}), flush=True)
 
 
 def _read_sizes(sg):
