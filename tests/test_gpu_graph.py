@@ -120,3 +120,28 @@ def test_graph_input_sparse_gemv(B):
 
     inputs = [synth.make_relu_inputs(1024, B, 0.3, seed=k, stream=B) for k in range(3)]
     _replays(run, lambda a: x.copy_(to_dev(a)), inputs)
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_graph_head_projections(B):
+    d, H, hd = 1024, 16, 64
+    w_qkv, b_qkv, w_o_t, b_o = synth.make_head_weights(d, H, hd, "f16", seed=13)
+    op = sg.Heads(to_dev(w_qkv), to_dev(w_o_t), hd, to_dev(b_qkv), to_dev(b_o))
+    x = torch.empty((B, d), dtype=torch.float16, device="cuda")
+    attn = torch.empty((B, H * hd), dtype=torch.float16, device="cuda")
+    hm = torch.zeros((B, 1), dtype=torch.uint64, device="cuda")
+    qkv = torch.empty((B, 3 * H * hd), dtype=torch.float32, device="cuda")
+    y = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(sg.sfnn_heads_workspace_bytes(op, B), dtype=torch.uint8, device="cuda")
+
+    def run():
+        sg.sfnn_head_qkv(op, x, B, hm, qkv)
+        sg.sfnn_head_out(op, attn, B, hm, y, ws)
+        return [qkv, y]
+
+    def set_input(k):
+        x.copy_(to_dev(synth.make_relu_inputs(d, B, 1.0, seed=k, stream=1)))
+        attn.copy_(to_dev(synth.make_relu_inputs(H * hd, B, 1.0, seed=k, stream=2)))
+        hm.copy_(to_dev(synth.make_head_masks(B, H, 0.3, seed=k)[1]))
+
+    _replays(run, set_input, [330, 331, 332])
