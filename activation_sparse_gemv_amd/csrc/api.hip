@@ -446,8 +446,9 @@ namespace {
 
 // The input-sparse GEMV once the arguments are checked; w: its workspace.
 sfnn_status run_isg(const sfnn_isg* op, const void* x, int32_t batch, float* y, int32_t* cols, int32_t* count,
-                    char* w, const IsgLayout& Lw, hipStream_t s) {
+                    char* w, const IsgLayout& Lw, hipStream_t s, bool listed = false) {
   IsgLaunch L;
+  L.listed = listed;
   L.wt = op->wtype == SFNN_F32 ? WT_F32 : WT_F16;
   L.n_in = op->n_in;
   L.n_out = op->n_out;
@@ -545,9 +546,12 @@ sfnn_status sfnn_head_out(const sfnn_heads* op, const void* attn, int32_t batch,
   const size_t gated = up((size_t)batch * g.n_in * (wt == WT_F32 ? 4 : 2));
   char* w = (char*)ws;
   const hipStream_t s = as_stream(stream);
-  if (launch_head_gate(wt, attn, batch, op->n_heads, op->head_dim, head_mask, w, s) != hipSuccess)
+  const IsgLayout Lw = isg_layout(&g, batch);
+  int32_t* ids = reinterpret_cast<int32_t*>(w + gated + Lw.ids);
+  int32_t* cnt = reinterpret_cast<int32_t*>(w + gated + Lw.count);
+  if (launch_head_gate(wt, attn, batch, op->n_heads, op->head_dim, head_mask, w, ids, cnt, s) != hipSuccess)
     return SFNN_E_HIP;
-  return run_isg(&g, w, batch, y, nullptr, nullptr, w + gated, isg_layout(&g, batch), s);
+  return run_isg(&g, w, batch, y, ids, cnt, w + gated, Lw, s, true);
 }
 
 const char* sfnn_status_str(sfnn_status s) {

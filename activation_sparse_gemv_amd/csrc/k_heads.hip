@@ -16,8 +16,10 @@
 //                and token; a token whose head is off gets 0.
 //   k_head_gate  x'[t][j] = attn[t][j] if head j / hd is on for token t, else
 //                0.  The output projection is then the input-sparse GEMV of
-//                x' (W_o^T stored input-major): the rows of heads that no
-//                token uses are skipped with their zeros.
+//                x' (W_o^T stored input-major) over the rows of the heads some
+//                token uses: workgroup 0 also lists those rows in ascending
+//                order (heads flagged per thread, ballot scan in head order),
+//                so the GEMV needs no nonzero scan and no compaction launch.
 //
 // Each sum is taken in a fixed order: results are bitwise deterministic.
 #include <type_traits>
@@ -127,16 +129,42 @@ __global__ __launch_bounds__(256) void k_head_qkv(HeadQkvArgs a) {
   }
 }
 
-// One thread per 16-byte vector of attn ([B][H hd] in x's type).
+// One thread per 16-byte vector of attn ([B][H hd] in x's type); workgroup 0
+// then writes the rows of the used heads to ids and their number to count.
 template <int WT>
-__global__ __launch_bounds__(256) void k_head_gate(const u32x4* __restrict__ attn, int B, int nvec_row, int hd_vec,
+__global__ __launch_bounds__(256) void k_head_gate(const u32x4* __restrict__ attn, int B, int H, int hd,
                                                    const uint64_t* __restrict__ hmask, int words,
-                                                   u32x4* __restrict__ out) {
+                                                   u32x4* __restrict__ out, int32_t* __restrict__ ids,
+                                                   int32_t* __restrict__ count) {
+  constexpr int E = WT == WT_F32 ? 4 : 8;
+  const int nvec_row = H * hd / E, hd_vec = hd / E;
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= B * nvec_row) return;
-  const int t = i / nvec_row, head = (i - t * nvec_row) / hd_vec;
-  const bool on = (hmask[(size_t)t * words + (head >> 6)] >> (head & 63)) & 1ull;
-  out[i] = on ? attn[i] : u32x4{0u, 0u, 0u, 0u};
+  if (i < B * nvec_row) {
+    const int t = i / nvec_row, head = (i - t * nvec_row) / hd_vec;
+    const bool on = (hmask[(size_t)t * words + (head >> 6)] >> (head & 63)) & 1ull;
+    out[i] = on ? attn[i] : u32x4{0u, 0u, 0u, 0u};
+  }
+  if (blockIdx.x != 0) return;  // uniform: the list below is workgroup 0's alone
+  __shared__ int wsum[4];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  int base = 0;
+  for (int h0 = 0; h0 < H; h0 += 256) {  // 256 heads per round, in head order
+    const int h = h0 + threadIdx.x;
+    bool used = false;
+    if (h < H)
+      for (int t = 0; t < B; ++t) used = used || ((hmask[(size_t)t * words + (h >> 6)] >> (h & 63)) & 1ull);
+    const unsigned long long bal = __ballot(used);
+    const int below = __popcll(bal & ((1ull << lane) - 1ull));
+    __syncthreads();  // the previous round's totals have been read
+    if (lane == 0) wsum[wave] = __popcll(bal);
+    __syncthreads();
+    int pos = base + below;
+    for (int w = 0; w < wave; ++w) pos += wsum[w];
+    if (used)
+      for (int r = 0; r < hd; ++r) ids[(size_t)pos * hd + r] = h * hd + r;
+    base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  }
+  if (threadIdx.x == 0) *count = base * hd;
 }
 
 // Largest token group (8, 4, 2 or 1) whose staged x fits 64 KB of LDS: each
@@ -192,16 +220,16 @@ hipError_t launch_head_qkv(const HeadQkvLaunch& p, hipStream_t s) {
 }
 
 hipError_t launch_head_gate(int wt, const void* attn, int batch, int H, int hd, const uint64_t* head_mask,
-                            void* out, hipStream_t s) {
+                            void* out, int32_t* ids, int32_t* count, hipStream_t s) {
   const int E = wt == WT_F32 ? 4 : 8;
-  const int nvec_row = H * hd / E, hd_vec = hd / E;
-  const int n = batch * nvec_row;
+  const int n = batch * (H * hd / E);
+  const dim3 grid((n + 255) / 256);
   if (wt == WT_F32)
-    hipLaunchKernelGGL(k_head_gate<WT_F32>, dim3((n + 255) / 256), dim3(256), 0, s, (const u32x4*)attn, batch,
-                       nvec_row, hd_vec, head_mask, (H + 63) / 64, (u32x4*)out);
+    hipLaunchKernelGGL(k_head_gate<WT_F32>, grid, dim3(256), 0, s, (const u32x4*)attn, batch, H, hd, head_mask,
+                       (H + 63) / 64, (u32x4*)out, ids, count);
   else
-    hipLaunchKernelGGL(k_head_gate<WT_F16>, dim3((n + 255) / 256), dim3(256), 0, s, (const u32x4*)attn, batch,
-                       nvec_row, hd_vec, head_mask, (H + 63) / 64, (u32x4*)out);
+    hipLaunchKernelGGL(k_head_gate<WT_F16>, grid, dim3(256), 0, s, (const u32x4*)attn, batch, H, hd, head_mask,
+                       (H + 63) / 64, (u32x4*)out, ids, count);
   return hipGetLastError();
 }
 

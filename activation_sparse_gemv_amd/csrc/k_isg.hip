@@ -209,15 +209,17 @@ static void isg_all(const IsgLaunch& p, hipStream_t s) {
 }
 
 hipError_t launch_isg(const IsgLaunch& p, hipStream_t s) {
-  const int words = p.n_in / 64;
-  if (p.wt == WT_F32)
-    hipLaunchKernelGGL(k_isg_mask<float>, dim3((words + 3) / 4), dim3(256), 0, s, (const float*)p.x, p.batch,
-                       p.n_in, p.mask);
-  else
-    hipLaunchKernelGGL(k_isg_mask<f16>, dim3((words + 3) / 4), dim3(256), 0, s, (const f16*)p.x, p.batch, p.n_in,
-                       p.mask);
-  hipError_t e = launch_compact(p.mask, 1, p.n_in, p.ids, p.count, nullptr, s);
-  if (e != hipSuccess) return e;
+  if (!p.listed) {
+    const int words = p.n_in / 64;
+    if (p.wt == WT_F32)
+      hipLaunchKernelGGL(k_isg_mask<float>, dim3((words + 3) / 4), dim3(256), 0, s, (const float*)p.x, p.batch,
+                         p.n_in, p.mask);
+    else
+      hipLaunchKernelGGL(k_isg_mask<f16>, dim3((words + 3) / 4), dim3(256), 0, s, (const f16*)p.x, p.batch,
+                         p.n_in, p.mask);
+    const hipError_t e = launch_compact(p.mask, 1, p.n_in, p.ids, p.count, nullptr, s);
+    if (e != hipSuccess) return e;
+  }
   int groups = p.groups;
   if (p.wt == WT_F16 && p.batch >= kIsgMfmaMinBatch && p.hbuf && p.sidbuf) {
     groups = mfma_groups(p.n_out, p.groups);

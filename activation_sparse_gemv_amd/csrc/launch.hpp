@@ -121,6 +121,7 @@ struct IsgLaunch {
   const void* bias;       // [n_out] or null
   const void* x;          // [B][n_in]
   int batch;
+  bool listed = false;    // ids / count already hold the inputs to read: no nonzero scan
   uint64_t* mask;         // [n_in/64] workspace: inputs nonzero for some token
   int32_t* ids;           // [n_in] the listed inputs
   int32_t* count;         // [1]
@@ -145,9 +146,10 @@ struct HeadQkvLaunch {
   float* out;                  // [B][3 H hd]
 };
 hipError_t launch_head_qkv(const HeadQkvLaunch& p, hipStream_t s);
-// out[t][j] = attn[t][j] if head j / hd is on for token t, else 0 ([B][H hd], x's type)
+// out[t][j] = attn[t][j] if head j / hd is on for token t, else 0 ([B][H hd], x's type);
+// ids / count: the rows of the heads some token uses, ascending, and how many
 hipError_t launch_head_gate(int wt, const void* attn, int batch, int H, int hd, const uint64_t* head_mask,
-                            void* out, hipStream_t s);
+                            void* out, int32_t* ids, int32_t* count, hipStream_t s);
 int isg_groups(int n_out, int max_groups);
 // fp16 inputs from this batch size on run on the matrix cores (the listed
 // rows' products through k_down_mfma); the IsgLaunch then needs hbuf / sidbuf.
