@@ -10,10 +10,11 @@
 //                row block run on one XCD, next to each other in the grid, so
 //                the second group onwards finds the rows in that XCD's L2.  A workgroup whose head is
 //                off for all its tokens writes zeros and reads no weight.
-//                Otherwise x is staged in LDS and each wavefront streams its
-//                two rows with 16-byte loads, kHeadUB vectors per lane per row
-//                in flight, fp32 accumulation, one wavefront reduction per row
-//                and token; a token whose head is off gets 0.
+//                Otherwise x is staged in LDS, in chunks of d_model that keep
+//                the group's x within 64 KB, and each wavefront streams its two
+//                rows chunk by chunk with 16-byte loads, kHeadUB vectors per
+//                lane per row in flight, fp32 accumulation, one wavefront
+//                reduction per row and token; a token whose head is off gets 0.
 //   k_head_gate  x'[t][j] = attn[t][j] if head j / hd is on for token t, else
 //                0.  The output projection is then the input-sparse GEMV of
 //                x' (W_o^T stored input-major) over the rows of the heads some
@@ -32,6 +33,12 @@ namespace {
 
 constexpr int kHeadRows = 8;  // rows of W_qkv per workgroup
 constexpr int kHeadUB = 4;    // 16-byte vectors per lane per row in flight
+
+// x vectors per token staged in LDS at a time: NT tokens fill at most 64 KB.
+template <int NT>
+__host__ __device__ constexpr int head_chunk(int nvec) {
+  return nvec < 4096 / NT ? nvec : 4096 / NT;
+}
 
 struct HeadQkvArgs {
   const uint8_t* w;       // [n][d]
@@ -71,14 +78,9 @@ __global__ __launch_bounds__(256) void k_head_qkv(HeadQkvArgs a) {
     return;
   }
 
-  const int nvec = a.d * (int)sizeof(XT) / 16;
-  for (int i = threadIdx.x; i < nt * nvec; i += blockDim.x) {
-    const int t = i / nvec, v = i - t * nvec;
-    reinterpret_cast<u32x4*>(xs)[i] = ld16(reinterpret_cast<const uint8_t*>(a.x) + ((size_t)(tok0 + t) * nvec + v) * 16);
-  }
-  __syncthreads();
-
   constexpr int E = WT == WT_F32 ? 4 : 8;  // elements per 16-byte vector
+  const int nvec = a.d * (int)sizeof(XT) / 16;
+  const int cvec = head_chunk<NT>(nvec);   // x vectors per token staged at a time
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int r0 = row0 + 2 * wave;
   const uint8_t* wr0 = a.w + (size_t)r0 * nvec * 16;
@@ -86,26 +88,36 @@ __global__ __launch_bounds__(256) void k_head_qkv(HeadQkvArgs a) {
   float acc0[NT], acc1[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc0[t] = acc1[t] = 0.0f;
-  for (int v0 = lane; v0 < nvec; v0 += kHeadUB * kWave) {
-    u32x4 w0[kHeadUB], w1[kHeadUB];
-#pragma unroll
-    for (int u = 0; u < kHeadUB; ++u) {
-      const int v = v0 + u * kWave;
-      const int vc = v < nvec ? v : 0;  // lanes past the row re-read its first vector
-      w0[u] = ld16_stream(wr0 + 16 * (size_t)vc);
-      w1[u] = ld16_stream(wr1 + 16 * (size_t)vc);
+  for (int c0 = 0; c0 < nvec; c0 += cvec) {  // d_model in chunks of cvec vectors
+    const int cn = nvec - c0 < cvec ? nvec - c0 : cvec;
+    if (c0) __syncthreads();  // every wavefront is done with the previous chunk
+    for (int i = threadIdx.x; i < nt * cn; i += blockDim.x) {
+      const int t = i / cn, v = i - t * cn;
+      reinterpret_cast<u32x4*>(xs)[t * cvec + v] =
+          ld16(reinterpret_cast<const uint8_t*>(a.x) + ((size_t)(tok0 + t) * nvec + c0 + v) * 16);
     }
-    __builtin_amdgcn_sched_barrier(0);  // both rows' loads go out before any math
+    __syncthreads();
+    for (int v0 = lane; v0 < cn; v0 += kHeadUB * kWave) {
+      u32x4 w0[kHeadUB], w1[kHeadUB];
 #pragma unroll
-    for (int u = 0; u < kHeadUB; ++u) {
-      const int v = v0 + u * kWave;
-      if (v < nvec) {
-        if constexpr (WT == WT_F32) {
-          vec_f32<NT>(w0[u], reinterpret_cast<const float*>(xs) + E * v, a.d, acc0);
-          vec_f32<NT>(w1[u], reinterpret_cast<const float*>(xs) + E * v, a.d, acc1);
-        } else {
-          vec_f16<NT>(w0[u], reinterpret_cast<const f16*>(xs) + E * v, a.d, acc0);
-          vec_f16<NT>(w1[u], reinterpret_cast<const f16*>(xs) + E * v, a.d, acc1);
+      for (int u = 0; u < kHeadUB; ++u) {
+        const int v = v0 + u * kWave;
+        const int vc = c0 + (v < cn ? v : 0);  // lanes past the chunk re-read its first vector
+        w0[u] = ld16_stream(wr0 + 16 * (size_t)vc);
+        w1[u] = ld16_stream(wr1 + 16 * (size_t)vc);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // both rows' loads go out before any math
+#pragma unroll
+      for (int u = 0; u < kHeadUB; ++u) {
+        const int v = v0 + u * kWave;
+        if (v < cn) {
+          if constexpr (WT == WT_F32) {
+            vec_f32<NT>(w0[u], reinterpret_cast<const float*>(xs) + E * v, cvec * E, acc0);
+            vec_f32<NT>(w1[u], reinterpret_cast<const float*>(xs) + E * v, cvec * E, acc1);
+          } else {
+            vec_f16<NT>(w0[u], reinterpret_cast<const f16*>(xs) + E * v, cvec * E, acc0);
+            vec_f16<NT>(w1[u], reinterpret_cast<const f16*>(xs) + E * v, cvec * E, acc1);
+          }
         }
       }
     }
@@ -167,18 +179,18 @@ __global__ __launch_bounds__(256) void k_head_gate(const u32x4* __restrict__ att
   if (threadIdx.x == 0) *count = base * hd;
 }
 
-// Largest token group (8, 4, 2 or 1) whose staged x fits 64 KB of LDS: each
-// group re-reads the rows, so fewer groups read fewer bytes.
-int head_group(int wt, int d, int batch) {
-  const int bytes = d * (wt == WT_F32 ? 4 : 2);
+// Token group: up to 8 tokens share each pass over the rows (x is staged in
+// chunks of d_model, so any d_model fits); each group re-reads the rows.
+int head_group(int batch) {
   int nt = 8;
-  while (nt > 1 && (nt * bytes > 65536 || nt / 2 >= batch)) nt /= 2;
+  while (nt > 1 && nt / 2 >= batch) nt /= 2;
   return nt;
 }
 
 template <int WT, int NT>
 void qkv_launch(const HeadQkvArgs& a, hipStream_t s) {
-  const size_t sh = (size_t)NT * a.d * (WT == WT_F32 ? 4 : 2);
+  const int nvec = a.d * (WT == WT_F32 ? 4 : 2) / 16;
+  const size_t sh = (size_t)NT * head_chunk<NT>(nvec) * 16;
   const int nrb8 = (a.n / kHeadRows + 7) / 8 * 8;  // row blocks, padded to whole XCD rounds
   const dim3 grid(nrb8 * ((a.B + NT - 1) / NT));
   hipLaunchKernelGGL((k_head_qkv<WT, NT>), grid, dim3(256), sh, s, a);
@@ -211,7 +223,7 @@ hipError_t launch_head_qkv(const HeadQkvLaunch& p, hipStream_t s) {
   a.n = 3 * p.H * p.hd;
   a.B = p.batch;
   a.words = (p.H + 63) / 64;
-  const int nt = head_group(p.wt, p.d, p.batch);
+  const int nt = head_group(p.batch);
   if (p.wt == WT_F32)
     qkv_dispatch<WT_F32>(a, nt, s);
   else

@@ -75,6 +75,14 @@ def test_heads_fp32(B):
     _case(768, 12, 64, B, 0.5, wtype="f32", seed=3)
 
 
+@pytest.mark.parametrize("wtype,d,H,hd,B", [("f16", 16384, 8, 64, 5), ("f16", 12288, 16, 128, 8),
+                                            ("f16", 12288, 16, 128, 11), ("f32", 4096, 8, 64, 8)])
+def test_heads_qkv_chunked_x(wtype, d, H, hd, B):
+    """x staged in several d_model chunks (8 tokens of a wide d_model do not fit
+    64 KB at once), including a ragged last token group."""
+    _case(d, H, hd, B, 0.5, wtype=wtype, seed=d + B)
+
+
 def test_heads_all_and_none():
     d, H, hd, B = 1024, 16, 64, 3
     w_qkv, b_qkv, w_o_t, b_o = synth.make_head_weights(d, H, hd, "f16", seed=9)
