@@ -27,7 +27,7 @@ EXPORTS = [
     "sfnn_layer", "sfnn_stack_decode", "sfnn_residual_rmsnorm", "sfnn_fire_counts", "sfnn_hot_first_perm",
     "sfnn_gather_rows", "sfnn_probe_read", "sfnn_probe_copy", "sfnn_status_str", "sfnn_version",
     "sfnn_isg_workspace_bytes", "sfnn_input_sparse_gemv", "sfnn_heads_workspace_bytes", "sfnn_head_qkv",
-    "sfnn_head_out",
+    "sfnn_head_out", "sfnn_layer_noalloc",
 ]
 
 
@@ -85,6 +85,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sfnn_sparse_ffn": (i32, [F, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
         "sfnn_dense_ffn": (i32, [F, vp, i32, vp, vp, sz, vp]),
         "sfnn_layer": (i32, [P, F, vp, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "sfnn_layer_noalloc": (i32, [P, F, vp, i32, vp, vp, vp, vp, vp]),
         "sfnn_stack_decode": (i32, [i32, P, F, i32, vp, vp, ctypes.c_float, i32, vp, vp, vp, vp, vp, vp, sz, vp]),
         "sfnn_residual_rmsnorm": (i32, [vp, vp, vp, i32, i32, ctypes.c_float, vp, i32, vp]),
         "sfnn_fire_counts": (i32, [vp, i32, i32, vp, vp]),
@@ -244,6 +245,14 @@ def sfnn_dense_ffn(ffn: FFN, x, batch: int, y, ws, stream=None):
 def sfnn_layer(pred: Pred, ffn: FFN, x, batch: int, y, mask=None, ids=None, count=None, ws=None, stream=None):
     _check("sfnn_layer", load().sfnn_layer(pred.ref, ffn.ref, _p(x), batch, _p(y), _p(mask), _p(ids), _p(count),
                                             _p(ws), ws.numel() * ws.element_size(), _s(stream)))
+
+
+SFNN_NOALLOC_SCRATCH_BYTES = 32 << 20  # the library's per-GPU scratch array (include/sfnn.h)
+
+
+def sfnn_layer_noalloc(pred: Pred, ffn: FFN, x, batch: int, y, mask=None, ids=None, count=None, stream=None):
+    _check("sfnn_layer_noalloc", load().sfnn_layer_noalloc(pred.ref, ffn.ref, _p(x), batch, _p(y), _p(mask), _p(ids),
+                                                            _p(count), _s(stream)))
 
 
 class Stack:

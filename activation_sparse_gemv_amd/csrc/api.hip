@@ -2,6 +2,7 @@
 // sequence of each entry point.  No allocation, no host<->device copies, no
 // synchronisation: everything is enqueued on the caller's stream.
 #include <algorithm>
+#include <mutex>
 #include <numeric>
 #include <vector>
 
@@ -239,24 +240,20 @@ static sfnn_status check_pair(const sfnn_pred* pred, const sfnn_ffn* ffn) {
   return SFNN_OK;
 }
 
-sfnn_status sfnn_layer(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x, int32_t batch, float* y,
-                       uint64_t* mask, int32_t* ids, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
-  sfnn_status st = check_pair(pred, ffn);
-  if (st != SFNN_OK) return st;
-  if (!x || !y || !ws) return SFNN_E_NULL;
-  if (!batch_ok(batch)) return SFNN_E_SHAPE;
-  if (!al16(x) || !al16(y) || !al16(mask) || !al16(ids) || !al4(count) || !al16(ws)) return SFNN_E_ALIGN;
-  const Layout Lw = layout(pred, ffn, batch);
-  if (ws_bytes < Lw.total) return SFNN_E_WORKSPACE;
-  char* w = (char*)ws;
+}  // extern "C"
+
+namespace {
+
+// predict -> compact -> sparse FFN of one layer on a checked workspace w.
+sfnn_status run_layer(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x, int32_t batch, float* y,
+                      uint64_t* mask, int32_t* ids, int32_t* count, char* w, const Layout& Lw, hipStream_t s) {
   if (!mask) mask = reinterpret_cast<uint64_t*>(w + Lw.mask);
   if (!ids) ids = reinterpret_cast<int32_t*>(w + Lw.ids);
   if (!count) count = reinterpret_cast<int32_t*>(w + Lw.count);
   uint64_t* uni = reinterpret_cast<uint64_t*>(w + Lw.uni);
-  hipStream_t s = as_stream(stream);
   // predictor (writes the batch's union mask), then the FFN compacts the
   // union in its first kernel and writes ids/count on the way
-  st = do_predict(pred, x, batch, mask, uni, nullptr, reinterpret_cast<float*>(w + Lw.z), s);
+  sfnn_status st = do_predict(pred, x, batch, mask, uni, nullptr, reinterpret_cast<float*>(w + Lw.z), s);
   if (st != SFNN_OK) return st;
   FfnLaunch L = ffn_launch(ffn, x, batch, batch > 1 ? mask : nullptr, y, w, Lw);
   L.src = SRC_UNION;
@@ -264,6 +261,70 @@ sfnn_status sfnn_layer(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x
   L.ids_out = ids;
   L.count_out = count;
   return hip_status(launch_ffn(L, s));
+}
+
+sfnn_status check_layer_args(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x, int32_t batch, float* y,
+                             uint64_t* mask, int32_t* ids, int32_t* count) {
+  sfnn_status st = check_pair(pred, ffn);
+  if (st != SFNN_OK) return st;
+  if (!x || !y) return SFNN_E_NULL;
+  if (!batch_ok(batch)) return SFNN_E_SHAPE;
+  if (!al16(x) || !al16(y) || !al16(mask) || !al16(ids) || !al4(count)) return SFNN_E_ALIGN;
+  return SFNN_OK;
+}
+
+}  // namespace
+
+// The no-allocation variant's workspace: one array per GPU, held until the
+// process ends.  Host code never uses this name as an address (on the host it
+// is only a stand-in for the symbol); scratch_ptr() gives each device's own
+// address, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[SFNN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+sfnn_status scratch_ptr(char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SFNN_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SFNN_E_HIP;
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = static_cast<char*>(g_scratch_dev[dev]);
+  return SFNN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sfnn_status sfnn_layer(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x, int32_t batch, float* y,
+                       uint64_t* mask, int32_t* ids, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  sfnn_status st = check_layer_args(pred, ffn, x, batch, y, mask, ids, count);
+  if (st != SFNN_OK) return st;
+  if (!ws) return SFNN_E_NULL;
+  if (!al16(ws)) return SFNN_E_ALIGN;
+  const Layout Lw = layout(pred, ffn, batch);
+  if (ws_bytes < Lw.total) return SFNN_E_WORKSPACE;
+  return run_layer(pred, ffn, x, batch, y, mask, ids, count, (char*)ws, Lw, as_stream(stream));
+}
+
+sfnn_status sfnn_layer_noalloc(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x, int32_t batch, float* y,
+                               uint64_t* mask, int32_t* ids, int32_t* count, void* stream) {
+  sfnn_status st = check_layer_args(pred, ffn, x, batch, y, mask, ids, count);
+  if (st != SFNN_OK) return st;
+  const Layout Lw = layout(pred, ffn, batch);
+  if (Lw.total > SFNN_NOALLOC_SCRATCH_BYTES) return SFNN_E_WORKSPACE;  // checked before any HIP call
+  char* w = nullptr;
+  st = scratch_ptr(&w);
+  if (st != SFNN_OK) return st;
+  return run_layer(pred, ffn, x, batch, y, mask, ids, count, w, Lw, as_stream(stream));
 }
 
 sfnn_status sfnn_stack_decode(int32_t n_layers, const sfnn_pred* preds, const sfnn_ffn* ffns, int32_t batch,

@@ -15,9 +15,11 @@
  * Conventions shared by every call
  * --------------------------------
  *  - Every array argument is a DEVICE pointer owned by the caller; the library
- *    allocates nothing, keeps no mutable global state, and never reads a device
- *    value back to the host (no implicit synchronisation; calls can be captured
- *    in a HIP graph).  Descriptor structs are host memory, read during the call.
+ *    allocates nothing and never reads a device value back to the host (no
+ *    implicit synchronisation; calls can be captured in a HIP graph).  Its only
+ *    state is sfnn_layer_noalloc's per-GPU scratch array (see there); every
+ *    other call keeps none.  Descriptor structs are host memory, read during
+ *    the call.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Every call is asynchronous on it and uses the caller's current device.
  *  - Arguments are validated on the host before anything is launched; a bad
@@ -168,6 +170,26 @@ sfnn_status sfnn_dense_ffn(const sfnn_ffn* ffn, const void* x, int32_t batch, fl
 sfnn_status sfnn_layer(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x,
                        int32_t batch, float* y, uint64_t* mask, int32_t* ids,
                        int32_t* count, void* ws, size_t ws_bytes, void* stream);
+
+/* sfnn_layer for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, and harnesses that forbid hipMalloc.
+ * Same arguments, results and execution rules as sfnn_layer, without ws /
+ * ws_bytes: the workspace is a library-owned device array of
+ * SFNN_NOALLOC_SCRATCH_BYTES on each GPU the library runs on, held until the
+ * process ends.  The call allocates nothing (no hipMalloc / hipFree, no
+ * allocating library routine).
+ *  - Returns SFNN_E_WORKSPACE, before touching the GPU, when
+ *    sfnn_workspace_bytes(pred, ffn, batch) exceeds SFNN_NOALLOC_SCRATCH_BYTES.
+ *  - The first call on a device looks up that device's copy of the array
+ *    (SFNN_E_HIP if the lookup fails).
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's contents (nothing in it needs to start at zero).  Calls that
+ *    overlap on one GPU (two streams, or two host threads) race on it and
+ *    give wrong results: serialise them. */
+#define SFNN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+sfnn_status sfnn_layer_noalloc(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x,
+                               int32_t batch, float* y, uint64_t* mask, int32_t* ids,
+                               int32_t* count, void* stream);
 
 /* One decode step through a stack of n_layers FFN layers joined by the
  * pre-norm residual chain without gain (the pages give no stack recipe; this

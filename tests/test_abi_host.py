@@ -146,3 +146,29 @@ def test_heads_validation_and_workspace(L):
     assert L.sfnn_head_qkv(ctypes.byref(ok), fake, 65, fake, fake, None) == 2
     assert L.sfnn_head_qkv(ctypes.byref(ok), fake + 4, 1, fake, fake, None) == 3
     assert L.sfnn_head_out(ctypes.byref(ok), fake, 1, fake, fake, fake, 16, None) == 5
+
+
+def test_layer_noalloc_validation(L):
+    """The no-allocation layer call checks its arguments and the scratch limit
+    on the host, before any HIP call (so this runs without a GPU)."""
+    import activation_sparse_gemv_amd as m
+    P, F = m._lib.sfnn_pred, m._lib.sfnn_ffn
+    fake = 1 << 20
+    assert m.SFNN_NOALLOC_SCRATCH_BYTES == 32 << 20
+    hdr = open(os.path.join(ROOT, "include", "sfnn.h")).read()
+    assert "#define SFNN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in hdr
+    # the largest workload (d_model 12288, d_ff 49152, INT4 FFN, fp16 rank-1024
+    # predictor): batch 64 needs more than the scratch array holds
+    p = P(12288, 49152, 1024, 1, fake, fake, fake)
+    f = F(12288, 49152, 2, 0, fake, None, fake, fake, None, fake, None, None, None)
+    big = L.sfnn_workspace_bytes(ctypes.byref(p), ctypes.byref(f), 64)
+    assert big > m.SFNN_NOALLOC_SCRATCH_BYTES
+    assert L.sfnn_layer_noalloc(ctypes.byref(p), ctypes.byref(f), fake, 64, fake, None, None, None, None) == 5
+    assert L.sfnn_workspace_bytes(ctypes.byref(p), ctypes.byref(f), 1) <= m.SFNN_NOALLOC_SCRATCH_BYTES
+    # the same argument checks as sfnn_layer
+    assert L.sfnn_layer_noalloc(None, ctypes.byref(f), fake, 1, fake, None, None, None, None) == 1
+    assert L.sfnn_layer_noalloc(ctypes.byref(p), ctypes.byref(f), None, 1, fake, None, None, None, None) == 1
+    assert L.sfnn_layer_noalloc(ctypes.byref(p), ctypes.byref(f), fake, 0, fake, None, None, None, None) == 2
+    assert L.sfnn_layer_noalloc(ctypes.byref(p), ctypes.byref(f), fake + 4, 1, fake, None, None, None, None) == 3
+    q = P(12288, 49152, 1024, 0, fake, fake, fake)     # fp32 predictor with an INT4 (fp16-input) FFN
+    assert L.sfnn_layer_noalloc(ctypes.byref(q), ctypes.byref(f), fake, 1, fake, None, None, None, None) == 4
