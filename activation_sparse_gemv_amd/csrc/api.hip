@@ -438,6 +438,11 @@ sfnn_status sfnn_gather_rows(const void* src, const int32_t* perm, int32_t n_row
   if (!src || !perm || !dst) return SFNN_E_NULL;
   if (n_rows < 1 || row_bytes < 2 || (row_bytes & 1)) return SFNN_E_SHAPE;
   if (!al16(src) || !al16(perm) || !al16(dst)) return SFNN_E_ALIGN;
+  // other workgroups write dst rows while row perm[k] of src is read: the two
+  // ranges must not overlap (an in-place relayout would race)
+  const uintptr_t n = (uintptr_t)n_rows * (uintptr_t)row_bytes;
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (s0 < d0 + n && d0 < s0 + n) return SFNN_E_SHAPE;
   return hip_status(launch_gather_rows(src, perm, n_rows, row_bytes, dst, as_stream(stream)));
 }
 

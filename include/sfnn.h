@@ -241,7 +241,9 @@ sfnn_status sfnn_fire_counts(const uint64_t* masks, int32_t n_masks, int32_t d_f
 sfnn_status sfnn_hot_first_perm(const uint32_t* counts, int32_t d_ff, int32_t* perm);
 
 /* dst row k = src row perm[k] for k < n_rows, rows of row_bytes bytes
- * (row_bytes % 2 == 0; applies a relayout to weights, scales and biases). */
+ * (row_bytes % 2 == 0; applies a relayout to weights, scales and biases).
+ * dst must not overlap src (an in-place relayout would race): overlapping
+ * ranges return SFNN_E_SHAPE without launching. */
 sfnn_status sfnn_gather_rows(const void* src, const int32_t* perm, int32_t n_rows,
                              int64_t row_bytes, void* dst, void* stream);
 

@@ -273,42 +273,66 @@ def _tau_for(w1_t: np.ndarray, w2_t: np.ndarray, p: np.ndarray) -> np.ndarray:
     return (sigma * z).astype(np.float32)
 
 
+def _row_blocks(rows: int, step: int):
+    return [(i, min(rows, i + step)) for i in range(0, rows, step)]
+
+
+def _map_blocks(fn, rows: int, step: int):
+    """Apply fn(lo, hi) to row blocks on a thread pool (NumPy releases the GIL
+    inside its array loops); each block writes only its own rows."""
+    blocks = _row_blocks(rows, step)
+    if len(blocks) == 1:
+        fn(*blocks[0])
+        return
+    with _cf.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(lambda b: fn(*b), blocks))
+
+
 def quant_int4_g128(w: np.ndarray):
     """Symmetric INT4, one fp16 scale per (row, 128 consecutive elements).
 
     Returns (q_packed uint8 [rows][cols/2], s fp16 [rows][cols/128]).
-    Element 2k sits in the low nibble of byte k, two's complement.
+    Element 2k sits in the low nibble of byte k, two's complement.  Rows are
+    independent, so row blocks are quantised in parallel.
     """
     rows, cols = w.shape
     assert cols % 128 == 0
-    wf = w.astype(np.float32).reshape(rows, cols // 128, 128)
-    amax = np.abs(wf).max(axis=2)
-    s16 = (amax / np.float32(7.0)).astype(np.float16)
-    s16 = np.where((s16 == 0) | ~np.isfinite(s16), np.float16(1.0), s16)
-    sf = s16.astype(np.float32)[:, :, None]
-    q = np.clip(np.rint(wf / sf), -8, 7).astype(np.int8).reshape(rows, cols)
-    u = (q.astype(np.int16) & 0xF).astype(np.uint8)
-    packed = (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
-    return np.ascontiguousarray(packed), np.ascontiguousarray(s16)
+    packed = np.empty((rows, cols // 2), dtype=np.uint8)
+    s_out = np.empty((rows, cols // 128), dtype=np.float16)
+
+    def block(lo, hi):
+        wf = w[lo:hi].astype(np.float32).reshape(hi - lo, cols // 128, 128)
+        amax = np.abs(wf).max(axis=2)
+        s16 = (amax / np.float32(7.0)).astype(np.float16)
+        s16 = np.where((s16 == 0) | ~np.isfinite(s16), np.float16(1.0), s16)
+        sf = s16.astype(np.float32)[:, :, None]
+        q = np.clip(np.rint(wf / sf), -8, 7).astype(np.int8).reshape(hi - lo, cols)
+        u = (q.astype(np.int16) & 0xF).astype(np.uint8)
+        packed[lo:hi] = u[:, 0::2] | (u[:, 1::2] << 4)
+        s_out[lo:hi] = s16
+
+    _map_blocks(block, rows, 1024)
+    return packed, s_out
 
 
 def _deq_norms_int4(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     """Row norms of the dequantised INT4 weights (used only to place biases)."""
     rows = q.shape[0]
     out = np.empty(rows, dtype=np.float64)
-    step = 2048
-    for i in range(0, rows, step):
-        qb = q[i:i + step]
-        lo = (qb & 0xF).astype(np.int16)
-        hi = (qb >> 4).astype(np.int16)
-        lo = np.where(lo >= 8, lo - 16, lo)
-        hi = np.where(hi >= 8, hi - 16, hi)
+
+    def block(lo, hi):
+        qb = q[lo:hi]
+        low = (qb & 0xF).astype(np.int16)
+        high = (qb >> 4).astype(np.int16)
+        low = np.where(low >= 8, low - 16, low)
+        high = np.where(high >= 8, high - 16, high)
         v = np.empty((qb.shape[0], qb.shape[1] * 2), dtype=np.float64)
-        v[:, 0::2] = lo
-        v[:, 1::2] = hi
-        sc = np.repeat(s[i:i + step].astype(np.float64), 128, axis=1)
-        v *= sc
-        out[i:i + step] = np.sqrt(np.einsum("ij,ij->i", v, v))
+        v[:, 0::2] = low
+        v[:, 1::2] = high
+        v *= np.repeat(s[lo:hi].astype(np.float64), 128, axis=1)
+        out[lo:hi] = np.sqrt(np.einsum("ij,ij->i", v, v))
+
+    _map_blocks(block, rows, 128)
     return out
 
 

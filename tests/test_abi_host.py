@@ -148,6 +148,14 @@ def test_heads_validation_and_workspace(L):
     assert L.sfnn_head_out(ctypes.byref(ok), fake, 1, fake, fake, fake, 16, None) == 5
 
 
+def test_gather_rows_rejects_overlap(L):
+    fake = 1 << 20
+    perm = 1 << 24
+    assert L.sfnn_gather_rows(fake, perm, 64, 256, fake, None) == 2            # in place
+    assert L.sfnn_gather_rows(fake, perm, 64, 256, fake + 4096, None) == 2     # dst inside src
+    assert L.sfnn_gather_rows(fake + 4096, perm, 64, 256, fake, None) == 2     # src inside dst
+
+
 def test_layer_noalloc_validation(L):
     """The no-allocation layer call checks its arguments and the scratch limit
     on the host, before any HIP call (so this runs without a GPU)."""
