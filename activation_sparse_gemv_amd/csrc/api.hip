@@ -21,14 +21,15 @@ bool al16(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) == 0; }
 bool al4(const void* p) { return p == nullptr || ((uintptr_t)p & 3u) == 0; }
 
 struct Layout {
-  size_t z = 0, partial = 0, mask = 0, uni = 0, ids = 0, count = 0, rbuf = 0, xbuf = 0, rtmp = 0, hbuf = 0,
-         sid = 0, total = 0;
+  size_t z = 0, hrow = 0, partial = 0, mask = 0, uni = 0, ids = 0, count = 0, rbuf = 0, xbuf = 0, rtmp = 0,
+         hbuf = 0, sid = 0, total = 0;
   int G = 0;
 };
 
-// Workspace: predictor stage-1 output z, the FFN workgroups' partial rows,
-// masks, union mask, ids, count, the residual chain's two fp32 rows and
-// layer input, and the matrix-core FFN's h (one 32-token pass) and slot ids.
+// Workspace: predictor stage-1 output z; the per-row FFN's activations h
+// (up -> down); the matrix-core FFN's partial rows; masks, union mask, ids,
+// count; the residual chain's two fp32 rows and layer input; the matrix-core
+// FFN's h (one 32-token pass) and slot ids.
 Layout layout(const sfnn_pred* p, const sfnn_ffn* f, int batch) {
   Layout L;
   size_t off = 0;
@@ -43,8 +44,10 @@ Layout layout(const sfnn_pred* p, const sfnn_ffn* f, int batch) {
   }
   if (f) {
     L.G = ffn_groups(f->d_model, f->d_ff);
+    L.hrow = off;
+    off += up((size_t)batch * f->d_ff * 4);
     L.partial = off;
-    off += up((size_t)L.G * batch * f->d_model * 4);
+    if (f->wtype != SFNN_F32) off += up((size_t)kMfmaPartRows * batch * f->d_model * 4);
   }
   L.mask = off;
   off += up((size_t)batch * (ff / 64) * 8);
@@ -160,6 +163,7 @@ FfnLaunch ffn_launch(const sfnn_ffn* f, const void* x, int batch, const uint64_t
   L.y = y;
   L.r_in = nullptr;
   L.r_out = nullptr;
+  L.hrow = reinterpret_cast<float*>(ws + Lw.hrow);
   L.partial = reinterpret_cast<float*>(ws + Lw.partial);
   L.groups = Lw.G;
   L.hbuf = ws + Lw.hbuf;

@@ -315,19 +315,21 @@ struct RowLoads {
   u32x4 w[UB];
   float sc[UB];
 
+  // INT4: the scales go out first, so that a wait for them (the compiler may
+  // convert them early) never covers this batch's weight loads
   __device__ __forceinline__ void issue(const uint8_t* __restrict__ row, const f16* __restrict__ srow, int nvec,
                                         int v0) {
-#pragma unroll
-    for (int u = 0; u < UB; ++u) {
-      const int v = v0 + u * LPR;
-      w[u] = ld16_stream(row + 16 * (size_t)(v < nvec ? v : v0));
-    }
     if constexpr (WT == WT_I4) {
 #pragma unroll
       for (int u = 0; u < UB; ++u) {
         const int v = v0 + u * LPR;
         sc[u] = (float)srow[(v < nvec ? v : v0) >> 2];  // one scale per 4 vectors (128 elements)
       }
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      const int v = v0 + u * LPR;
+      w[u] = ld16_stream(row + 16 * (size_t)(v < nvec ? v : v0));
     }
   }
 

@@ -1,0 +1,362 @@
+// Column-tiled down projection over a list of rows, with no partial rows:
+//   y[t][c] = bias[c] + sum over slots j < count of  h[t][j] * W[row_j][c]
+// W is row-major [rows][d]: the FFN's neuron-major W_down^T (row i is column i
+// of W_down), or an input-major projection w_t.  Only the listed rows are
+// read: a zero activation zeroes the whole row it multiplies, so that row
+// need not be loaded at all (53ai.com sparsity survey, section 激活稀疏).
+//
+// A workgroup owns one tile of TB = 16 * LPR bytes of every row and walks ALL
+// listed rows, so it ends holding the complete sums of its columns: y is
+// written directly, with no partial rows to store and add up afterwards.
+// LPR lanes cover a row's tile (one 16-byte load each), a wavefront covers
+// 64 / LPR rows per load, eight wavefronts 512 / LPR.  The tiles of one
+// 128-byte line go to workgroups on the same XCD (see down_tile), so each line
+// is fetched from HBM once and the other tiles find it in that XCD's L2.
+//
+// Pipelining: slots are taken in chunks of KB rows per lane; the row ids of
+// chunk c+2 and the weights of chunk c+1 are requested before chunk c is
+// used, so a lane always has one or two chunks of 16-byte loads in flight and
+// the id of a row arrives before its weight load is issued.
+//
+// Reduction: every lane adds its rows in slot order; lanes that share a column
+// are then added with row rotations inside each 16-lane row, the four rows and
+// eight wavefronts through LDS, always in the same order (deterministic, no
+// atomics).
+#pragma once
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace sfnn {
+
+// Source of the coefficient of slot j for token t.
+enum { CO_H = 0, CO_X16 = 1, CO_X32 = 2 };  // h[t][j] fp32 | x[t][row_j] fp16 | fp32
+
+struct DownArgs {
+  const uint8_t* w;      // [n_rows][d] storage rows (INT4: [n_rows][d/2] nibbles)
+  const f16* s;          // INT4: [n_rows][d/128] fp16 scales
+  const int32_t* ids;    // row of slot j (null: slot j is row j)
+  const int32_t* count;  // device slot count (null: n_slots)
+  int n_slots;           // slots when count is null, and the upper clamp for *count
+  int n_rows;            // rows of w: listed ids outside [0, n_rows) add nothing
+  const void* co;        // coefficients: h [B][co_stride] fp32, or x [B][co_stride]
+  int co_stride;
+  const void* bias;      // [d] (bias_f32 ? fp32 : fp16) or null
+  int bias_f32;
+  float* y;              // [B][d] or null
+  const float* r_in;     // residual add r_out = r_in + y (null to skip)
+  float* r_out;
+  int d, tok0, nt;
+};
+
+template <int WT>
+constexpr int cols_per_vec() { return WT == WT_F32 ? 4 : (WT == WT_F16 ? 8 : 32); }
+
+// Bytes of one row (without INT4 scales).
+__host__ __device__ inline int down_row_bytes(int wt, int d) { return wt == WT_F32 ? 4 * d : (wt == WT_F16 ? 2 * d : d / 2); }
+
+// Tile of workgroup vb.  Workgroups are dealt to the 8 XCDs in turn (vb % 8);
+// the 128 / TB tiles that share a 128-byte line of every row go to
+// consecutive workgroups of one XCD.
+__device__ __forceinline__ int down_tile(int vb, int ntiles, int per_line) {
+  if (per_line <= 1 || ntiles % (8 * per_line)) return vb;
+  const int xcd = vb & 7, k = vb >> 3;        // k-th workgroup on this XCD
+  const int per_xcd = ntiles >> 3;            // tiles per XCD (a multiple of per_line)
+  return xcd * per_xcd + k;
+}
+
+constexpr int kDownThreads = 512;
+#ifndef SFNN_DOWN_STREAM
+#define SFNN_DOWN_STREAM 0  // 1: weight loads with the streaming hint
+#endif
+
+// Rows per lane per chunk (two chunks of 16-byte loads in flight): 8, or 4
+// where the token group's accumulators leave fewer registers.
+#ifndef SFNN_DOWN_KB
+#define SFNN_DOWN_KB 4
+#endif
+template <int WT, int NT>
+constexpr int down_kb() { return (NT <= 2 && NT * cols_per_vec<WT>() <= 32) ? SFNN_DOWN_KB : 4; }
+
+template <int WT, int NT, int LPR>
+struct DownRed {
+  static constexpr int CPL = cols_per_vec<WT>();
+  static constexpr int NW = kDownThreads / kWave;
+  static constexpr int floats = NW * 4 * LPR * NT * CPL;  // [wave][row16][lane c][t][col]
+};
+
+// One workgroup's tile, in phases so that a fused launch can put other work
+// between them (the look-ahead stack's launch B issues predictor stage 2's
+// loads between the row ids and the first weights):
+//   count()   the slot count (a scalar load);
+//   ids01()   the row ids of chunks 0 and 1, read without waiting for the
+//             count (the id list holds n_slots entries; ids past the count
+//             are read but never used);
+//   first()   chunk 0's weights and coefficients;
+//   loop()    every chunk: the ids two chunks ahead and the weights one chunk
+//             ahead go out before the chunk is used;
+//   finish()  the reduction and y / the residual row.
+// LISTED: rows come from a.ids (else slot j is row j), a compile-time choice
+// so the id loads are never inside a branch (a load in a branch makes every
+// later wait cover all loads in flight).  Every load is unconditional: slots
+// past the count read row 0's tile and are cancelled at use, and the loop
+// leaves by break.
+template <int WT, int NT, int LPR, int CO, bool LISTED>
+struct DownTile {
+  static constexpr int CPL = cols_per_vec<WT>();
+  static constexpr int NW = kDownThreads / kWave;
+  static constexpr int RPW = kWave / LPR;  // rows per wavefront per step
+  static constexpr int RPS = NW * RPW;     // rows per workgroup per step
+  static constexpr int KB = down_kb<WT, NT>();
+  static_assert(LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8, "lanes per row");
+
+  int tile, rr, n, nch, sgrp, ngrp;
+  size_t rowb, cofs;
+  int idb[2][KB];       // ids of the chunks ahead
+  u32x4 wv[2][KB];      // weights of the chunk in use and the next one
+  float hv[2][KB][NT];  // coefficients
+  float sv[2][KB];      // INT4 scales
+  float acc[NT][CPL];
+  float sb[WT == WT_I4 ? NT : 1];
+
+  // has == false: a workgroup with no tile of its own (n = 0: it reads slot
+  // 0's row of tile 0 and writes nothing)
+  __device__ __forceinline__ void count(const DownArgs& a, int tile_, bool has) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int c = lane % LPR;
+    tile = has ? tile_ : 0;
+    rr = wave * RPW + lane / LPR;
+    const int col = (tile * LPR + c) * CPL;  // first output column of this lane
+    rowb = (size_t)down_row_bytes(WT, a.d);
+    cofs = (size_t)down_row_bytes(WT, col);  // byte offset of the lane's 16 bytes
+    sgrp = col / 128;
+    ngrp = a.d / 128;
+    n = a.n_slots;
+    if (a.count) {
+      const int cn = *a.count;
+      n = cn < 0 ? 0 : (cn > a.n_slots ? a.n_slots : cn);
+    }
+    if (!has) n = 0;
+    nch = (n + RPS * KB - 1) / (RPS * KB);  // chunks of KB steps
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) acc[t][k] = 0.0f;
+      if constexpr (WT == WT_I4) sb[t] = 0.0f;
+    }
+  }
+
+  __device__ __forceinline__ int slot_clamp(int j) const { return j < n ? j : (n > 0 ? n - 1 : 0); }
+
+  // ids depend on the slot only (not on the count), so they can go out
+  // before the count has arrived
+  __device__ __forceinline__ void issue_ids(const DownArgs& a, int ch, int (&dst)[KB]) const {
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int j = (ch * KB + k) * RPS + rr;
+      const int jc = j < a.n_slots ? j : a.n_slots - 1;
+      if constexpr (LISTED)
+        dst[k] = a.ids[jc];
+      else
+        dst[k] = jc;
+    }
+  }
+
+  __device__ __forceinline__ void issue_w(const DownArgs& a, int ch, const int (&id)[KB], u32x4 (&w)[KB],
+                                          float (&h)[KB][NT], float (&sc)[KB]) const {
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int i = id[k];
+      const bool live = (ch * KB + k) * RPS + rr < n;
+      const int ic = (live && (unsigned)i < (unsigned)a.n_rows) ? i : 0;
+      // a plain (cached) load: the other tiles of this 128-byte line are
+      // read by neighbouring workgroups of the same XCD, from its L2
+#if SFNN_DOWN_STREAM
+      w[k] = ld16_stream(a.w + (size_t)ic * rowb + cofs);
+#else
+      w[k] = ld16(a.w + (size_t)ic * rowb + cofs);
+#endif
+      if constexpr (WT == WT_I4) sc[k] = (float)a.s[(size_t)ic * ngrp + sgrp];
+      const int jc = slot_clamp((ch * KB + k) * RPS + rr);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int tc = t < a.nt ? a.tok0 + t : a.tok0;
+        if constexpr (CO == CO_H) {
+          h[k][t] = reinterpret_cast<const float*>(a.co)[(size_t)tc * a.co_stride + jc];
+        } else if constexpr (CO == CO_X16) {
+          h[k][t] = (float)reinterpret_cast<const f16*>(a.co)[(size_t)tc * a.co_stride + ic];
+        } else {
+          h[k][t] = reinterpret_cast<const float*>(a.co)[(size_t)tc * a.co_stride + ic];
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void use(const DownArgs& a, int ch, const int (&id)[KB], const u32x4 (&w)[KB],
+                                      const float (&h)[KB][NT], const float (&sc)[KB]) {
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int j = (ch * KB + k) * RPS + rr;
+      const bool ok = j < n && (unsigned)id[k] < (unsigned)a.n_rows;
+      float hk[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) hk[t] = (ok && t < a.nt) ? h[k][t] : 0.0f;  // a select: nothing else enters
+      if constexpr (WT == WT_I4) {
+        float hs[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          hs[t] = ok ? hk[t] * sc[k] : 0.0f;
+          sb[t] += hs[t];
+        }
+        const uint32_t q[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          // nibbles as q + 8 (offset binary), each converted as a byte; the
+          // 8 * sum h s this adds to every column comes off in finish()
+          const uint32_t v = q[m] ^ 0x88888888u;
+          const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
+          float e[8];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            e[2 * b] = (float)((lo >> (8 * b)) & 0xFFu);
+            e[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu);
+          }
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int b = 0; b < 8; ++b) acc[t][8 * m + b] = __builtin_fmaf(hs[t], e[b], acc[t][8 * m + b]);
+        }
+      } else {
+        const u32x4 wz = ok ? w[k] : u32x4{0u, 0u, 0u, 0u};
+        float e[CPL];
+        if constexpr (WT == WT_F32) {
+          e[0] = bitcast<float>(wz.x);
+          e[1] = bitcast<float>(wz.y);
+          e[2] = bitcast<float>(wz.z);
+          e[3] = bitcast<float>(wz.w);
+        } else {
+          const uint32_t u[4] = {wz.x, wz.y, wz.z, wz.w};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const f16x2 hh = bitcast<f16x2>(u[m]);
+            e[2 * m] = (float)hh.x;
+            e[2 * m + 1] = (float)hh.y;
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int b = 0; b < CPL; ++b) acc[t][b] = __builtin_fmaf(hk[t], e[b], acc[t][b]);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void ids01(const DownArgs& a) {
+    issue_ids(a, 0, idb[0]);
+    issue_ids(a, 1, idb[1]);
+  }
+
+  __device__ __forceinline__ void first(const DownArgs& a) { issue_w(a, 0, idb[0], wv[0], hv[0], sv[0]); }
+
+  // one chunk: idc holds chunk cc's ids (replaced by chunk cc+2's), idn chunk
+  // cc+1's
+  __device__ __forceinline__ void step(const DownArgs& a, int cc, int (&idc)[KB], const int (&idn)[KB],
+                                       const u32x4 (&wc)[KB], const float (&hc)[KB][NT], const float (&sc)[KB],
+                                       u32x4 (&wn)[KB], float (&hn)[KB][NT], float (&sn)[KB]) {
+    int cur[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) cur[k] = idc[k];
+    issue_ids(a, cc + 2, idc);
+    issue_w(a, cc + 1, idn, wn, hn, sn);
+    __builtin_amdgcn_sched_barrier(0);  // the next requests go out before this chunk is used
+    use(a, cc, cur, wc, hc, sc);
+  }
+
+  // every chunk (at least one: with n = 0 it adds nothing)
+  __device__ __forceinline__ void loop(const DownArgs& a) {
+    for (int ch = 0;; ch += 2) {
+      step(a, ch, idb[0], idb[1], wv[0], hv[0], sv[0], wv[1], hv[1], sv[1]);
+      if (ch + 1 >= nch) break;
+      step(a, ch + 1, idb[1], idb[0], wv[1], hv[1], sv[1], wv[0], hv[0], sv[0]);
+      if (ch + 2 >= nch) break;
+    }
+  }
+
+  // red: DownRed<WT, NT, LPR>::floats of LDS.  Every thread of the workgroup
+  // calls it (one barrier); has == false writes nothing.
+  __device__ __forceinline__ void finish(const DownArgs& a, float* red, bool has) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if constexpr (WT == WT_I4) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) acc[t][k] = __builtin_fmaf(-8.0f, sb[t], acc[t][k]);
+    }
+    // lanes of one 16-lane row that share a column chunk (lane % LPR): rotate-add
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        float v = acc[t][k];
+        v += dpp_f<0x128>(v);                          // row_ror:8
+        if constexpr (LPR <= 4) v += dpp_f<0x124>(v);  // row_ror:4
+        if constexpr (LPR <= 2) v += dpp_f<0x122>(v);  // row_ror:2
+        if constexpr (LPR == 1) v += dpp_f<0x121>(v);  // row_ror:1
+        acc[t][k] = v;
+      }
+    // red[wave][row16][c][t][k]: lanes 16 r + c (c < LPR) hold the row sums
+    const int r16 = lane >> 4, l16 = lane & 15;
+    if (l16 < LPR) {
+      float* dst = red + ((((size_t)wave * 4 + r16) * LPR + l16) * NT) * CPL;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int k = 0; k < CPL; k += 4)
+          *reinterpret_cast<f32x4*>(dst + t * CPL + k) =
+              f32x4{acc[t][k], acc[t][k + 1], acc[t][k + 2], acc[t][k + 3]};
+    }
+    __syncthreads();
+    constexpr int TE = LPR * CPL;  // columns of the tile
+    if (!has) return;
+    for (int e = threadIdx.x; e < NT * TE; e += kDownThreads) {
+      const int t = e / TE, ce = e % TE;
+      const int cl = ce / CPL, k = ce % CPL;
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s += red[((((size_t)w * 4 + r) * LPR + cl) * NT + t) * CPL + k];
+      if (t < a.nt) {
+        const int cidx = tile * TE + ce;
+        float b = 0.0f;
+        if (a.bias)
+          b = a.bias_f32 ? reinterpret_cast<const float*>(a.bias)[cidx]
+                         : (float)reinterpret_cast<const f16*>(a.bias)[cidx];
+        const float v = b + s;
+        const size_t o = (size_t)(a.tok0 + t) * a.d + cidx;
+        if (a.y) a.y[o] = v;
+        if (a.r_in) a.r_out[o] = a.r_in[o] + v;
+      }
+    }
+  }
+};
+
+// The whole tile on its own (k_down).
+template <int WT, int NT, int LPR, int CO, bool LISTED>
+__device__ __forceinline__ void down_body(const DownArgs& a, int tile, float* red) {
+  DownTile<WT, NT, LPR, CO, LISTED> D;
+  D.count(a, tile, true);
+  D.ids01(a);
+  D.first(a);
+  D.loop(a);
+  D.finish(a, red, true);
+}
+
+// Host side: tile width (lanes per row), tile count and tokens per pass for
+// rows of this type and length; the arguments of an FFN's down projection.
+struct DownShape {
+  int lpr, tiles, nt;
+};
+DownShape down_shape(int wt, int d, int batch);
+DownArgs ffn_down_args(const FfnLaunch& p);
+
+}  // namespace sfnn

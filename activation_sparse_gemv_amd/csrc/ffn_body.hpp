@@ -1,5 +1,5 @@
-// Workgroup bodies of the neuron-gathered FFN: only the listed neurons' rows
-// are read.
+// Up-projection body of the neuron-gathered FFN: only the listed neurons'
+// rows are read.
 //
 // A zero activation zeroes the whole row of the down projection it multiplies,
 // so that row need not be loaded at all (53ai.com sparsity survey, section
@@ -7,26 +7,20 @@
 // columns (same survey, PowerInfer 概述).  Storage is neuron-major: neuron i
 // owns row i of W_up, W_gate and W_down^T, each a contiguous d_model run.
 //
-// ffn_body: one workgroup does the whole gathered FFN for a contiguous run of
-//         the active slots:
+// up_body: one workgroup computes the activations of a contiguous run of the
+//   active slots:
 //   1. the run and its neuron ids come from the caller's list, from the
 //      identity (dense), or from compacting the union mask in the prologue
 //      (popcounts + a lane prefix sum over all mask words in every
 //      wavefront; no separate compaction launch between the predictor and
 //      the FFN);
 //   2. up (+ gate): one wavefront per neuron row, 16-byte coalesced loads,
-//      activations in LDS, ReLU / ReGLU and the per-token select fused; h goes
-//      to LDS;
-//   3. down: every thread owns CPT consecutive output columns and adds
-//      h_j * W_down^T[id_j][cols] over the run's rows in slot order.
-//   The first batch of W_down^T rows is requested right behind the first up
-//   loads, so both projections' rows are in flight together.  Each workgroup
-//   writes one fp32 partial row per token.
-// sum_body: y = b_down + the workgroups' partials in a fixed order (and
-//         optionally the residual add).  No atomics anywhere, so results are
-//         run-to-run deterministic.
-// The bodies take a virtual workgroup index so that a launch can run them
-// beside other work (the look-ahead stack fuses them with the predictor).
+//      activations in LDS, ReLU / ReGLU and the per-token select fused;
+//   3. h[t][slot] goes to global memory (and the run's ids, when compacting),
+//      for the column-tiled down projection of the next launch
+//      (down_body.hpp), which writes y without partial rows.
+// The body takes a virtual workgroup index so that a launch can run it beside
+// other work (the look-ahead stack adds the next layer's predictor rows).
 #pragma once
 #include "common.hpp"
 #include "launch.hpp"
@@ -47,7 +41,8 @@ struct FfnArgs {
   int32_t* ids_out;
   int32_t* count_out;
   const uint64_t* mask;  // per-token gate or null
-  float* partial;        // [G][B][d]
+  float* hout;           // h [B][hstride] fp32, slot order
+  int hstride;
   const float* r_in;     // residual rows (chain prologue: x = r / rms(r)) or null
   void* x_out;           // chain prologue: x written here by workgroup 0 (or null)
   float eps;
@@ -57,120 +52,58 @@ struct FfnArgs {
   int d, f, B, tok0, nt, write_ids;
 };
 
-// CPT consecutive output columns of one W_down^T row, kept in storage form
-// until use (fp32: 4 B, fp16: 2 B, INT4: 1/2 B per column + the fp16 scale of
-// their 128-column group).  CPT is 8, 16 or 32.
-template <int WT, int CPT>
-struct DownCols {
-  static constexpr int NV = (WT == WT_F32) ? CPT / 4 : (WT == WT_F16 ? CPT / 8 : 1);  // 16-byte loads
-  static constexpr int NQ = (WT == WT_I4) ? CPT / 8 : 1;                            // INT4: dwords held
-  u32x4 a[WT == WT_I4 ? 1 : NV];
-  uint32_t q[NQ];
-  float s;
-
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ w, const f16* __restrict__ sc, int i, int col,
-                                       int d) {
-    if constexpr (WT == WT_F32) {
-      const uint8_t* p = w + ((size_t)i * d + col) * 4;
-#pragma unroll
-      for (int k = 0; k < NV; ++k) a[k] = ld16_stream(p + 16 * k);
-    } else if constexpr (WT == WT_F16) {
-      const uint8_t* p = w + ((size_t)i * d + col) * 2;
-#pragma unroll
-      for (int k = 0; k < NV; ++k) a[k] = ld16_stream(p + 16 * k);
-    } else {
-      const uint8_t* p = w + (size_t)i * (d / 2) + col / 2;
-      if constexpr (CPT == 8) {
-        q[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-      } else if constexpr (CPT == 16) {
-        const uint64_t v = __builtin_nontemporal_load(reinterpret_cast<const uint64_t*>(p));
-        q[0] = (uint32_t)v;
-        q[1] = (uint32_t)(v >> 32);
-      } else {
-        const u32x4 v = ld16_stream(p);
-        q[0] = v.x;
-        q[1] = v.y;
-        q[2] = v.z;
-        q[3] = v.w;
-      }
-      s = (float)sc[(size_t)i * (d / 128) + col / 128];  // CPT <= 32 columns share one group
-    }
-  }
-
-  __device__ __forceinline__ void unpack(float* w) const {
-    if constexpr (WT == WT_F32) {
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        w[4 * k] = bitcast<float>(a[k].x);
-        w[4 * k + 1] = bitcast<float>(a[k].y);
-        w[4 * k + 2] = bitcast<float>(a[k].z);
-        w[4 * k + 3] = bitcast<float>(a[k].w);
-      }
-    } else if constexpr (WT == WT_F16) {
-#pragma unroll
-      for (int k = 0; k < NV; ++k) {
-        const uint32_t u[4] = {a[k].x, a[k].y, a[k].z, a[k].w};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const f16x2 hh = bitcast<f16x2>(u[m]);
-          w[8 * k + 2 * m] = (float)hh.x;
-          w[8 * k + 2 * m + 1] = (float)hh.y;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < CPT; ++k) {
-        const int n = (int)(q[k >> 3] << (28 - 4 * (k & 7))) >> 28;  // sign-extended nibble
-        w[k] = (float)n * s;
-      }
-    }
-  }
+// One batch of an up (+ gate) row in flight: the weight vectors, and the
+// row's bias and per-token mask word, requested with them so that finishing
+// a row needs no load of its own (a load in a branch there would make the
+// next wait cover every load in flight, the next batch's included).
+template <int WT, int UBU>
+struct UpBatch {
+  RowLoads<WT, kWave, UBU> u, g;
+  float bu, bg;  // b_up[i], b_gate[i] (0 without biases)
+  uint64_t mw;   // mask word of neuron i for this lane's token (all ones without a gate)
+  int i;         // neuron id (< 0: a slot that adds nothing)
 };
 
-// One FFN workgroup (virtual index vb of vg).  CHAIN: the layer input is
+// One up-projection workgroup (virtual index vb of vg).  CHAIN: the layer input is
 // x = r_in / rms(r_in), built in the prologue instead of staged from a.x.
 // P1: the workgroup also computes its share of predictor stage 1 of the next
-// layer on the same x (look-ahead): rows [vb*pr, vb*pr + pr) of W1^T, taken by
-// the wavefronts from the last one down.
+// layer on the same x (look-ahead): rows [vb*pr, vb*pr + pr) of W1^T.  Each
+// row is split in NW equal column chunks, one per wavefront, so every
+// wavefront carries the same share; all of a pass's loads go out first thing
+// (they wait for nothing) and the wavefronts' partial dots are added in LDS,
+// in wavefront order, at the end.
 // Every wavefront derives the workgroup's slot list by itself (mask words,
 // popcounts, one lane scan, then the 64 bits of each word that holds slots
 // of the run emitted by the 64 lanes at once into the wavefront's own LDS
 // list), so no workgroup barrier stands between the mask and the first
 // weight loads: the barriers that stage x come after those loads are issued.
-template <int WT, int ACT, int NT, int SRC, int NTH, int CPT, bool CHAIN, bool P1, int UW>
-__device__ __forceinline__ void ffn_body(const FfnArgs& a, int vb, int vg) {
+// RV: float4 vectors per thread per token of the residual row (CHAIN only;
+// d_model <= 4 RV NTH).
+template <int WT, int ACT, int NT, int SRC, int NTH, int RV, bool CHAIN, bool P1, int UW>
+__device__ __forceinline__ void up_body(const FfnArgs& a, int vb, int vg) {
   using XT = typename std::conditional<WT == WT_F32, float, f16>::type;
   static_assert(!P1 || SRC == SRC_UNION, "predictor rows ride along with the union-mask FFN only");
   constexpr int NW = NTH / kWave;
-  // W_down^T rows in flight per thread per buffer: 8 x 16 bytes of columns,
-  // fewer where the accumulators leave few registers
-  constexpr int NV = DownCols<WT, CPT>::NV;
-  constexpr int kDB0 = NV >= 8 ? 1 : (NV >= 4 ? 2 : (NV == 2 ? 4 : 8));
-  constexpr int kDB1 = (NT * CPT >= 64 && kDB0 > 2) ? kDB0 / 4 : ((NT * CPT >= 32 && kDB0 > 2) ? kDB0 / 2 : kDB0);
-  constexpr int kDB = kDB1 * CPT > 128 ? 128 / CPT : kDB1;
-  constexpr int UB = 8;                  // predictor-row vectors per lane per batch
   // up-row vectors per lane per batch, two batches in flight: 8 (4 for the
-  // short INT4 rows), halved for ReGLU's second row and for 4+ tokens
-  constexpr int UBU0 = (WT == WT_I4 ? 4 : 8) / (ACT == ACT_REGLU ? 2 : 1) / (NT >= 4 ? 2 : 1);
+  // INT4 rows from two tokens on), halved for ReGLU's second row and for 4+
+  // tokens
+  constexpr int UBU0 = (WT == WT_I4 && NT > 1 ? 4 : 8) / (ACT == ACT_REGLU ? 2 : 1) / (NT >= 4 ? 2 : 1);
   constexpr int UBU = UBU0 < 2 ? 2 : UBU0;
   constexpr int SP = NT == 2 ? 8 : 4;    // staged x vectors per thread held in registers
   extern __shared__ __align__(16) unsigned char smem[];
   XT* xs = reinterpret_cast<XT*>(smem);
   __shared__ int s_idw[NW][kMaxPer];     // each wavefront's copy of the run's neuron ids
-  __shared__ float s_h[NT][kMaxPer];
   __shared__ float s_red[NT][16];
 
   const int d = a.d, f = a.f;
   const int G = vg, g = vb;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform, in a scalar register
   int* ids_w = s_idw[wave];
   const int row_bytes = (WT == WT_F32) ? d * 4 : (WT == WT_F16 ? d * 2 : d / 2);
   const int nvec = row_bytes / 16;
   const int ngroups = d / 128;
   const int words = f / 64;
-  const int col0 = threadIdx.x * CPT;
-  const bool colok = col0 < d;
-  const int col = colok ? col0 : 0;  // keeps every address in bounds
 
   // ---- 1. loads that wait for nothing: the mask words (lane-major: lane l
   // of every wavefront holds words l*UW .. l*UW + UW-1, read in 16-byte
@@ -196,30 +129,42 @@ __device__ __forceinline__ void ffn_body(const FfnArgs& a, int vb, int vg) {
   int n_ids = 0;
   if constexpr (SRC == SRC_IDS) n_ids = *a.count;
   StageSplit<XT, WT == WT_I4, SP> stage;
-  constexpr int CV = CHAIN ? ffn_chain_vecs(NT, CPT) : 1;
+  constexpr int CV = CHAIN ? NT * RV : 1;
   f32x4 rv[CV];
   if constexpr (CHAIN)
     chain_issue<NT, CV, true>(a.r_in, rv, d, a.tok0, a.nt);  // CV is sized to the shape
   else
     stage.issue(reinterpret_cast<const XT*>(a.x), d, a.tok0, a.nt, NT);
 
-  constexpr int PWT = WT == WT_F32 ? WT_F32 : WT_F16;
+  // P1: PR rows per pass, PV vectors per lane of each row's chunk (PV * 64
+  // * NW vectors cover d_model <= 4 RV NTH)
+  constexpr int PV = P1 ? (WT == WT_F32 ? 2 : 1) * RV / 2 : 1;
+  constexpr int PR = P1 ? (PV <= 2 ? 8 : 4) : 1;
   const int pr = P1 ? (a.r + G - 1) / G : 0;
   const int p0 = g * pr;
-  const int pnvec = d * (int)sizeof(XT) / 16;
-  const int pk0 = NW - 1 - wave;  // this wavefront's first predictor row (local)
-  RowLoads<PWT, kWave, UB> Lp;
-  if constexpr (P1) {
-    // a wavefront without a predictor row reads one shared vector of the
-    // mask instead (w1_t is null when there is no next layer)
-    const bool have = pk0 < pr && p0 + pk0 < a.r;
-    const uint8_t* prow = have ? a.w1_t + (size_t)(p0 + pk0) * d * sizeof(XT)
-                               : reinterpret_cast<const uint8_t*>(a.union_mask);
-    Lp.issue(prow, nullptr, have ? pnvec : 1, (have && lane < pnvec) ? lane : 0);
-  }
+  const int pcw = d * (int)sizeof(XT) / 16 / NW;  // vectors per wavefront chunk of a row
+  u32x4 pw[PR][PV];
+  // issue one pass of W1^T rows (k0 .. k0 + PR - 1 of this workgroup's); a
+  // row past the workgroup's share or the rank (or no next layer: w1_t null)
+  // reads one shared vector of the mask instead, so no load is in a branch
+  auto p1_issue = [&](int k0) {
+#pragma unroll
+    for (int k = 0; k < PR; ++k) {
+      const bool have = a.w1_t && k0 + k < pr && p0 + k0 + k < a.r;
+      const uint8_t* prow = have ? a.w1_t + (size_t)(p0 + k0 + k) * d * sizeof(XT)
+                                 : reinterpret_cast<const uint8_t*>(a.union_mask);
+#pragma unroll
+      for (int v = 0; v < PV; ++v) {
+        const int vi = lane + kWave * v;
+        const bool ok = have && vi < pcw;
+        pw[k][v] = ld16_stream(prow + (ok ? 16 * (size_t)(wave * pcw + vi) : 0));
+      }
+    }
+  };
+  if constexpr (P1) p1_issue(0);
 
-  // ---- 2. the run [s0, s1) of active slots and its neuron ids ----------------
-  int cnt;
+  // ---- 2. the run [s0, s0 + cnt) of active slots and its neuron ids --------
+  int cnt, s0;
   if constexpr (SRC == SRC_UNION) {
     int c = 0;
 #pragma unroll
@@ -228,7 +173,7 @@ __device__ __forceinline__ void ffn_body(const FfnArgs& a, int vb, int vg) {
     const int total = __builtin_amdgcn_readlane(incl, kWave - 1);
     const int ex = incl - c;  // slots before this lane's words
     const int per = (total + G - 1) / G;
-    const int s0 = g * per;
+    s0 = g * per;
     const int s1 = (s0 + per < total) ? s0 + per : total;
     cnt = s1 > s0 ? s1 - s0 : 0;
     const bool wr = a.write_ids && wave == 0;
@@ -263,7 +208,7 @@ __device__ __forceinline__ void ffn_body(const FfnArgs& a, int vb, int vg) {
     int n = f;
     if constexpr (SRC == SRC_IDS) n = n_ids < 0 ? 0 : (n_ids > f ? f : n_ids);
     const int per = (n + G - 1) / G;
-    const int s0 = g * per;
+    s0 = g * per;
     cnt = (s0 + per < n) ? per : (n > s0 ? n - s0 : 0);
     for (int j = lane; j < cnt; j += kWave) {
       const int id = (SRC == SRC_IDS) ? a.ids[s0 + j] : s0 + j;
@@ -273,24 +218,40 @@ __device__ __forceinline__ void ffn_body(const FfnArgs& a, int vb, int vg) {
   __builtin_amdgcn_wave_barrier();  // the wavefront's list is written before any lane reads it
 
   // ---- 3. first weight loads, before x is ready: this wavefront's first up
-  // (+ gate) batch and the first batch of W_down^T rows --------------------
-  RowLoads<WT, kWave, UBU> Lu, Lg;
-  {
-    const int i = wave < cnt ? ids_w[wave] : -1;
-    const bool have = i >= 0;  // else one shared vector of row 0
-    const size_t ro = have ? (size_t)i * row_bytes : 0;
-    const size_t so = have ? (size_t)i * ngroups : 0;
-    const int n0 = have ? nvec : 1;
-    const int v0 = (have && lane < nvec) ? lane : 0;
-    Lu.issue(a.w_up + ro, a.s_up ? a.s_up + so : nullptr, n0, v0);
-    if constexpr (ACT == ACT_REGLU) Lg.issue(a.w_gate + ro, a.s_gate ? a.s_gate + so : nullptr, n0, v0);
-  }
-  DownCols<WT, CPT> wd[2][kDB];
-#pragma unroll
-  for (int u2 = 0; u2 < kDB; ++u2) {
-    const int iu = u2 < cnt ? ids_w[u2] : (cnt > 0 ? ids_w[0] : 0);
-    wd[0][u2].load(a.w_down_t, a.s_down_t, iu >= 0 ? iu : 0, col, d);
-  }
+  // (+ gate) batch ------------------------------------------------------------
+  // Batch (k, pb) of this wavefront: batch pb of its k-th row (slot
+  // wave + k NW).  Every load is unconditional: a slot past the run (or an
+  // invalid id) reads row 0's vectors and adds nothing; a missing bias or
+  // gate reads element 0 of x instead and is not used.
+  const int bstep = UBU * kWave;
+  const int tt = lane < a.nt ? lane : 0;  // the token this lane finishes (lanes >= nt repeat token 0)
+  auto up_issue = [&](UpBatch<WT, UBU>& Bt, int k, int pb) {
+    const int j = wave + k * NW;
+    const int i = j < cnt ? ids_w[j < kMaxPer ? j : 0] : -1;
+    const bool have = i >= 0;
+    const int inc = have ? i : 0;
+    const int v0 = lane + pb * bstep;
+    const int v0c = (have && v0 < nvec) ? v0 : 0;  // lanes past a short row read its first vector
+    Bt.i = i;
+    // the small loads first: a wait for them then never covers this batch's
+    // weight loads
+    const uint64_t* msrc = a.mask ? a.mask + (size_t)(a.tok0 + tt) * words + (inc >> 6)
+                                  : reinterpret_cast<const uint64_t*>(a.x);
+    Bt.mw = *msrc;
+    const void* bsu = a.b_up ? a.b_up : a.x;
+    Bt.bu = load_as_float<XT>(bsu, a.b_up ? inc : 0);
+    if constexpr (ACT == ACT_REGLU) {
+      const void* bsg = a.b_gate ? a.b_gate : a.x;
+      Bt.bg = load_as_float<XT>(bsg, a.b_gate ? inc : 0);
+    }
+    Bt.u.issue(a.w_up + (size_t)inc * row_bytes, a.s_up ? a.s_up + (size_t)inc * ngroups : nullptr,
+               have ? nvec : 1, v0c);
+    if constexpr (ACT == ACT_REGLU)
+      Bt.g.issue(a.w_gate + (size_t)inc * row_bytes, a.s_gate ? a.s_gate + (size_t)inc * ngroups : nullptr,
+                 have ? nvec : 1, v0c);
+  };
+  UpBatch<WT, UBU> Bq[2];
+  up_issue(Bq[0], 0, 0);
   __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the staging waits
 
   // ---- 4. x into LDS: staged activations, or the residual chain -------------
@@ -300,212 +261,124 @@ __device__ __forceinline__ void ffn_body(const FfnArgs& a, int vb, int vg) {
     stage.commit(xs, reinterpret_cast<const XT*>(a.x), d, a.tok0, a.nt, NT);
   __syncthreads();
 
+  // ---- P1: the next layer's predictor stage 1 on the staged x (its loads
+  // were issued first and have had the longest to arrive; computing them here
+  // frees their registers before the up rows)
+  if constexpr (P1) {
+    // z[t][p0 + k] = W1^T[p0 + k] . x[t]: this wavefront's chunk of every row
+    // of the pass, then the chunks added in wavefront order.  x is staged in
+    // the INT4 pairing order when the FFN is INT4, so W1's fp16 vectors are
+    // paired the same way.
+    __shared__ float s_pz[NT][PR][NW];
+    for (int k0 = 0; k0 < pr; k0 += PR) {  // workgroup-uniform
+      if (k0 > 0) p1_issue(k0);
+      float pacc[PR][NT];
+#pragma unroll
+      for (int k = 0; k < PR; ++k) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) pacc[k][t] = 0.0f;
+#pragma unroll
+        for (int v = 0; v < PV; ++v) {
+          const int vi = lane + kWave * v;
+          const bool ok = vi < pcw;
+          const int vc = ok ? wave * pcw + vi : 0;
+          u32x4 wv = ok ? pw[k][v] : u32x4{0u, 0u, 0u, 0u};
+          if constexpr (WT == WT_F32) {
+            vec_f32<NT>(wv, reinterpret_cast<const float*>(xs) + 4 * vc, d, pacc[k]);
+          } else {
+            if constexpr (WT == WT_I4) wv = StageSplit<XT, true, 1>::perm8(wv);
+            vec_f16<NT>(wv, reinterpret_cast<const f16*>(xs) + 8 * vc, d, pacc[k]);
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < PR; ++k)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const float sw = wave_sum(pacc[k][t]);
+          if (lane == 0) s_pz[t][k][wave] = sw;
+        }
+      __syncthreads();
+      if ((int)threadIdx.x < NT * PR) {
+        const int t = threadIdx.x / PR, k = threadIdx.x % PR;
+        float z = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) z += s_pz[t][k][w];
+        if (t < a.nt && k0 + k < pr && p0 + k0 + k < a.r) a.z[(size_t)(a.tok0 + t) * a.r + p0 + k0 + k] = z;
+      }
+      __syncthreads();  // s_pz is reused by the next pass
+    }
+  }
+
   // ---- 5. up (+ gate) rows: one wavefront per slot -------------------------
   // The wavefront's rows (slots wave, wave + NW, ...) are walked as one
   // sequence of batches of UBU vectors per lane, two buffers deep: batch q+1
   // (of this row or the next) is requested before batch q is used, so a
-  // wavefront with many rows keeps a row in flight while it computes.
+  // wavefront with many rows keeps a row in flight while it computes.  The
+  // loop leaves by break and requests a harmless repeat of the last batch at
+  // the end, so no load and no store sits in a branch.
   {
-    const int bstep = UBU * kWave;
-    const int nb = (nvec + bstep - 1) / bstep;                    // batches per row
-    const int nrow = wave < cnt ? (cnt - 1 - wave) / NW + 1 : 0;  // this wavefront's rows
+    const int nb = (nvec + bstep - 1) / bstep;  // batches per row
+    // this wavefront's rows and batches (wave-uniform: scalar loop control)
+    const int nrow = __builtin_amdgcn_readfirstlane(wave < cnt ? (cnt - 1 - wave) / NW + 1 : 0);
     const int nq = nrow * nb;
-    RowLoads<WT, kWave, UBU> Lu2, Lg2;  // Lu / Lg hold batch 0 (step 3)
-    int pk = 0, pb = 0;                 // row and batch of the last request
-    int ck = 0, cb = 0;                 // row and batch being used
+    int pk = 0, pb = 0;  // row and batch of the last request
+    int ck = 0, cb = 0;  // row and batch being used
     float au[NT], ag[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) au[t] = ag[t] = 0.0f;
-    for (int q = 0; q < nq; q += 2) {
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        if (q + hb < nq) {  // wave-uniform
-          RowLoads<WT, kWave, UBU>& Lc = hb ? Lu2 : Lu;
-          RowLoads<WT, kWave, UBU>& Ln = hb ? Lu : Lu2;
-          RowLoads<WT, kWave, UBU>& Gc = hb ? Lg2 : Lg;
-          RowLoads<WT, kWave, UBU>& Gn = hb ? Lg : Lg2;
-          if (q + hb + 1 < nq) {  // request the next batch into the other buffer
-            if (++pb == nb) {
-              pb = 0;
-              ++pk;
-            }
-            const int in = ids_w[wave + pk * NW];
-            const int inc = in >= 0 ? in : 0;
-            const int v0 = lane + pb * bstep;
-            const int v0c = v0 < nvec ? v0 : 0;  // lanes past a short row read its first vector
-            Ln.issue(a.w_up + (size_t)inc * row_bytes, a.s_up ? a.s_up + (size_t)inc * ngroups : nullptr, nvec,
-                     v0c);
-            if constexpr (ACT == ACT_REGLU)
-              Gn.issue(a.w_gate + (size_t)inc * row_bytes, a.s_gate ? a.s_gate + (size_t)inc * ngroups : nullptr,
-                       nvec, v0c);
-          }
-          __builtin_amdgcn_sched_barrier(0);  // the next batch is requested before this one is used
-          const int v0 = lane + cb * bstep;
-          Lc.template consume<NT>(nvec, v0, xs, d, au);
-          if constexpr (ACT == ACT_REGLU) Gc.template consume<NT>(nvec, v0, xs, d, ag);
-          if (++cb == nb) {  // the row is done: h for its slot
-            const int j = wave + ck * NW;
-            const int i = ids_w[j];
-            const bool ok = i >= 0;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-              au[t] = group_sum<kWave>(au[t]);
-              if (ACT == ACT_REGLU) ag[t] = group_sum<kWave>(ag[t]);
-            }
-            // lane t finishes token t
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-              if (lane == t) {
-                float hv = 0.0f;
-                if (ok && t < a.nt) {
-                  const float up = au[t] + (a.b_up ? load_as_float<XT>(a.b_up, i) : 0.0f);
-                  if (ACT == ACT_RELU) {
-                    hv = up > 0.0f ? up : 0.0f;
-                  } else {
-                    const float gt = ag[t] + (a.b_gate ? load_as_float<XT>(a.b_gate, i) : 0.0f);
-                    hv = (gt > 0.0f ? gt : 0.0f) * up;
-                  }
-                  if (a.mask) {
-                    const uint64_t wv = a.mask[(size_t)(a.tok0 + t) * words + (i >> 6)];
-                    if (!((wv >> (i & 63)) & 1ull)) hv = 0.0f;  // select: gated-off neurons add nothing
-                  }
-                }
-                s_h[t][j] = hv;
-              }
-            }
-#pragma unroll
-            for (int t = 0; t < NT; ++t) au[t] = ag[t] = 0.0f;
-            cb = 0;
-            ++ck;
-          }
-        }
+    auto up_step = [&](UpBatch<WT, UBU>& Bc, UpBatch<WT, UBU>& Bn) {
+      // request the next batch into the other buffer (past the end: the last
+      // batch again)
+      if (++pb == nb) {
+        pb = 0;
+        ++pk;
       }
-    }
-  }
-  if constexpr (P1) {
-    // z[t][row] = W1^T[row] . x[t]; x is staged in the INT4 pairing order when
-    // the FFN is INT4, so W1's fp16 vectors are paired the same way
-    for (int k = pk0; k < pr && p0 + k < a.r; k += NW) {  // wave-uniform
-      const uint8_t* prow = a.w1_t + (size_t)(p0 + k) * d * sizeof(XT);
-      float acc[NT];
+      const bool past = pk >= nrow;
+      up_issue(Bn, past ? nrow - 1 : pk, past ? nb - 1 : pb);
+      __builtin_amdgcn_sched_barrier(0);  // the next batch is requested before this one is used
+      const int v0 = lane + cb * bstep;
+      Bc.u.template consume<NT>(nvec, v0, xs, d, au);
+      if constexpr (ACT == ACT_REGLU) Bc.g.template consume<NT>(nvec, v0, xs, d, ag);
+      if (++cb == nb) {  // the row is done: h for its slot
+        const int j = wave + ck * NW;
+        const int i = Bc.i;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] = 0.0f;
-      for (int v0 = lane; v0 < pnvec; v0 += UB * kWave) {
-        if (!(k == pk0 && v0 == lane)) Lp.issue(prow, nullptr, pnvec, v0);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < UB; ++u) {
-          const int v = v0 + u * kWave;
-          const bool ok = v < pnvec;
-          const int vc = ok ? v : 0;
-          u32x4 wv = ok ? Lp.w[u] : u32x4{0u, 0u, 0u, 0u};
-          if constexpr (WT == WT_F32) {
-            vec_f32<NT>(wv, reinterpret_cast<const float*>(xs) + 4 * vc, d, acc);
-          } else {
-            if constexpr (WT == WT_I4) wv = StageSplit<XT, true, 1>::perm8(wv);
-            vec_f16<NT>(wv, reinterpret_cast<const f16*>(xs) + 8 * vc, d, acc);
-          }
+        for (int t = 0; t < NT; ++t) {
+          au[t] = group_sum<kWave>(au[t]);
+          if (ACT == ACT_REGLU) ag[t] = group_sum<kWave>(ag[t]);
         }
+        // lane l finishes token tt (every lane stores; lanes >= nt repeat
+        // token 0's value at its address)
+        float ut = 0.0f, gt = 0.0f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          ut = tt == t ? au[t] : ut;
+          gt = tt == t ? ag[t] : gt;
+        }
+        const float up = ut + (a.b_up ? Bc.bu : 0.0f);
+        float hv;
+        if constexpr (ACT == ACT_RELU) {
+          hv = up > 0.0f ? up : 0.0f;
+        } else {
+          const float g = gt + (a.b_gate ? Bc.bg : 0.0f);
+          hv = (g > 0.0f ? g : 0.0f) * up;
+        }
+        const bool on = !a.mask || ((Bc.mw >> (i & 63)) & 1ull);  // select: gated-off neurons add nothing
+        hv = (i >= 0 && on) ? hv : 0.0f;
+        a.hout[(size_t)(a.tok0 + tt) * a.hstride + s0 + j] = hv;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) au[t] = ag[t] = 0.0f;
+        cb = 0;
+        ++ck;
       }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] = group_sum<kWave>(acc[t]);
-      if (lane == 0) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          if (t < a.nt) a.z[(size_t)(a.tok0 + t) * a.r + p0 + k] = acc[t];
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- 6. down: acc[t][k] += h[t][j] * W_down^T[id_j][col + k], slots in order
-  // INT4: acc[t][k] += (h[t][j] * s_j) * (q_jk + 8) with q + 8 read straight
-  // from the offset-binary nibble as a byte; the 8 * sum_j h s_j that this adds
-  // to every column is taken off at the end (sb).
-  float acc[NT][CPT];
-  float sb[WT == WT_I4 ? NT : 1];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-#pragma unroll
-    for (int k = 0; k < CPT; ++k) acc[t][k] = 0.0f;
-    if constexpr (WT == WT_I4) sb[t] = 0.0f;
-  }
-
-  for (int j0 = 0; j0 < cnt; j0 += 2 * kDB) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int jb = j0 + half * kDB;  // batch held in buffer `half`
-      if (jb < cnt) {
-        // request the batch after this one into the other buffer
-        const int jn = jb + kDB;
-        if (jn < cnt) {
-#pragma unroll
-          for (int u = 0; u < kDB; ++u) {
-            const int jj = (jn + u < cnt) ? jn + u : jn;
-            const int iu = ids_w[jj];
-            wd[half ^ 1][u].load(a.w_down_t, a.s_down_t, iu >= 0 ? iu : 0, col, d);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < kDB; ++u) {
-          const int jj = jb + u;
-          const int jc = jj < cnt ? jj : jb;
-          const bool ok = jj < cnt && ids_w[jc] >= 0 && colok;
-          if constexpr (WT == WT_I4) {
-            float hs[NT];
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-              hs[t] = ok ? s_h[t][jc] * wd[half][u].s : 0.0f;  // a select: a poisoned scale never enters
-              sb[t] += hs[t];
-            }
-#pragma unroll
-            for (int m = 0; m < CPT / 8; ++m) {
-              const uint32_t v = wd[half][u].q[m] ^ 0x88888888u;  // nibbles as q + 8
-              const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
-              float n[8];
-#pragma unroll
-              for (int b = 0; b < 4; ++b) {
-                n[2 * b] = (float)((lo >> (8 * b)) & 0xFFu);
-                n[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu);
-              }
-#pragma unroll
-              for (int t = 0; t < NT; ++t)
-#pragma unroll
-                for (int k = 0; k < 8; ++k) acc[t][8 * m + k] = __builtin_fmaf(hs[t], n[k], acc[t][8 * m + k]);
-            }
-          } else {
-            float wf[CPT];
-            wd[half][u].unpack(wf);
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-              const float hv = ok ? s_h[t][jc] : 0.0f;
-#pragma unroll
-              for (int k = 0; k < CPT; ++k) acc[t][k] = __builtin_fmaf(hv, ok ? wf[k] : 0.0f, acc[t][k]);
-            }
-          }
-        }
-      }
-    }
-  }
-
-  if constexpr (WT == WT_I4) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int k = 0; k < CPT; ++k) acc[t][k] = __builtin_fmaf(-8.0f, sb[t], acc[t][k]);
-  }
-  if (colok) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t < a.nt) {
-        float* dst = a.partial + ((size_t)g * a.B + a.tok0 + t) * d + col0;
-#pragma unroll
-        for (int k = 0; k < CPT; k += 4) {
-          const f32x4 v = f32x4{acc[t][k], acc[t][k + 1], acc[t][k + 2], acc[t][k + 3]};
-          // streamed past L2: the sum kernel reads it once, and the end of
-          // this kernel need not write back megabytes of dirty lines
-          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst + k));
-        }
+    };
+    if (nq > 0) {  // wave-uniform
+      for (int q = 0;; q += 2) {
+        up_step(Bq[0], Bq[1]);
+        if (q + 1 >= nq) break;
+        up_step(Bq[1], Bq[0]);
+        if (q + 2 >= nq) break;
       }
     }
   }
@@ -593,11 +466,11 @@ __device__ __forceinline__ void sum_body(const SumArgs& a, int vb, int gs) {
 
 // Shape choices and argument builders shared by the launchers.
 struct FfnShape {
-  int cpt, nth, nt;
+  int rv, nth, nt;  // residual float4 vectors per thread per token, threads, tokens per pass
 };
 FfnShape ffn_shape(int wt, int d, int batch);
 FfnArgs ffn_args(const FfnLaunch& p, int tok0, int nt, bool first);
-SumArgs sum_args(const FfnLaunch& p);
+SumArgs sum_args(const FfnLaunch& p, int rows);  // rows: partial rows per token
 int sum_groups(int batch, int d);
 
 }  // namespace sfnn

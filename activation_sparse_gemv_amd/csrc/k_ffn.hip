@@ -1,10 +1,10 @@
-// FFN launches: k_ffn (the one-launch gathered FFN) and k_sum (fixed-order
-// sum of the workgroups' partials).  The workgroup bodies live in
-// ffn_body.hpp.
+// Host side of the per-row FFN (k_up + k_down, bodies in ffn_body.hpp and
+// down_body.hpp) and k_sum / k_sum_wide, the fixed-order sums of the
+// matrix-core paths' partial rows.
 #include "ffn_launch.hpp"
 
 #ifndef SFNN_FFN_WGS
-#define SFNN_FFN_WGS 256  // FFN workgroups (raised when d_ff / kMaxPer needs more)
+#define SFNN_FFN_WGS 256  // up-projection workgroups (raised when d_ff / kMaxPer needs more)
 #endif
 
 namespace sfnn {
@@ -43,24 +43,47 @@ __global__ __launch_bounds__(256) void k_sum_wide(SumArgs a) {
   }
 }
 
-// Threads own CPT columns each for the down projection (at most 512
-// threads); the token group is bounded by the staged activations (LDS) and by
-// 64 accumulators per thread.
+// Up projection: 512 threads; the token group is bounded by the staged
+// activations (LDS).  rv: float4 vectors per thread per token that hold a
+// residual row in the look-ahead prologue (d_model <= 4 rv 512).
 FfnShape ffn_shape(int wt, int d, int batch) {
   FfnShape s;
-  s.cpt = d <= 4096 ? 8 : (d <= 8192 ? 16 : 32);
-  const int need = d / s.cpt;
-  s.nth = need <= 256 ? 256 : 512;
+  s.rv = d <= 4096 ? 2 : (d <= 8192 ? 4 : 8);
+  s.nth = 512;
   const int xb = (wt == WT_F32) ? 4 : 2;
   int cap = kStageBytes / (d * xb);
-  const int acc_cap = 64 / s.cpt;
-  if (cap > acc_cap) cap = acc_cap;
   if (cap < 1) cap = 1;
   if (cap > kMaxNT) cap = kMaxNT;
   int c2 = 1;
   while (c2 * 2 <= cap) c2 *= 2;
   s.nt = 1;
   while (s.nt < batch && s.nt < c2) s.nt *= 2;
+  return s;
+}
+
+// Down projection: the narrowest tile (16 bytes times 1, 2, 4 or 8 lanes) with
+// at most 256 tiles per row, so one launch has up to 256 workgroups that each
+// read every listed row's tile; tokens per pass bounded by 64 accumulators
+// per lane (fp32: 4, fp16: 8, INT4: 32 columns per lane).
+#ifndef SFNN_DOWN_MIN_LPR
+#define SFNN_DOWN_MIN_LPR 1  // narrowest tile, in 16-byte lanes per row
+#endif
+#ifndef SFNN_DOWN_MAX_TILES
+#define SFNN_DOWN_MAX_TILES 256  // most tiles (workgroups) per row
+#endif
+
+DownShape down_shape(int wt, int d, int batch) {
+  DownShape s;
+  const int vecs = down_row_bytes(wt, d) / 16;  // 16-byte vectors per row
+  s.lpr = 1;
+  while (s.lpr < SFNN_DOWN_MIN_LPR && (vecs % (2 * s.lpr)) == 0) s.lpr *= 2;
+  while (s.lpr < 8 && vecs / s.lpr > SFNN_DOWN_MAX_TILES && (vecs % (2 * s.lpr)) == 0) s.lpr *= 2;
+  s.tiles = vecs / s.lpr;
+  const int cpl = wt == WT_F32 ? 4 : (wt == WT_F16 ? 8 : 32);
+  int cap = 64 / cpl;
+  if (cap > kMaxNT) cap = kMaxNT;
+  s.nt = 1;
+  while (s.nt < batch && s.nt < cap) s.nt *= 2;
   return s;
 }
 
@@ -90,7 +113,8 @@ FfnArgs ffn_args(const FfnLaunch& p, int tok0, int nt, bool first) {
   a.ids_out = p.ids_out;
   a.count_out = p.count_out;
   a.mask = p.mask;
-  a.partial = p.partial;
+  a.hout = p.hrow;
+  a.hstride = p.f;
   a.r_in = nullptr;
   a.x_out = nullptr;
   a.eps = 0.0f;
@@ -106,10 +130,39 @@ FfnArgs ffn_args(const FfnLaunch& p, int tok0, int nt, bool first) {
   return a;
 }
 
-SumArgs sum_args(const FfnLaunch& p) {
+DownArgs ffn_down_args(const FfnLaunch& p) {
+  DownArgs a;
+  a.w = (const uint8_t*)p.w_down_t;
+  a.s = (const f16*)p.s_down_t;
+  if (p.src == SRC_UNION) {
+    a.ids = p.ids_out;
+    a.count = p.count_out;
+  } else if (p.src == SRC_IDS) {
+    a.ids = p.ids;
+    a.count = p.count;
+  } else {
+    a.ids = nullptr;
+    a.count = nullptr;
+  }
+  a.n_slots = p.f;
+  a.n_rows = p.f;
+  a.co = p.hrow;
+  a.co_stride = p.f;
+  a.bias = p.b_down;
+  a.bias_f32 = p.wt == WT_F32 ? 1 : 0;
+  a.y = p.y;
+  a.r_in = p.r_in;
+  a.r_out = p.r_out;
+  a.d = p.d;
+  a.tok0 = 0;
+  a.nt = p.batch;
+  return a;
+}
+
+SumArgs sum_args(const FfnLaunch& p, int rows) {
   SumArgs a;
   a.partial = p.partial;
-  a.G = ffn_uses_mfma(p) ? mfma_groups(p.d, p.groups) : p.groups;
+  a.G = rows;
   a.B = p.batch;
   a.d = p.d;
   a.xtype = p.wt == WT_F32 ? WT_F32 : WT_F16;
@@ -122,8 +175,8 @@ SumArgs sum_args(const FfnLaunch& p) {
 
 int sum_groups(int batch, int d) { return (batch * d + kSumEPW - 1) / kSumEPW; }  // 512-thread workgroups
 
-hipError_t launch_sum(const FfnLaunch& p, hipStream_t s) {
-  const SumArgs a = sum_args(p);
+hipError_t launch_sum(const FfnLaunch& p, int rows, hipStream_t s) {
+  const SumArgs a = sum_args(p, rows);
   if (a.G <= 32) {
     const int n4 = (p.batch * p.d) / 4;
     hipLaunchKernelGGL(k_sum_wide, dim3((n4 + 255) / 256), dim3(256), 0, s, a);

@@ -242,7 +242,7 @@ hipError_t launch_isg(const IsgLaunch& p, hipStream_t s) {
   f.groups = groups;
   f.b_down = p.bias;
   f.y = p.y;
-  return launch_sum(f, s);
+  return launch_sum(f, groups, s);
 }
 
 }  // namespace sfnn

@@ -3,10 +3,12 @@
 // (53ai.com sparsity survey, DejaVu section 如何充分利用结构化稀疏进行加速).
 // Layer l+1's predictor reads layer l's input x_l, so its two stages share
 // launches with layer l's FFN and sum:
-//   launch A(l): FFN_l workgroups (x_l = RMSNorm(r_l) built in their
-//                prologue) + predictor stage 1 of layer l+1 on the same x_l;
-//   launch B(l): sum of FFN_l's partials (y_l, r_{l+1} = r_l + y_l)
-//                + predictor stage 2 of layer l+1 (mask, union).
+//   launch A(l): FFN_l's up (+gate) rows (x_l = RMSNorm(r_l) built in every
+//                workgroup's prologue) + predictor stage 1 of layer l+1 on
+//                the same x_l;
+//   launch B(l): FFN_l's column-tiled down projection (y_l and
+//                r_{l+1} = r_l + y_l, no partial rows) + predictor stage 2 of
+//                layer l+1 (mask, union).
 // Two launches per layer instead of four, and the predictor's weight stream
 // overlaps the FFN's.  Layer 0's mask comes from its own input.
 #include "la_launch.hpp"
@@ -22,7 +24,7 @@ static int la_group(const FfnLaunch& F, const PredLaunch& P) {
   if (sh.nt < nt) nt = sh.nt;
   const int pwt = F.wt == WT_F32 ? WT_F32 : WT_F16;
   if (pred2_group(pwt, P.r, F.batch) < F.batch || pred2_vpl(pwt, P.r) > 4) return 0;
-  if (!chain_fits(F.d, nt, sh.nth, sh.cpt)) return 0;  // residual rows must fit the prologue's registers
+  if (nt * sh.rv > kChainMaxV || F.d > 4 * sh.rv * sh.nth) return 0;  // residual rows must fit the prologue's registers
   return nt;
 }
 
@@ -58,15 +60,10 @@ hipError_t launch_stack_lookahead(const PredLaunch* P, const FfnLaunch* F, const
       e = launch_residual_rmsnorm(R[l], nullptr, rtmp, F[l].batch, F[l].d, eps, const_cast<void*>(F[l].x),
                               F[l].wt == WT_F32 ? WT_F32 : WT_F16, s);
     }
-    FfnLaunch Fl = F[l];
-    Fl.y = nullptr;
-    Fl.r_in = nullptr;
-    Fl.r_out = nullptr;
-    if (e == hipSuccess) e = launch_ffn(Fl, s);
-    FfnLaunch Fs = F[l];
+    FfnLaunch Fs = F[l];  // y_l, and r_{l+1} = r_l + y_l
     Fs.r_in = R[l];
     Fs.r_out = const_cast<float*>(R[l + 1]);
-    if (e == hipSuccess) e = launch_sum(Fs, s);
+    if (e == hipSuccess) e = launch_ffn(Fs, s);
     if (e == hipSuccess && l + 1 < L) e = launch_predict_stage2(P[l + 1], s);
     if (e != hipSuccess) return e;
   }

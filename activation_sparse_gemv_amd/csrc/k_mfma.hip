@@ -438,7 +438,7 @@ void launch_rows_mfma(const void* w_t, const int32_t* sid, const int32_t* count,
 
 template <int ACT>
 static void mfma_all(const FfnLaunch& p, const int32_t* ids, const int32_t* count, hipStream_t s) {
-  const int kg = mfma_groups(p.d, p.groups);
+  const int kg = mfma_groups(p.d, kMfmaPartRows);
   for (int tok0 = 0; tok0 < p.batch; tok0 += 32) {
     const int nt = p.batch - tok0 < 32 ? p.batch - tok0 : 32;
     if (nt > 16)
@@ -462,12 +462,12 @@ hipError_t launch_ffn_mfma(const FfnLaunch& p, hipStream_t s) {
     count = p.count;
   }
   if (p.wt == WT_I4)
-    mfma_all_i4(p, ids, count, mfma_groups(p.d, p.groups), s);
+    mfma_all_i4(p, ids, count, mfma_groups(p.d, kMfmaPartRows), s);
   else if (p.act == ACT_RELU)
     mfma_all<ACT_RELU>(p, ids, count, s);
   else
     mfma_all<ACT_REGLU>(p, ids, count, s);
-  if (p.y || p.r_out) return launch_sum(p, s);
+  if (p.y || p.r_out) return launch_sum(p, mfma_groups(p.d, kMfmaPartRows), s);
   return hipGetLastError();
 }
 

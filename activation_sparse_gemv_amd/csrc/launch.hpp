@@ -62,8 +62,9 @@ struct FfnLaunch {
   int32_t* ids_out;       // SRC_UNION: compacted ids are written here ([f], first count valid)
   int32_t* count_out;     // SRC_UNION
   const uint64_t* mask;   // per-token gate [B][f/64] or null
-  float* partial;         // [groups][B][d] workspace
-  int groups;             // FFN workgroups (= partial rows per token)
+  float* hrow = nullptr;  // per-row path: h [B][f] fp32 workspace (slot order), up -> down
+  float* partial;         // matrix-core path: [kMfmaPartRows][B][d] workspace
+  int groups;             // up-projection workgroups of the per-row path
   float* y;               // [B][d] or null
   const float* r_in;      // residual add: r_out = r_in + y (both null to skip)
   float* r_out;
@@ -84,12 +85,15 @@ constexpr int kMfmaMinBatchDefault = 8;
 constexpr int kMfmaMinBatchI4Default = 3;
 bool ffn_uses_mfma(const FfnLaunch& p);
 int mfma_groups(int d, int max_groups);  // partial rows per token on that path
+// Partial rows per token the workspace holds for the matrix-core FFN.
+constexpr int kMfmaPartRows = 32;
 hipError_t launch_ffn_mfma(const FfnLaunch& p, hipStream_t s);
 // INT4 passes of that path (h in the workspace as fp32 [32][f]).
 void mfma_all_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int kg, hipStream_t s);
 int ffn_groups(int d, int f);
-// The fixed-order sum of an FFN's partials alone (y and / or the residual add).
-hipError_t launch_sum(const FfnLaunch& p, hipStream_t s);
+// The fixed-order sum of `rows` partial rows per token (p.partial) into y
+// and / or the residual add, with b_down.
+hipError_t launch_sum(const FfnLaunch& p, int rows, hipStream_t s);
 // Batches at or above this size run the fp16 predictor on the matrix cores
 // (k_pred1_mfma + k_pred2_mfma, up to 32 tokens per pass).
 constexpr int kPredMfmaMinBatch = 8;

@@ -28,20 +28,10 @@ namespace sfnn {
 
 constexpr int kChainMaxV = 16;  // float4 vectors of the residual rows kept per thread (at most)
 
-// Residual vectors per thread held by an FFN workgroup's chain prologue: the
-// FFN's shape rule ties the output columns per thread (cpt 8 / 16 / 32) to
-// d_model (<= 4096 / 8192 / 16384, 256 threads only at d_model <= 2048), so
-// cpt / 4 vectors per token cover one residual row.
-constexpr int ffn_chain_vecs(int nt, int cpt) { return nt * (cpt / 4); }
-// Whether nt residual rows of d_model floats fit those registers.
-constexpr bool chain_fits(int d, int nt, int nth, int cpt) {
-  return ffn_chain_vecs(nt, cpt) <= kChainMaxV && (d / 4) <= (cpt / 4) * nth;
-}
-
 // Residual-chain prologue, issue half: this thread's float4 vectors of the
 // nt residual rows.  Slot (t, k) holds vector threadIdx.x + k * blockDim.x of
 // token t's row, k < CV / NT.  Requires d / 4 <= (CV / NT) * blockDim.x
-// (chain_fits on the host).
+// (checked on the host).
 // UNCOND = false: slots past the row load nothing and hold zeros; use it where
 // many slots are spare (redundant loads of one shared address serialise in
 // the cache).  The loads sit in branches, so a later wait for anything
@@ -245,43 +235,23 @@ struct Pred2Args {
   int hot;              // mask words [0, hot) form the dense hot prefix
 };
 
-// Stage 2 for virtual workgroup vb (mask word vb): 8 waves (512 threads) of 8
-// rows; VPL 16-byte vectors per lane per row; RB rows in flight per wave.
+// Stage 2 for mask word vb: 8 waves (512 threads) of 8 rows; VPL 16-byte
+// vectors per lane per row; RB rows in flight per wave.  In two phases so
+// that a fused launch can issue other loads between them: issue() sends z,
+// tau and the first RB rows' weights, finish() adds them up (loading the
+// rest, when RB < 8), thresholds and writes the mask words.  Dense hot-prefix
+// words are the caller's (pred2_hot_word).
 template <int WT, int NT, int VPL, int RB>
-__device__ __forceinline__ void pred2_body(const Pred2Args& a, int vb) {
-  constexpr int E = vec_elems<WT>();  // 4 (fp32) or 8 (fp16) weights per vector
-  __shared__ float lg[NT][64];
-  __shared__ unsigned long long wsh[NT];
-  if (vb < a.hot) {  // uniform over the workgroup: no barrier below is reached
-    pred2_hot_word(a.mask, a.union_mask, a.logits, a.f, a.tok0, a.nt, vb);
-    return;
-  }
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int r = a.r, f = a.f;
-  const int row_bytes = r * (WT == WT_F32 ? 4 : 2);
-  const int nvec = row_bytes / 16;
-
-  // z elements of this lane's vectors (lane + 64u), straight to registers.
-  // Out-of-range vectors and tokens read an in-bounds z element and are
-  // cancelled later (zero weights / unused token), so nothing here waits for
-  // the loads and the weight loads below go out right behind them.
+struct Pred2Tile {
+  static constexpr int E = vec_elems<WT>();  // 4 (fp32) or 8 (fp16) weights per vector
   f32x4 zf[NT][VPL][E / 4];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int u = 0; u < VPL; ++u) {
-      const int v = lane + kWave * u;
-      const bool ok = v < nvec && t < a.nt;
-      const float* src = a.z + (size_t)(a.tok0 + (t < a.nt ? t : 0)) * r + (size_t)(ok ? v : 0) * E;
-#pragma unroll
-      for (int q = 0; q < E / 4; ++q) zf[t][u][q] = *reinterpret_cast<const f32x4*>(src + 4 * q);
-    }
-  const float tv = a.tau[vb * 64 + lane];
+  u32x4 w[RB][VPL];
+  float tv;
 
-#pragma unroll
-  for (int rb0 = 0; rb0 < 8; rb0 += RB) {
-    u32x4 w[RB][VPL];
+  __device__ __forceinline__ void load_rows(const Pred2Args& a, int vb, int rb0) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int row_bytes = a.r * (WT == WT_F32 ? 4 : 2);
+    const int nvec = row_bytes / 16;
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
       const int i = vb * 64 + wave * 8 + rb0 + k;
@@ -291,58 +261,106 @@ __device__ __forceinline__ void pred2_body(const Pred2Args& a, int vb) {
         w[k][u] = ld16_stream(a.w2_t + (size_t)i * row_bytes + 16 * (size_t)(v < nvec ? v : 0));
       }
     }
-    __builtin_amdgcn_sched_barrier(0);  // the rows' loads all issue before any math
-    constexpr int SH = 6 - log2c<RB>();
+  }
+
+  // z elements of this lane's vectors (lane + 64u), straight to registers.
+  // Out-of-range vectors and tokens read an in-bounds z element and are
+  // cancelled later (zero weights / unused token), so nothing here waits for
+  // the loads and the weight loads go out right behind them.
+  __device__ __forceinline__ void issue(const Pred2Args& a, int vb) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int r = a.r;
+    const int nvec = r * (WT == WT_F32 ? 4 : 2) / 16;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      float acc[RB];
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int k = 0; k < RB; ++k) {
-        float s = 0.0f;
+      for (int u = 0; u < VPL; ++u) {
+        const int v = lane + kWave * u;
+        const bool ok = v < nvec && t < a.nt;
+        const float* src = a.z + (size_t)(a.tok0 + (t < a.nt ? t : 0)) * r + (size_t)(ok ? v : 0) * E;
 #pragma unroll
-        for (int u = 0; u < VPL; ++u) {
-          const u32x4 wv = (lane + kWave * u < nvec) ? w[k][u] : u32x4{0u, 0u, 0u, 0u};
-          const float* zz = reinterpret_cast<const float*>(&zf[t][u][0]);
-          if constexpr (WT == WT_F32) {
-            s = __builtin_fmaf(bitcast<float>(wv.x), zz[0], s);
-            s = __builtin_fmaf(bitcast<float>(wv.y), zz[1], s);
-            s = __builtin_fmaf(bitcast<float>(wv.z), zz[2], s);
-            s = __builtin_fmaf(bitcast<float>(wv.w), zz[3], s);
-          } else {
-            const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+        for (int q = 0; q < E / 4; ++q) zf[t][u][q] = *reinterpret_cast<const f32x4*>(src + 4 * q);
+      }
+    tv = a.tau[vb * 64 + lane];
+    load_rows(a, vb, 0);
+  }
+
+  // write == false: the same loads, math and barriers, no output (a
+  // workgroup of a fused launch with no mask word of its own)
+  __device__ __forceinline__ void finish(const Pred2Args& a, int vb, bool write = true) {
+    __shared__ float lg[NT][64];
+    __shared__ unsigned long long wsh[NT];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int f = a.f;
+    const int nvec = a.r * (WT == WT_F32 ? 4 : 2) / 16;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              const f16x2 h = bitcast<f16x2>(ww[m]);
-              s = __builtin_fmaf((float)h.x, zz[2 * m], s);
-              s = __builtin_fmaf((float)h.y, zz[2 * m + 1], s);
+    for (int rb0 = 0; rb0 < 8; rb0 += RB) {
+      if (rb0 > 0) load_rows(a, vb, rb0);
+      __builtin_amdgcn_sched_barrier(0);  // the rows' loads all issue before any math
+      constexpr int SH = 6 - log2c<RB>();
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float acc[RB];
+#pragma unroll
+        for (int k = 0; k < RB; ++k) {
+          float s = 0.0f;
+#pragma unroll
+          for (int u = 0; u < VPL; ++u) {
+            const u32x4 wv = (lane + kWave * u < nvec) ? w[k][u] : u32x4{0u, 0u, 0u, 0u};
+            const float* zz = reinterpret_cast<const float*>(&zf[t][u][0]);
+            if constexpr (WT == WT_F32) {
+              s = __builtin_fmaf(bitcast<float>(wv.x), zz[0], s);
+              s = __builtin_fmaf(bitcast<float>(wv.y), zz[1], s);
+              s = __builtin_fmaf(bitcast<float>(wv.z), zz[2], s);
+              s = __builtin_fmaf(bitcast<float>(wv.w), zz[3], s);
+            } else {
+              const uint32_t ww[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+              for (int m = 0; m < 4; ++m) {
+                const f16x2 h = bitcast<f16x2>(ww[m]);
+                s = __builtin_fmaf((float)h.x, zz[2 * m], s);
+                s = __builtin_fmaf((float)h.y, zz[2 * m + 1], s);
+              }
             }
           }
+          acc[k] = s;
         }
-        acc[k] = s;
+        const float tot = rows_sum<RB>(acc);
+        if ((lane & ((1 << SH) - 1)) == 0) lg[t][wave * 8 + rb0 + ((lane >> SH) & (RB - 1))] = tot;
       }
-      const float tot = rows_sum<RB>(acc);
-      if ((lane & ((1 << SH) - 1)) == 0) lg[t][wave * 8 + rb0 + ((lane >> SH) & (RB - 1))] = tot;
     }
-  }
-  __syncthreads();
+    __syncthreads();
 
-  if (wave < a.nt) {
-    const int tok = a.tok0 + wave;
-    const float v = lg[wave][lane];
-    const bool on = v > tv;
-    const unsigned long long word = __ballot(on);
-    if (lane == 0) {
-      a.mask[(size_t)tok * (f / 64) + vb] = (uint64_t)word;
-      wsh[wave] = word;
+    if (write && wave < a.nt) {
+      const int tok = a.tok0 + wave;
+      const float v = lg[wave][lane];
+      const bool on = v > tv;
+      const unsigned long long word = __ballot(on);
+      if (lane == 0) {
+        a.mask[(size_t)tok * (f / 64) + vb] = (uint64_t)word;
+        wsh[wave] = word;
+      }
+      if (a.logits) a.logits[(size_t)tok * f + vb * 64 + lane] = v;
     }
-    if (a.logits) a.logits[(size_t)tok * f + vb * 64 + lane] = v;
+    __syncthreads();
+    if (write && threadIdx.x == 0) {
+      uint64_t u = a.first_pass ? 0ull : a.union_mask[vb];
+      for (int t = 0; t < a.nt; ++t) u |= wsh[t];
+      a.union_mask[vb] = u;
+    }
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t u = a.first_pass ? 0ull : a.union_mask[vb];
-    for (int t = 0; t < a.nt; ++t) u |= wsh[t];
-    a.union_mask[vb] = u;
+};
+
+template <int WT, int NT, int VPL, int RB>
+__device__ __forceinline__ void pred2_body(const Pred2Args& a, int vb) {
+  if (vb < a.hot) {  // uniform over the workgroup: no barrier below is reached
+    pred2_hot_word(a.mask, a.union_mask, a.logits, a.f, a.tok0, a.nt, vb);
+    return;
   }
+  Pred2Tile<WT, NT, VPL, RB> P;
+  P.issue(a, vb);
+  P.finish(a, vb);
 }
 
 // Token-group and shape choices and argument builders shared by the launchers.

@@ -149,7 +149,10 @@ sfnn_status sfnn_compact(const uint64_t* mask, int32_t batch, int32_t d_ff,
                          void* stream);
 
 /* Sparse FFN (step 3) over the neurons ids[0..*count) (ascending, unique,
- * < d_ff; entries >= d_ff are skipped and *count is clamped to d_ff).
+ * < d_ff; entries >= d_ff are skipped and *count is clamped to d_ff).  ids
+ * must have room for d_ff entries, as sfnn_compact writes them: entries past
+ * *count may be read (and are never used), so the kernels need not wait for
+ * the count before reading the list.
  * If mask != NULL each token b only takes neuron i when bit i of mask[b] is
  * set (a select, not a multiply); with mask == NULL every token takes every
  * listed neuron.  Writes y [batch][d_model] fp32. */

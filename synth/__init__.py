@@ -17,6 +17,7 @@ from .workload import (  # noqa: F401
     zipf_probs,
     uniform_probs,
     union_density,
+    layer_probs,
     quant_int4_g128,
     random_masks,
     pack_bits,

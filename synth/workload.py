@@ -242,6 +242,11 @@ def _probs_for(spec: LayerSpec, seed: int, layer: int) -> np.ndarray:
     return p
 
 
+def layer_probs(spec: LayerSpec, layer: int = 0, seed: int = 0) -> np.ndarray:
+    """The per-neuron fire probabilities make_layer draws layer ``layer`` with."""
+    return _probs_for(spec, seed, layer)
+
+
 def _bias_for(norms: np.ndarray, p: np.ndarray) -> np.ndarray:
     """-||w|| Phi^-1(1-p); p = 1 -> +6||w|| (always on), p = 0 -> -6||w||."""
     pc = np.clip(p, 0.0, 1.0)
@@ -252,10 +257,12 @@ def _bias_for(norms: np.ndarray, p: np.ndarray) -> np.ndarray:
 
 def _row_norms(w: np.ndarray) -> np.ndarray:
     out = np.empty(w.shape[0], dtype=np.float64)
-    step = 4096
-    for i in range(0, w.shape[0], step):
-        blk = w[i:i + step].astype(np.float64)
-        out[i:i + step] = np.sqrt(np.einsum("ij,ij->i", blk, blk))
+
+    def block(lo, hi):
+        blk = w[lo:hi].astype(np.float64)
+        out[lo:hi] = np.sqrt(np.einsum("ij,ij->i", blk, blk))
+
+    _map_blocks(block, w.shape[0], 256)
     return out
 
 

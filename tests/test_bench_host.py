@@ -34,3 +34,31 @@ def test_auto_hot_prefix_rule():
     u[256:] = 1.0
     assert 4.0 < limit < 5.0
     assert b._auto_hot_prefix(spec, u) == 192
+
+
+def test_row_sample_is_the_first_neurons():
+    """The dense-FFN row sample is the layer cut to its first k neurons: its
+    dense output equals the full layer's masked FFN over those neurons."""
+    import oracle
+    b = _bench()
+    spec = synth.config("c1", d_model=256, d_ff=512, rank=32)
+    lay = synth.make_layer(spec, layer=0)
+    x = synth.make_tokens(spec, 2, stream=3)
+    sub = b._row_sample(lay, 128)
+    assert sub.spec.d_ff == 128 and sub.w_up.shape == (128, 256) and lay.w_up.shape == (512, 256)
+    bits = np.zeros((2, 512), dtype=bool)
+    bits[:, :128] = True
+    assert np.array_equal(oracle.dense_ffn(sub, x), oracle.masked_ffn(lay, x, bits))
+
+
+def test_cpu_baseline_fields():
+    """The CPU baseline reports the cores this process may use and both the
+    sparse and the dense oracle rates (a tiny layer, a short budget)."""
+    b = _bench()
+    spec = synth.config("c1", d_model=256, d_ff=512, rank=32)
+    hosts = [synth.make_layer(spec, layer=l) for l in range(2)]
+    r = b._cpu_baseline(hosts, spec, 1, 4, 0.5)
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s"
+    assert r["cores"] == len(os.sched_getaffinity(0))
+    assert r["value"] > 0 and r["dense_ffn_tokens_s"] > 0
+    assert r["dense_ffn_ms_per_layer"] > 0 and "median" in r["sample"]
