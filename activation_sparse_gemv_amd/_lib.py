@@ -40,7 +40,7 @@ class SfnnError(RuntimeError):
 class sfnn_pred(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("wtype", ctypes.c_int32), ("w1_t", ctypes.c_void_p), ("w2_t", ctypes.c_void_p),
-                ("tau", ctypes.c_void_p), ("hot_prefix", ctypes.c_int32)]
+                ("tau", ctypes.c_void_p), ("hot_prefix", ctypes.c_int32), ("dense_min_batch", ctypes.c_int32)]
 
 
 class sfnn_ffn(ctypes.Structure):
@@ -147,11 +147,12 @@ def _wtype_of(t: torch.Tensor) -> int:
 class Pred:
     """Device predictor descriptor (keeps its tensors alive)."""
 
-    def __init__(self, w1_t: torch.Tensor, w2_t: torch.Tensor, tau: torch.Tensor, hot_prefix: int = 0):
+    def __init__(self, w1_t: torch.Tensor, w2_t: torch.Tensor, tau: torch.Tensor, hot_prefix: int = 0,
+                 dense_min_batch: int = 0):
         self.w1_t, self.w2_t, self.tau = w1_t, w2_t, tau
         r, d = w1_t.shape
         f = w2_t.shape[0]
-        self.c = sfnn_pred(d, f, r, _wtype_of(w1_t), _p(w1_t), _p(w2_t), _p(tau), hot_prefix)
+        self.c = sfnn_pred(d, f, r, _wtype_of(w1_t), _p(w1_t), _p(w2_t), _p(tau), hot_prefix, dense_min_batch)
 
     @property
     def hot_prefix(self) -> int:
@@ -160,6 +161,15 @@ class Pred:
     @hot_prefix.setter
     def hot_prefix(self, h: int):
         self.c.hot_prefix = h
+
+    @property
+    def dense_min_batch(self) -> int:
+        """Batch from which sfnn_layer / sfnn_stack_decode run dense (0: default 16, < 0: never)."""
+        return self.c.dense_min_batch
+
+    @dense_min_batch.setter
+    def dense_min_batch(self, b: int):
+        self.c.dense_min_batch = b
 
     @property
     def ref(self):

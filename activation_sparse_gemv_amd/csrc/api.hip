@@ -103,6 +103,14 @@ sfnn_status check_ffn(const sfnn_ffn* f) {
   return SFNN_OK;
 }
 
+constexpr int kDenseMinBatchDefault = 16;
+
+// The dense switch: from this batch on a layer skips the predictor.
+bool runs_dense(const sfnn_pred* p, int batch) {
+  const int t = p->dense_min_batch == 0 ? kDenseMinBatchDefault : p->dense_min_batch;
+  return t > 0 && batch >= t;
+}
+
 int x_type_of_ffn(const sfnn_ffn* f) { return f->wtype == SFNN_F32 ? SFNN_F32 : SFNN_F16; }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -254,6 +262,12 @@ sfnn_status run_layer(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x,
   if (!mask) mask = reinterpret_cast<uint64_t*>(w + Lw.mask);
   if (!ids) ids = reinterpret_cast<int32_t*>(w + Lw.ids);
   if (!count) count = reinterpret_cast<int32_t*>(w + Lw.count);
+  if (runs_dense(pred, batch)) {
+    // past the crossover: every neuron for every token, reported as an all-ones mask
+    if (launch_fill_dense(mask, (size_t)batch * (pred->d_ff / 64), ids, 1, pred->d_ff, count, 1, s) != hipSuccess)
+      return SFNN_E_HIP;
+    return hip_status(launch_ffn(ffn_launch(ffn, x, batch, nullptr, y, w, Lw), s));
+  }
   uint64_t* uni = reinterpret_cast<uint64_t*>(w + Lw.uni);
   // predictor (writes the batch's union mask), then the FFN compacts the
   // union in its first kernel and writes ids/count on the way
@@ -379,6 +393,24 @@ sfnn_status sfnn_stack_decode(int32_t n_layers, const sfnn_pred* preds, const sf
     F.count_out = c_of(l);
     return F;
   };
+
+  if (runs_dense(&preds[0], batch)) {
+    // past the crossover: no predictor; each layer is RMSNorm then the dense FFN
+    if ((mask_cap || ids_cap || count_cap) &&
+        launch_fill_dense(mask_cap, (size_t)n_layers * batch * W, ids_cap, n_layers, f, count_cap, n_layers, s) !=
+            hipSuccess)
+      return SFNN_E_HIP;
+    for (int l = 0; l < n_layers; ++l) {
+      if (launch_residual_rmsnorm(r_of(l), nullptr, nullptr, batch, d, eps, x_of(l), xb == 4 ? WT_F32 : WT_F16, s) !=
+          hipSuccess)
+        return SFNN_E_HIP;
+      FfnLaunch F = ffn_launch(&ffns[l], x_of(l), batch, nullptr, y_of(l), w, Lw);
+      F.r_in = r_of(l);
+      F.r_out = r_of(l + 1);
+      if (launch_ffn(F, s) != hipSuccess) return SFNN_E_HIP;
+    }
+    return SFNN_OK;
+  }
 
   if (flags & SFNN_STACK_LOOKAHEAD) {
     std::vector<PredLaunch> P((size_t)n_layers);
@@ -637,6 +669,6 @@ const char* sfnn_status_str(sfnn_status s) {
   return "unknown status";
 }
 
-int32_t sfnn_version(void) { return 330; }  // 300: sfnn_ffn.mfma_min_batch; 310: sfnn_input_sparse_gemv; 320: sfnn_pred.hot_prefix; 330: head-gated projections
+int32_t sfnn_version(void) { return 340; }  // 300: sfnn_ffn.mfma_min_batch; 310: sfnn_input_sparse_gemv; 320: sfnn_pred.hot_prefix; 330: head-gated projections; 340: sfnn_pred.dense_min_batch
 
 }  // extern "C"

@@ -1,5 +1,6 @@
 // Mask compaction, offline fire counting, row relayout, the stack's
 // residual + RMSNorm step, and two bandwidth probes.
+#include <algorithm>
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -157,6 +158,22 @@ __global__ __launch_bounds__(256) void k_residual_rmsnorm(const float* r_in, con
   }
 }
 
+// What a layer that ran dense reports: every mask bit set (mask_words 64-bit
+// words), every id in order (id_rows rows of f ids) and count = f
+// (count_n entries).  Each pointer may be null.
+__global__ __launch_bounds__(256) void k_fill_dense(uint64_t* __restrict__ mask, size_t mask_words,
+                                                    int32_t* __restrict__ ids, int id_rows, int f,
+                                                    int32_t* __restrict__ count, int count_n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t t0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (mask)
+    for (size_t i = t0; i < mask_words; i += stride) mask[i] = ~0ull;
+  if (ids)
+    for (size_t i = t0; i < (size_t)id_rows * f; i += stride) ids[i] = (int32_t)(i % (size_t)f);
+  if (count)
+    for (size_t i = t0; i < (size_t)count_n; i += stride) count[i] = f;
+}
+
 __global__ __launch_bounds__(256) void k_probe_read(const u32x4* __restrict__ buf, size_t nvec,
                                                     float* __restrict__ sink) {
   uint32_t acc = 0;
@@ -196,6 +213,17 @@ hipError_t launch_gather_rows(const void* src, const int32_t* perm, int n, int64
 hipError_t launch_residual_rmsnorm(const float* r_in, const float* y, float* r_out, int batch, int d,
                                    float eps, void* x_out, int xtype, hipStream_t s) {
   hipLaunchKernelGGL(k_residual_rmsnorm, dim3(batch), dim3(256), 0, s, r_in, y, r_out, d, eps, x_out, xtype);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_dense(uint64_t* mask, size_t mask_words, int32_t* ids, int id_rows, int f, int32_t* count,
+                             int count_n, hipStream_t s) {
+  const size_t n = std::max(mask_words, std::max((size_t)id_rows * f, (size_t)count_n));
+  size_t grid = (n + 255) / 256;
+  if (grid > 1024) grid = 1024;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(k_fill_dense, dim3((unsigned)grid), dim3(256), 0, s, mask, mask_words, ids, id_rows, f, count,
+                     count_n);
   return hipGetLastError();
 }
 

@@ -171,6 +171,9 @@ hipError_t launch_gather_rows(const void* src, const int32_t* perm, int n, int64
                               hipStream_t s);
 hipError_t launch_residual_rmsnorm(const float* r_in, const float* y, float* r_out, int batch, int d,
                                    float eps, void* x_out, int xtype, hipStream_t s);
+// all-ones masks, identity ids, count = f (a layer that ran dense); null pointers skipped
+hipError_t launch_fill_dense(uint64_t* mask, size_t mask_words, int32_t* ids, int id_rows, int f, int32_t* count,
+                             int count_n, hipStream_t s);
 hipError_t launch_probe_read(const void* buf, size_t bytes, float* sink, hipStream_t s);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 

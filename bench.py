@@ -66,12 +66,16 @@ def _parse():
     ap.add_argument("--hot-prefix", default="0",
                     help="dense hot prefix of power-law workloads: a neuron count (multiple of 64) or 'auto' "
                          "(chosen per layer from the profiled fire rates of the batch's union)")
+    ap.add_argument("--dense-min-batch", type=int, default=0,
+                    help="the predictor descriptors' dense switch: from this batch on a layer skips the predictor "
+                         "and runs the dense FFN (0: the library default, 16; negative: never)")
     ap.add_argument("--isg", action="store_true",
                     help="time the input-sparse GEMV (ReLU after the norm) over input densities and batches")
     return ap.parse_args()
 
 
 HBM_PEAK_GBS = 8000.0
+DENSE_MIN_BATCH_DEFAULT = 16  # the library's default dense switch (sfnn_pred.dense_min_batch = 0)
 COPY_PROBE_BYTES = 1 << 30
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 
@@ -195,6 +199,10 @@ def _stack_run(args, spec, B, headline):
             hosts.append(lay)  # kept for the oracle check and the CPU baseline
         del lay
     layers = [distinct[l % nd] for l in range(L)]
+    for pred, _ in distinct:
+        pred.dense_min_batch = args.dense_min_batch
+    thr = DENSE_MIN_BATCH_DEFAULT if args.dense_min_batch == 0 else args.dense_min_batch
+    dense = 0 < thr <= B  # past the switch every layer runs the dense FFN, no predictor
     torch.cuda.synchronize()
     t_setup = time.time() - t0
     print(f"# {L} layers of {spec.name} ({nd} distinct) resident in HBM after {t_setup:.1f}s",
@@ -292,13 +300,16 @@ def _stack_run(args, spec, B, headline):
     nmat = spec.n_mat
     ffn_bytes_u = lambda u: u * nmat * row_bytes + u * (nmat - 1) * xb          # noqa: E731
     pred_bytes = (d * r + r * (f - hot_mean)) * pb + 4 * (f - hot_mean)  # hot-prefix rows are not read
+    if dense:
+        pred_bytes = 0
     ffn_bytes = ffn_bytes_u(mean_u)
     cycled = "" if nd == L else f" (weights of {nd} distinct layers, {nd * layer_gb:.1f} GB, cycled)"
     workload = (f"{spec.name} FFN stack: {L} layers{cycled}, d_model {d}, d_ff {f}, rank-{r} predictor, "
                 f"{spec.act}, {spec.wtype}, "
                 f"{'zipf phi=%.2f ' % spec.phi if spec.profile == 'zipf' else ''}rho={spec.rho}, batch {B}"
                 f"{', dense hot prefix %s' % args.hot_prefix if hot_mean else ''}"
-                f"{', look-ahead predictor' if lookahead else ', per-layer predictor'}")
+                + (f", dense switch (batch >= {thr}): dense FFN, no predictor" if dense else
+                   (", look-ahead predictor" if lookahead else ", per-layer predictor")))
     per_sorted = np.sort(np.asarray(per_step))
     out = {
         "metric": "sparse-FFN decode tokens/sec at batch 1 + effective HBM GB/s on active bytes",
@@ -317,12 +328,13 @@ def _stack_run(args, spec, B, headline):
         "data": "synthetic (seeded N(0,0.02) weights, calibrated biases/thresholds, x~N(0,1))",
         "config": {"workload": workload, "global_batch": B, "decode_steps": steps, "layers": L,
                    "distinct_layers": nd,
-                   "predictor": "look-ahead (layer l+1 from x_l)" if lookahead else "per layer (layer l from x_l)"},
+                   "predictor": ("none: dense switch at batch >= %d" % thr) if dense else
+                   ("look-ahead (layer l+1 from x_l)" if lookahead else "per layer (layer l from x_l)")},
     }
     extra = {"mean_active_neurons": round(mean_u, 1), "active_fraction": round(mean_u / f, 4),
              "expected_union_fraction": round(synth.union_density(synth.layer_probs(spec, 0), B), 4),
              "ffn_active_bytes_per_layer": int(ffn_bytes), "predictor_bytes_per_layer": int(pred_bytes),
-             "setup_s": round(t_setup, 1)}
+             "setup_s": round(t_setup, 1), "dense_min_batch": thr, "ran_dense": bool(dense)}
     if hot_mean:
         extra["hot_prefix_per_layer"] = hots
     extra["layer_GBps_stack"] = round(L * (ffn_bytes + pred_bytes) / (ms_per_step / 1e3) / 1e9, 1)
@@ -331,7 +343,7 @@ def _stack_run(args, spec, B, headline):
 
     # ---- the oracle on sampled layers of the captured step ------------------
     if headline:
-        out.update(_oracle_check(spec, hosts, nd, L, B, xcap, ycap, masks, ids, counts, lookahead))
+        out.update(_oracle_check(spec, hosts, nd, L, B, xcap, ycap, masks, ids, counts, lookahead, dense))
 
     # ---- per-call timings: each call captured for all layers in one graph ----
     if headline and not args.no_extra:
@@ -400,16 +412,17 @@ def _stack_run(args, spec, B, headline):
     # predictor; its time: the step's HIP-event time divided by the layers
     us_layer_stack = ms_per_step * 1e3 / L
     layer_bytes = ffn_bytes + pred_bytes
-    workload_key = (f"{spec.name}/b{B}/{'lookahead' if lookahead else 'per-layer'}"
+    workload_key = (f"{spec.name}/b{B}/{'dense' if dense else ('lookahead' if lookahead else 'per-layer')}"
                     f"{'/hot%s' % args.hot_prefix if hot_mean else ''}")
     tr = _stored_traffic(workload_key)
     out["roofline"] = {
         "bound": "hbm", "achieved": round(layer_bytes / us_layer_stack / 1e3, 1), "peak": HBM_PEAK_GBS,
         "unit": "GB/s", "frac": round(layer_bytes / us_layer_stack / 1e3 / HBM_PEAK_GBS, 4),
         "traffic": (int(tr["fetch_bytes_per_layer"] + tr["write_bytes_per_layer"]) if tr else None),
-        "kernel": ("stack layer, look-ahead: k_la_up_pred1 (FFN_l up rows + predictor stage 1 of l+1) "
-                   "+ k_la_down_pred2 (FFN_l column-tiled down rows + predictor stage 2 of l+1)") if lookahead else
-                  ("stack layer, per-layer predictor: k_pred1 + k_pred2 + k_up + k_down"),
+        "kernel": ("stack layer, dense switch: RMSNorm + the dense FFN" if dense else
+                   ("stack layer, look-ahead: k_la_up_pred1 (FFN_l up rows + predictor stage 1 of l+1) "
+                    "+ k_la_down_pred2 (FFN_l column-tiled down rows + predictor stage 2 of l+1)") if lookahead else
+                   ("stack layer, per-layer predictor: k_pred1 + k_pred2 + k_up + k_down")),
         "bytes_per_launch": int(layer_bytes), "us_per_launch": round(us_layer_stack, 3),
         "launch": "one stack layer (two kernels in the look-ahead schedule)",
     }
@@ -438,11 +451,13 @@ def _host_relayout(lay, dev_layer):
     return h
 
 
-def _oracle_check(spec, hosts, nd, L, B, xcap, ycap, masks, ids, counts, lookahead):
+def _oracle_check(spec, hosts, nd, L, B, xcap, ycap, masks, ids, counts, lookahead, dense=False):
     """Layers 0 and L-1 of the captured step against the fp64 oracle on the
     same inputs: the ids and count of the mask the GPU used (bit-exact), the
     FFN output for that mask (normwise relative error), and for layer 0 the
-    predicted mask (bit-exact outside the fp32 rounding band)."""
+    predicted mask (bit-exact outside the fp32 rounding band).  Past the
+    dense switch the mask is all ones (no predictor ran), so the FFN check is
+    the oracle's dense FFN."""
     import oracle
     f = spec.d_ff
     errs, ids_ok, flips = [], True, 0
@@ -460,7 +475,9 @@ def _oracle_check(spec, hosts, nd, L, B, xcap, ycap, masks, ids, counts, lookahe
         ids_ok = ids_ok and rc == int(cnt_h[l]) and np.array_equal(rid, ids_h[l][:rc])
         ref = oracle.masked_ffn(lay, x, oracle.unpack_mask(ms[l], f))
         errs.append(float(np.abs(ys[l] - ref).max() / max(np.abs(ref).max(), 1e-30)))
-        if l == 0 or not lookahead:
+        if dense:
+            ids_ok = ids_ok and bool((oracle.unpack_mask(ms[l], f)).all())
+        elif l == 0 or not lookahead:
             lg, ob = oracle.predict(lay.w1_t, lay.w2_t, lay.tau, x)
             band = oracle.guard_band(lay.w1_t, lay.w2_t, x)
             gb = oracle.unpack_mask(ms[l], f)
@@ -493,6 +510,8 @@ def _sweep(args, spec):
     for rho in rhos:
         sp = synth.config(args.config, rho=rho)
         layers = [upload_layer(synth.make_layer(sp, layer=l), device=dev) for l in range(nl)]
+        for pred, _ in layers:
+            pred.dense_min_batch = -1  # the predictor's union at every batch (the switch is timed below)
         if sp.profile == "zipf":
             _hot_first(sg, layers, sp, 8, dev)
         for B in batches:
@@ -554,6 +573,15 @@ def _sweep(args, spec):
                     pt[f"us_dense_ffn_{name}"] = round(t_dense(), 2)
                 for _, ffn in layers:
                     ffn.mfma_min_batch = 0
+            # last (it overwrites the masks, ids and counts past the switch): the
+            # layer call with the library's dense switch, dense from batch 16 on
+            for pred, _ in layers:
+                pred.dense_min_batch = 0
+            pt["us_layer_default_switch"] = round(
+                timed(lambda: [sg.sfnn_layer(pred, ffn, x[l], B, y, masks[l], ids[l], cnt[l:l + 1], ws)
+                               for l, (pred, ffn) in enumerate(layers)]), 2)
+            for pred, _ in layers:
+                pred.dense_min_batch = -1
             points.append(pt)
             print(json.dumps(points[-1]), file=sys.stderr, flush=True)
         del layers

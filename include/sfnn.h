@@ -81,7 +81,20 @@ typedef enum { SFNN_RELU = 0, SFNN_REGLU = 1 } sfnn_act;
  * FFN computes them for every token, so their own ReLU / ReGLU decides their
  * share exactly.  This saves their rank * element-size predictor bytes per
  * neuron; it pays when the union of the batch fires them nearly always.
- * Outside [0, d_ff] or not a multiple of 64: SFNN_E_SHAPE. */
+ * Outside [0, d_ff] or not a multiple of 64: SFNN_E_SHAPE.
+ *
+ * Dense switch (sfnn_layer, sfnn_layer_noalloc, sfnn_stack_decode).  The
+ * sparse path pays off while the batch's union of active neurons stays a
+ * small share of d_ff (DejaVu's contextual sparsity is per token; the union
+ * of B tokens grows with B, and past a crossover the gathered rows cost more
+ * than reading the matrices whole: 53ai.com sparsity survey, DejaVu section).
+ * From batch >= dense_min_batch on (0 selects the default, 16; a negative
+ * value never) these calls skip the predictor and run the dense FFN: every
+ * neuron for every token, its own ReLU / ReGLU deciding its share, which is
+ * the masked FFN under an all-ones mask.  They then report that mask (all
+ * bits set), ids 0..d_ff-1 and count = d_ff.  The stack reads the switch of
+ * preds[0] for every layer.  The crossover depends on the fire rate and the
+ * hardware; the field is read per call. */
 typedef struct sfnn_pred {
   int32_t d_model, d_ff, rank;
   int32_t wtype;       /* sfnn_wtype: F32 or F16                         */
@@ -89,6 +102,7 @@ typedef struct sfnn_pred {
   const void* w2_t;    /* [d_ff][rank] (rows below hot_prefix unread)    */
   const float* tau;    /* [d_ff]       (entries below hot_prefix unread) */
   int32_t hot_prefix;  /* dense hot prefix, see above; 0: none           */
+  int32_t dense_min_batch; /* dense switch, see above; 0: default (16)   */
 } sfnn_pred;
 
 /* One FFN layer.  ReLU:  y = b_down + sum_i relu(W_up[i].x + b_up[i]) W_down[:, i]
@@ -169,7 +183,8 @@ sfnn_status sfnn_dense_ffn(const sfnn_ffn* ffn, const void* x, int32_t batch, fl
  * calls in sequence; the compaction runs inside the FFN's first kernel).
  * mask/ids/count are outputs the caller may inspect; any of them may be NULL,
  * then they live in ws.  With batch > 1 every token is gated by its own mask.
- * pred and ffn must agree on d_model, d_ff and the activation type. */
+ * pred and ffn must agree on d_model, d_ff and the activation type.  From
+ * batch >= pred->dense_min_batch on the layer runs dense (see sfnn_pred). */
 sfnn_status sfnn_layer(const sfnn_pred* pred, const sfnn_ffn* ffn, const void* x,
                        int32_t batch, float* y, uint64_t* mask, int32_t* ids,
                        int32_t* count, void* ws, size_t ws_bytes, void* stream);
@@ -323,7 +338,7 @@ sfnn_status sfnn_head_out(const sfnn_heads* op, const void* attn, int32_t batch,
                           float* y, void* ws, size_t ws_bytes, void* stream);
 size_t sfnn_heads_workspace_bytes(const sfnn_heads* op, int32_t batch);
 
-int32_t sfnn_version(void);  /* 300 and up: sfnn_ffn has mfma_min_batch; 310 and up: sfnn_input_sparse_gemv; 320 and up: sfnn_pred has hot_prefix; 330 and up: sfnn_head_qkv, sfnn_head_out */
+int32_t sfnn_version(void);  /* 300 and up: sfnn_ffn has mfma_min_batch; 310 and up: sfnn_input_sparse_gemv; 320 and up: sfnn_pred has hot_prefix; 330 and up: sfnn_head_qkv, sfnn_head_out; 340 and up: sfnn_pred has dense_min_batch */
 
 #ifdef __cplusplus
 }

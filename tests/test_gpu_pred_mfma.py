@@ -55,6 +55,7 @@ def test_mfma_predict_union_over_two_passes():
     B = 40
     x = synth.make_tokens(spec, B, stream=72)
     pred, ffn = upload_layer(lay)
+    pred.dense_min_batch = -1
     out = gpu_layer(pred, ffn, x)
     rid, rc, _ = oracle.compact(out["mask"], B, 2048)
     assert out["count"] == rc and np.array_equal(out["ids"], rid)

@@ -27,6 +27,7 @@ def _stack_case(spec, L, B, seed=0, lookahead=False, mfma_min_batch=0, hot_prefi
     for pred, ffn in dev:
         ffn.mfma_min_batch = mfma_min_batch
         pred.hot_prefix = hot_prefix
+        pred.dense_min_batch = -1  # the sparse path at every batch
     r_in = synth.make_tokens(spec, B, stream=200 + B, dtype=np.float32) * np.float32(3.0)
     xdt = torch.float32 if spec.wtype == "f32" else torch.float16
     out = gpu_stack(dev, r_in, 1e-6, xdt, flags=1 if lookahead else 0)
@@ -47,6 +48,8 @@ def _stack_case(spec, L, B, seed=0, lookahead=False, mfma_min_batch=0, hot_prefi
         gb = oracle.unpack_mask(out["mask"][l], f)
         outside = np.abs(ol - lay.tau[None, :].astype(np.float64)) > band
         assert not ((gb != ob) & outside).any(), l
+        # inside the band a bit may go either way, but only for a handful of neurons
+        assert ((gb != ob) & ~outside).sum() <= max(1, int(1e-4 * gb.size)), l
         # ids / count: compaction of the GPU's own mask, bit-exact
         rid, rc, _ = oracle.compact(out["mask"][l], B, f)
         assert out["count"][l] == rc and np.array_equal(out["ids"][l][:rc], rid), l
