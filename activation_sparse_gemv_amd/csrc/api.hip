@@ -22,14 +22,14 @@ bool al4(const void* p) { return p == nullptr || ((uintptr_t)p & 3u) == 0; }
 
 struct Layout {
   size_t z = 0, hrow = 0, partial = 0, mask = 0, uni = 0, ids = 0, count = 0, rbuf = 0, xbuf = 0, rtmp = 0,
-         hbuf = 0, sid = 0, total = 0;
+         hbuf = 0, hmax = 0, sid = 0, total = 0;
   int G = 0;
 };
 
 // Workspace: predictor stage-1 output z; the per-row FFN's activations h
 // (up -> down); the matrix-core FFN's partial rows; masks, union mask, ids,
 // count; the residual chain's two fp32 rows and layer input; the matrix-core
-// FFN's h (one 32-token pass) and slot ids.
+// FFN's h (one 32-token pass), its per-step token maxima and slot ids.
 Layout layout(const sfnn_pred* p, const sfnn_ffn* f, int batch) {
   Layout L;
   size_t off = 0;
@@ -64,9 +64,12 @@ Layout layout(const sfnn_pred* p, const sfnn_ffn* f, int batch) {
   L.rtmp = off;
   off += up((size_t)batch * dm * 4);
   if (f) {
-    // matrix-core FFN: h of one 32-token pass (two fp16 planes) and the slot ids
+    // matrix-core FFN: h of one 32-token pass (fp32), the largest |h| per
+    // 32-slot step and token, and the slot ids
     L.hbuf = off;
-    off += up((size_t)2 * 32 * f->d_ff * 2);
+    off += up((size_t)32 * f->d_ff * 4);
+    L.hmax = off;
+    off += up((size_t)(f->d_ff / 32) * 32 * 4);
     L.sid = off;
     off += up((size_t)f->d_ff * 4);
   }
@@ -175,6 +178,7 @@ FfnLaunch ffn_launch(const sfnn_ffn* f, const void* x, int batch, const uint64_t
   L.partial = reinterpret_cast<float*>(ws + Lw.partial);
   L.groups = Lw.G;
   L.hbuf = ws + Lw.hbuf;
+  L.hmax = reinterpret_cast<float*>(ws + Lw.hmax);
   L.sidbuf = reinterpret_cast<int32_t*>(ws + Lw.sid);
   L.mfma_min_batch = f->mfma_min_batch;
   return L;
@@ -519,7 +523,7 @@ IsgLayout isg_layout(const sfnn_isg* op, int batch) {
   off += up((size_t)L.G * batch * op->n_out * 4);
   if (op->wtype == SFNN_F16) {  // matrix-core path: one 32-token pass of h and the slot map
     L.hbuf = off;
-    off += up((size_t)2 * 32 * op->n_in * 2);
+    off += up((size_t)32 * op->n_in * 4);
     L.sid = off;
     off += up((size_t)op->n_in * 4);
   }

@@ -45,7 +45,50 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 
 // Eight fp32 values as two fp16 planes, hi = fp16(v) and lo = fp16(v - hi):
 // 22 of fp32's 24 significant bits, exact for integers below 2^22 (|v| must
-// stay within fp16's range).
+// stay within fp16's range: callers scale v by range_scale first).
+// Power-of-two range scaling for the two-plane split.  A token whose largest
+// |value| is m is carried as v * 2^-e with e = range_exp(m), which puts m in
+// [2^14, 2^15): no plane overflows fp16, and the low plane stays clear of
+// fp16's subnormals for every value within 2^-11 of m, so each value keeps
+// its 22 bits relative to the token's largest.  The products are multiplied by
+// 2^e afterwards; both steps are exact (powers of two) unless fp32 itself
+// under- or overflows.  m = 0 and non-finite m leave the values unscaled.
+__device__ __forceinline__ int range_exp(float m) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, m) & 0x7fffffffu;
+  const int ef = (int)(b >> 23);
+  if (b == 0u || ef == 0xff) return 0;
+  const int e = (ef == 0 ? 1 : ef) - 126 - 15;  // m = f 2^k, f in [0.5, 1), k = ef - 126
+  return e < -100 ? -100 : e;
+}
+
+// s_hm[t] = max(s_hm[t], hmax[st][t]) over the 32-slot steps st0 <= st <
+// st1 of a [steps][32] array of non-negative floats (compared as their bit
+// patterns, which order like the values), shared by a 512-thread workgroup,
+// four loads in flight per thread (indices past the end re-read the last).
+__device__ __forceinline__ void token_max_steps(const float* hmax, int st0, int st1, uint32_t* s_hm) {
+  const int n = (st1 - st0) * 32;
+  const float* base = hmax + (size_t)st0 * 32;
+  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * 512) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + 512 * j;
+      v[j] = base[i < n ? i : n - 1];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + 512 * j;
+      atomicMax(&s_hm[(i < n ? i : n - 1) & 31], __builtin_bit_cast(uint32_t, v[j]));
+    }
+  }
+}
+
+// 2^e in fp32 for e in [-126, 127].
+__device__ __forceinline__ float pow2f(int e) {
+  e = e < -126 ? -126 : (e > 127 ? 127 : e);
+  return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+}
+
 __device__ __forceinline__ void split_hi_lo(const f32x4 a, const f32x4 b, u32x4& hi, u32x4& lo) {
   const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint32_t h[4], l[4];

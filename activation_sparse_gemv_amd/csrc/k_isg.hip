@@ -145,13 +145,14 @@ __global__ __launch_bounds__(256) void k_isg(IsgArgs a) {
   }
 }
 
-// Matrix-core path: the pass's x at the listed inputs in slot order as the
-// high fp16 plane (x is fp16 already, so the low plane is zero), tokens past
-// the pass and slots past the list zero, and the slot -> input map (slots past
-// the list re-read the last listed row), for slots below |J| rounded up to 32.
+// Matrix-core path: the pass's x at the listed inputs in slot order as fp32
+// [32][n_in] (fp16 values, so k_down_mfma's split leaves its low plane zero
+// and needs no range scaling), tokens past the pass and slots past the list
+// zero, and the slot -> input map (slots past the list re-read the last
+// listed row), for slots below |J| rounded up to 32.
 __global__ __launch_bounds__(256) void k_isg_gather(const f16* __restrict__ x, const int32_t* __restrict__ ids,
                                                     const int32_t* __restrict__ count, int n_in, int tok0, int nt,
-                                                    f16* __restrict__ h, int32_t* __restrict__ sid) {
+                                                    float* __restrict__ h, int32_t* __restrict__ sid) {
   const int s = blockIdx.x * 256 + threadIdx.x;
   int cnt = *count;
   cnt = cnt < 0 ? 0 : (cnt > n_in ? n_in : cnt);
@@ -160,10 +161,7 @@ __global__ __launch_bounds__(256) void k_isg_gather(const f16* __restrict__ x, c
   const bool ok = s < cnt && j >= 0 && j < n_in;
   j = j >= 0 && j < n_in ? j : 0;
   sid[s] = j;
-  for (int t = 0; t < 32; ++t) {
-    h[(size_t)t * n_in + s] = (ok && t < nt) ? x[(size_t)(tok0 + t) * n_in + j] : (f16)0.0f;
-    h[(size_t)(32 + t) * n_in + s] = (f16)0.0f;
-  }
+  for (int t = 0; t < 32; ++t) h[(size_t)t * n_in + s] = (ok && t < nt) ? (float)x[(size_t)(tok0 + t) * n_in + j] : 0.0f;
 }
 
 // ---- host side ---------------------------------------------------------------
@@ -226,7 +224,7 @@ hipError_t launch_isg(const IsgLaunch& p, hipStream_t s) {
     for (int tok0 = 0; tok0 < p.batch; tok0 += 32) {
       const int nt = p.batch - tok0 < 32 ? p.batch - tok0 : 32;
       hipLaunchKernelGGL(k_isg_gather, dim3((p.n_in + 255) / 256), dim3(256), 0, s, (const f16*)p.x, p.ids,
-                         p.count, p.n_in, tok0, nt, (f16*)p.hbuf, p.sidbuf);
+                         p.count, p.n_in, tok0, nt, (float*)p.hbuf, p.sidbuf);
       launch_rows_mfma(p.w_t, p.sidbuf, p.count, p.hbuf, p.partial, p.n_out, p.n_in, p.batch, tok0, nt, groups, s);
     }
   } else if (p.wt == WT_F32) {

@@ -12,14 +12,18 @@
 //              takes pairs w, w+8, ...), each holding a 16x16 fp32 block per
 //              (tile, 16 tokens); the blocks are added in wavefront order in
 //              LDS, then bias, activation and the per-token select give
-//              h [token][slot], kept as two fp16 planes hi + lo (hi = fp16(h),
-//              lo = fp16(h - hi): 22 of fp32's 24 significant bits, exact for
-//              integers below 2^22; |h| must stay within fp16's range).
+//              h [token][slot] in fp32, and the largest |h| of each token
+//              over the workgroup's 32 slots.
 //  k_down_mfma workgroup = 128 (one token tile) or 64 (two) output columns
 //              x one group of slots; its 8
-//              wavefronts split the group's 32-slot steps and multiply both
-//              h planes; one fp32 partial row per group and token, added in a
-//              fixed order by k_sum.
+//              wavefronts split the group's 32-slot steps.  Each token's h is
+//              scaled by a power of two chosen from its largest |h| over the
+//              group's slots and split into two fp16 planes hi + lo (hi =
+//              fp16(h), lo = fp16(h - hi): 22 of fp32's 24 significant bits,
+//              exact for integers below 2^22, no overflow at any |h|); both
+//              planes are multiplied and the product scaled back.  One fp32
+//              partial row per group and token, added in a fixed order by
+//              k_sum.
 //
 // MFMA operands (16x16x32): lane l holds 8 consecutive K values of row
 // l % 16 of A and of column l % 16 of B, K block l / 16; D row 4*(l/16) + q,
@@ -40,7 +44,8 @@ struct MfmaUpArgs {
   const int32_t* ids;          // compacted ids, or null: slot s is neuron s
   const int32_t* count;        // |U|, or null: f
   const uint64_t* mask;        // per-token gate [B][f/64] or null
-  f16* h;                      // [2][32][f] this pass's h (hi, lo planes), token-major, slot-contiguous
+  float* h;                    // [32][f] this pass's h, token-major, slot-contiguous
+  float* hmax;                 // [f / 32][32] largest |h| of each 32-slot step and token
   int32_t* sid;                // [f] the row each slot reads (dropped slots: the last listed row)
   int d, f, tok0, nt;          // tokens tok0 .. tok0 + nt - 1, nt <= 16 * NB
 };
@@ -49,7 +54,8 @@ struct MfmaDownArgs {
   const f16* w_down_t;         // [f][d]
   const int32_t* sid;          // as written by k_up_mfma
   const int32_t* count;
-  const f16* h;                // as written by k_up_mfma ([2][32][f])
+  const float* h;              // as written by k_up_mfma ([32][f])
+  const float* hmax;           // as written by k_up_mfma, or null: h within fp16's range, not scaled
   float* partial;              // [KG][B][d]
   int d, f, B, tok0, nt, KG;
 };
@@ -107,9 +113,11 @@ __global__ __launch_bounds__(512) void k_up_mfma(MfmaUpArgs a) {
   constexpr int NM = ACT == ACT_REGLU ? 2 : 1;
   __shared__ f32x4 red[8][2][NB][kWave];  // one matrix's blocks at a time
   __shared__ int s_id[kUpSlots];
+  __shared__ uint32_t s_hm[32];  // largest |h| per token (fp32 bits: non-negative floats order as integers)
   const int cnt = slot_count(a.count, a.f);
   const int s0 = blockIdx.x * kUpSlots;
   if (s0 >= cnt) return;  // the whole workgroup
+  if (threadIdx.x < 32) s_hm[threadIdx.x] = 0u;  // ordered before the maxima by the sums' barriers
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int r = lane & 15, g = lane >> 4;
   const int d = a.d;
@@ -208,18 +216,19 @@ __global__ __launch_bounds__(512) void k_up_mfma(MfmaUpArgs a) {
         if (!((wv >> (id & 63)) & 1ull)) hv = 0.0f;  // select: gated-off neurons add nothing
       }
     }
-    const f16 hi = (f16)hv;
-    a.h[(size_t)tk * a.f + s0 + row] = hi;
-    a.h[(size_t)(32 + tk) * a.f + s0 + row] = (f16)(hv - (float)hi);
+    a.h[(size_t)tk * a.f + s0 + row] = hv;
+    atomicMax(&s_hm[tk], __builtin_bit_cast(uint32_t, __builtin_fabsf(hv)));
   }
+  __syncthreads();
+  if (threadIdx.x < 32) a.hmax[(size_t)blockIdx.x * 32 + threadIdx.x] = __builtin_bit_cast(float, s_hm[threadIdx.x]);
 }
 
 // One 32-slot step of the down projection for this lane: 8 rows (its K
-// block), CPL consecutive columns of each, and both h planes of its tokens.
+// block), CPL consecutive columns of each, and h of its tokens over the 8 slots.
 template <int NB, int CPL>
 struct DownFrag {
   uint32_t w[8][CPL / 2];
-  u32x4 h[2][NB];  // [plane][token tile]
+  f32x4 h[NB][2];  // [token tile][first, last four slots]
 };
 
 __device__ __forceinline__ void down_ids(const MfmaDownArgs& a, int st, int g, int (&id)[8]) {
@@ -232,7 +241,7 @@ __device__ __forceinline__ void down_ids(const MfmaDownArgs& a, int st, int g, i
 
 template <int NB, int CPL>
 __device__ __forceinline__ void down_issue(DownFrag<NB, CPL>& F, const MfmaDownArgs& a, const int (&id)[8], int col0,
-                                           const f16* (&hr)[NB], int st) {
+                                           const float* (&hr)[NB], int st) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const f16* src = a.w_down_t + (size_t)id[e] * a.d + col0;
@@ -247,8 +256,8 @@ __device__ __forceinline__ void down_issue(DownFrag<NB, CPL>& F, const MfmaDownA
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    F.h[0][nb] = ld16(hr[nb] + st * 32);
-    F.h[1][nb] = ld16(hr[nb] + (size_t)32 * a.f + st * 32);
+    F.h[nb][0] = *reinterpret_cast<const f32x4*>(hr[nb] + st * 32);
+    F.h[nb][1] = *reinterpret_cast<const f32x4*>(hr[nb] + st * 32 + 4);
   }
 }
 
@@ -256,8 +265,12 @@ __device__ __forceinline__ uint32_t pick16(uint32_t lo, uint32_t hi, int odd) {
   return odd ? ((hi & 0xffff0000u) | (lo >> 16)) : ((hi << 16) | (lo & 0xffffu));
 }
 
+// scin[nb]: the range scale of this lane's A token (n + 16 nb).
 template <int NB, int CPL>
-__device__ __forceinline__ void down_mul(const DownFrag<NB, CPL>& F, f32x4 (&acc)[CPL][NB]) {
+__device__ __forceinline__ void down_mul(const DownFrag<NB, CPL>& F, const float (&scin)[NB], f32x4 (&acc)[CPL][NB]) {
+  u32x4 ah[NB], al[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) split_hi_lo(F.h[nb][0] * scin[nb], F.h[nb][1] * scin[nb], ah[nb], al[nb]);
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     // column i of this lane's CPL columns, over its 8 rows (K)
@@ -268,8 +281,8 @@ __device__ __forceinline__ void down_mul(const DownFrag<NB, CPL>& F, f32x4 (&acc
     b.w = pick16(F.w[6][i >> 1], F.w[7][i >> 1], i & 1);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      acc[i][nb] = mfma_16x16x32(F.h[0][nb], b, acc[i][nb]);
-      acc[i][nb] = mfma_16x16x32(F.h[1][nb], b, acc[i][nb]);
+      acc[i][nb] = mfma_16x16x32(ah[nb], b, acc[i][nb]);
+      acc[i][nb] = mfma_16x16x32(al[nb], b, acc[i][nb]);
     }
   }
 }
@@ -284,6 +297,7 @@ __global__ __launch_bounds__(512) void k_down_mfma(MfmaDownArgs a) {
   constexpr int CPL = down_cpl<NB>();
   constexpr int WC = 16 * CPL;  // columns per workgroup
   __shared__ f32x4 red[8][2][NB][kWave];
+  __shared__ uint32_t s_hm[32];
   const int cnt = slot_count(a.count, a.f);
   const int cs = blockIdx.x / a.KG, kg = blockIdx.x % a.KG;  // slot group b % KG: one XCD's slots, see mfma_groups
   const int nsteps = (cnt + 31) >> 5;
@@ -293,9 +307,17 @@ __global__ __launch_bounds__(512) void k_down_mfma(MfmaDownArgs a) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int n = lane & 15, g = lane >> 4;
   const int col0 = cs * WC + CPL * n;
-  const f16* hr[NB];  // rows of tokens past the pass hold zeros
+  const float* hr[NB];  // rows of tokens past the pass hold zeros
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) hr[nb] = a.h + (size_t)(nb * 16 + n) * a.f + 8 * g;
+  // each token's largest |h| over this group's slots, and the range scales
+  if (threadIdx.x < 32) s_hm[threadIdx.x] = 0u;
+  __syncthreads();
+  if (a.hmax) token_max_steps(a.hmax, st0, st1, s_hm);
+  __syncthreads();
+  float scin[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) scin[nb] = pow2f(-range_exp(__builtin_bit_cast(float, s_hm[nb * 16 + n])));
   f32x4 acc[CPL][NB];
 #pragma unroll
   for (int i = 0; i < CPL; ++i)
@@ -321,13 +343,13 @@ __global__ __launch_bounds__(512) void k_down_mfma(MfmaDownArgs a) {
       down_ids(a, sc, g, idA);
       down_issue(Bf, a, idB, col0, hr, sb);
       __builtin_amdgcn_sched_barrier(0);
-      down_mul(A, acc);
+      down_mul(A, scin, acc);
       if (it + 1 >= iters) break;
       const int sd = it + 3 < iters ? S(it + 3) : sc;
       down_ids(a, sd, g, idB);
       down_issue(A, a, idA, col0, hr, sc);
       __builtin_amdgcn_sched_barrier(0);
-      down_mul(Bf, acc);
+      down_mul(Bf, scin, acc);
     }
   }
 
@@ -353,7 +375,8 @@ __global__ __launch_bounds__(512) void k_down_mfma(MfmaDownArgs a) {
       const int tk = nb * 16 + 4 * (ln >> 4) + q;
       if (tk >= a.nt) continue;
       const int col = cs * WC + CPL * (ln & 15) + qt * 2 + i;
-      a.partial[((size_t)kg * a.B + a.tok0 + tk) * a.d + col] = s;
+      a.partial[((size_t)kg * a.B + a.tok0 + tk) * a.d + col] =
+          s * pow2f(range_exp(__builtin_bit_cast(float, s_hm[tk])));
     }
   }
 }
@@ -394,7 +417,8 @@ static void mfma_pass(const FfnLaunch& p, const int32_t* ids, const int32_t* cou
   u.ids = ids;
   u.count = count;
   u.mask = p.mask;
-  u.h = (f16*)p.hbuf;
+  u.h = (float*)p.hbuf;
+  u.hmax = p.hmax;
   u.sid = p.sidbuf;
   u.d = p.d;
   u.f = p.f;
@@ -405,7 +429,8 @@ static void mfma_pass(const FfnLaunch& p, const int32_t* ids, const int32_t* cou
   dn.w_down_t = (const f16*)p.w_down_t;
   dn.sid = p.sidbuf;
   dn.count = count;
-  dn.h = (const f16*)p.hbuf;
+  dn.h = (const float*)p.hbuf;
+  dn.hmax = p.hmax;
   dn.partial = p.partial;
   dn.d = p.d;
   dn.f = p.f;
@@ -422,7 +447,8 @@ void launch_rows_mfma(const void* w_t, const int32_t* sid, const int32_t* count,
   dn.w_down_t = (const f16*)w_t;
   dn.sid = sid;
   dn.count = count;
-  dn.h = (const f16*)h;
+  dn.h = (const float*)h;
+  dn.hmax = nullptr;  // fp16 inputs: within range
   dn.partial = partial;
   dn.d = d;
   dn.f = f;
@@ -451,6 +477,10 @@ static void mfma_all(const FfnLaunch& p, const int32_t* ids, const int32_t* coun
 hipError_t launch_ffn_mfma(const FfnLaunch& p, hipStream_t s) {
   const int32_t* ids = nullptr;
   const int32_t* count = nullptr;
+  if (p.wt == WT_I4) {
+    const int kg = mfma_groups(p.d, kMfmaPartRows);
+    if ((p.f / 32 + kg - 1) / kg * 32 > kMfmaI4MaxGroupSlots) return hipErrorInvalidValue;  // not for d_ff <= 65536
+  }
   if (p.src == SRC_UNION) {
     // the union's ids in ascending order (and |U|), as the FFN kernels write them
     const hipError_t e = launch_compact(p.union_mask, 1, p.f, p.ids_out, p.count_out, nullptr, s);

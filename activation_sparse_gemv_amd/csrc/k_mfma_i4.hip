@@ -15,18 +15,22 @@
 //                 acc += s_row * (that sum), with the
 //                 workgroup's scales staged in LDS.  Blocks added in wavefront
 //                 order; bias, activation and per-token select give h [token]
-//                 [slot] in fp32.
+//                 [slot] in fp32, and the largest |h| of each token over
+//                 each 32-slot step.
 //  k_down_mfma_i4 workgroup = one 128-column scale group x one group of
 //                 slots.  In that column group row k has a single scale s_k,
 //                 so y = sum_k h_k s_k q_k: each step of 32 slots scales h by
-//                 its rows' scales (fp32), splits the product into two fp16
-//                 planes (22 bits), and multiplies them with the nibbles of 8
-//                 consecutive columns per lane (4 bytes per row), regrouped
-//                 per column with byte permutes.  The row ids and this column
-//                 group's scales of up to 8192 slots at a time are staged in
-//                 LDS, so a wavefront issues the row loads of several steps
-//                 back to back.  One fp32 partial row per slot group and
-//                 token, added in a fixed order by k_sum.
+//                 its rows' scales and by the token's power-of-two range
+//                 scale (fp32; chosen from the token's largest |h| over the
+//                 group's slots times the group's largest |s_k|), splits the
+//                 product into two fp16 planes (22 bits, no overflow), and
+//                 multiplies them with the nibbles of 8 consecutive columns
+//                 per lane (4 bytes per row), regrouped per column with byte
+//                 permutes.  The group's row ids and this column group's
+//                 scales (at most 8192 slots) are staged in LDS, so a
+//                 wavefront issues the row loads of several steps back to
+//                 back.  One fp32 partial row per slot group and token,
+//                 scaled back and added in a fixed order by k_sum.
 //
 // Workgroups of neighbouring column groups read the two 64-byte halves of the
 // same 128-byte lines; with the slot group as the fast block index they run
@@ -46,6 +50,7 @@ struct MfmaUpI4Args {
   const int32_t* count;          // |U|, or null: f
   const uint64_t* mask;          // per-token gate [B][f/64] or null
   float* h;                      // [32][f] this pass's h, token-major, slot-contiguous
+  float* hmax;                   // [f / 32][32] largest |h| of each 32-slot step and token
   int32_t* sid;                  // [f] the row each slot reads (dropped slots: the last listed row)
   int d, f, tok0, nt;
 };
@@ -56,6 +61,7 @@ struct MfmaDownI4Args {
   const int32_t* sid;
   const int32_t* count;
   const float* h;           // [32][f]
+  const float* hmax;        // [f / 32][32]
   float* partial;           // [KG][B][d]
   int d, f, B, tok0, nt, KG;
 };
@@ -96,9 +102,11 @@ __global__ __launch_bounds__(512) void k_up_mfma_i4(MfmaUpI4Args a) {
   __shared__ f16 ssc[NM][kMaxGroups][ROWS];          // scales, group-major
   __shared__ int s_id[ROWS];   // neuron of each row, -1 for a dropped slot
   __shared__ int s_idc[ROWS];  // the row actually read (dropped slots: the pad row)
+  __shared__ uint32_t s_hm[RT / 2][32];  // largest |h| per step and token (fp32 bits)
   const int cnt = slot_count_i4(a.count, a.f);
   const int s0 = blockIdx.x * ROWS;
   if (s0 >= cnt) return;  // the whole workgroup
+  if (threadIdx.x < RT / 2 * 32) s_hm[threadIdx.x / 32][threadIdx.x % 32] = 0u;  // before the first barrier
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int r = lane & 15, g = lane >> 4;
   const int d = a.d, G = d >> 7;
@@ -273,13 +281,21 @@ __global__ __launch_bounds__(512) void k_up_mfma_i4(MfmaUpI4Args a) {
         }
       }
       if (s0 + row < a.f) a.h[(size_t)tk * a.f + s0 + row] = hv;
+      atomicMax(&s_hm[tp][tk], __builtin_bit_cast(uint32_t, __builtin_fabsf(hv)));
     }
+  }
+  __syncthreads();
+  if (threadIdx.x < RT / 2 * 32) {
+    const int st = s0 / 32 + threadIdx.x / 32;  // the last workgroup's steps may run past d_ff
+    if (st < a.f / 32) a.hmax[(size_t)st * 32 + threadIdx.x % 32] = __builtin_bit_cast(float, s_hm[threadIdx.x / 32][threadIdx.x % 32]);
   }
 }
 
-// Slots per LDS chunk of the down projection: their row ids and this column
-// group's scales (48 KB).
-constexpr int kDownChunk = 8192;
+// Slots staged in LDS by a down workgroup: their row ids and this column
+// group's scales (48 KB).  One slot group never holds more: d_ff <= 65536 is
+// at most 2048 steps of 32 slots, and there are at least 8 slot groups
+// (mfma_groups), so a group has at most 256 steps.
+constexpr int kDownChunk = kMfmaI4MaxGroupSlots;
 
 // Steps of loads a wavefront issues before multiplying (registers allow four
 // with one token tile, three with two).
@@ -313,9 +329,11 @@ __device__ __forceinline__ void down_issue_i4(DownI4Frag<NB>& F, const MfmaDownI
   }
 }
 
-// sc: the 8 rows' scales of this column group (LDS).
+// sc: the 8 rows' scales of this column group (LDS); scin[nb]: the range
+// scale of this lane's A token (n + 16 nb).
 template <int NB>
-__device__ __forceinline__ void down_mul_i4(const DownI4Frag<NB>& F, const f16* sc, f32x4 (&acc)[8][NB]) {
+__device__ __forceinline__ void down_mul_i4(const DownI4Frag<NB>& F, const f16* sc, const float (&scin)[NB],
+                                            f32x4 (&acc)[8][NB]) {
   const u32x4 sraw = *reinterpret_cast<const u32x4*>(sc);
   const f16x2 s01 = bitcast<f16x2>(sraw.x), s23 = bitcast<f16x2>(sraw.y);
   const f16x2 s45 = bitcast<f16x2>(sraw.z), s67 = bitcast<f16x2>(sraw.w);
@@ -323,10 +341,9 @@ __device__ __forceinline__ void down_mul_i4(const DownI4Frag<NB>& F, const f16* 
   u32x4 ah[NB], al[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const f32x4 p0 = {F.h[nb][0].x * (float)s01.x, F.h[nb][0].y * (float)s01.y, F.h[nb][0].z * (float)s23.x,
-                      F.h[nb][0].w * (float)s23.y};
-    const f32x4 p1 = {F.h[nb][1].x * (float)s45.x, F.h[nb][1].y * (float)s45.y, F.h[nb][1].z * (float)s67.x,
-                      F.h[nb][1].w * (float)s67.y};
+    const f32x4 h0 = F.h[nb][0] * scin[nb], h1 = F.h[nb][1] * scin[nb];
+    const f32x4 p0 = {h0.x * (float)s01.x, h0.y * (float)s01.y, h0.z * (float)s23.x, h0.w * (float)s23.y};
+    const f32x4 p1 = {h1.x * (float)s45.x, h1.y * (float)s45.y, h1.z * (float)s67.x, h1.w * (float)s67.y};
     split_hi_lo(p0, p1, ah[nb], al[nb]);
   }
   // B operands: column i over the 8 rows, nibbles as fp16 integers.  Offset
@@ -363,8 +380,10 @@ __device__ __forceinline__ void down_mul_i4(const DownI4Frag<NB>& F, const f16* 
 template <int NB>
 __global__ __launch_bounds__(512) void k_down_mfma_i4(MfmaDownI4Args a) {
   __shared__ f32x4 red[8][2][NB][kWave];
-  __shared__ __align__(16) int lid[kDownChunk];  // the chunk's row ids
+  __shared__ __align__(16) int lid[kDownChunk];  // the group's row ids
   __shared__ __align__(16) f16 lsc[kDownChunk];  // their scales in this column group
+  __shared__ uint32_t s_hm[32];                  // largest |h| per token over the group's steps (fp32 bits)
+  __shared__ uint32_t s_sm;                      // largest |s_k| over the group's rows (fp32 bits)
   const int cnt = slot_count_i4(a.count, a.f);
   // slot group b % KG (one XCD's slots, see mfma_groups); neighbouring column
   // groups b and b + KG share an XCD and the halves of 128-byte lines
@@ -385,14 +404,16 @@ __global__ __launch_bounds__(512) void k_down_mfma_i4(MfmaDownI4Args a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[i][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  constexpr int CST = kDownChunk / 32;  // steps per chunk
   constexpr int PER = kDownChunk / 512;
   constexpr int NBT = down_i4_batch<NB>();
   const int G = a.d >> 7;
-  for (int c0 = st0; c0 < st1; c0 += CST) {
-    const int c1 = c0 + CST < st1 ? c0 + CST : st1;
-    const int ns = (c1 - c0) * 32;  // slots of this chunk (sid holds them all)
-    __syncthreads();                // the previous chunk's LDS reads are done
+  if (threadIdx.x < 32) s_hm[threadIdx.x] = 0u;
+  if (threadIdx.x == 0) s_sm = 0u;
+  __syncthreads();
+  float scin[NB] = {};
+  if (st0 < st1) {  // workgroup-uniform; st1 - st0 <= kDownChunk / 32 (the host checks)
+    const int c0 = st0, c1 = st1;
+    const int ns = (c1 - c0) * 32;  // slots of this group (sid holds them all)
     {
       // ids, then their scales: every load of a kind goes out before any use
       int idv[PER];
@@ -404,6 +425,8 @@ __global__ __launch_bounds__(512) void k_down_mfma_i4(MfmaDownI4Args a) {
       f16 sv[PER];
 #pragma unroll
       for (int j = 0; j < PER; ++j) sv[j] = a.s_down_t[(size_t)idv[j] * G + cs];
+      token_max_steps(a.hmax, c0, c1, s_hm);
+      float sm = 0.0f;
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int i = threadIdx.x + 512 * j;
@@ -411,9 +434,15 @@ __global__ __launch_bounds__(512) void k_down_mfma_i4(MfmaDownI4Args a) {
           lid[i] = idv[j];
           lsc[i] = sv[j];
         }
+        sm = __builtin_fmaxf(sm, __builtin_fabsf((float)sv[j]));  // re-read values are the group's too
       }
+      atomicMax(&s_sm, __builtin_bit_cast(uint32_t, sm));
     }
     __syncthreads();
+    const float smax = __builtin_bit_cast(float, s_sm);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      scin[nb] = pow2f(-range_exp(__builtin_bit_cast(float, s_hm[nb * 16 + n]) * smax));
     // steps c0 + wave, + 8, ... in batches of NBT: every batch's loads go out
     // before any of its products (a step past the last re-reads the last)
     const int first = c0 + wave;
@@ -426,9 +455,10 @@ __global__ __launch_bounds__(512) void k_down_mfma_i4(MfmaDownI4Args a) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NBT; ++j)
-        if (b0 + j < iters) down_mul_i4(F[j], lsc + (first + 8 * (b0 + j) - c0) * 32 + 8 * g, acc);
+        if (b0 + j < iters) down_mul_i4(F[j], lsc + (first + 8 * (b0 + j) - c0) * 32 + 8 * g, scin, acc);
     }
   }
+  const float smax = __builtin_bit_cast(float, s_sm);  // 0 for an empty group: its rows are zeros
 
   // add the 8 wavefronts' blocks in order, two columns at a time; every
   // workgroup writes its rows (zeros when its slot group is empty)
@@ -452,7 +482,8 @@ __global__ __launch_bounds__(512) void k_down_mfma_i4(MfmaDownI4Args a) {
       const int tk = nb * 16 + 4 * (ln >> 4) + q;
       if (tk >= a.nt) continue;
       const int col = cs * 128 + 8 * (ln & 15) + qt * 2 + i;
-      a.partial[((size_t)kg * a.B + a.tok0 + tk) * a.d + col] = s;
+      a.partial[((size_t)kg * a.B + a.tok0 + tk) * a.d + col] =
+          s * pow2f(range_exp(__builtin_bit_cast(float, s_hm[tk]) * smax));
     }
   }
 }
@@ -482,6 +513,7 @@ static void mfma_pass_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* 
   u.count = count;
   u.mask = p.mask;
   u.h = (float*)p.hbuf;
+  u.hmax = p.hmax;
   u.sid = p.sidbuf;
   u.d = p.d;
   u.f = p.f;
@@ -494,6 +526,7 @@ static void mfma_pass_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* 
   dn.sid = p.sidbuf;
   dn.count = count;
   dn.h = (const float*)p.hbuf;
+  dn.hmax = p.hmax;
   dn.partial = p.partial;
   dn.d = p.d;
   dn.f = p.f;

@@ -68,7 +68,8 @@ struct FfnLaunch {
   float* y;               // [B][d] or null
   const float* r_in;      // residual add: r_out = r_in + y (both null to skip)
   float* r_out;
-  void* hbuf = nullptr;   // matrix-core path: h of one 32-token pass, 128 f bytes: fp16 [2][32][f]
+  void* hbuf = nullptr;   // matrix-core path: h of one 32-token pass, fp32 [32][f]
+  float* hmax = nullptr;  // matrix-core path: largest |h| per 32-slot step and token, [f / 32][32]
                           // (hi, lo planes), fp32 [32][f] for INT4 (null: path off)
   int32_t* sidbuf = nullptr;  // matrix-core path: slot ids [f]
   int mfma_min_batch = 0;     // matrix-core path from this batch on (0: default, < 0: never)
@@ -88,6 +89,9 @@ int mfma_groups(int d, int max_groups);  // partial rows per token on that path
 // Partial rows per token the workspace holds for the matrix-core FFN.
 constexpr int kMfmaPartRows = 32;
 hipError_t launch_ffn_mfma(const FfnLaunch& p, hipStream_t s);
+// Slots of one slot group the INT4 down kernel stages in LDS (ids and
+// scales); launch_ffn_mfma refuses a shape whose groups would hold more.
+constexpr int kMfmaI4MaxGroupSlots = 8192;
 // INT4 passes of that path (h in the workspace as fp32 [32][f]).
 void mfma_all_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int kg, hipStream_t s);
 int ffn_groups(int d, int f);
@@ -132,7 +136,7 @@ struct IsgLaunch {
   float* partial;         // [groups][B][n_out] workspace
   int groups;             // row groups (= partial rows per token)
   float* y;               // [B][n_out]
-  void* hbuf = nullptr;   // matrix-core path: [2][32][n_in] fp16 (x at the listed inputs, zero low plane)
+  void* hbuf = nullptr;   // matrix-core path: [32][n_in] fp32 (x at the listed inputs)
   int32_t* sidbuf = nullptr;  // matrix-core path: [n_in] slot -> input
 };
 hipError_t launch_isg(const IsgLaunch& p, hipStream_t s);

@@ -118,8 +118,10 @@ typedef struct sfnn_pred {
  * whose per-row kernels hold only a few tokens per pass; a negative value
  * never) runs it on the matrix cores: the up projection over the gathered
  * rows and the down projection over column slices, fp32 accumulation, h
- * carried between them as two fp16 parts (22 significant bits; |h| must lie
- * within fp16's range), the partial rows added in a fixed order
+ * carried between them in fp32 and entering the down products as two fp16
+ * parts of h times a per-token power of two (22 significant bits relative to
+ * the token's largest |h|, no overflow at any finite |h|), the partial rows
+ * added in a fixed order
  * (deterministic, no atomics).  I4G128 nibbles enter as exact fp16 integers
  * and the group scales are applied in fp32, so no weight is rounded.  Smaller
  * batches and F32 weights take the per-row kernels.  The field is read per
