@@ -46,8 +46,9 @@ Layout layout(const sfnn_pred* p, const sfnn_ffn* f, int batch) {
     L.G = ffn_groups(f->d_model, f->d_ff);
     L.hrow = off;
     off += up((size_t)batch * f->d_ff * 4);
+    // matrix-core partial rows, or the per-row down projection's row groups
     L.partial = off;
-    if (f->wtype != SFNN_F32) off += up((size_t)kMfmaPartRows * batch * f->d_model * 4);
+    off += up((size_t)kMfmaPartRows * batch * f->d_model * 4);
   }
   L.mask = off;
   off += up((size_t)batch * (ff / 64) * 8);

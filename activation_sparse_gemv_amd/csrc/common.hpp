@@ -174,20 +174,6 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
   return ((uint64_t)hi << 32) | lo;
 }
 
-// INT4 nibbles of one dword as four fp16 pairs (e0,e4) (e1,e5) (e2,e6) (e3,e7).
-// Each nibble t is two's complement; (t ^ 8) is t + 8 in offset binary, and
-// the fp16 bit pattern 0x6400 | n is 1024 + n, so subtracting 1032 leaves t.
-__device__ __forceinline__ void int4_pairs(uint32_t u, uint32_t out[4]) {
-  const uint32_t v = u ^ 0x88888888u;
-  const f16x2 bias = {(f16)1032.0f, (f16)1032.0f};
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t p = ((v >> (4 * k)) & 0x000F000Fu) | 0x64006400u;
-    const f16x2 q = bitcast<f16x2>(p) - bias;
-    out[k] = __builtin_bit_cast(uint32_t, q);
-  }
-}
-
 // Stage tokens [tok0, tok0+nt) of x [*, K] into LDS xs [NT][K] (rows of
 // tokens >= nt are zero) in two parts, so that loads issued later (weight
 // rows) can be in flight while the activations arrive: issue() starts the
@@ -318,27 +304,42 @@ __device__ __forceinline__ void vec_f16_f32x(const u32x4 w, const float* xs, int
 }
 
 // INT4 weights (32 elements, one 128-group scale) x fp16 activations staged
-// in the INT4 pairing order.
+// in the INT4 pairing order.  The nibbles enter the dot products as fp16
+// subnormals, with no conversion: in offset binary (t ^ 8 = t + 8 = n), a
+// nibble masked in place in bits 0-3 of a half is the fp16 value n 2^-24, and
+// in bits 4-7 it is 16 n 2^-24, so two masks of the dword and two of it
+// shifted by 8 give its eight nibbles as four pairs, (n0,n4) (n2,n6) at 2^-24
+// and (n1,n5) (n3,n7) at 2^-20.  Every product is exact in fp32; the pairs
+// are summed at their own scale and brought to 2^-24 together.  m8 holds -8
+// times the sum of the same 32 activations (the offset's share, one value per
+// token, stride mstride), so
+//   acc += scale * (2^24 sum(n x) - 8 sum(x)) = scale * sum(t x).
 template <int NT>
-__device__ __forceinline__ void vec_i4(const u32x4 w, float scale, const f16* xs, int xstride,
-                                       float* acc) {
-  uint32_t q[4][4];
-  int4_pairs(w.x, q[0]);
-  int4_pairs(w.y, q[1]);
-  int4_pairs(w.z, q[2]);
-  int4_pairs(w.w, q[3]);
+__device__ __forceinline__ void vec_i4(const u32x4 w, float scale, const f16* xs, const float* m8, int xstride,
+                                       int mstride, float* acc) {
+  const uint32_t v[4] = {w.x ^ 0x88888888u, w.y ^ 0x88888888u, w.z ^ 0x88888888u, w.w ^ 0x88888888u};
+  uint32_t e[4][2], o[4][2];  // per dword: (n0,n4) (n2,n6) and 16 (n1,n5) 16 (n3,n7)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t sh = v[j] >> 8;
+    e[j][0] = v[j] & 0x000F000Fu;
+    o[j][0] = v[j] & 0x00F000F0u;
+    e[j][1] = sh & 0x000F000Fu;
+    o[j][1] = sh & 0x00F000F0u;
+  }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    float d = 0.0f;
+    float de = 0.0f, dd = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + t * xstride + 8 * j);
-      d = dot2(q[j][0], xv.x, d);
-      d = dot2(q[j][1], xv.y, d);
-      d = dot2(q[j][2], xv.z, d);
-      d = dot2(q[j][3], xv.w, d);
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + t * xstride + 8 * j);  // (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+      de = dot2(e[j][0], xv.x, de);
+      dd = dot2(o[j][0], xv.y, dd);
+      de = dot2(e[j][1], xv.z, de);
+      dd = dot2(o[j][1], xv.w, dd);
     }
-    acc[t] = __builtin_fmaf(d, scale, acc[t]);
+    const float sn = __builtin_fmaf(dd, 0.0625f, de);  // sum(n x) 2^-24
+    acc[t] = __builtin_fmaf(scale, __builtin_fmaf(sn, 16777216.0f, m8[t * mstride]), acc[t]);
   }
 }
 
@@ -377,19 +378,26 @@ struct RowLoads {
   }
 
   // acc[t] += (this batch of the row) . (staged row t of xs); XT is the staged type.
+  // INT4: m8 / mstride as vec_i4 takes them (per 32-element vector of the row).
+  // vb: v0 of the wavefront's first lane when LPR is the wavefront (its
+  // vectors are then v0 .. v0 + 63), else -1; vectors that no lane of the
+  // wavefront holds are skipped by a uniform branch (no load sits in it).
   template <int NT, typename XT>
-  __device__ __forceinline__ void consume(int nvec, int v0, const XT* xs, int xstride, float* acc) const {
+  __device__ __forceinline__ void consume(int nvec, int v0, const XT* xs, int xstride, float* acc,
+                                          const float* m8 = nullptr, int mstride = 0, int vb = -1) const {
     constexpr int E = vec_elems<WT>();
 #pragma unroll
     for (int u = 0; u < UB; ++u) {
+      if (vb >= 0 && vb + u * LPR >= nvec) break;
       const int v = v0 + u * LPR;
       const bool ok = v < nvec;
       // a slot past the row uses vector 0 of the staged rows (finite values)
       // and zero weights / a zero scale, so it adds exactly zero; v0 itself
-      // can lie past a short row
+      // can lie past a short row.  (INT4 needs only the zero scale: the
+      // re-read weights of a row are finite.)
       const int vc = ok ? v : 0;
       const u32x4 z = {0u, 0u, 0u, 0u};
-      const u32x4 wv = ok ? w[u] : z;
+      const u32x4 wv = (WT == WT_I4 || ok) ? w[u] : z;
       if constexpr (WT == WT_F32) {
         vec_f32<NT>(wv, reinterpret_cast<const float*>(xs) + E * vc, xstride, acc);
       } else if constexpr (WT == WT_F16) {
@@ -398,7 +406,7 @@ struct RowLoads {
         else
           vec_f16<NT>(wv, reinterpret_cast<const f16*>(xs) + E * vc, xstride, acc);
       } else {
-        vec_i4<NT>(wv, ok ? sc[u] : 0.0f, reinterpret_cast<const f16*>(xs) + E * vc, xstride, acc);
+        vec_i4<NT>(wv, ok ? sc[u] : 0.0f, reinterpret_cast<const f16*>(xs) + E * vc, m8 + vc, xstride, mstride, acc);
       }
     }
   }

@@ -1,17 +1,22 @@
-// Column-tiled down projection over a list of rows, with no partial rows:
+// Column-tiled down projection over a list of rows:
 //   y[t][c] = bias[c] + sum over slots j < count of  h[t][j] * W[row_j][c]
 // W is row-major [rows][d]: the FFN's neuron-major W_down^T (row i is column i
 // of W_down), or an input-major projection w_t.  Only the listed rows are
 // read: a zero activation zeroes the whole row it multiplies, so that row
 // need not be loaded at all (53ai.com sparsity survey, section 激活稀疏).
 //
-// A workgroup owns one tile of TB = 16 * LPR bytes of every row and walks ALL
-// listed rows, so it ends holding the complete sums of its columns: y is
-// written directly, with no partial rows to store and add up afterwards.
-// LPR lanes cover a row's tile (one 16-byte load each), a wavefront covers
-// 64 / LPR rows per load, eight wavefronts 512 / LPR.  The tiles of one
-// 128-byte line go to workgroups on the same XCD (see down_tile), so each line
-// is fetched from HBM once and the other tiles find it in that XCD's L2.
+// A workgroup owns one tile of TB = 16 * LPR bytes (a whole 128-byte line
+// where the row allows) of the rows of one row group: the listed slots are
+// cut into RG equal runs, so a launch has tiles * RG workgroups whatever the
+// row length.  LPR lanes cover a row's tile (one 16-byte load each), a
+// wavefront covers 64 / LPR rows per load, eight wavefronts 512 / LPR.  With
+// one row group the workgroup ends holding the complete sums of its columns
+// and writes y directly.  With several, each writes its group's column sums
+// to a partial row, and a small launch after it (k_sum) adds the RG partial
+// rows in group order (deterministic) into y and the residual row.  (Adding
+// them inside the launch, by the last group of a tile to arrive, needs a
+// device-scope release from every workgroup, which writes back and
+// invalidates the L2 of its XCD: far slower than the extra launch.)
 //
 // Pipelining: slots are taken in chunks of KB rows per lane; the row ids of
 // chunk c+2 and the weights of chunk c+1 are requested before chunk c is
@@ -46,6 +51,9 @@ struct DownArgs {
   const float* r_in;     // residual add r_out = r_in + y (null to skip)
   float* r_out;
   int d, tok0, nt;
+  int rg;                // row groups (>= 1)
+  float* part;           // rg > 1: partial rows [rg][batch][d] (k_sum's layout)
+  int batch;             // tokens of the whole call (the partial rows' stride)
 };
 
 template <int WT>
@@ -54,14 +62,20 @@ constexpr int cols_per_vec() { return WT == WT_F32 ? 4 : (WT == WT_F16 ? 8 : 32)
 // Bytes of one row (without INT4 scales).
 __host__ __device__ inline int down_row_bytes(int wt, int d) { return wt == WT_F32 ? 4 * d : (wt == WT_F16 ? 2 * d : d / 2); }
 
-// Tile of workgroup vb.  Workgroups are dealt to the 8 XCDs in turn (vb % 8);
-// the 128 / TB tiles that share a 128-byte line of every row go to
+// Tile of workgroup vb < ntiles.  Workgroups are dealt to the 8 XCDs in turn
+// (vb % 8); the 128 / TB tiles that share a 128-byte line of every row go to
 // consecutive workgroups of one XCD.
 __device__ __forceinline__ int down_tile(int vb, int ntiles, int per_line) {
   if (per_line <= 1 || ntiles % (8 * per_line)) return vb;
   const int xcd = vb & 7, k = vb >> 3;        // k-th workgroup on this XCD
   const int per_xcd = ntiles >> 3;            // tiles per XCD (a multiple of per_line)
   return xcd * per_xcd + k;
+}
+
+// Work item vb < ntiles * rg: row group vb / ntiles, tile down_tile(vb % ntiles).
+__device__ __forceinline__ void down_item(int vb, int ntiles, int per_line, int& tile, int& grp) {
+  grp = vb / ntiles;
+  tile = down_tile(vb - grp * ntiles, ntiles, per_line);
 }
 
 constexpr int kDownThreads = 512;
@@ -109,7 +123,7 @@ struct DownTile {
   static constexpr int KB = down_kb<WT, NT>();
   static_assert(LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8, "lanes per row");
 
-  int tile, rr, n, nch, sgrp, ngrp;
+  int tile, grp, rr, j0, n, nch, sgrp, ngrp;  // n: slots of this row group, from slot j0
   size_t rowb, cofs;
   int idb[2][KB];       // ids of the chunks ahead
   u32x4 wv[2][KB];      // weights of the chunk in use and the next one
@@ -120,22 +134,29 @@ struct DownTile {
 
   // has == false: a workgroup with no tile of its own (n = 0: it reads slot
   // 0's row of tile 0 and writes nothing)
-  __device__ __forceinline__ void count(const DownArgs& a, int tile_, bool has) {
+  __device__ __forceinline__ void count(const DownArgs& a, int tile_, int grp_, bool has) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int c = lane % LPR;
     tile = has ? tile_ : 0;
+    grp = has ? grp_ : 0;
     rr = wave * RPW + lane / LPR;
     const int col = (tile * LPR + c) * CPL;  // first output column of this lane
     rowb = (size_t)down_row_bytes(WT, a.d);
     cofs = (size_t)down_row_bytes(WT, col);  // byte offset of the lane's 16 bytes
     sgrp = col / 128;
     ngrp = a.d / 128;
-    n = a.n_slots;
+    int na = a.n_slots;
     if (a.count) {
       const int cn = *a.count;
-      n = cn < 0 ? 0 : (cn > a.n_slots ? a.n_slots : cn);
+      na = cn < 0 ? 0 : (cn > a.n_slots ? a.n_slots : cn);
     }
+    // this row group's run: slots j0 .. j0 + n - 1
+    const int spr = (na + a.rg - 1) / a.rg;
+    j0 = grp * spr;
+    n = na - j0 < spr ? na - j0 : spr;
+    if (n < 0) n = 0;
     if (!has) n = 0;
+    if (j0 >= a.n_slots) j0 = a.n_slots - 1;  // an empty run past the list (its reads stay in bounds)
     nch = (n + RPS * KB - 1) / (RPS * KB);  // chunks of KB steps
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -145,14 +166,18 @@ struct DownTile {
     }
   }
 
-  __device__ __forceinline__ int slot_clamp(int j) const { return j < n ? j : (n > 0 ? n - 1 : 0); }
+  // slot of the run's j-th entry, clamped into the run (an empty run: j0)
+  __device__ __forceinline__ int slot_clamp(const DownArgs& a, int j) const {
+    const int s = j0 + (j < n ? j : (n > 0 ? n - 1 : 0));
+    return s < a.n_slots ? s : a.n_slots - 1;
+  }
 
   // ids depend on the slot only (not on the count), so they can go out
-  // before the count has arrived
+  // before the count has arrived; past the list they re-read its last entry
   __device__ __forceinline__ void issue_ids(const DownArgs& a, int ch, int (&dst)[KB]) const {
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
-      const int j = (ch * KB + k) * RPS + rr;
+      const int j = j0 + (ch * KB + k) * RPS + rr;
       const int jc = j < a.n_slots ? j : a.n_slots - 1;
       if constexpr (LISTED)
         dst[k] = a.ids[jc];
@@ -176,7 +201,7 @@ struct DownTile {
       w[k] = ld16(a.w + (size_t)ic * rowb + cofs);
 #endif
       if constexpr (WT == WT_I4) sc[k] = (float)a.s[(size_t)ic * ngrp + sgrp];
-      const int jc = slot_clamp((ch * KB + k) * RPS + rr);
+      const int jc = slot_clamp(a, (ch * KB + k) * RPS + rr);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int tc = t < a.nt ? a.tok0 + t : a.tok0;
@@ -201,29 +226,40 @@ struct DownTile {
 #pragma unroll
       for (int t = 0; t < NT; ++t) hk[t] = (ok && t < a.nt) ? h[k][t] : 0.0f;  // a select: nothing else enters
       if constexpr (WT == WT_I4) {
-        float hs[NT];
+        // nibbles in offset binary (n = t + 8) enter as fp16 subnormals with
+        // no conversion: masked in place in bits 0-3 of a half a nibble is the
+        // value n 2^-24, in bits 4-7 it is 16 n 2^-24 (see vec_i4), and the
+        // fp16 operand of a mixed fma is exact in fp32; the coefficient
+        // carries 2^24 or 2^20 to match.  The 8 sum(h s) the offset adds to
+        // every column comes off in finish().
+        float hs[NT], h24[NT], h20[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           hs[t] = ok ? hk[t] * sc[k] : 0.0f;
           sb[t] += hs[t];
+          h24[t] = hs[t] * 16777216.0f;
+          h20[t] = hs[t] * 1048576.0f;
         }
         const uint32_t q[4] = {w[k].x, w[k].y, w[k].z, w[k].w};
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          // nibbles as q + 8 (offset binary), each converted as a byte; the
-          // 8 * sum h s this adds to every column comes off in finish()
-          const uint32_t v = q[m] ^ 0x88888888u;
-          const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
-          float e[8];
+          const uint32_t v = q[m] ^ 0x88888888u, sh = v >> 8;
+          const f16x2 p04 = bitcast<f16x2>(v & 0x000F000Fu);   // columns 8m, 8m+4
+          const f16x2 p15 = bitcast<f16x2>(v & 0x00F000F0u);   // 8m+1, 8m+5 (x16)
+          const f16x2 p26 = bitcast<f16x2>(sh & 0x000F000Fu);  // 8m+2, 8m+6
+          const f16x2 p37 = bitcast<f16x2>(sh & 0x00F000F0u);  // 8m+3, 8m+7 (x16)
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            e[2 * b] = (float)((lo >> (8 * b)) & 0xFFu);
-            e[2 * b + 1] = (float)((hi >> (8 * b)) & 0xFFu);
+          for (int t = 0; t < NT; ++t) {
+            float* c = &acc[t][8 * m];
+            c[0] = __builtin_fmaf(h24[t], (float)p04.x, c[0]);
+            c[4] = __builtin_fmaf(h24[t], (float)p04.y, c[4]);
+            c[1] = __builtin_fmaf(h20[t], (float)p15.x, c[1]);
+            c[5] = __builtin_fmaf(h20[t], (float)p15.y, c[5]);
+            c[2] = __builtin_fmaf(h24[t], (float)p26.x, c[2]);
+            c[6] = __builtin_fmaf(h24[t], (float)p26.y, c[6]);
+            c[3] = __builtin_fmaf(h20[t], (float)p37.x, c[3]);
+            c[7] = __builtin_fmaf(h20[t], (float)p37.y, c[7]);
           }
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int b = 0; b < 8; ++b) acc[t][8 * m + b] = __builtin_fmaf(hs[t], e[b], acc[t][8 * m + b]);
         }
       } else {
         const u32x4 wz = ok ? w[k] : u32x4{0u, 0u, 0u, 0u};
@@ -317,6 +353,7 @@ struct DownTile {
     __syncthreads();
     constexpr int TE = LPR * CPL;  // columns of the tile
     if (!has) return;
+    const bool whole = a.rg == 1;  // workgroup-uniform
     for (int e = threadIdx.x; e < NT * TE; e += kDownThreads) {
       const int t = e / TE, ce = e % TE;
       const int cl = ce / CPL, k = ce % CPL;
@@ -327,36 +364,45 @@ struct DownTile {
         for (int r = 0; r < 4; ++r) s += red[((((size_t)w * 4 + r) * LPR + cl) * NT + t) * CPL + k];
       if (t < a.nt) {
         const int cidx = tile * TE + ce;
-        float b = 0.0f;
-        if (a.bias)
-          b = a.bias_f32 ? reinterpret_cast<const float*>(a.bias)[cidx]
-                         : (float)reinterpret_cast<const f16*>(a.bias)[cidx];
-        const float v = b + s;
-        const size_t o = (size_t)(a.tok0 + t) * a.d + cidx;
-        if (a.y) a.y[o] = v;
-        if (a.r_in) a.r_out[o] = a.r_in[o] + v;
+        if (whole)
+          write_out(a, t, cidx, s);
+        else
+          a.part[((size_t)grp * a.batch + a.tok0 + t) * a.d + cidx] = s;
       }
     }
   }
+
+  // y / the residual row of token t, column c, from the column sum s
+  __device__ __forceinline__ static void write_out(const DownArgs& a, int t, int c, float s) {
+    float b = 0.0f;
+    if (a.bias)
+      b = a.bias_f32 ? reinterpret_cast<const float*>(a.bias)[c] : (float)reinterpret_cast<const f16*>(a.bias)[c];
+    const float v = b + s;
+    const size_t o = (size_t)(a.tok0 + t) * a.d + c;
+    if (a.y) a.y[o] = v;
+    if (a.r_in) a.r_out[o] = a.r_in[o] + v;
+  }
 };
 
-// The whole tile on its own (k_down).
+// One work item on its own (k_down).
 template <int WT, int NT, int LPR, int CO, bool LISTED>
-__device__ __forceinline__ void down_body(const DownArgs& a, int tile, float* red) {
+__device__ __forceinline__ void down_body(const DownArgs& a, int tile, int grp, float* red) {
   DownTile<WT, NT, LPR, CO, LISTED> D;
-  D.count(a, tile, true);
+  D.count(a, tile, grp, true);
   D.ids01(a);
   D.first(a);
   D.loop(a);
   D.finish(a, red, true);
 }
 
-// Host side: tile width (lanes per row), tile count and tokens per pass for
-// rows of this type and length; the arguments of an FFN's down projection.
+// Host side: tile width (lanes per row), tile count, row groups and tokens
+// per pass for rows of this type and length, aiming at about `items` work
+// items (tiles * row groups); the arguments of an FFN's down projection.
 struct DownShape {
-  int lpr, tiles, nt;
+  int lpr, tiles, rg, nt;
 };
-DownShape down_shape(int wt, int d, int batch);
+DownShape down_shape(int wt, int d, int batch, int items);
+hipError_t launch_down_sum(const DownArgs& a, hipStream_t s);  // rg > 1: the partial rows into y
 DownArgs ffn_down_args(const FfnLaunch& p);
 
 }  // namespace sfnn

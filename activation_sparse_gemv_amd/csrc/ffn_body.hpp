@@ -30,6 +30,13 @@ namespace sfnn {
 
 constexpr int kMaxPer = 512;  // slots one FFN workgroup can own
 
+// Up-row batches a wavefront keeps in flight (2 to 4).
+#ifndef SFNN_UP_NBUF
+#define SFNN_UP_NBUF 2
+#endif
+template <int WT, int NT>
+constexpr int up_nbuf() { return SFNN_UP_NBUF; }
+
 struct FfnArgs {
   const uint8_t *w_up, *w_gate, *w_down_t;
   const f16 *s_up, *s_gate, *s_down_t;
@@ -89,9 +96,12 @@ __device__ __forceinline__ void up_body(const FfnArgs& a, int vb, int vg) {
   // tokens
   constexpr int UBU0 = (WT == WT_I4 && NT > 1 ? 4 : 8) / (ACT == ACT_REGLU ? 2 : 1) / (NT >= 4 ? 2 : 1);
   constexpr int UBU = UBU0 < 2 ? 2 : UBU0;
+  constexpr int NBUF = up_nbuf<WT, NT>();
   constexpr int SP = NT == 2 ? 8 : 4;    // staged x vectors per thread held in registers
   extern __shared__ __align__(16) unsigned char smem[];
   XT* xs = reinterpret_cast<XT*>(smem);
+  // INT4: -8 times the sum of each 32 staged activations, [NT][d / 32], behind xs
+  float* m8 = reinterpret_cast<float*>(smem + (size_t)NT * a.d * sizeof(XT));
   __shared__ int s_idw[NW][kMaxPer];     // each wavefront's copy of the run's neuron ids
   __shared__ float s_red[NT][16];
 
@@ -250,8 +260,24 @@ __device__ __forceinline__ void up_body(const FfnArgs& a, int vb, int vg) {
       Bt.g.issue(a.w_gate + (size_t)inc * row_bytes, a.s_gate ? a.s_gate + (size_t)inc * ngroups : nullptr,
                  have ? nvec : 1, v0c);
   };
-  UpBatch<WT, UBU> Bq[2];
+  // this wavefront's rows and batches (wave-uniform: scalar loop control)
+  const int nb = (nvec + bstep - 1) / bstep;  // batches per row
+  const int nrow = __builtin_amdgcn_readfirstlane(wave < cnt ? (cnt - 1 - wave) / NW + 1 : 0);
+  const int nq = nrow * nb;
+  int pk = 0, pb = 0;  // row and batch of the last request
+  // request the batch after the last one (past the end: the last batch again)
+  auto up_next = [&](UpBatch<WT, UBU>& Bn) {
+    if (++pb == nb) {
+      pb = 0;
+      ++pk;
+    }
+    const bool past = pk >= nrow;
+    up_issue(Bn, past ? (nrow > 0 ? nrow - 1 : 0) : pk, past ? nb - 1 : pb);
+  };
+  UpBatch<WT, UBU> Bq[NBUF];
   up_issue(Bq[0], 0, 0);
+#pragma unroll
+  for (int j = 1; j < NBUF - 1; ++j) up_next(Bq[j]);
   __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the staging waits
 
   // ---- 4. x into LDS: staged activations, or the residual chain -------------
@@ -260,6 +286,27 @@ __device__ __forceinline__ void up_body(const FfnArgs& a, int vb, int vg) {
   else
     stage.commit(xs, reinterpret_cast<const XT*>(a.x), d, a.tok0, a.nt, NT);
   __syncthreads();
+  if constexpr (WT == WT_I4) {
+    // the offset's share of every 32-element vector (vec_i4), once per token
+    const int nv = d / 32;
+    for (int i = threadIdx.x; i < NT * nv; i += NTH) {
+      const f16* xp = reinterpret_cast<const f16*>(xs) + (size_t)(i / nv) * d + 32 * (i % nv);
+      float sx = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(xp + 8 * k);
+        const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const f16x2 h2 = bitcast<f16x2>(u[m]);
+          sx += (float)h2.x;
+          sx += (float)h2.y;
+        }
+      }
+      m8[i] = -8.0f * sx;
+    }
+    __syncthreads();
+  }
 
   // ---- P1: the next layer's predictor stage 1 on the staged x (its loads
   // were issued first and have had the longest to arrive; computing them here
@@ -312,34 +359,23 @@ __device__ __forceinline__ void up_body(const FfnArgs& a, int vb, int vg) {
 
   // ---- 5. up (+ gate) rows: one wavefront per slot -------------------------
   // The wavefront's rows (slots wave, wave + NW, ...) are walked as one
-  // sequence of batches of UBU vectors per lane, two buffers deep: batch q+1
-  // (of this row or the next) is requested before batch q is used, so a
-  // wavefront with many rows keeps a row in flight while it computes.  The
-  // loop leaves by break and requests a harmless repeat of the last batch at
-  // the end, so no load and no store sits in a branch.
+  // sequence of batches of UBU vectors per lane, NBUF buffers deep: batches
+  // q+1 .. q+NBUF-1 (of this row or the next) are requested before batch q is
+  // used, so a wavefront keeps rows in flight while it computes.  The loop
+  // leaves by break and requests harmless repeats of the last batch at the
+  // end, so no load and no store sits in a branch.
   {
-    const int nb = (nvec + bstep - 1) / bstep;  // batches per row
-    // this wavefront's rows and batches (wave-uniform: scalar loop control)
-    const int nrow = __builtin_amdgcn_readfirstlane(wave < cnt ? (cnt - 1 - wave) / NW + 1 : 0);
-    const int nq = nrow * nb;
-    int pk = 0, pb = 0;  // row and batch of the last request
     int ck = 0, cb = 0;  // row and batch being used
     float au[NT], ag[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) au[t] = ag[t] = 0.0f;
     auto up_step = [&](UpBatch<WT, UBU>& Bc, UpBatch<WT, UBU>& Bn) {
-      // request the next batch into the other buffer (past the end: the last
-      // batch again)
-      if (++pb == nb) {
-        pb = 0;
-        ++pk;
-      }
-      const bool past = pk >= nrow;
-      up_issue(Bn, past ? nrow - 1 : pk, past ? nb - 1 : pb);
+      up_next(Bn);  // into the buffer used last
       __builtin_amdgcn_sched_barrier(0);  // the next batch is requested before this one is used
       const int v0 = lane + cb * bstep;
-      Bc.u.template consume<NT>(nvec, v0, xs, d, au);
-      if constexpr (ACT == ACT_REGLU) Bc.g.template consume<NT>(nvec, v0, xs, d, ag);
+      const int vb = cb * bstep;  // lane 0's v0 (wave-uniform)
+      Bc.u.template consume<NT>(nvec, v0, xs, d, au, m8, d / 32, vb);
+      if constexpr (ACT == ACT_REGLU) Bc.g.template consume<NT>(nvec, v0, xs, d, ag, m8, d / 32, vb);
       if (++cb == nb) {  // the row is done: h for its slot
         const int j = wave + ck * NW;
         const int i = Bc.i;
@@ -374,11 +410,19 @@ __device__ __forceinline__ void up_body(const FfnArgs& a, int vb, int vg) {
       }
     };
     if (nq > 0) {  // wave-uniform
-      for (int q = 0;; q += 2) {
-        up_step(Bq[0], Bq[1]);
+      for (int q = 0;; q += NBUF) {
+        up_step(Bq[0], Bq[NBUF - 1]);
         if (q + 1 >= nq) break;
         up_step(Bq[1], Bq[0]);
         if (q + 2 >= nq) break;
+        if constexpr (NBUF >= 3) {
+          up_step(Bq[2], Bq[1]);
+          if (q + 3 >= nq) break;
+        }
+        if constexpr (NBUF >= 4) {
+          up_step(Bq[3], Bq[2]);
+          if (q + 4 >= nq) break;
+        }
       }
     }
   }
@@ -471,6 +515,7 @@ struct FfnShape {
 FfnShape ffn_shape(int wt, int d, int batch);
 FfnArgs ffn_args(const FfnLaunch& p, int tok0, int nt, bool first);
 SumArgs sum_args(const FfnLaunch& p, int rows);  // rows: partial rows per token
+hipError_t launch_sum_args(const SumArgs& a, hipStream_t s);
 int sum_groups(int batch, int d);
 
 }  // namespace sfnn

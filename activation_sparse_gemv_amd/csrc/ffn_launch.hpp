@@ -16,7 +16,9 @@ __global__ __launch_bounds__(NTH) void k_up(FfnArgs a) {
 template <int WT, int NT, int LPR, int CO, bool LISTED>
 __global__ __launch_bounds__(kDownThreads) void k_down(DownArgs a, int ntiles) {
   __shared__ __align__(16) float red[DownRed<WT, NT, LPR>::floats];
-  down_body<WT, NT, LPR, CO, LISTED>(a, down_tile(blockIdx.x, ntiles, 8 / LPR), red);
+  int tile, grp;
+  down_item(blockIdx.x, ntiles, 8 / LPR, tile, grp);
+  down_body<WT, NT, LPR, CO, LISTED>(a, tile, grp, red);
 }
 
 // Union-mask words each lane holds: 4 covers d_ff <= 16384, 16 covers 65536.
@@ -26,7 +28,7 @@ template <int WT, int ACT, int NT>
 static void up_pass(const FfnLaunch& p, int tok0, int nt, bool first, hipStream_t s) {
   using XT = typename std::conditional<WT == WT_F32, float, f16>::type;
   const FfnArgs a = ffn_args(p, tok0, nt, first);
-  const size_t sh = (size_t)NT * p.d * sizeof(XT);
+  const size_t sh = (size_t)NT * p.d * sizeof(XT) + (WT == WT_I4 ? (size_t)NT * (p.d / 32) * 4 : 0);  // + vec_i4's m8
   const int G = p.groups;
   constexpr int NTH = 512;
   if (p.src == SRC_UNION) {
@@ -44,7 +46,7 @@ static void up_pass(const FfnLaunch& p, int tok0, int nt, bool first, hipStream_
 // One down pass over tokens [tok0, tok0 + nt) with coefficients `co`.
 template <int WT, int NT, int CO, bool LISTED>
 static void down_pass_l(const DownArgs& a, const DownShape& sh, hipStream_t s) {
-  const dim3 grid(sh.tiles), blk(kDownThreads);
+  const dim3 grid(sh.tiles * sh.rg), blk(kDownThreads);
   switch (sh.lpr) {
     case 1: hipLaunchKernelGGL((k_down<WT, NT, 1, CO, LISTED>), grid, blk, 0, s, a, sh.tiles); break;
     case 2: hipLaunchKernelGGL((k_down<WT, NT, 2, CO, LISTED>), grid, blk, 0, s, a, sh.tiles); break;
@@ -64,7 +66,13 @@ static void down_pass(const DownArgs& a, const DownShape& sh, hipStream_t s) {
 // Every down pass of a batch (token groups of sh.nt).
 template <int WT, int CO>
 void down_all(DownArgs a, int batch, hipStream_t s) {
-  const DownShape sh = down_shape(WT, a.d, batch);
+  int items = kDownItemsDense;
+  if (a.ids) {
+    const DownShape narrow = down_shape(WT, a.d, batch, 0);
+    items = (size_t)a.n_slots * 16 * narrow.lpr > kDownRowGroupBytes ? kDownItemsListed : 0;
+  }
+  const DownShape sh = down_shape(WT, a.d, batch, items);
+  a.rg = sh.rg;
   for (int tok0 = 0; tok0 < batch; tok0 += sh.nt) {
     a.tok0 = tok0;
     a.nt = batch - tok0 < sh.nt ? batch - tok0 : sh.nt;
@@ -79,6 +87,7 @@ void down_all(DownArgs a, int batch, hipStream_t s) {
         break;
     }
   }
+  if (sh.rg > 1) launch_down_sum(a, s);
 }
 
 template <int WT, int ACT>

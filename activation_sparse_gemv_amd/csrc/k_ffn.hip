@@ -12,13 +12,26 @@ namespace sfnn {
 __global__ __launch_bounds__(512) void k_sum(SumArgs a) { sum_body(a, blockIdx.x, gridDim.x); }
 
 // The same sum when there are few partial rows (the matrix-core paths write 8
-// or 16 per token): 4 consecutive elements per thread, the rows added one
-// after another from zero, then the bias, then the residual, exactly the
-// order k_sum takes with at most 32 rows, so both give the same bits.
-__global__ __launch_bounds__(256) void k_sum_wide(SumArgs a) {
+// to 32 per token, the per-row down projection's row groups up to 16): 4
+// consecutive elements per thread, the rows added one after another from
+// zero, then the bias, then the residual, exactly the order k_sum takes with
+// at most 32 rows, so both give the same bits.  64-thread workgroups, so a
+// single token's row spreads over many CUs; the bias and residual loads go
+// out with the partial rows.
+constexpr int kSumWideThreads = 64;
+__global__ __launch_bounds__(kSumWideThreads) void k_sum_wide(SumArgs a) {
   const int n = a.B * a.d;
-  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;  // d is a multiple of 128: 4 elements never straddle
+  const int e = (blockIdx.x * kSumWideThreads + threadIdx.x) * 4;  // d is a multiple of 128: 4 elements never straddle
   if (e >= n) return;
+  const int c = e % a.d;
+  float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (a.b_down) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      b[k] = (a.xtype == WT_F32) ? load_as_float<float>(a.b_down, c + k) : load_as_float<f16>(a.b_down, c + k);
+  }
+  f32x4 r = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (a.r_in) r = *reinterpret_cast<const f32x4*>(a.r_in + e);
   float t[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 8
   for (int g = 0; g < a.G; ++g) {
@@ -28,19 +41,11 @@ __global__ __launch_bounds__(256) void k_sum_wide(SumArgs a) {
     t[2] += p.z;
     t[3] += p.w;
   }
-  const int c = e % a.d;
   float v[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float b = 0.0f;
-    if (a.b_down) b = (a.xtype == WT_F32) ? load_as_float<float>(a.b_down, c + k) : load_as_float<f16>(a.b_down, c + k);
-    v[k] = b + t[k];
-  }
+  for (int k = 0; k < 4; ++k) v[k] = b[k] + t[k];
   if (a.y) *reinterpret_cast<f32x4*>(a.y + e) = f32x4{v[0], v[1], v[2], v[3]};
-  if (a.r_in) {
-    const f32x4 r = *reinterpret_cast<const f32x4*>(a.r_in + e);
-    *reinterpret_cast<f32x4*>(a.r_out + e) = f32x4{r.x + v[0], r.y + v[1], r.z + v[2], r.w + v[3]};
-  }
+  if (a.r_in) *reinterpret_cast<f32x4*>(a.r_out + e) = f32x4{r.x + v[0], r.y + v[1], r.z + v[2], r.w + v[3]};
 }
 
 // Up projection: 512 threads; the token group is bounded by the staged
@@ -61,24 +66,28 @@ FfnShape ffn_shape(int wt, int d, int batch) {
   return s;
 }
 
-// Down projection: the narrowest tile (16 bytes times 1, 2, 4 or 8 lanes) with
-// at most 256 tiles per row, so one launch has up to 256 workgroups that each
-// read every listed row's tile; tokens per pass bounded by 64 accumulators
-// per lane (fp32: 4, fp16: 8, INT4: 32 columns per lane).
-#ifndef SFNN_DOWN_MIN_LPR
-#define SFNN_DOWN_MIN_LPR 1  // narrowest tile, in 16-byte lanes per row
-#endif
-#ifndef SFNN_DOWN_MAX_TILES
-#define SFNN_DOWN_MAX_TILES 256  // most tiles (workgroups) per row
-#endif
-
-DownShape down_shape(int wt, int d, int batch) {
+// Down projection: with items > 0, tiles of whole 128-byte lines (8 lanes of
+// 16 bytes) where the row is a multiple of them, else 64 or 32 bytes, and as
+// many row groups as bring the work items near `items` (at most
+// kDownMaxGroups); with items == 0, one row group; tokens per pass
+// bounded by 64 accumulators per lane (fp32: 4, fp16: 8, INT4: 32 columns per
+// lane).
+DownShape down_shape(int wt, int d, int batch, int items) {
   DownShape s;
-  const int vecs = down_row_bytes(wt, d) / 16;  // 16-byte vectors per row
-  s.lpr = 1;
-  while (s.lpr < SFNN_DOWN_MIN_LPR && (vecs % (2 * s.lpr)) == 0) s.lpr *= 2;
-  while (s.lpr < 8 && vecs / s.lpr > SFNN_DOWN_MAX_TILES && (vecs % (2 * s.lpr)) == 0) s.lpr *= 2;
-  s.tiles = vecs / s.lpr;
+  const int vecs = down_row_bytes(wt, d) / 16;  // 16-byte vectors per row (a multiple of 4)
+  if (items > 0) {
+    s.lpr = vecs % 8 == 0 ? 8 : (vecs % 4 == 0 ? 4 : 2);
+    s.tiles = vecs / s.lpr;
+    s.rg = (items + s.tiles / 2) / s.tiles;
+    if (s.rg < 1) s.rg = 1;
+    if (s.rg > kDownMaxGroups) s.rg = kDownMaxGroups;
+  } else {
+    // no row groups: the narrowest tile with at most 256 tiles per row
+    s.lpr = 1;
+    while (s.lpr < 8 && vecs / s.lpr > 256 && (vecs % (2 * s.lpr)) == 0) s.lpr *= 2;
+    s.tiles = vecs / s.lpr;
+    s.rg = 1;
+  }
   const int cpl = wt == WT_F32 ? 4 : (wt == WT_F16 ? 8 : 32);
   int cap = 64 / cpl;
   if (cap > kMaxNT) cap = kMaxNT;
@@ -156,7 +165,26 @@ DownArgs ffn_down_args(const FfnLaunch& p) {
   a.d = p.d;
   a.tok0 = 0;
   a.nt = p.batch;
+  a.rg = 1;
+  a.part = p.partial;
+  a.batch = p.batch;
   return a;
+}
+
+// The row groups' partial rows of a down projection added into y / the
+// residual row (fixed order), with the bias.
+hipError_t launch_down_sum(const DownArgs& d, hipStream_t s) {
+  SumArgs a;
+  a.partial = d.part;
+  a.G = d.rg;
+  a.B = d.batch;
+  a.d = d.d;
+  a.xtype = d.bias_f32 ? WT_F32 : WT_F16;
+  a.b_down = d.bias;
+  a.y = d.y;
+  a.r_in = d.r_in;
+  a.r_out = d.r_out;
+  return launch_sum_args(a, s);
 }
 
 SumArgs sum_args(const FfnLaunch& p, int rows) {
@@ -175,16 +203,17 @@ SumArgs sum_args(const FfnLaunch& p, int rows) {
 
 int sum_groups(int batch, int d) { return (batch * d + kSumEPW - 1) / kSumEPW; }  // 512-thread workgroups
 
-hipError_t launch_sum(const FfnLaunch& p, int rows, hipStream_t s) {
-  const SumArgs a = sum_args(p, rows);
+hipError_t launch_sum_args(const SumArgs& a, hipStream_t s) {
   if (a.G <= 32) {
-    const int n4 = (p.batch * p.d) / 4;
-    hipLaunchKernelGGL(k_sum_wide, dim3((n4 + 255) / 256), dim3(256), 0, s, a);
+    const int n4 = (a.B * a.d) / 4;
+    hipLaunchKernelGGL(k_sum_wide, dim3((n4 + kSumWideThreads - 1) / kSumWideThreads), dim3(kSumWideThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL(k_sum, dim3(sum_groups(p.batch, p.d)), dim3(512), 0, s, a);
+    hipLaunchKernelGGL(k_sum, dim3(sum_groups(a.B, a.d)), dim3(512), 0, s, a);
   }
   return hipGetLastError();
 }
+
+hipError_t launch_sum(const FfnLaunch& p, int rows, hipStream_t s) { return launch_sum_args(sum_args(p, rows), s); }
 
 hipError_t launch_ffn(const FfnLaunch& p, hipStream_t s) {
   if (ffn_uses_mfma(p)) return launch_ffn_mfma(p, s);

@@ -16,16 +16,16 @@ __global__ __launch_bounds__(NTH) void k_la_up_pred1(FfnArgs fa) {
 }
 
 // Launch B of layer l: workgroup vb predicts mask word vb of the next layer
-// if vb < gp, and computes down-projection tile vb of FFN_l (y_l and
-// r_{l+1} = r_l + y_l for its columns) if vb < tiles.  A workgroup with a
-// tile interleaves the two streams: the tile's row ids, then the predictor's
-// z and W2^T rows, then the tile's first weights, then the predictor's math
-// (whose waits stop short of those weights), then the rest of the tile; its
-// loads sit in no branch (with no word of its own it reads the last word's
-// rows and writes nothing).  A workgroup without a tile only predicts (an
-// early exit, so the tile path stays branch-free).  With a dense hot prefix
-// (HOT) a word may need no loads at all, and the two parts run one after the
-// other.
+// if vb < gp, and computes down-projection work item vb of FFN_l (one tile of
+// one row group; y_l and r_{l+1} = r_l + y_l for the tile's columns once its
+// row groups are in) if vb < tiles * row groups.  A workgroup with an item
+// interleaves the two streams: the item's row ids, then the predictor's z and
+// W2^T rows, then the item's first weights, then the predictor's math (whose
+// waits stop short of those weights), then the rest of the item; its loads
+// sit in no branch (with no word of its own it reads the last word's rows and
+// writes nothing).  A workgroup without an item only predicts (an early exit,
+// so the item path stays branch-free).  With a dense hot prefix (HOT) a word
+// may need no loads at all, and the two parts run one after the other.
 template <int WT, int NTD, int LPR, int PWT, int NT2, int VPL, bool HOT>
 #ifndef SFNN_LA_B_WAVES
 #define SFNN_LA_B_WAVES 2  // waves per SIMD the launch-B kernel is built for (4 would force two workgroups per CU: spills)
@@ -35,13 +35,15 @@ __global__ __launch_bounds__(512, SFNN_LA_B_WAVES) void k_la_down_pred2(DownArgs
   constexpr int RB = VPL <= 2 ? 8 : (VPL == 4 ? 4 : 2);
   __shared__ __align__(16) float red[DownRed<WT, NTD, LPR>::floats];
   const int vb = blockIdx.x;
-  if (vb >= tiles) {  // workgroup-uniform
-    pred2_body<PWT, NT2, VPL, RB>(pa, vb);  // vb < gp: the grid is max(tiles, gp)
+  if (vb >= tiles * da.rg) {  // workgroup-uniform
+    pred2_body<PWT, NT2, VPL, RB>(pa, vb);  // vb < gp: the grid is max(items, gp)
     return;
   }
   const bool hasp = vb < gp;
   DownTile<WT, NTD, LPR, CO_H, true> D;
-  D.count(da, down_tile(vb, tiles, 8 / LPR), true);
+  int tile, grp;
+  down_item(vb, tiles, 8 / LPR, tile, grp);
+  D.count(da, tile, grp, true);
   if constexpr (HOT) {
     if (hasp) pred2_body<PWT, NT2, VPL, RB>(pa, vb);
     D.ids01(da);
@@ -74,7 +76,7 @@ static void launch_a(const FfnLaunch& F, const float* r_l, float eps, const Pred
     fa.z = next->z;
     fa.r = next->r;
   }
-  const size_t sh = (size_t)NT * F.d * sizeof(XT);
+  const size_t sh = (size_t)NT * F.d * sizeof(XT) + (WT == WT_I4 ? (size_t)NT * (F.d / 32) * 4 : 0);  // + vec_i4's m8
   if (union_words_per_lane(F.f) == 4)
     hipLaunchKernelGGL((k_la_up_pred1<WT, ACT, NT, NTH, RV, 4>), dim3(F.groups), dim3(NTH), sh, s, fa);
   else
@@ -106,7 +108,8 @@ static void launch_a_all(const FfnLaunch& F, int NT, const FfnShape& sh, const f
 
 template <int WT, int NTD, int PWT, int NT2, int VPL, bool HOT>
 static void launch_b_lpr(const DownArgs& da, const DownShape& ds, const Pred2Args& pa, int gp, hipStream_t s) {
-  const dim3 grid(ds.tiles > gp ? ds.tiles : gp), blk(512);
+  const int items = ds.tiles * ds.rg;
+  const dim3 grid(items > gp ? items : gp), blk(512);
   switch (ds.lpr) {
     case 1: hipLaunchKernelGGL((k_la_down_pred2<WT, NTD, 1, PWT, NT2, VPL, HOT>), grid, blk, 0, s, da, ds.tiles, pa, gp); break;
     case 2: hipLaunchKernelGGL((k_la_down_pred2<WT, NTD, 2, PWT, NT2, VPL, HOT>), grid, blk, 0, s, da, ds.tiles, pa, gp); break;
@@ -125,11 +128,19 @@ static void launch_b_hot(const DownArgs& da, const DownShape& ds, const Pred2Arg
 
 // Launch B: the down projection of this layer (every token, batch <= 2) and
 // the next layer's predictor stage 2.
+// Down work items launch B aims at (0: one row group of narrow tiles, the
+// tiles' workgroups each also predicting a word).
+#ifndef SFNN_LA_B_ITEMS
+#define SFNN_LA_B_ITEMS 0
+#endif
+constexpr int kLaBItems = SFNN_LA_B_ITEMS;
+
 template <int WT, int PWT, int NT2>
-static void launch_b(const DownArgs& da, int batch, const PredLaunch& next, hipStream_t s) {
-  const DownShape ds = down_shape(WT, da.d, batch);
-  const Pred2Args pa = pred2_args(next, 0, next.batch);
+static void launch_b(DownArgs da, int batch, const PredLaunch& next, hipStream_t s) {
   const int gp = next.f / 64;
+  const DownShape ds = down_shape(WT, da.d, batch, kLaBItems);
+  da.rg = ds.rg;
+  const Pred2Args pa = pred2_args(next, 0, next.batch);
   const int vpl = pred2_vpl(PWT, next.r);
   if (ds.nt == 1) {
     if (vpl == 1) launch_b_hot<WT, 1, PWT, NT2, 1>(da, ds, pa, gp, s);
@@ -140,6 +151,7 @@ static void launch_b(const DownArgs& da, int batch, const PredLaunch& next, hipS
     else if (vpl == 2) launch_b_hot<WT, 2, PWT, NT2, 2>(da, ds, pa, gp, s);
     else launch_b_hot<WT, 2, PWT, NT2, 4>(da, ds, pa, gp, s);
   }
+  if (ds.rg > 1) launch_down_sum(da, s);
 }
 
 template <int WT, int ACT>

@@ -63,14 +63,13 @@ struct FfnLaunch {
   int32_t* count_out;     // SRC_UNION
   const uint64_t* mask;   // per-token gate [B][f/64] or null
   float* hrow = nullptr;  // per-row path: h [B][f] fp32 workspace (slot order), up -> down
-  float* partial;         // matrix-core path: [kMfmaPartRows][B][d] workspace
+  float* partial;         // [kMfmaPartRows][B][d] workspace: matrix-core partial rows, per-row down row groups
   int groups;             // up-projection workgroups of the per-row path
   float* y;               // [B][d] or null
   const float* r_in;      // residual add: r_out = r_in + y (both null to skip)
   float* r_out;
   void* hbuf = nullptr;   // matrix-core path: h of one 32-token pass, fp32 [32][f]
   float* hmax = nullptr;  // matrix-core path: largest |h| per 32-slot step and token, [f / 32][32]
-                          // (hi, lo planes), fp32 [32][f] for INT4 (null: path off)
   int32_t* sidbuf = nullptr;  // matrix-core path: slot ids [f]
   int mfma_min_batch = 0;     // matrix-core path from this batch on (0: default, < 0: never)
 };
@@ -86,8 +85,20 @@ constexpr int kMfmaMinBatchDefault = 8;
 constexpr int kMfmaMinBatchI4Default = 3;
 bool ffn_uses_mfma(const FfnLaunch& p);
 int mfma_groups(int d, int max_groups);  // partial rows per token on that path
-// Partial rows per token the workspace holds for the matrix-core FFN.
+// Partial rows per token the workspace holds for the matrix-core FFN (and
+// for the row groups of the per-row down projection).
 constexpr int kMfmaPartRows = 32;
+// Per-row down projection: most row groups per tile (partial rows per token,
+// at most kMfmaPartRows).
+constexpr int kDownMaxGroups = 16;
+// Work items (tiles x row groups) a stand-alone down launch aims at: over
+// every row (dense) about three 512-thread workgroups per CU; over a listed
+// subset one per CU, and only where the whole list could bring a narrow tile
+// more than kDownRowGroupBytes (else one row group of narrow tiles, no
+// partial rows, no sum launch).
+constexpr int kDownItemsDense = 768;
+constexpr int kDownItemsListed = 256;
+constexpr size_t kDownRowGroupBytes = (size_t)1 << 20;
 hipError_t launch_ffn_mfma(const FfnLaunch& p, hipStream_t s);
 // Slots of one slot group the INT4 down kernel stages in LDS (ids and
 // scales); launch_ffn_mfma refuses a shape whose groups would hold more.
