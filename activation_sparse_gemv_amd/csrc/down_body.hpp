@@ -98,9 +98,7 @@ struct DownRed {
   static constexpr int floats = NW * 4 * LPR * NT * CPL;  // [wave][row16][lane c][t][col]
 };
 
-// One workgroup's tile, in phases so that a fused launch can put other work
-// between them (the look-ahead stack's launch B issues predictor stage 2's
-// loads between the row ids and the first weights):
+// One workgroup's work item, in phases:
 //   count()   the slot count (a scalar load);
 //   ids01()   the row ids of chunks 0 and 1, read without waiting for the
 //             count (the id list holds n_slots entries; ids past the count

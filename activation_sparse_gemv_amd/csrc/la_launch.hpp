@@ -15,50 +15,31 @@ __global__ __launch_bounds__(NTH) void k_la_up_pred1(FfnArgs fa) {
   up_body<WT, ACT, NT, SRC_UNION, NTH, RV, true, true, UW>(fa, blockIdx.x, gridDim.x);
 }
 
-// Launch B of layer l: workgroup vb predicts mask word vb of the next layer
-// if vb < gp, and computes down-projection work item vb of FFN_l (one tile of
-// one row group; y_l and r_{l+1} = r_l + y_l for the tile's columns once its
-// row groups are in) if vb < tiles * row groups.  A workgroup with an item
-// interleaves the two streams: the item's row ids, then the predictor's z and
-// W2^T rows, then the item's first weights, then the predictor's math (whose
-// waits stop short of those weights), then the rest of the item; its loads
-// sit in no branch (with no word of its own it reads the last word's rows and
-// writes nothing).  A workgroup without an item only predicts (an early exit,
-// so the item path stays branch-free).  With a dense hot prefix (HOT) a word
-// may need no loads at all, and the two parts run one after the other.
-template <int WT, int NTD, int LPR, int PWT, int NT2, int VPL, bool HOT>
+// Launch B of layer l: the first tiles * rg workgroups compute the down-
+// projection work items of FFN_l (one tile of one row group each; y_l and
+// r_{l+1} = r_l + y_l for the tile's columns when there is one row group),
+// the next gp workgroups predict one mask word each of the next layer
+// (predictor stage 2).  The two kinds carry about the same bytes (a tile of
+// every listed row, or 64 rows of W2^T), so the CUs take them in any order.
+// (Interleaving a tile and a word in one workgroup, with the tile's loads
+// issued between the word's, measured 3% slower at OPT-6.7B batch 1 and the
+// same at OPT-175B.)
 #ifndef SFNN_LA_B_WAVES
-#define SFNN_LA_B_WAVES 2  // waves per SIMD the launch-B kernel is built for (4 would force two workgroups per CU: spills)
+#define SFNN_LA_B_WAVES 2  // waves per SIMD the launch-B kernel is built for
 #endif
-__global__ __launch_bounds__(512, SFNN_LA_B_WAVES) void k_la_down_pred2(DownArgs da, int tiles, Pred2Args pa,
-                                                                         int gp) {
+template <int WT, int NTD, int LPR, int PWT, int NT2, int VPL>
+__global__ __launch_bounds__(512, SFNN_LA_B_WAVES) void k_la_down_pred2(DownArgs da, int tiles, Pred2Args pa) {
   constexpr int RB = VPL <= 2 ? 8 : (VPL == 4 ? 4 : 2);
   __shared__ __align__(16) float red[DownRed<WT, NTD, LPR>::floats];
   const int vb = blockIdx.x;
-  if (vb >= tiles * da.rg) {  // workgroup-uniform
-    pred2_body<PWT, NT2, VPL, RB>(pa, vb);  // vb < gp: the grid is max(items, gp)
+  const int items = tiles * da.rg;
+  if (vb >= items) {  // workgroup-uniform
+    pred2_body<PWT, NT2, VPL, RB>(pa, vb - items);
     return;
   }
-  const bool hasp = vb < gp;
-  DownTile<WT, NTD, LPR, CO_H, true> D;
   int tile, grp;
   down_item(vb, tiles, 8 / LPR, tile, grp);
-  D.count(da, tile, grp, true);
-  if constexpr (HOT) {
-    if (hasp) pred2_body<PWT, NT2, VPL, RB>(pa, vb);
-    D.ids01(da);
-    D.first(da);
-    D.loop(da);
-  } else {
-    D.ids01(da);
-    Pred2Tile<PWT, NT2, VPL, RB> P;
-    const int vp = hasp ? vb : gp - 1;
-    P.issue(pa, vp);
-    D.first(da);
-    P.finish(pa, vp, hasp);
-    D.loop(da);
-  }
-  D.finish(da, red, true);
+  down_body<WT, NTD, LPR, CO_H, true>(da, tile, grp, red);
 }
 
 // Launch A for one token group.  next == null: the last layer (FFN only).
@@ -106,52 +87,33 @@ static void launch_a_all(const FfnLaunch& F, int NT, const FfnShape& sh, const f
   }
 }
 
-template <int WT, int NTD, int PWT, int NT2, int VPL, bool HOT>
+template <int WT, int NTD, int PWT, int NT2, int VPL>
 static void launch_b_lpr(const DownArgs& da, const DownShape& ds, const Pred2Args& pa, int gp, hipStream_t s) {
-  const int items = ds.tiles * ds.rg;
-  const dim3 grid(items > gp ? items : gp), blk(512);
+  const dim3 grid(ds.tiles * ds.rg + gp), blk(512);
   switch (ds.lpr) {
-    case 1: hipLaunchKernelGGL((k_la_down_pred2<WT, NTD, 1, PWT, NT2, VPL, HOT>), grid, blk, 0, s, da, ds.tiles, pa, gp); break;
-    case 2: hipLaunchKernelGGL((k_la_down_pred2<WT, NTD, 2, PWT, NT2, VPL, HOT>), grid, blk, 0, s, da, ds.tiles, pa, gp); break;
-    case 4: hipLaunchKernelGGL((k_la_down_pred2<WT, NTD, 4, PWT, NT2, VPL, HOT>), grid, blk, 0, s, da, ds.tiles, pa, gp); break;
-    default: hipLaunchKernelGGL((k_la_down_pred2<WT, NTD, 8, PWT, NT2, VPL, HOT>), grid, blk, 0, s, da, ds.tiles, pa, gp); break;
+    case 1: hipLaunchKernelGGL((k_la_down_pred2<WT, NTD, 1, PWT, NT2, VPL>), grid, blk, 0, s, da, ds.tiles, pa); break;
+    case 2: hipLaunchKernelGGL((k_la_down_pred2<WT, NTD, 2, PWT, NT2, VPL>), grid, blk, 0, s, da, ds.tiles, pa); break;
+    case 4: hipLaunchKernelGGL((k_la_down_pred2<WT, NTD, 4, PWT, NT2, VPL>), grid, blk, 0, s, da, ds.tiles, pa); break;
+    default: hipLaunchKernelGGL((k_la_down_pred2<WT, NTD, 8, PWT, NT2, VPL>), grid, blk, 0, s, da, ds.tiles, pa); break;
   }
 }
-
-template <int WT, int NTD, int PWT, int NT2, int VPL>
-static void launch_b_hot(const DownArgs& da, const DownShape& ds, const Pred2Args& pa, int gp, hipStream_t s) {
-  if (pa.hot > 0)
-    launch_b_lpr<WT, NTD, PWT, NT2, VPL, true>(da, ds, pa, gp, s);
-  else
-    launch_b_lpr<WT, NTD, PWT, NT2, VPL, false>(da, ds, pa, gp, s);
-}
-
-// Launch B: the down projection of this layer (every token, batch <= 2) and
-// the next layer's predictor stage 2.
-// Down work items launch B aims at (0: one row group of narrow tiles, the
-// tiles' workgroups each also predicting a word).
-#ifndef SFNN_LA_B_ITEMS
-#define SFNN_LA_B_ITEMS 0
-#endif
-constexpr int kLaBItems = SFNN_LA_B_ITEMS;
 
 template <int WT, int PWT, int NT2>
 static void launch_b(DownArgs da, int batch, const PredLaunch& next, hipStream_t s) {
   const int gp = next.f / 64;
-  const DownShape ds = down_shape(WT, da.d, batch, kLaBItems);
-  da.rg = ds.rg;
+  const DownShape ds = down_shape(WT, da.d, batch, 0);  // one row group: y and the residual row directly
+  da.rg = 1;
   const Pred2Args pa = pred2_args(next, 0, next.batch);
   const int vpl = pred2_vpl(PWT, next.r);
   if (ds.nt == 1) {
-    if (vpl == 1) launch_b_hot<WT, 1, PWT, NT2, 1>(da, ds, pa, gp, s);
-    else if (vpl == 2) launch_b_hot<WT, 1, PWT, NT2, 2>(da, ds, pa, gp, s);
-    else launch_b_hot<WT, 1, PWT, NT2, 4>(da, ds, pa, gp, s);
+    if (vpl == 1) launch_b_lpr<WT, 1, PWT, NT2, 1>(da, ds, pa, gp, s);
+    else if (vpl == 2) launch_b_lpr<WT, 1, PWT, NT2, 2>(da, ds, pa, gp, s);
+    else launch_b_lpr<WT, 1, PWT, NT2, 4>(da, ds, pa, gp, s);
   } else {
-    if (vpl == 1) launch_b_hot<WT, 2, PWT, NT2, 1>(da, ds, pa, gp, s);
-    else if (vpl == 2) launch_b_hot<WT, 2, PWT, NT2, 2>(da, ds, pa, gp, s);
-    else launch_b_hot<WT, 2, PWT, NT2, 4>(da, ds, pa, gp, s);
+    if (vpl == 1) launch_b_lpr<WT, 2, PWT, NT2, 1>(da, ds, pa, gp, s);
+    else if (vpl == 2) launch_b_lpr<WT, 2, PWT, NT2, 2>(da, ds, pa, gp, s);
+    else launch_b_lpr<WT, 2, PWT, NT2, 4>(da, ds, pa, gp, s);
   }
-  if (ds.rg > 1) launch_down_sum(da, s);
 }
 
 template <int WT, int ACT>
