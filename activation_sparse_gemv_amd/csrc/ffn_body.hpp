@@ -53,9 +53,9 @@ struct FfnArgs {
   const float* r_in;     // residual rows (chain prologue: x = r / rms(r)) or null
   void* x_out;           // chain prologue: x written here by workgroup 0 (or null)
   float eps;
-  const uint8_t* w1_t;   // P1: the next layer's predictor W1^T [r][d] (stage 1 on the same x)
-  float* z;              // P1: its output [B][r]
-  int r;                 // P1: rank (0: no predictor rows)
+  const uint8_t* w1_t;   // p1_body: the next layer's predictor W1^T [r][d] (stage 1 on the same x)
+  float* z;              // p1_body: its output [B][r]
+  int r;                 // p1_body: rank
   int d, f, B, tok0, nt, write_ids;
 };
 
@@ -73,12 +73,6 @@ struct UpBatch {
 
 // One up-projection workgroup (virtual index vb of vg).  CHAIN: the layer input is
 // x = r_in / rms(r_in), built in the prologue instead of staged from a.x.
-// P1: the workgroup also computes its share of predictor stage 1 of the next
-// layer on the same x (look-ahead): rows [vb*pr, vb*pr + pr) of W1^T.  Each
-// row is split in NW equal column chunks, one per wavefront, so every
-// wavefront carries the same share; all of a pass's loads go out first thing
-// (they wait for nothing) and the wavefronts' partial dots are added in LDS,
-// in wavefront order, at the end.
 // Every wavefront derives the workgroup's slot list by itself (mask words,
 // popcounts, one lane scan, then the 64 bits of each word that holds slots
 // of the run emitted by the 64 lanes at once into the wavefront's own LDS
@@ -86,10 +80,9 @@ struct UpBatch {
 // weight loads: the barriers that stage x come after those loads are issued.
 // RV: float4 vectors per thread per token of the residual row (CHAIN only;
 // d_model <= 4 RV NTH).
-template <int WT, int ACT, int NT, int SRC, int NTH, int RV, bool CHAIN, bool P1, int UW>
+template <int WT, int ACT, int NT, int SRC, int NTH, int RV, bool CHAIN, int UW>
 __device__ __forceinline__ void up_body(const FfnArgs& a, int vb, int vg) {
   using XT = typename std::conditional<WT == WT_F32, float, f16>::type;
-  static_assert(!P1 || SRC == SRC_UNION, "predictor rows ride along with the union-mask FFN only");
   constexpr int NW = NTH / kWave;
   // up-row vectors per lane per batch, two batches in flight: 8 (4 for the
   // INT4 rows from two tokens on), halved for ReGLU's second row and for 4+
@@ -117,9 +110,8 @@ __device__ __forceinline__ void up_body(const FfnArgs& a, int vb, int vg) {
 
   // ---- 1. loads that wait for nothing: the mask words (lane-major: lane l
   // of every wavefront holds words l*UW .. l*UW + UW-1, read in 16-byte
-  // pairs), the layer input, the first batch of this wavefront's predictor
-  // row.  The guarded loads come first; the weight loads after them are
-  // unconditional, so later waits can skip those.
+  // pairs) and the layer input.  The guarded loads come first; the weight
+  // loads after them are unconditional, so later waits can skip those.
   static_assert(UW % 2 == 0, "mask words are read in pairs");
   uint64_t u[SRC == SRC_UNION ? UW : 1];
   if constexpr (SRC == SRC_UNION) {
@@ -145,33 +137,6 @@ __device__ __forceinline__ void up_body(const FfnArgs& a, int vb, int vg) {
     chain_issue<NT, CV, true>(a.r_in, rv, d, a.tok0, a.nt);  // CV is sized to the shape
   else
     stage.issue(reinterpret_cast<const XT*>(a.x), d, a.tok0, a.nt, NT);
-
-  // P1: PR rows per pass, PV vectors per lane of each row's chunk (PV * 64
-  // * NW vectors cover d_model <= 4 RV NTH)
-  constexpr int PV = P1 ? (WT == WT_F32 ? 2 : 1) * RV / 2 : 1;
-  constexpr int PR = P1 ? (PV <= 2 ? 8 : 4) : 1;
-  const int pr = P1 ? (a.r + G - 1) / G : 0;
-  const int p0 = g * pr;
-  const int pcw = d * (int)sizeof(XT) / 16 / NW;  // vectors per wavefront chunk of a row
-  u32x4 pw[PR][PV];
-  // issue one pass of W1^T rows (k0 .. k0 + PR - 1 of this workgroup's); a
-  // row past the workgroup's share or the rank (or no next layer: w1_t null)
-  // reads one shared vector of the mask instead, so no load is in a branch
-  auto p1_issue = [&](int k0) {
-#pragma unroll
-    for (int k = 0; k < PR; ++k) {
-      const bool have = a.w1_t && k0 + k < pr && p0 + k0 + k < a.r;
-      const uint8_t* prow = have ? a.w1_t + (size_t)(p0 + k0 + k) * d * sizeof(XT)
-                                 : reinterpret_cast<const uint8_t*>(a.union_mask);
-#pragma unroll
-      for (int v = 0; v < PV; ++v) {
-        const int vi = lane + kWave * v;
-        const bool ok = have && vi < pcw;
-        pw[k][v] = ld16_stream(prow + (ok ? 16 * (size_t)(wave * pcw + vi) : 0));
-      }
-    }
-  };
-  if constexpr (P1) p1_issue(0);
 
   // ---- 2. the run [s0, s0 + cnt) of active slots and its neuron ids --------
   int cnt, s0;
@@ -308,55 +273,6 @@ __device__ __forceinline__ void up_body(const FfnArgs& a, int vb, int vg) {
     __syncthreads();
   }
 
-  // ---- P1: the next layer's predictor stage 1 on the staged x (its loads
-  // were issued first and have had the longest to arrive; computing them here
-  // frees their registers before the up rows)
-  if constexpr (P1) {
-    // z[t][p0 + k] = W1^T[p0 + k] . x[t]: this wavefront's chunk of every row
-    // of the pass, then the chunks added in wavefront order.  x is staged in
-    // the INT4 pairing order when the FFN is INT4, so W1's fp16 vectors are
-    // paired the same way.
-    __shared__ float s_pz[NT][PR][NW];
-    for (int k0 = 0; k0 < pr; k0 += PR) {  // workgroup-uniform
-      if (k0 > 0) p1_issue(k0);
-      float pacc[PR][NT];
-#pragma unroll
-      for (int k = 0; k < PR; ++k) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) pacc[k][t] = 0.0f;
-#pragma unroll
-        for (int v = 0; v < PV; ++v) {
-          const int vi = lane + kWave * v;
-          const bool ok = vi < pcw;
-          const int vc = ok ? wave * pcw + vi : 0;
-          u32x4 wv = ok ? pw[k][v] : u32x4{0u, 0u, 0u, 0u};
-          if constexpr (WT == WT_F32) {
-            vec_f32<NT>(wv, reinterpret_cast<const float*>(xs) + 4 * vc, d, pacc[k]);
-          } else {
-            if constexpr (WT == WT_I4) wv = StageSplit<XT, true, 1>::perm8(wv);
-            vec_f16<NT>(wv, reinterpret_cast<const f16*>(xs) + 8 * vc, d, pacc[k]);
-          }
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < PR; ++k)
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const float sw = wave_sum(pacc[k][t]);
-          if (lane == 0) s_pz[t][k][wave] = sw;
-        }
-      __syncthreads();
-      if ((int)threadIdx.x < NT * PR) {
-        const int t = threadIdx.x / PR, k = threadIdx.x % PR;
-        float z = 0.0f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) z += s_pz[t][k][w];
-        if (t < a.nt && k0 + k < pr && p0 + k0 + k < a.r) a.z[(size_t)(a.tok0 + t) * a.r + p0 + k0 + k] = z;
-      }
-      __syncthreads();  // s_pz is reused by the next pass
-    }
-  }
-
   // ---- 5. up (+ gate) rows: one wavefront per slot -------------------------
   // The wavefront's rows (slots wave, wave + NW, ...) are walked as one
   // sequence of batches of UBU vectors per lane, NBUF buffers deep: batches
@@ -425,6 +341,92 @@ __device__ __forceinline__ void up_body(const FfnArgs& a, int vb, int vg) {
         }
       }
     }
+  }
+}
+
+// Predictor stage 1 of the next layer for virtual workgroup vb of vg (the
+// look-ahead stack's launch A runs these beside the up-projection
+// workgroups, on the same layer input): z[t][p0 + k] = W1^T[p0 + k] . x[t]
+// for this workgroup's rows [p0, p0 + pr).  x = r_in / rms(r_in) is built in
+// the prologue, as in up_body.  Each row is split in NW equal column chunks,
+// one per wavefront, so every wavefront carries the same share; a pass of PR
+// rows has all its loads in flight at once (issued before the prologue
+// waits), and the wavefronts' partial dots are added in LDS in wavefront
+// order.  RV as in up_body.
+template <int WT, int NT, int NTH, int RV>
+__device__ __forceinline__ void p1_body(const FfnArgs& a, int vb, int vg) {
+  using XT = typename std::conditional<WT == WT_F32, float, f16>::type;
+  constexpr int NW = NTH / kWave;
+  constexpr int PV = (WT == WT_F32 ? 2 : 1) * RV / 2;  // PV * 64 * NW vectors cover d_model <= 4 RV NTH
+  constexpr int PR = PV <= 2 ? 8 : 4;
+  extern __shared__ __align__(16) unsigned char smem[];
+  XT* xs = reinterpret_cast<XT*>(smem);
+  __shared__ float s_red[NT][16];
+  __shared__ float s_pz[NT][PR][NW];
+  const int d = a.d;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int pr = (a.r + vg - 1) / vg;
+  const int p0 = vb * pr;
+  const int pcw = d * (int)sizeof(XT) / 16 / NW;  // vectors per wavefront chunk of a row
+  constexpr int CV = NT * RV;
+  f32x4 rv[CV];
+  chain_issue<NT, CV, true>(a.r_in, rv, d, a.tok0, a.nt);
+  u32x4 pw[PR][PV];
+  // one pass of rows (k0 .. k0 + PR - 1 of this workgroup's); a row past the
+  // share or the rank reads row 0's vectors and is not written
+  auto issue = [&](int k0) {
+#pragma unroll
+    for (int k = 0; k < PR; ++k) {
+      const int j = p0 + k0 + k;
+      const bool have = k0 + k < pr && j < a.r;
+      const uint8_t* prow = a.w1_t + (size_t)(have ? j : 0) * d * sizeof(XT);
+#pragma unroll
+      for (int v = 0; v < PV; ++v) {
+        const int vi = lane + kWave * v;
+        pw[k][v] = ld16_stream(prow + 16 * (size_t)(wave * pcw + (vi < pcw ? vi : 0)));
+      }
+    }
+  };
+  issue(0);
+  __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the prologue waits
+  chain_finish<XT, NT, false, CV>(rv, xs, s_red, nullptr, false, a.eps, d, a.tok0, a.nt);
+  __syncthreads();
+  for (int k0 = 0; k0 < pr; k0 += PR) {  // workgroup-uniform
+    if (k0 > 0) issue(k0);
+    float pacc[PR][NT];
+#pragma unroll
+    for (int k = 0; k < PR; ++k) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) pacc[k][t] = 0.0f;
+#pragma unroll
+      for (int v = 0; v < PV; ++v) {
+        const int vi = lane + kWave * v;
+        const bool ok = vi < pcw;
+        const int vc = ok ? wave * pcw + vi : 0;
+        const u32x4 wv = ok ? pw[k][v] : u32x4{0u, 0u, 0u, 0u};
+        if constexpr (WT == WT_F32)
+          vec_f32<NT>(wv, reinterpret_cast<const float*>(xs) + 4 * vc, d, pacc[k]);
+        else
+          vec_f16<NT>(wv, reinterpret_cast<const f16*>(xs) + 8 * vc, d, pacc[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < PR; ++k)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float sw = wave_sum(pacc[k][t]);
+        if (lane == 0) s_pz[t][k][wave] = sw;
+      }
+    __syncthreads();
+    if ((int)threadIdx.x < NT * PR) {
+      const int t = threadIdx.x / PR, k = threadIdx.x % PR;
+      float z = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) z += s_pz[t][k][w];
+      if (t < a.nt && k0 + k < pr && p0 + k0 + k < a.r) a.z[(size_t)(a.tok0 + t) * a.r + p0 + k0 + k] = z;
+    }
+    __syncthreads();  // s_pz is reused by the next pass
   }
 }
 

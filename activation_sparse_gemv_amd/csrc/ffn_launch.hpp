@@ -10,7 +10,7 @@ namespace sfnn {
 
 template <int WT, int ACT, int NT, int SRC, int NTH, int RV, int UW>
 __global__ __launch_bounds__(NTH) void k_up(FfnArgs a) {
-  up_body<WT, ACT, NT, SRC, NTH, RV, false, false, UW>(a, blockIdx.x, gridDim.x);
+  up_body<WT, ACT, NT, SRC, NTH, RV, false, UW>(a, blockIdx.x, gridDim.x);
 }
 
 template <int WT, int NT, int LPR, int CO, bool LISTED>

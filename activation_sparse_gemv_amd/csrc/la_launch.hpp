@@ -6,14 +6,25 @@
 
 namespace sfnn {
 
-// Launch A of layer l: every workgroup computes its run of FFN_l's up (+gate)
-// rows (input x_l = RMSNorm(r_l) built in its prologue; h to the workspace)
-// and its share of the next layer's predictor stage 1 on the same x_l
-// (w1_t / z / r in the arguments; r = 0 on the last layer).
+// Launch A of layer l: the first gup workgroups compute their runs of FFN_l's
+// up (+gate) rows (input x_l = RMSNorm(r_l) built in the prologue; h to the
+// workspace), the rest the next layer's predictor stage 1 on the same x_l
+// (w1_t / z / r in the arguments), a few rows each.  Separate workgroups
+// rather than both kinds of work in each: the up workgroups then need no
+// registers for predictor rows.
 template <int WT, int ACT, int NT, int NTH, int RV, int UW>
-__global__ __launch_bounds__(NTH) void k_la_up_pred1(FfnArgs fa) {
-  up_body<WT, ACT, NT, SRC_UNION, NTH, RV, true, true, UW>(fa, blockIdx.x, gridDim.x);
+__global__ __launch_bounds__(NTH) void k_la_up_pred1(FfnArgs fa, int gup) {
+  if ((int)blockIdx.x < gup)  // workgroup-uniform
+    up_body<WT, ACT, NT, SRC_UNION, NTH, RV, true, UW>(fa, blockIdx.x, gup);
+  else
+    p1_body<WT == WT_F32 ? WT_F32 : WT_F16, NT, NTH, RV>(fa, blockIdx.x - gup, gridDim.x - gup);
 }
+
+// Predictor-stage-1 workgroups of launch A: about SFNN_LA_P1_ROWS rows of W1^T each.
+#ifndef SFNN_LA_P1_ROWS
+#define SFNN_LA_P1_ROWS 4
+#endif
+inline int la_p1_groups(int r) { return r / SFNN_LA_P1_ROWS > 0 ? r / SFNN_LA_P1_ROWS : 1; }
 
 // Launch B of layer l: the first tiles * rg workgroups compute the down-
 // projection work items of FFN_l (one tile of one row group each; y_l and
@@ -58,10 +69,11 @@ static void launch_a(const FfnLaunch& F, const float* r_l, float eps, const Pred
     fa.r = next->r;
   }
   const size_t sh = (size_t)NT * F.d * sizeof(XT) + (WT == WT_I4 ? (size_t)NT * (F.d / 32) * 4 : 0);  // + vec_i4's m8
+  const int grid = F.groups + (next ? la_p1_groups(next->r) : 0);
   if (union_words_per_lane(F.f) == 4)
-    hipLaunchKernelGGL((k_la_up_pred1<WT, ACT, NT, NTH, RV, 4>), dim3(F.groups), dim3(NTH), sh, s, fa);
+    hipLaunchKernelGGL((k_la_up_pred1<WT, ACT, NT, NTH, RV, 4>), dim3(grid), dim3(NTH), sh, s, fa, F.groups);
   else
-    hipLaunchKernelGGL((k_la_up_pred1<WT, ACT, NT, NTH, RV, 16>), dim3(F.groups), dim3(NTH), sh, s, fa);
+    hipLaunchKernelGGL((k_la_up_pred1<WT, ACT, NT, NTH, RV, 16>), dim3(grid), dim3(NTH), sh, s, fa, F.groups);
 }
 
 template <int WT, int ACT, int NT>
