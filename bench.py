@@ -457,9 +457,16 @@ def _oracle_check(spec, hosts, nd, L, B, xcap, ycap, masks, ids, counts, lookahe
     FFN output for that mask (normwise relative error), and for layer 0 the
     predicted mask (bit-exact outside the fp32 rounding band).  Past the
     dense switch the mask is all ones (no predictor ran), so the FFN check is
-    the oracle's dense FFN."""
+    the oracle's dense FFN, on token 0 only, and only where its float64 rows
+    stay small (d_model * d_ff <= 2^27): over every row of a larger layer the
+    host would need minutes per token."""
     import oracle
     f = spec.d_ff
+    if dense and spec.d_model * f > (1 << 27):
+        return {"max_rel_err_vs_oracle": None,
+                "oracle_check": {"skipped": "dense FFN of d_model %d x d_ff %d: the float64 oracle over every "
+                                            "row takes minutes per token on the host; the dense switch's parity "
+                                            "is in tests/test_gpu_dense_switch.py" % (spec.d_model, f)}}
     errs, ids_ok, flips = [], True, 0
     xs = xcap.float().cpu().numpy()
     ys = ycap.cpu().numpy()
@@ -473,8 +480,9 @@ def _oracle_check(spec, hosts, nd, L, B, xcap, ycap, masks, ids, counts, lookahe
         x = xs[l].astype(spec.x_dtype)
         rid, rc, _ = oracle.compact(ms[l], B, f)
         ids_ok = ids_ok and rc == int(cnt_h[l]) and np.array_equal(rid, ids_h[l][:rc])
-        ref = oracle.masked_ffn(lay, x, oracle.unpack_mask(ms[l], f))
-        errs.append(float(np.abs(ys[l] - ref).max() / max(np.abs(ref).max(), 1e-30)))
+        nb = 1 if dense else B
+        ref = oracle.masked_ffn(lay, x[:nb], oracle.unpack_mask(ms[l][:nb], f))
+        errs.append(float(np.abs(ys[l][:nb] - ref).max() / max(np.abs(ref).max(), 1e-30)))
         if dense:
             ids_ok = ids_ok and bool((oracle.unpack_mask(ms[l], f)).all())
         elif l == 0 or not lookahead:
