@@ -35,7 +35,7 @@ def test_exports_match_header(L):
 
 def test_version_and_status_strings(L):
     import activation_sparse_gemv_amd as m
-    assert m.sfnn_version() >= 320
+    assert m.sfnn_version() >= 340  # 340: sfnn_pred.dense_min_batch
     assert m.sfnn_status_str(0) == "ok"
     assert "workspace" in m.sfnn_status_str(5)
 
@@ -180,3 +180,16 @@ def test_layer_noalloc_validation(L):
     assert L.sfnn_layer_noalloc(ctypes.byref(p), ctypes.byref(f), fake + 4, 1, fake, None, None, None, None) == 3
     q = P(12288, 49152, 1024, 0, fake, fake, fake)     # fp32 predictor with an INT4 (fp16-input) FFN
     assert L.sfnn_layer_noalloc(ctypes.byref(q), ctypes.byref(f), fake, 1, fake, None, None, None, None) == 4
+
+
+def test_pred_descriptor_layout_matches_header():
+    """The ctypes mirror of sfnn_pred ends with hot_prefix and dense_min_batch
+    (two int32 after three pointers), as include/sfnn.h declares it."""
+    import activation_sparse_gemv_amd as m
+    P = m._lib.sfnn_pred
+    assert [f[0] for f in P._fields_][-2:] == ["hot_prefix", "dense_min_batch"]
+    assert P.dense_min_batch.offset == P.hot_prefix.offset + 4
+    assert ctypes.sizeof(P) == 48
+    src = open(os.path.join(os.path.dirname(__file__), "..", "include", "sfnn.h")).read()
+    body = src[src.index("typedef struct sfnn_pred {"):src.index("} sfnn_pred;")]
+    assert body.index("hot_prefix") < body.index("dense_min_batch")

@@ -145,3 +145,49 @@ def test_graph_head_projections(B):
         hm.copy_(to_dev(synth.make_head_masks(B, H, 0.3, seed=k)[1]))
 
     _replays(run, set_input, [330, 331, 332])
+
+
+@pytest.mark.parametrize("wtype", ["f16", "i4g128"])
+def test_graph_layer_dense_switch(wtype):
+    """Past the dense switch (batch 16): the fill of the reported mask / ids /
+    count is a kernel, so the call captures and replays like the sparse one."""
+    B = 16
+    spec = synth.config("c2", d_model=512, d_ff=2048, rank=64, wtype=wtype)
+    lay = synth.make_layer(spec, layer=0)
+    pred, ffn = upload_layer(lay)
+    f, d = spec.d_ff, spec.d_model
+    x = torch.empty((B, d), dtype=torch.float16, device="cuda")
+    y = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    mask = torch.zeros((B, f // 64), dtype=torch.uint64, device="cuda")
+    ids = torch.empty(f, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(4, dtype=torch.int32, device="cuda")
+    ws = workspace(pred, ffn, B)
+
+    def run():
+        sg.sfnn_layer(pred, ffn, x, B, y, mask, ids, cnt, ws)
+        return [y, mask, ids, cnt[:1]]
+
+    inputs = [synth.make_tokens(spec, B, stream=320 + k) for k in range(3)]
+    _replays(run, lambda a: x.copy_(to_dev(a)), inputs)
+
+
+def test_graph_stack_dense_switch():
+    B = 20
+    spec = synth.config("c2", d_model=768, d_ff=3072, rank=96, n_layers=3)
+    lays = [synth.make_layer(spec, layer=l) for l in range(3)]
+    dev = [upload_layer(l) for l in lays]
+    st = sg.Stack(dev)
+    d, f = spec.d_model, spec.d_ff
+    r_in = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    r_out = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    mc = torch.zeros((3, B, f // 64), dtype=torch.uint64, device="cuda")
+    cc = torch.empty(3, dtype=torch.int32, device="cuda")
+    ws = workspace(dev[0][0], dev[0][1], B)
+
+    def run():
+        sg.sfnn_stack_decode(st, B, r_in, r_out, 1e-6, ws, flags=sg.SFNN_STACK_LOOKAHEAD, mask_cap=mc,
+                             count_cap=cc)
+        return [r_out, mc, cc]
+
+    inputs = [synth.make_tokens(spec, B, stream=330 + k, dtype=np.float32) for k in range(3)]
+    _replays(run, lambda a: r_in.copy_(to_dev(a)), inputs)
