@@ -27,7 +27,7 @@ EXPORTS = [
     "sfnn_layer", "sfnn_stack_decode", "sfnn_residual_rmsnorm", "sfnn_fire_counts", "sfnn_hot_first_perm",
     "sfnn_gather_rows", "sfnn_probe_read", "sfnn_probe_copy", "sfnn_status_str", "sfnn_version",
     "sfnn_isg_workspace_bytes", "sfnn_input_sparse_gemv", "sfnn_heads_workspace_bytes", "sfnn_head_qkv",
-    "sfnn_head_out", "sfnn_layer_noalloc",
+    "sfnn_head_out", "sfnn_layer_noalloc", "sfnn_dense_min_batch",
 ]
 
 
@@ -90,6 +90,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "sfnn_residual_rmsnorm": (i32, [vp, vp, vp, i32, i32, ctypes.c_float, vp, i32, vp]),
         "sfnn_fire_counts": (i32, [vp, i32, i32, vp, vp]),
         "sfnn_hot_first_perm": (i32, [vp, i32, vp]),
+        "sfnn_dense_min_batch": (i32, [vp, i32, i32, ctypes.c_float, i32, vp]),
         "sfnn_gather_rows": (i32, [vp, vp, i32, i64, vp, vp]),
         "sfnn_probe_read": (i32, [vp, sz, vp, vp]),
         "sfnn_probe_copy": (i32, [vp, vp, sz, vp]),
@@ -164,7 +165,7 @@ class Pred:
 
     @property
     def dense_min_batch(self) -> int:
-        """Batch from which sfnn_layer / sfnn_stack_decode run dense (0: default 16, < 0: never)."""
+        """Batch from which sfnn_layer / sfnn_stack_decode run dense (<= 0: never)."""
         return self.c.dense_min_batch
 
     @dense_min_batch.setter
@@ -266,7 +267,9 @@ def sfnn_layer_noalloc(pred: Pred, ffn: FFN, x, batch: int, y, mask=None, ids=No
 
 
 class Stack:
-    """Host arrays of per-layer descriptors for sfnn_stack_decode (keeps the layers alive)."""
+    """Host arrays of per-layer descriptors for sfnn_stack_decode (keeps the layers alive).
+    The descriptors are copied here: a later change to a layer's Pred or FFN
+    fields (hot_prefix, dense_min_batch, ...) needs a new Stack."""
 
     def __init__(self, layers):
         self.layers = list(layers)  # [(Pred, FFN)]
@@ -303,6 +306,17 @@ def sfnn_hot_first_perm(counts_host, d_ff: int, perm_host):
     cp = counts_host.ctypes.data if hasattr(counts_host, "ctypes") else counts_host.data_ptr()
     pp = perm_host.ctypes.data if hasattr(perm_host, "ctypes") else perm_host.data_ptr()
     _check("sfnn_hot_first_perm", load().sfnn_hot_first_perm(cp, d_ff, pp))
+
+
+def sfnn_dense_min_batch(counts_host, n_profiled: int, d_ff: int, crossover: float, max_batch: int) -> int:
+    """Host call: the dense-switch threshold for fire counts (uint32 CPU tensor
+    or numpy array) over n_profiled tokens; -1 when no batch up to max_batch
+    reaches the crossover share."""
+    cp = counts_host.ctypes.data if hasattr(counts_host, "ctypes") else counts_host.data_ptr()
+    out = ctypes.c_int32(0)
+    _check("sfnn_dense_min_batch",
+           load().sfnn_dense_min_batch(cp, n_profiled, d_ff, float(crossover), max_batch, ctypes.byref(out)))
+    return out.value
 
 
 def sfnn_gather_rows(src, perm, n_rows: int, row_bytes: int, dst, stream=None):

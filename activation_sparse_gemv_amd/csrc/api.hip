@@ -107,13 +107,9 @@ sfnn_status check_ffn(const sfnn_ffn* f) {
   return SFNN_OK;
 }
 
-constexpr int kDenseMinBatchDefault = 16;
-
-// The dense switch: from this batch on a layer skips the predictor.
-bool runs_dense(const sfnn_pred* p, int batch) {
-  const int t = p->dense_min_batch == 0 ? kDenseMinBatchDefault : p->dense_min_batch;
-  return t > 0 && batch >= t;
-}
+// The dense switch: from this batch on a layer skips the predictor (a
+// positive threshold; zero and negative values never switch).
+bool runs_dense(const sfnn_pred* p, int batch) { return p->dense_min_batch > 0 && batch >= p->dense_min_batch; }
 
 int x_type_of_ffn(const sfnn_ffn* f) { return f->wtype == SFNN_F32 ? SFNN_F32 : SFNN_F16; }
 
@@ -399,20 +395,38 @@ sfnn_status sfnn_stack_decode(int32_t n_layers, const sfnn_pred* preds, const sf
     return F;
   };
 
-  if (runs_dense(&preds[0], batch)) {
-    // past the crossover: no predictor; each layer is RMSNorm then the dense FFN
-    if ((mask_cap || ids_cap || count_cap) &&
-        launch_fill_dense(mask_cap, (size_t)n_layers * batch * W, ids_cap, n_layers, f, count_cap, n_layers, s) !=
-            hipSuccess)
-      return SFNN_E_HIP;
+  // the dense switch, per layer: such a layer has no predictor and runs the
+  // dense FFN; its reports (when captured) are the all-ones mask, 0..f-1, f
+  std::vector<char> dense((size_t)n_layers);
+  int n_dense = 0;
+  for (int l = 0; l < n_layers; ++l) n_dense += dense[l] = runs_dense(&preds[l], batch);
+  auto dense_ffn_of = [&](int l) {
+    FfnLaunch F = ffn_launch(&ffns[l], x_of(l), batch, nullptr, y_of(l), w, Lw);
+    F.r_in = r_of(l);
+    F.r_out = r_of(l + 1);
+    return F;
+  };
+  if (n_dense && (mask_cap || ids_cap || count_cap)) {
+    if (n_dense == n_layers) {
+      if (launch_fill_dense(mask_cap, (size_t)n_layers * batch * W, ids_cap, n_layers, f, count_cap, n_layers, s) !=
+          hipSuccess)
+        return SFNN_E_HIP;
+    } else {
+      for (int l = 0; l < n_layers; ++l)
+        if (dense[l] && launch_fill_dense(mask_cap ? m_of(l) : nullptr, (size_t)batch * W,
+                                          ids_cap ? i_of(l) : nullptr, 1, f, count_cap ? c_of(l) : nullptr, 1,
+                                          s) != hipSuccess)
+          return SFNN_E_HIP;
+    }
+  }
+
+  if (n_dense == n_layers) {
+    // every layer past its switch: RMSNorm then the dense FFN
     for (int l = 0; l < n_layers; ++l) {
       if (launch_residual_rmsnorm(r_of(l), nullptr, nullptr, batch, d, eps, x_of(l), xb == 4 ? WT_F32 : WT_F16, s) !=
           hipSuccess)
         return SFNN_E_HIP;
-      FfnLaunch F = ffn_launch(&ffns[l], x_of(l), batch, nullptr, y_of(l), w, Lw);
-      F.r_in = r_of(l);
-      F.r_out = r_of(l + 1);
-      if (launch_ffn(F, s) != hipSuccess) return SFNN_E_HIP;
+      if (launch_ffn(dense_ffn_of(l), s) != hipSuccess) return SFNN_E_HIP;
     }
     return SFNN_OK;
   }
@@ -423,14 +437,22 @@ sfnn_status sfnn_stack_decode(int32_t n_layers, const sfnn_pred* preds, const sf
     std::vector<const float*> R((size_t)n_layers + 1);
     for (int l = 0; l < n_layers; ++l) {
       P[l] = pred_launch(&preds[l], nullptr, batch, m_of(l), uni, nullptr, z);
-      F[l] = ffn_of(l);
+      F[l] = dense[l] ? dense_ffn_of(l) : ffn_of(l);
     }
     for (int l = 0; l <= n_layers; ++l) R[l] = r_of(l);
     return hip_status(launch_stack_lookahead(P.data(), F.data(), R.data(), n_layers, eps,
-                                             reinterpret_cast<float*>(w + Lw.rtmp), s));
+                                             reinterpret_cast<float*>(w + Lw.rtmp), n_dense ? dense.data() : nullptr,
+                                             s));
   }
 
   for (int l = 0; l < n_layers; ++l) {
+    if (dense[l]) {
+      if (launch_residual_rmsnorm(r_of(l), nullptr, nullptr, batch, d, eps, x_of(l), xb == 4 ? WT_F32 : WT_F16, s) !=
+              hipSuccess ||
+          launch_ffn(dense_ffn_of(l), s) != hipSuccess)
+        return SFNN_E_HIP;
+      continue;
+    }
     // x_l = RMSNorm(r_l), built inside the predictor's first kernel
     PredLaunch P = pred_launch(&preds[l], nullptr, batch, m_of(l), uni, nullptr, z);
     P.norm.r_in = r_of(l);
@@ -471,6 +493,28 @@ sfnn_status sfnn_hot_first_perm(const uint32_t* counts, int32_t d_ff, int32_t* p
   std::iota(idx.begin(), idx.end(), 0);
   std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) { return counts[a] > counts[b]; });
   std::copy(idx.begin(), idx.end(), perm);
+  return SFNN_OK;
+}
+
+sfnn_status sfnn_dense_min_batch(const uint32_t* counts, int32_t n_profiled, int32_t d_ff, float crossover,
+                                 int32_t max_batch, int32_t* out) {
+  if (!counts || !out) return SFNN_E_NULL;
+  if (n_profiled < 1 || d_ff < 1 || max_batch < 1 || !(crossover > 0.0f && crossover <= 1.0f)) return SFNN_E_SHAPE;
+  // q_i = 1 - p_i, the chance a token leaves neuron i off; u(b) = 1 - mean_i q_i^b
+  std::vector<double> q((size_t)d_ff), qb((size_t)d_ff, 1.0);
+  for (int i = 0; i < d_ff; ++i) {
+    if (counts[i] > (uint32_t)n_profiled) return SFNN_E_SHAPE;
+    q[i] = 1.0 - (double)counts[i] / (double)n_profiled;
+  }
+  for (int b = 1; b <= max_batch; ++b) {
+    double off = 0.0;  // sum_i q_i^b
+    for (int i = 0; i < d_ff; ++i) off += (qb[i] *= q[i]);
+    if (1.0 - off / d_ff >= (double)crossover) {
+      *out = b;
+      return SFNN_OK;
+    }
+  }
+  *out = -1;
   return SFNN_OK;
 }
 
@@ -674,6 +718,6 @@ const char* sfnn_status_str(sfnn_status s) {
   return "unknown status";
 }
 
-int32_t sfnn_version(void) { return 340; }  // 300: sfnn_ffn.mfma_min_batch; 310: sfnn_input_sparse_gemv; 320: sfnn_pred.hot_prefix; 330: head-gated projections; 340: sfnn_pred.dense_min_batch
+int32_t sfnn_version(void) { return 350; }  // 300: sfnn_ffn.mfma_min_batch; 310: sfnn_input_sparse_gemv; 320: sfnn_pred.hot_prefix; 330: head-gated projections; 340: sfnn_pred.dense_min_batch; 350: sfnn_dense_min_batch, per-layer stack switch, no default threshold
 
 }  // extern "C"

@@ -29,15 +29,21 @@ static int la_group(const FfnLaunch& F, const PredLaunch& P) {
 }
 
 hipError_t launch_stack_lookahead(const PredLaunch* P, const FfnLaunch* F, const float* const* R, int L, float eps,
-                                  float* rtmp, hipStream_t s) {
-  // layer 0 predicts from its own input
-  PredLaunch P0 = P[0];
-  P0.norm.r_in = R[0];
-  P0.norm.x_out = const_cast<void*>(F[0].x);
-  P0.norm.eps = eps;
-  hipError_t e = launch_predict(P0, s);
-  if (e != hipSuccess) return e;
-  const int NT = la_group(F[0], P[0]);
+                                  float* rtmp, const char* dense, hipStream_t s) {
+  auto sparse = [&](int l) { return !dense || !dense[l]; };
+  hipError_t e = hipSuccess;
+  if (sparse(0)) {
+    // layer 0 predicts from its own input
+    PredLaunch P0 = P[0];
+    P0.norm.r_in = R[0];
+    P0.norm.x_out = const_cast<void*>(F[0].x);
+    P0.norm.eps = eps;
+    e = launch_predict(P0, s);
+    if (e != hipSuccess) return e;
+  }
+  // the fused launches pair every layer with the next one's predictor, so a
+  // stack with dense layers takes the per-stage schedule below
+  const int NT = dense ? 0 : la_group(F[0], P[0]);
   if (NT > 0) {
     if (F[0].wt == WT_F32)
       stack_fused_f32(P, F, R, L, eps, NT, s);
@@ -47,16 +53,18 @@ hipError_t launch_stack_lookahead(const PredLaunch* P, const FfnLaunch* F, const
       stack_fused_i4(P, F, R, L, eps, NT, s);
     return hipGetLastError();
   }
-  // larger batches: the same schedule, one launch per stage
+  // larger batches: the same schedule, one launch per stage; a dense layer
+  // has no predictor stages, and the layer before it builds x_l on its own
   for (int l = 0; l < L; ++l) {
-    if (l + 1 < L) {
+    const bool next_predicts = l + 1 < L && sparse(l + 1);
+    if (next_predicts) {
       PredLaunch Pn = P[l + 1];  // stage 1 of the next layer also writes x_l for this layer's FFN
       Pn.norm.r_in = R[l];
       Pn.norm.x_out = const_cast<void*>(F[l].x);
       Pn.norm.eps = eps;
       e = launch_predict_stage1(Pn, s);
     } else {
-      // the last layer's input: RMSNorm of its residual row (the row copy goes to rtmp)
+      // RMSNorm of the residual row alone (the row copy goes to rtmp)
       e = launch_residual_rmsnorm(R[l], nullptr, rtmp, F[l].batch, F[l].d, eps, const_cast<void*>(F[l].x),
                               F[l].wt == WT_F32 ? WT_F32 : WT_F16, s);
     }
@@ -64,7 +72,7 @@ hipError_t launch_stack_lookahead(const PredLaunch* P, const FfnLaunch* F, const
     Fs.r_in = R[l];
     Fs.r_out = const_cast<float*>(R[l + 1]);
     if (e == hipSuccess) e = launch_ffn(Fs, s);
-    if (e == hipSuccess && l + 1 < L) e = launch_predict_stage2(P[l + 1], s);
+    if (e == hipSuccess && next_predicts) e = launch_predict_stage2(P[l + 1], s);
     if (e != hipSuccess) return e;
   }
   return hipGetLastError();

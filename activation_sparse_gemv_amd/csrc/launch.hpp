@@ -127,9 +127,11 @@ hipError_t launch_predict_stage2(const PredLaunch& p, hipStream_t s);
 // input (layer 0 from its own).  pred / ffn: per-layer launch descriptors
 // whose mask, union, ids, count, z, x, y and partial pointers are set; r:
 // n_layers + 1 residual rows (r[0] the input, r[n_layers] the output);
-// rtmp: one scratch residual row set [B][d].
+// rtmp: one scratch residual row set [B][d].  dense: NULL, or per layer
+// nonzero where the layer runs dense (no predictor; ffn[l] is then the dense
+// launch with no mask or union).
 hipError_t launch_stack_lookahead(const PredLaunch* pred, const FfnLaunch* ffn, const float* const* r,
-                                  int n_layers, float eps, float* rtmp, hipStream_t s);
+                                  int n_layers, float eps, float* rtmp, const char* dense, hipStream_t s);
 
 // ---- input-sparse GEMV -------------------------------------------------------
 

@@ -66,16 +66,20 @@ def _parse():
     ap.add_argument("--hot-prefix", default="0",
                     help="dense hot prefix of power-law workloads: a neuron count (multiple of 64) or 'auto' "
                          "(chosen per layer from the profiled fire rates of the batch's union)")
-    ap.add_argument("--dense-min-batch", type=int, default=0,
+    ap.add_argument("--dense-min-batch", default="0",
                     help="the predictor descriptors' dense switch: from this batch on a layer skips the predictor "
-                         "and runs the dense FFN (0: the library default, 16; negative: never)")
+                         "and runs the dense FFN (0, the library default, or negative: never; 'auto': per layer "
+                         "from fire counts profiled on the stack, the union law and the measured crossover)")
     ap.add_argument("--isg", action="store_true",
                     help="time the input-sparse GEMV (ReLU after the norm) over input densities and batches")
     return ap.parse_args()
 
 
 HBM_PEAK_GBS = 8000.0
-DENSE_MIN_BATCH_DEFAULT = 16  # the library's default dense switch (sfnn_pred.dense_min_batch = 0)
+# Union share of d_ff from which the dense FFN beats predictor + sparse FFN
+# (the sparse-vs-dense sweeps on MI355X: OPT-6.7B fp16 and OPT-175B INT4-g128
+# shapes; the fp32 figure is the fp16 one, not measured on its own).
+DENSE_CROSSOVER = {"f16": 0.45, "i4g128": 0.65, "f32": 0.45}
 COPY_PROBE_BYTES = 1 << 30
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 
@@ -199,10 +203,9 @@ def _stack_run(args, spec, B, headline):
             hosts.append(lay)  # kept for the oracle check and the CPU baseline
         del lay
     layers = [distinct[l % nd] for l in range(L)]
+    auto_switch = args.dense_min_batch == "auto"
     for pred, _ in distinct:
-        pred.dense_min_batch = args.dense_min_batch
-    thr = DENSE_MIN_BATCH_DEFAULT if args.dense_min_batch == 0 else args.dense_min_batch
-    dense = 0 < thr <= B  # past the switch every layer runs the dense FFN, no predictor
+        pred.dense_min_batch = -1 if auto_switch else int(args.dense_min_batch)
     torch.cuda.synchronize()
     t_setup = time.time() - t0
     print(f"# {L} layers of {spec.name} ({nd} distinct) resident in HBM after {t_setup:.1f}s",
@@ -218,6 +221,14 @@ def _stack_run(args, spec, B, headline):
     elif args.hot_prefix != "0":
         sys.exit("a dense hot prefix needs the hot-first relayout of a power-law workload (c3, c4)")
     hot_mean = float(np.mean([hots[l % nd] for l in range(L)]))
+
+    # ---- dense switch per layer (past it: the dense FFN, no predictor) ------
+    if auto_switch:
+        _auto_dense_switch(sg, distinct, spec, dev, 0 if args.per_layer_predictor else sg.SFNN_STACK_LOOKAHEAD)
+    thr = [pred.dense_min_batch for pred, _ in distinct]
+    dense_l = [0 < thr[l % nd] <= B for l in range(L)]
+    n_dense = int(sum(dense_l))
+    dense = n_dense == L
 
     xdt = torch.float32 if spec.wtype == "f32" else torch.float16
     steps, warmup = (args.steps, args.warmup) if headline else (min(args.steps, 64), min(args.warmup, 8))
@@ -300,16 +311,16 @@ def _stack_run(args, spec, B, headline):
     nmat = spec.n_mat
     ffn_bytes_u = lambda u: u * nmat * row_bytes + u * (nmat - 1) * xb          # noqa: E731
     pred_bytes = (d * r + r * (f - hot_mean)) * pb + 4 * (f - hot_mean)  # hot-prefix rows are not read
-    if dense:
-        pred_bytes = 0
+    pred_bytes *= (L - n_dense) / L  # dense layers run no predictor
     ffn_bytes = ffn_bytes_u(mean_u)
     cycled = "" if nd == L else f" (weights of {nd} distinct layers, {nd * layer_gb:.1f} GB, cycled)"
     workload = (f"{spec.name} FFN stack: {L} layers{cycled}, d_model {d}, d_ff {f}, rank-{r} predictor, "
                 f"{spec.act}, {spec.wtype}, "
                 f"{'zipf phi=%.2f ' % spec.phi if spec.profile == 'zipf' else ''}rho={spec.rho}, batch {B}"
                 f"{', dense hot prefix %s' % args.hot_prefix if hot_mean else ''}"
-                + (f", dense switch (batch >= {thr}): dense FFN, no predictor" if dense else
-                   (", look-ahead predictor" if lookahead else ", per-layer predictor")))
+                + (f", dense switch: every layer dense (thresholds {thr}), no predictor" if dense else
+                   (", look-ahead predictor" if lookahead else ", per-layer predictor")
+                   + (f", dense switch: {n_dense} of {L} layers dense (thresholds {thr})" if n_dense else "")))
     per_sorted = np.sort(np.asarray(per_step))
     out = {
         "metric": "sparse-FFN decode tokens/sec at batch 1 + effective HBM GB/s on active bytes",
@@ -328,13 +339,14 @@ def _stack_run(args, spec, B, headline):
         "data": "synthetic (seeded N(0,0.02) weights, calibrated biases/thresholds, x~N(0,1))",
         "config": {"workload": workload, "global_batch": B, "decode_steps": steps, "layers": L,
                    "distinct_layers": nd,
-                   "predictor": ("none: dense switch at batch >= %d" % thr) if dense else
+                   "predictor": ("none: every layer past its dense switch") if dense else
                    ("look-ahead (layer l+1 from x_l)" if lookahead else "per layer (layer l from x_l)")},
     }
     extra = {"mean_active_neurons": round(mean_u, 1), "active_fraction": round(mean_u / f, 4),
              "expected_union_fraction": round(synth.union_density(synth.layer_probs(spec, 0), B), 4),
              "ffn_active_bytes_per_layer": int(ffn_bytes), "predictor_bytes_per_layer": int(pred_bytes),
-             "setup_s": round(t_setup, 1), "dense_min_batch": thr, "ran_dense": bool(dense)}
+             "setup_s": round(t_setup, 1), "dense_min_batch_per_distinct_layer": thr,
+             "dense_switch": "auto" if auto_switch else args.dense_min_batch, "dense_layers": n_dense}
     if hot_mean:
         extra["hot_prefix_per_layer"] = hots
     extra["layer_GBps_stack"] = round(L * (ffn_bytes + pred_bytes) / (ms_per_step / 1e3) / 1e9, 1)
@@ -343,7 +355,7 @@ def _stack_run(args, spec, B, headline):
 
     # ---- the oracle on sampled layers of the captured step ------------------
     if headline:
-        out.update(_oracle_check(spec, hosts, nd, L, B, xcap, ycap, masks, ids, counts, lookahead, dense))
+        out.update(_oracle_check(spec, hosts, nd, L, B, xcap, ycap, masks, ids, counts, lookahead, dense_l))
 
     # ---- per-call timings: each call captured for all layers in one graph ----
     if headline and not args.no_extra:
@@ -413,6 +425,7 @@ def _stack_run(args, spec, B, headline):
     us_layer_stack = ms_per_step * 1e3 / L
     layer_bytes = ffn_bytes + pred_bytes
     workload_key = (f"{spec.name}/b{B}/{'dense' if dense else ('lookahead' if lookahead else 'per-layer')}"
+                    f"{'/mixed%d' % n_dense if n_dense and not dense else ''}"
                     f"{'/hot%s' % args.hot_prefix if hot_mean else ''}")
     tr = _stored_traffic(workload_key)
     out["roofline"] = {
@@ -420,6 +433,8 @@ def _stack_run(args, spec, B, headline):
         "unit": "GB/s", "frac": round(layer_bytes / us_layer_stack / 1e3 / HBM_PEAK_GBS, 4),
         "traffic": (int(tr["fetch_bytes_per_layer"] + tr["write_bytes_per_layer"]) if tr else None),
         "kernel": ("stack layer, dense switch: RMSNorm + the dense FFN" if dense else
+                   ("stack layer, %d of %d layers dense (RMSNorm + the dense FFN), the others predictor-gated"
+                    % (n_dense, L)) if n_dense else
                    ("stack layer, look-ahead: k_la_up_pred1 (FFN_l up rows + predictor stage 1 of l+1) "
                     "+ k_la_down_pred2 (FFN_l column-tiled down rows + predictor stage 2 of l+1)") if lookahead else
                    ("stack layer, per-layer predictor: k_pred1 + k_pred2 + k_up + k_down")),
@@ -451,18 +466,20 @@ def _host_relayout(lay, dev_layer):
     return h
 
 
-def _oracle_check(spec, hosts, nd, L, B, xcap, ycap, masks, ids, counts, lookahead, dense=False):
+def _oracle_check(spec, hosts, nd, L, B, xcap, ycap, masks, ids, counts, lookahead, dense_l):
     """Layers 0 and L-1 of the captured step against the fp64 oracle on the
     same inputs: the ids and count of the mask the GPU used (bit-exact), the
     FFN output for that mask (normwise relative error), and for layer 0 the
-    predicted mask (bit-exact outside the fp32 rounding band).  Past the
-    dense switch the mask is all ones (no predictor ran), so the FFN check is
-    the oracle's dense FFN, on token 0 only, and only where its float64 rows
-    stay small (d_model * d_ff <= 2^27): over every row of a larger layer the
-    host would need minutes per token."""
+    predicted mask (bit-exact outside the fp32 rounding band).  A layer past
+    its dense switch (dense_l[l]) has the all-ones mask (no predictor ran),
+    so its FFN check is the oracle's dense FFN, on token 0 only, and only
+    where its float64 rows stay small (d_model * d_ff <= 2^27): over every
+    row of a larger layer the host would need minutes per token."""
     import oracle
     f = spec.d_ff
-    if dense and spec.d_model * f > (1 << 27):
+    big = spec.d_model * f > (1 << 27)
+    checked = [l for l in sorted({0, L - 1}) if not (dense_l[l] and big)]
+    if not checked:
         return {"max_rel_err_vs_oracle": None,
                 "oracle_check": {"skipped": "dense FFN of d_model %d x d_ff %d: the float64 oracle over every "
                                             "row takes minutes per token on the host; the dense switch's parity "
@@ -473,7 +490,8 @@ def _oracle_check(spec, hosts, nd, L, B, xcap, ycap, masks, ids, counts, lookahe
     ms = masks.cpu().numpy()
     ids_h = ids.cpu().numpy()
     cnt_h = counts.cpu().numpy()
-    for l in sorted({0, L - 1}):
+    for l in checked:
+        dense = dense_l[l]
         lay = hosts[l % nd] if l % nd < len(hosts) else None
         if lay is None:
             continue
@@ -492,7 +510,7 @@ def _oracle_check(spec, hosts, nd, L, B, xcap, ycap, masks, ids, counts, lookahe
             outside = np.abs(lg - lay.tau[None, :].astype(np.float64)) > band
             flips += int(((gb != ob) & outside).sum())
     return {"max_rel_err_vs_oracle": round(max(errs), 8) if errs else None,
-            "oracle_check": {"layers": sorted({0, L - 1}), "ids_count_bit_exact": bool(ids_ok),
+            "oracle_check": {"layers": checked, "ids_count_bit_exact": bool(ids_ok),
                              "mask_bits_outside_rounding_band_differing": flips, "tolerance": 2e-3}}
 
 
@@ -522,6 +540,7 @@ def _sweep(args, spec):
             pred.dense_min_batch = -1  # the predictor's union at every batch (the switch is timed below)
         if sp.profile == "zipf":
             _hot_first(sg, layers, sp, 8, dev)
+        auto_thr = _thresholds_from_predictor(sg, layers, sp, dev)
         for B in batches:
             ws = workspace(layers[0][0], layers[0][1], B)
             x = [to_dev(synth.make_tokens(sp, B, stream=500 + l).astype(xdt)) for l in range(nl)]
@@ -581,13 +600,16 @@ def _sweep(args, spec):
                     pt[f"us_dense_ffn_{name}"] = round(t_dense(), 2)
                 for _, ffn in layers:
                     ffn.mfma_min_batch = 0
-            # last (it overwrites the masks, ids and counts past the switch): the
-            # layer call with the library's dense switch, dense from batch 16 on
-            for pred, _ in layers:
-                pred.dense_min_batch = 0
-            pt["us_layer_default_switch"] = round(
-                timed(lambda: [sg.sfnn_layer(pred, ffn, x[l], B, y, masks[l], ids[l], cnt[l:l + 1], ws)
-                               for l, (pred, ffn) in enumerate(layers)]), 2)
+            # last (they overwrite the masks, ids and counts past the switch):
+            # the layer call with the dense switch at batch 16, and at the
+            # threshold profiled from fire counts (union law + crossover)
+            for key, th in (("us_layer_switch_at_16", [16] * nl), ("us_layer_auto_switch", auto_thr)):
+                for (pred, _), t in zip(layers, th):
+                    pred.dense_min_batch = t
+                pt[key] = round(
+                    timed(lambda: [sg.sfnn_layer(pred, ffn, x[l], B, y, masks[l], ids[l], cnt[l:l + 1], ws)
+                                   for l, (pred, ffn) in enumerate(layers)]), 2)
+            pt["auto_dense_min_batch"] = auto_thr
             for pred, _ in layers:
                 pred.dense_min_batch = -1
             points.append(pt)
@@ -812,6 +834,66 @@ def _hot_first(sg, layers, spec, B, dev, hot_arg="0"):
         pred.hot_prefix = _auto_hot_prefix(spec, hits[k] / n[k])
         hots.append(pred.hot_prefix)
     return hots
+
+
+def _switch_thresholds(sg, counts, n_prof, spec):
+    """dense_min_batch per layer from its fire counts ([layers][d_ff] int32 on
+    the device) over n_prof[k] tokens: the smallest batch whose expected union
+    share reaches the weight type's crossover, -1 if none up to 64 does."""
+    ch = counts.cpu().numpy().view(np.uint32)
+    return [sg.sfnn_dense_min_batch(np.ascontiguousarray(c), n, spec.d_ff, DENSE_CROSSOVER[spec.wtype], 64)
+            for c, n in zip(ch, n_prof)]
+
+
+def _thresholds_from_predictor(sg, layers, spec, dev, nprof=256):
+    """Dense switch of single layers: fire counts of the predictor's masks on
+    seeded fresh tokens (the layer calls' own workload)."""
+    import torch
+    import synth
+    from activation_sparse_gemv_amd.device import to_dev, workspace
+    f, W = spec.d_ff, spec.d_ff // 64
+    xs = to_dev(synth.make_tokens(spec, nprof, stream=97))
+    counts = torch.zeros((len(layers), f), dtype=torch.int32, device=dev)
+    m = torch.zeros((nprof, W), dtype=torch.uint64, device=dev)
+    for k, (pred, _) in enumerate(layers):
+        ws = workspace(pred, None, 8)
+        for i in range(0, nprof, 8):
+            sg.sfnn_predict(pred, xs[i:i + 8], 8, m[i:i + 8], None, ws)
+        sg.sfnn_fire_counts(m, nprof, f, counts[k])
+    torch.cuda.synchronize()
+    return _switch_thresholds(sg, counts, [nprof] * len(layers), spec)
+
+
+def _auto_dense_switch(sg, distinct, spec, dev, flags, steps=64):
+    """Dense switch of a stack's layers: fire counts of the masks each
+    distinct layer's predictor makes on the decode path itself (a batch-1
+    stack over seeded tokens, every layer sparse), then the union law.
+    Sets each Pred's dense_min_batch; a Stack built afterwards carries it."""
+    import torch
+    import synth
+    from activation_sparse_gemv_amd.device import to_dev, workspace
+    f, d, L, nd = spec.d_ff, spec.d_model, spec.n_layers, len(distinct)
+    W = f // 64
+    st = sg.Stack([distinct[l % nd] for l in range(L)])
+    xr = to_dev(synth.make_tokens(spec, steps, stream=96, dtype=np.float32)).view(steps, 1, d)
+    rout = torch.empty((1, d), dtype=torch.float32, device=dev)
+    ws = workspace(distinct[0][0], distinct[0][1], 1)
+    mc = torch.zeros((steps, L, W), dtype=torch.uint64, device=dev)
+    for t in range(steps):
+        sg.sfnn_stack_decode(st, 1, xr[t], rout, 1e-6, ws, flags=flags, mask_cap=mc[t])
+    counts = torch.zeros((nd, f), dtype=torch.int32, device=dev)
+    n_prof = []
+    for k in range(nd):
+        mk = mc[:, k::nd].reshape(-1, W).contiguous()  # every position of distinct layer k, every step
+        sg.sfnn_fire_counts(mk, mk.shape[0], f, counts[k])
+        n_prof.append(mk.shape[0])
+    torch.cuda.synchronize()
+    thr = _switch_thresholds(sg, counts, n_prof, spec)
+    for (pred, _), t in zip(distinct, thr):
+        pred.dense_min_batch = t
+    print(f"# dense switch per distinct layer (auto, crossover {DENSE_CROSSOVER[spec.wtype]}): {thr}",
+          file=sys.stderr, flush=True)
+    return thr
 
 
 def _auto_hot_prefix(spec, urate):

@@ -88,13 +88,17 @@ typedef enum { SFNN_RELU = 0, SFNN_REGLU = 1 } sfnn_act;
  * small share of d_ff (DejaVu's contextual sparsity is per token; the union
  * of B tokens grows with B, and past a crossover the gathered rows cost more
  * than reading the matrices whole: 53ai.com sparsity survey, DejaVu section).
- * From batch >= dense_min_batch on (0 selects the default, 16; a negative
- * value never) these calls skip the predictor and run the dense FFN: every
- * neuron for every token, its own ReLU / ReGLU deciding its share, which is
- * the masked FFN under an all-ones mask.  They then report that mask (all
- * bits set), ids 0..d_ff-1 and count = d_ff.  The stack reads the switch of
- * preds[0] for every layer.  The crossover depends on the fire rate and the
- * hardware; the field is read per call. */
+ * From batch >= dense_min_batch on (a positive value; 0, the default, and
+ * negative values never switch) these calls skip the predictor and run the
+ * dense FFN: every neuron for every token, its own ReLU / ReGLU deciding its
+ * share, which is the masked FFN under an all-ones mask.  They then report
+ * that mask (all bits set), ids 0..d_ff-1 and count = d_ff.  The stack reads
+ * each layer's own field, so one step may mix sparse and dense layers.  How
+ * fast the union grows depends on how the layer's neurons fire: under a
+ * power law it stays far below d_ff at batches where uniform firing fills it
+ * (same page, throughput paragraph), so there is no default threshold;
+ * sfnn_dense_min_batch derives one from profiled fire counts.  The field is
+ * read per call. */
 typedef struct sfnn_pred {
   int32_t d_model, d_ff, rank;
   int32_t wtype;       /* sfnn_wtype: F32 or F16                         */
@@ -102,7 +106,7 @@ typedef struct sfnn_pred {
   const void* w2_t;    /* [d_ff][rank] (rows below hot_prefix unread)    */
   const float* tau;    /* [d_ff]       (entries below hot_prefix unread) */
   int32_t hot_prefix;  /* dense hot prefix, see above; 0: none           */
-  int32_t dense_min_batch; /* dense switch, see above; 0: default (16)   */
+  int32_t dense_min_batch; /* dense switch, see above; <= 0: never       */
 } sfnn_pred;
 
 /* One FFN layer.  ReLU:  y = b_down + sum_i relu(W_up[i].x + b_up[i]) W_down[:, i]
@@ -227,6 +231,8 @@ sfnn_status sfnn_layer_noalloc(const sfnn_pred* pred, const sfnn_ffn* ffn, const
  *     layer's sparsity is predicted one step ahead so the predictor runs
  *     beside the current layer's FFN (53ai.com sparsity survey, DejaVu
  *     section 如何充分利用结构化稀疏进行加速).
+ * A layer whose preds[l].dense_min_batch is positive and <= batch runs dense
+ * instead (see sfnn_pred): no predictor, m_l all ones, y_l the dense FFN.
  * preds / ffns are HOST arrays of n_layers descriptors that share one shape
  * and type (d_model, d_ff, rank, wtype, act); their device pointers may differ.
  * r_in, r_out: [batch][d_model] fp32 (r_out may alias r_in).  Optional
@@ -259,6 +265,22 @@ sfnn_status sfnn_fire_counts(const uint64_t* masks, int32_t n_masks, int32_t d_f
 /* Hot-first order (HOST memory in and out): perm[new] = original neuron id,
  * by descending count, ties by ascending id. */
 sfnn_status sfnn_hot_first_perm(const uint32_t* counts, int32_t d_ff, int32_t* perm);
+
+/* Dense-switch threshold from a fire-count profile (HOST memory; no GPU call).
+ * With p_i = counts[i] / n_profiled the fire rate of neuron i over
+ * n_profiled independent tokens, a batch of b such tokens is expected to
+ * touch the share u(b) = mean_i (1 - (1 - p_i)^b) of the d_ff neurons
+ * (53ai.com sparsity survey, DejaVu section, throughput paragraph: the share
+ * grows with the batch, sub-linearly when firing follows a power law).
+ * *out = the smallest b in [1, max_batch] with u(b) >= crossover, or -1 when
+ * none reaches it; crossover is the union share from which the dense FFN
+ * beats predictor + sparse FFN on the target (measured per weight type).
+ * Store *out in sfnn_pred.dense_min_batch.  Errors: counts or out NULL ->
+ * SFNN_E_NULL; n_profiled < 1, d_ff < 1, max_batch < 1, crossover outside
+ * (0, 1] or not a number, or a count above n_profiled -> SFNN_E_SHAPE
+ * (*out untouched). */
+sfnn_status sfnn_dense_min_batch(const uint32_t* counts, int32_t n_profiled, int32_t d_ff, float crossover,
+                                 int32_t max_batch, int32_t* out);
 
 /* dst row k = src row perm[k] for k < n_rows, rows of row_bytes bytes
  * (row_bytes % 2 == 0; applies a relayout to weights, scales and biases).
@@ -340,7 +362,7 @@ sfnn_status sfnn_head_out(const sfnn_heads* op, const void* attn, int32_t batch,
                           float* y, void* ws, size_t ws_bytes, void* stream);
 size_t sfnn_heads_workspace_bytes(const sfnn_heads* op, int32_t batch);
 
-int32_t sfnn_version(void);  /* 300 and up: sfnn_ffn has mfma_min_batch; 310 and up: sfnn_input_sparse_gemv; 320 and up: sfnn_pred has hot_prefix; 330 and up: sfnn_head_qkv, sfnn_head_out; 340 and up: sfnn_pred has dense_min_batch */
+int32_t sfnn_version(void);  /* 300 and up: sfnn_ffn has mfma_min_batch; 310 and up: sfnn_input_sparse_gemv; 320 and up: sfnn_pred has hot_prefix; 330 and up: sfnn_head_qkv, sfnn_head_out; 340 and up: sfnn_pred has dense_min_batch; 350 and up: sfnn_dense_min_batch, per-layer switch in the stack, no default threshold */
 
 #ifdef __cplusplus
 }

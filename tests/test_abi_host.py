@@ -1,6 +1,6 @@
 """Host-side checks of the C-ABI library (no GPU needed): it loads, exports
 every symbol the header declares, validates arguments before launching, and
-the host-only hot-first ordering matches the oracle's."""
+the host-only helpers (hot-first ordering, dense-switch threshold) are right."""
 import ctypes
 import os
 import re
@@ -35,7 +35,7 @@ def test_exports_match_header(L):
 
 def test_version_and_status_strings(L):
     import activation_sparse_gemv_amd as m
-    assert m.sfnn_version() >= 340  # 340: sfnn_pred.dense_min_batch
+    assert m.sfnn_version() >= 350  # 350: sfnn_dense_min_batch, per-layer stack switch
     assert m.sfnn_status_str(0) == "ok"
     assert "workspace" in m.sfnn_status_str(5)
 
@@ -193,3 +193,81 @@ def test_pred_descriptor_layout_matches_header():
     src = open(os.path.join(os.path.dirname(__file__), "..", "include", "sfnn.h")).read()
     body = src[src.index("typedef struct sfnn_pred {"):src.index("} sfnn_pred;")]
     assert body.index("hot_prefix") < body.index("dense_min_batch")
+
+
+# ---- dense-switch threshold from fire counts (host only) ---------------------
+
+def _enumerated_union_share(p, b):
+    """Expected share of neurons touched by b independent tokens, by summing
+    over every joint firing outcome (2^(len(p) * b) of them): no closed form."""
+    import itertools
+    n = len(p)
+    total = 0.0
+    for bits in itertools.product((0, 1), repeat=n * b):
+        prob = 1.0
+        for k, on in enumerate(bits):
+            pk = p[k % n]
+            prob *= pk if on else 1.0 - pk
+        touched = sum(1 for i in range(n) if any(bits[t * n + i] for t in range(b)))
+        total += prob * touched / n
+    return total
+
+
+def test_dense_min_batch_matches_enumeration(L):
+    import activation_sparse_gemv_amd as m
+    counts = np.array([2, 1, 3], dtype=np.uint32)   # over 4 tokens: p = 0.5, 0.25, 0.75
+    u = [_enumerated_union_share([0.5, 0.25, 0.75], b) for b in (1, 2, 3, 4)]
+    assert all(u[k] < u[k + 1] for k in range(3))
+    assert abs(u[0] - 0.5) < 1e-12
+    for b in range(1, 5):
+        lo = u[b - 2] if b > 1 else 0.0
+        for c in (lo + 1e-6, (lo + u[b - 1]) / 2, u[b - 1] - 1e-6):
+            assert m.sfnn_dense_min_batch(counts, 4, 3, c, 64) == b, (b, c)
+    # beyond max_batch: never
+    assert m.sfnn_dense_min_batch(counts, 4, 3, (u[2] + u[3]) / 2, 3) == -1
+
+
+@pytest.mark.parametrize("k,n,c", [(1, 10, 0.45), (1, 20, 0.65), (3, 100, 0.5), (7, 70, 0.9)])
+def test_dense_min_batch_uniform_closed_form(L, k, n, c):
+    """Every neuron firing with p = k/n: the share after b tokens is
+    1 - (1 - p)^b, so the threshold is ceil(log(1 - c) / log(1 - p))."""
+    import math
+    import activation_sparse_gemv_amd as m
+    p = k / n
+    want = math.ceil(math.log(1 - c) / math.log(1 - p))
+    assert abs(math.log(1 - c) / math.log(1 - p) - round(math.log(1 - c) / math.log(1 - p))) > 1e-6
+    counts = np.full(2048, k, dtype=np.uint32)
+    assert m.sfnn_dense_min_batch(counts, n, 2048, c, 4096) == want
+    assert m.sfnn_dense_min_batch(counts, n, 2048, c, want - 1) == -1
+
+
+def test_dense_min_batch_special_profiles(L):
+    import activation_sparse_gemv_amd as m
+    f = 1024
+    half = np.zeros(f, dtype=np.uint32)
+    half[: f // 2] = 50                      # half always fire, half never: the share is 1/2 at any batch
+    assert m.sfnn_dense_min_batch(half, 50, f, 0.5, 1000) == 1
+    assert m.sfnn_dense_min_batch(half, 50, f, 0.5001, 1000) == -1
+    assert m.sfnn_dense_min_batch(np.zeros(f, dtype=np.uint32), 10, f, 1e-6, 1000) == -1   # nothing fires
+    assert m.sfnn_dense_min_batch(np.full(f, 10, dtype=np.uint32), 10, f, 1.0, 1) == 1    # everything fires
+    # same mean rate, power law vs uniform: the power law's union grows slower
+    rng = np.random.default_rng(5)
+    w = 1.0 / np.arange(1, f + 1) ** 0.9
+    pz = np.minimum(w * (0.1 * f / w.sum()), 1.0)
+    zipf = np.round(pz * 1000).astype(np.uint32)
+    uni = np.full(f, int(round(zipf.mean())), dtype=np.uint32)
+    rng.shuffle(zipf)
+    assert m.sfnn_dense_min_batch(zipf, 1000, f, 0.45, 4096) > m.sfnn_dense_min_batch(uni, 1000, f, 0.45, 4096)
+
+
+def test_dense_min_batch_rejects_bad_arguments(L):
+    c = np.full(64, 3, dtype=np.uint32)
+    out = ctypes.c_int32(77)
+    cp = c.ctypes.data
+    fn = L.sfnn_dense_min_batch
+    assert fn(None, 10, 64, ctypes.c_float(0.5), 8, ctypes.byref(out)) == 1
+    assert fn(cp, 10, 64, ctypes.c_float(0.5), 8, None) == 1
+    for n, f, cr, mb in [(0, 64, 0.5, 8), (10, 0, 0.5, 8), (10, 64, 0.5, 0), (10, 64, 0.0, 8), (10, 64, 1.5, 8),
+                         (10, 64, float("nan"), 8), (2, 64, 0.5, 8)]:   # the last: counts 3 > 2 profiled tokens
+        assert fn(cp, n, f, ctypes.c_float(cr), mb, ctypes.byref(out)) == 2, (n, f, cr, mb)
+    assert out.value == 77

@@ -5,7 +5,9 @@ of d_ff and the calls run the dense FFN instead (53ai.com sparsity survey,
 DejaVu section: contextual sparsity is per token, so a batch's union grows
 with its size).  The dense FFN is the masked FFN under an all-ones mask, so
 the oracle here is oracle.dense_ffn, and the reported mask / ids / count are
-the all-ones mask, 0..d_ff-1 and d_ff.
+the all-ones mask, 0..d_ff-1 and d_ff.  The switch is off unless the
+descriptor sets a positive threshold (the stack's per-layer mix is covered
+in test_gpu_stack.py).
 """
 import numpy as np
 import pytest
@@ -25,7 +27,7 @@ def _check_dense_report(out, B, f):
     assert out["count"] == f and np.array_equal(out["ids"], np.arange(f, dtype=np.int32))
 
 
-def _dense_layer_case(lay, x, dense_min_batch=0, check_tokens=None):
+def _dense_layer_case(lay, x, dense_min_batch=16, check_tokens=None):
     f = lay.spec.d_ff
     B = x.shape[0]
     pred, ffn = upload_layer(lay)
@@ -42,7 +44,7 @@ def _dense_layer_case(lay, x, dense_min_batch=0, check_tokens=None):
 
 
 @pytest.mark.parametrize("wtype,act", [("f16", "relu"), ("f16", "reglu"), ("i4g128", "relu"), ("f32", "relu")])
-def test_layer_switches_at_default_batch(wtype, act):
+def test_layer_switches_at_threshold(wtype, act):
     spec = synth.config("c4" if act == "reglu" else "c2", d_model=512, d_ff=2048, rank=64, wtype=wtype,
                         pred_dtype="f32" if wtype == "f32" else "f16")
     lay = synth.make_layer(spec, layer=0)
@@ -50,24 +52,29 @@ def test_layer_switches_at_default_batch(wtype, act):
     _dense_layer_case(lay, x)
 
 
-def test_layer_below_default_batch_stays_sparse():
+@pytest.mark.parametrize("thr,B", [(16, 15), (0, 40)])
+def test_layer_below_threshold_or_default_stays_sparse(thr, B):
     spec = synth.config("c2", d_model=512, d_ff=2048, rank=64)
     lay = synth.make_layer(spec, layer=0)
-    x = synth.make_tokens(spec, 15, stream=301)
+    x = synth.make_tokens(spec, B, stream=301)
     pred, ffn = upload_layer(lay)
+    pred.dense_min_batch = thr
     out = gpu_layer(pred, ffn, x)
     ol, ob = oracle.predict(lay.w1_t, lay.w2_t, lay.tau, x)
     band = oracle.guard_band(lay.w1_t, lay.w2_t, x)
     gb = oracle.unpack_mask(out["mask"], 2048)
     outside = np.abs(ol - lay.tau[None, :].astype(np.float64)) > band
     assert not ((gb != ob) & outside).any()
-    assert out["count"] < 2048  # the predictor's union, not every neuron
+    rid, rc, _ = oracle.compact(out["mask"], B, 2048)
+    assert out["count"] == rc and np.array_equal(out["ids"][:rc], rid)
+    assert not gb.all()  # the predictor's masks, not all ones
     ref = oracle.masked_ffn(lay, x, out["mask"])
-    for b in range(15):
+    for b in range(B):
         assert rel_err(out["y"][b], ref[b]) <= TOL, b
 
 
-@pytest.mark.parametrize("thr,B,dense", [(4, 4, True), (4, 3, False), (-1, 40, False), (40, 40, True)])
+@pytest.mark.parametrize("thr,B,dense", [(4, 4, True), (4, 3, False), (-1, 40, False), (0, 40, False),
+                                         (40, 40, True), (1, 1, True)])
 def test_layer_threshold_field(thr, B, dense):
     spec = synth.config("c5", d_model=768, d_ff=3072, rank=64)
     lay = synth.make_layer(spec, layer=1)
@@ -79,8 +86,8 @@ def test_layer_threshold_field(thr, B, dense):
     pred.dense_min_batch = thr
     out = gpu_layer(pred, ffn, x)
     rid, rc, _ = oracle.compact(out["mask"], B, 3072)
-    assert out["count"] == rc and np.array_equal(out["ids"], rid)
-    assert rc < 3072
+    assert out["count"] == rc and np.array_equal(out["ids"][:rc], rid)
+    assert not oracle.unpack_mask(out["mask"], 3072).all()
     ref = oracle.masked_ffn(lay, x, out["mask"])
     for b in (0, B - 1):
         assert rel_err(out["y"][b], ref[b]) <= TOL, b
@@ -112,6 +119,8 @@ def test_stack_dense(cfg, B, lookahead):
     L = 3
     lays = [synth.make_layer(spec, layer=l, seed=5) for l in range(L)]
     dev = [upload_layer(lay) for lay in lays]
+    for pred, _ in dev:
+        pred.dense_min_batch = 16
     r_in = synth.make_tokens(spec, B, stream=310 + B, dtype=np.float32) * np.float32(3.0)
     out = gpu_stack(dev, r_in, 1e-6, torch.float16, flags=1 if lookahead else 0)
     f = spec.d_ff

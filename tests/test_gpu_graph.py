@@ -48,6 +48,7 @@ def test_graph_layer(B):
     spec = synth.config("c2", d_model=1024, d_ff=4096, rank=128)
     lay = synth.make_layer(spec, layer=0)
     pred, ffn = upload_layer(lay)
+    pred.dense_min_batch = 16
     f, d = spec.d_ff, spec.d_model
     x = torch.empty((B, d), dtype=torch.float16, device="cuda")
     y = torch.empty((B, d), dtype=torch.float32, device="cuda")
@@ -155,6 +156,7 @@ def test_graph_layer_dense_switch(wtype):
     spec = synth.config("c2", d_model=512, d_ff=2048, rank=64, wtype=wtype)
     lay = synth.make_layer(spec, layer=0)
     pred, ffn = upload_layer(lay)
+    pred.dense_min_batch = 16
     f, d = spec.d_ff, spec.d_model
     x = torch.empty((B, d), dtype=torch.float16, device="cuda")
     y = torch.empty((B, d), dtype=torch.float32, device="cuda")
@@ -171,11 +173,16 @@ def test_graph_layer_dense_switch(wtype):
     _replays(run, lambda a: x.copy_(to_dev(a)), inputs)
 
 
-def test_graph_stack_dense_switch():
+@pytest.mark.parametrize("dense_layers", [(0, 1, 2), (1,)])
+def test_graph_stack_dense_switch(dense_layers):
+    """Every layer dense, or one dense layer between sparse ones (the
+    look-ahead schedule then runs stage by stage)."""
     B = 20
     spec = synth.config("c2", d_model=768, d_ff=3072, rank=96, n_layers=3)
     lays = [synth.make_layer(spec, layer=l) for l in range(3)]
     dev = [upload_layer(l) for l in lays]
+    for l, (pred, _) in enumerate(dev):
+        pred.dense_min_batch = 16 if l in dense_layers else 0
     st = sg.Stack(dev)
     d, f = spec.d_model, spec.d_ff
     r_in = torch.empty((B, d), dtype=torch.float32, device="cuda")

@@ -21,13 +21,15 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3
 
 
-def _stack_case(spec, L, B, seed=0, lookahead=False, mfma_min_batch=0, hot_prefix=0):
+def _stack_case(spec, L, B, seed=0, lookahead=False, mfma_min_batch=0, hot_prefix=0, dense_layers=()):
+    """dense_layers: layers whose dense switch is set at this batch (the
+    others stay sparse)."""
     lays = [synth.make_layer(spec, layer=l, seed=seed) for l in range(L)]
     dev = [upload_layer(lay) for lay in lays]
-    for pred, ffn in dev:
+    for l, (pred, ffn) in enumerate(dev):
         ffn.mfma_min_batch = mfma_min_batch
         pred.hot_prefix = hot_prefix
-        pred.dense_min_batch = -1  # the sparse path at every batch
+        pred.dense_min_batch = B if l in dense_layers else -1
     r_in = synth.make_tokens(spec, B, stream=200 + B, dtype=np.float32) * np.float32(3.0)
     xdt = torch.float32 if spec.wtype == "f32" else torch.float16
     out = gpu_stack(dev, r_in, 1e-6, xdt, flags=1 if lookahead else 0)
@@ -40,6 +42,17 @@ def _stack_case(spec, L, B, seed=0, lookahead=False, mfma_min_batch=0, hot_prefi
         assert rel_err(x, x_ref) <= (1e-6 if spec.wtype == "f32" else 1e-3), l
         xs = x.astype(spec.x_dtype)
         assert np.array_equal(xs.astype(np.float32), x)
+        if l in dense_layers:
+            # no predictor: all-ones mask, every id, the dense FFN
+            assert np.array_equal(out["mask"][l], np.full((B, f // 64), np.uint64(2 ** 64 - 1))), l
+            assert out["count"][l] == f and np.array_equal(out["ids"][l], np.arange(f, dtype=np.int32)), l
+            ref = oracle.dense_ffn(lay, xs)
+            for b in range(B):
+                assert rel_err(out["y"][l][b], ref[b]) <= TOL, (l, b)
+            one = gpu_layer(dev[l][0], dev[l][1], xs)
+            assert np.array_equal(one["y"], out["y"][l]), l
+            r = (r + out["y"][l]).astype(np.float32)
+            continue
         # mask: threshold of the predictor on its input (x_l, or x_{l-1} when
         # looking ahead), outside the fp32 rounding band
         xp = xs if (not lookahead or l == 0) else out["x"][l - 1].astype(spec.x_dtype)
@@ -156,6 +169,31 @@ def test_stack_hot_prefix(B):
 def test_stack_lookahead_hot_prefix(B):
     _stack_case(synth.config("c2", d_model=1024, d_ff=4096, rank=128, n_layers=3), 3, B, lookahead=True,
                 hot_prefix=1024)
+
+
+# per-layer dense switch: a step mixes dense layers (no predictor) with
+# sparse ones; with look-ahead, a sparse layer still predicts from the input
+# of the layer before it, dense or not
+@pytest.mark.parametrize("lookahead", [False, True])
+@pytest.mark.parametrize("B,dense_layers", [(1, (1,)), (2, (0, 2)), (4, (1, 3)), (9, (0,)), (9, (3,))])
+def test_stack_mixed_dense_fp16(B, dense_layers, lookahead):
+    _stack_case(synth.config("c2", d_model=1024, d_ff=4096, rank=128, n_layers=4), 4, B, lookahead=lookahead,
+                dense_layers=dense_layers)
+
+
+@pytest.mark.parametrize("B,dense_layers", [(1, (0,)), (3, (1,))])
+def test_stack_mixed_dense_int4_lookahead(B, dense_layers):
+    _stack_case(synth.config("c5", d_model=1536, d_ff=3072, rank=128, n_layers=3), 3, B, lookahead=True,
+                dense_layers=dense_layers)
+
+
+def test_stack_mixed_dense_fp32_lookahead():
+    _stack_case(synth.config("c1", n_layers=3), 3, 2, lookahead=True, dense_layers=(1,))
+
+
+def test_stack_mixed_dense_reglu_hot_prefix_lookahead():
+    _stack_case(synth.config("c4", d_model=768, d_ff=2048, rank=64, n_layers=3), 3, 2, lookahead=True,
+                hot_prefix=512, dense_layers=(2,))
 
 
 def test_stack_bad_flags_rejected():
