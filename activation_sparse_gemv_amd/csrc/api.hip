@@ -596,8 +596,8 @@ size_t sfnn_isg_workspace_bytes(const sfnn_isg* op, int32_t batch) {
 namespace {
 
 // The input-sparse GEMV once the arguments are checked; w: its workspace.
-sfnn_status run_isg(const sfnn_isg* op, const void* x, int32_t batch, float* y, int32_t* cols, int32_t* count,
-                    char* w, const IsgLayout& Lw, hipStream_t s, bool listed = false) {
+IsgLaunch isg_launch_of(const sfnn_isg* op, const void* x, int32_t batch, float* y, int32_t* cols, int32_t* count,
+                        char* w, const IsgLayout& Lw, bool listed) {
   IsgLaunch L;
   L.listed = listed;
   L.wt = op->wtype == SFNN_F32 ? WT_F32 : WT_F16;
@@ -617,7 +617,12 @@ sfnn_status run_isg(const sfnn_isg* op, const void* x, int32_t batch, float* y, 
     L.hbuf = w + Lw.hbuf;
     L.sidbuf = reinterpret_cast<int32_t*>(w + Lw.sid);
   }
-  return hip_status(launch_isg(L, s));
+  return L;
+}
+
+sfnn_status run_isg(const sfnn_isg* op, const void* x, int32_t batch, float* y, int32_t* cols, int32_t* count,
+                    char* w, const IsgLayout& Lw, hipStream_t s, bool listed = false) {
+  return hip_status(launch_isg(isg_launch_of(op, x, batch, y, cols, count, w, Lw, listed), s));
 }
 
 // Head-gated projections: shapes the kernels and the input-sparse GEMV accept.
@@ -698,6 +703,10 @@ sfnn_status sfnn_head_out(const sfnn_heads* op, const void* attn, int32_t batch,
   char* w = (char*)ws;
   const hipStream_t s = as_stream(stream);
   const IsgLayout Lw = isg_layout(&g, batch);
+  // one launch where the GEMV's workgroups can list the heads' rows
+  // themselves; else the gate (gated copy + row list) and the GEMV
+  const IsgLaunch one = isg_launch_of(&g, attn, batch, y, nullptr, nullptr, w + gated, Lw, true);
+  if (isg_single_launch(one)) return hip_status(launch_isg_heads(one, head_mask, op->n_heads, op->head_dim, s));
   int32_t* ids = reinterpret_cast<int32_t*>(w + gated + Lw.ids);
   int32_t* cnt = reinterpret_cast<int32_t*>(w + gated + Lw.count);
   if (launch_head_gate(wt, attn, batch, op->n_heads, op->head_dim, head_mask, w, ids, cnt, s) != hipSuccess)

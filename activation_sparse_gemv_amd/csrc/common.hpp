@@ -445,4 +445,54 @@ __device__ __forceinline__ void pred2_hot_word(uint64_t* mask, uint64_t* union_m
   if (threadIdx.x == 0) union_mask[vb] = ~0ull;
 }
 
+// Slots s0 .. s0 + N - 1 of the union's ascending neuron list, and |U|, from
+// the union mask words um[0 .. words) (words <= 1024), for a workgroup of 512
+// threads: each thread takes two words; popcounts, a workgroup prefix sum (a
+// lane scan per wavefront, the 8 wavefront totals through LDS), then the
+// threads whose words hold ranks in [s0, s0 + N) write those neuron ids to
+// ids[rank - s0]; ids past |U| stay -1.  ids: N ints of LDS, s_wt: 8.  Every
+// thread calls it; on return ids and the count are the whole workgroup's.
+// (The FFN's compaction inside its first matrix-core kernel: no separate
+// compaction launch between the predictor and the FFN.)
+template <int N>
+__device__ __forceinline__ int union_window(const uint64_t* __restrict__ um, int words, int s0, int* ids, int* s_wt) {
+  static_assert(N <= 512, "one id per thread at most");
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int w0 = 2 * tid;
+  const uint64_t a0 = w0 < words ? um[w0] : 0ull;
+  const uint64_t a1 = w0 + 1 < words ? um[w0 + 1] : 0ull;
+  const int c0 = __popcll(a0), c = c0 + __popcll(a1);
+  int incl = c;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == kWave - 1) s_wt[wave] = incl;
+  if (tid < N) ids[tid] = -1;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const int v = s_wt[w];
+    before += w < wave ? v : 0;
+    total += v;
+  }
+  const int r0 = before + incl - c;  // rank of a0's lowest set bit
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint64_t word = h ? a1 : a0;
+    int rank = h ? r0 + c0 : r0;
+    if (rank < s0 + N && rank + __popcll(word) > s0) {
+      while (word && rank < s0 + N) {
+        if (rank >= s0) ids[rank - s0] = 64 * (w0 + h) + __builtin_ctzll(word);
+        ++rank;
+        word &= word - 1;
+      }
+    }
+  }
+  __syncthreads();
+  return total;
+}
+
 }  // namespace sfnn

@@ -33,8 +33,22 @@
 
 namespace sfnn {
 
-// Source of the coefficient of slot j for token t.
-enum { CO_H = 0, CO_X16 = 1, CO_X32 = 2 };  // h[t][j] fp32 | x[t][row_j] fp16 | fp32
+// Source of the coefficient of slot j for token t: h[t][j] fp32 | x[t][row_j]
+// fp16 | fp32 | the same x entries taken only where the row's head (row_j /
+// hd) is on for token t, else 0 (a select: the entries of heads that are off
+// may hold anything).
+enum { CO_H = 0, CO_X16 = 1, CO_X32 = 2, CO_X16H = 3, CO_X32H = 4 };
+
+// A row list a workgroup builds in its own LDS (the input-sparse GEMV's
+// single-launch form): the count in the first word of the dynamic LDS, the
+// 16-bit row ids from byte 16 on.
+__device__ __forceinline__ int* lds_list_base() {
+  extern __shared__ __align__(16) int lds_dyn[];
+  return lds_dyn;
+}
+__device__ __forceinline__ uint16_t* lds_list_ids() { return reinterpret_cast<uint16_t*>(lds_list_base() + 4); }
+// The packed form (one token): entry j = row id | fp16 coefficient bits << 16.
+__device__ __forceinline__ uint32_t* lds_list_packed() { return reinterpret_cast<uint32_t*>(lds_list_base() + 4); }
 
 struct DownArgs {
   const uint8_t* w;      // [n_rows][d] storage rows (INT4: [n_rows][d/2] nibbles)
@@ -54,6 +68,8 @@ struct DownArgs {
   int rg;                // row groups (>= 1)
   float* part;           // rg > 1: partial rows [rg][batch][d] (k_sum's layout)
   int batch;             // tokens of the whole call (the partial rows' stride)
+  const uint32_t* hmask; // CO_X16H / CO_X32H: per-token head bits [B][hw32] (32-bit words)
+  int hd, hw32;          // rows per head, 32-bit mask words per token
 };
 
 template <int WT>
@@ -91,6 +107,12 @@ constexpr int kDownThreads = 512;
 template <int WT, int NT>
 constexpr int down_kb() { return (NT <= 2 && NT * cols_per_vec<WT>() <= 32) ? SFNN_DOWN_KB : 4; }
 
+// The LDS-list kernels' loop: 1, batches (loop_batches); 0, the prefetching
+// loop of the other kernels.
+#ifndef SFNN_DOWN_BATCHES
+#define SFNN_DOWN_BATCHES 1
+#endif
+
 template <int WT, int NT, int LPR>
 struct DownRed {
   static constexpr int CPL = cols_per_vec<WT>();
@@ -109,11 +131,17 @@ struct DownRed {
 //   finish()  the reduction and y / the residual row.
 // LISTED: rows come from a.ids (else slot j is row j), a compile-time choice
 // so the id loads are never inside a branch (a load in a branch makes every
-// later wait cover all loads in flight).  Every load is unconditional: slots
-// past the count read row 0's tile and are cancelled at use, and the loop
-// leaves by break.
-template <int WT, int NT, int LPR, int CO, bool LISTED>
+// later wait cover all loads in flight).  LDSL: the ids and the count come
+// from the workgroup's own LDS list instead (lds_list_base): 1, 16-bit ids;
+// 2, packed entries that carry the one token's coefficient too, so the loop's
+// only global loads are weights.  Every load is unconditional: slots past the
+// count read row 0's tile and are cancelled at use, and the loop leaves by
+// break.
+template <int WT, int NT, int LPR, int CO, bool LISTED, int LDSL = 0>
 struct DownTile {
+  static_assert(LDSL != 2 || (NT == 1 && WT == WT_F16 && (CO == CO_X16 || CO == CO_X16H)),
+                "packed list entries carry one fp16 coefficient");
+  static constexpr bool HEADS = CO == CO_X16H || CO == CO_X32H;
   static constexpr int CPL = cols_per_vec<WT>();
   static constexpr int NW = kDownThreads / kWave;
   static constexpr int RPW = kWave / LPR;  // rows per wavefront per step
@@ -127,6 +155,7 @@ struct DownTile {
   u32x4 wv[2][KB];      // weights of the chunk in use and the next one
   float hv[2][KB][NT];  // coefficients
   float sv[2][KB];      // INT4 scales
+  uint32_t hb[2][KB][HEADS ? NT : 1];  // CO_X16H / CO_X32H: the mask word holding the row's head bit
   float acc[NT][CPL];
   float sb[WT == WT_I4 ? NT : 1];
 
@@ -144,7 +173,10 @@ struct DownTile {
     sgrp = col / 128;
     ngrp = a.d / 128;
     int na = a.n_slots;
-    if (a.count) {
+    if constexpr (LDSL) {
+      const int cn = lds_list_base()[0];
+      na = cn < 0 ? 0 : (cn > a.n_slots ? a.n_slots : cn);
+    } else if (a.count) {
       const int cn = *a.count;
       na = cn < 0 ? 0 : (cn > a.n_slots ? a.n_slots : cn);
     }
@@ -164,6 +196,14 @@ struct DownTile {
     }
   }
 
+  // the row of an id register (packed entries: the low 16 bits)
+  __device__ __forceinline__ static int row_of(int e) {
+    if constexpr (LDSL == 2)
+      return e & 0xffff;
+    else
+      return e;
+  }
+
   // slot of the run's j-th entry, clamped into the run (an empty run: j0)
   __device__ __forceinline__ int slot_clamp(const DownArgs& a, int j) const {
     const int s = j0 + (j < n ? j : (n > 0 ? n - 1 : 0));
@@ -177,7 +217,11 @@ struct DownTile {
     for (int k = 0; k < KB; ++k) {
       const int j = j0 + (ch * KB + k) * RPS + rr;
       const int jc = j < a.n_slots ? j : a.n_slots - 1;
-      if constexpr (LISTED)
+      if constexpr (LDSL == 2)
+        dst[k] = (int)lds_list_packed()[jc];
+      else if constexpr (LDSL == 1)
+        dst[k] = lds_list_ids()[jc];
+      else if constexpr (LISTED)
         dst[k] = a.ids[jc];
       else
         dst[k] = jc;
@@ -185,10 +229,11 @@ struct DownTile {
   }
 
   __device__ __forceinline__ void issue_w(const DownArgs& a, int ch, const int (&id)[KB], u32x4 (&w)[KB],
-                                          float (&h)[KB][NT], float (&sc)[KB]) const {
+                                          float (&h)[KB][NT], float (&sc)[KB],
+                                          uint32_t (&hbw)[KB][HEADS ? NT : 1]) const {
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
-      const int i = id[k];
+      const int i = row_of(id[k]);
       const bool live = (ch * KB + k) * RPS + rr < n;
       const int ic = (live && (unsigned)i < (unsigned)a.n_rows) ? i : 0;
       // a plain (cached) load: the other tiles of this 128-byte line are
@@ -203,26 +248,36 @@ struct DownTile {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int tc = t < a.nt ? a.tok0 + t : a.tok0;
+        if constexpr (LDSL == 2) {
+          h[k][t] = (float)__builtin_bit_cast(f16, (uint16_t)((uint32_t)id[k] >> 16));
+          continue;  // the coefficient came with the id (the row's head is on)
+        }
         if constexpr (CO == CO_H) {
           h[k][t] = reinterpret_cast<const float*>(a.co)[(size_t)tc * a.co_stride + jc];
-        } else if constexpr (CO == CO_X16) {
+        } else if constexpr (CO == CO_X16 || CO == CO_X16H) {
           h[k][t] = (float)reinterpret_cast<const f16*>(a.co)[(size_t)tc * a.co_stride + ic];
         } else {
           h[k][t] = reinterpret_cast<const float*>(a.co)[(size_t)tc * a.co_stride + ic];
         }
+        if constexpr (HEADS && LDSL != 2) hbw[k][t] = a.hmask[(size_t)tc * a.hw32 + (ic / a.hd >> 5)];
       }
     }
   }
 
   __device__ __forceinline__ void use(const DownArgs& a, int ch, const int (&id)[KB], const u32x4 (&w)[KB],
-                                      const float (&h)[KB][NT], const float (&sc)[KB]) {
+                                      const float (&h)[KB][NT], const float (&sc)[KB],
+                                      const uint32_t (&hbw)[KB][HEADS ? NT : 1]) {
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
       const int j = (ch * KB + k) * RPS + rr;
-      const bool ok = j < n && (unsigned)id[k] < (unsigned)a.n_rows;
+      const bool ok = j < n && (unsigned)row_of(id[k]) < (unsigned)a.n_rows;
       float hk[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) hk[t] = (ok && t < a.nt) ? h[k][t] : 0.0f;  // a select: nothing else enters
+      for (int t = 0; t < NT; ++t) {
+        bool on = ok && t < a.nt;
+        if constexpr (HEADS && LDSL != 2) on = on && ((hbw[k][t] >> ((id[k] / a.hd) & 31)) & 1u);
+        hk[t] = on ? h[k][t] : 0.0f;  // a select: nothing else enters
+      }
       if constexpr (WT == WT_I4) {
         // nibbles in offset binary (n = t + 8) enter as fp16 subnormals with
         // no conversion: masked in place in bits 0-3 of a half a nibble is the
@@ -289,29 +344,47 @@ struct DownTile {
     issue_ids(a, 1, idb[1]);
   }
 
-  __device__ __forceinline__ void first(const DownArgs& a) { issue_w(a, 0, idb[0], wv[0], hv[0], sv[0]); }
+  __device__ __forceinline__ void first(const DownArgs& a) { issue_w(a, 0, idb[0], wv[0], hv[0], sv[0], hb[0]); }
 
   // one chunk: idc holds chunk cc's ids (replaced by chunk cc+2's), idn chunk
   // cc+1's
   __device__ __forceinline__ void step(const DownArgs& a, int cc, int (&idc)[KB], const int (&idn)[KB],
                                        const u32x4 (&wc)[KB], const float (&hc)[KB][NT], const float (&sc)[KB],
-                                       u32x4 (&wn)[KB], float (&hn)[KB][NT], float (&sn)[KB]) {
+                                       const uint32_t (&bc)[KB][HEADS ? NT : 1], u32x4 (&wn)[KB],
+                                       float (&hn)[KB][NT], float (&sn)[KB], uint32_t (&bn)[KB][HEADS ? NT : 1]) {
     int cur[KB];
 #pragma unroll
     for (int k = 0; k < KB; ++k) cur[k] = idc[k];
     issue_ids(a, cc + 2, idc);
-    issue_w(a, cc + 1, idn, wn, hn, sn);
+    issue_w(a, cc + 1, idn, wn, hn, sn, bn);
     __builtin_amdgcn_sched_barrier(0);  // the next requests go out before this chunk is used
-    use(a, cc, cur, wc, hc, sc);
+    use(a, cc, cur, wc, hc, sc, bc);
   }
 
   // every chunk (at least one: with n = 0 it adds nothing)
   __device__ __forceinline__ void loop(const DownArgs& a) {
     for (int ch = 0;; ch += 2) {
-      step(a, ch, idb[0], idb[1], wv[0], hv[0], sv[0], wv[1], hv[1], sv[1]);
+      step(a, ch, idb[0], idb[1], wv[0], hv[0], sv[0], hb[0], wv[1], hv[1], sv[1], hb[1]);
       if (ch + 1 >= nch) break;
-      step(a, ch + 1, idb[1], idb[0], wv[1], hv[1], sv[1], wv[0], hv[0], sv[0]);
+      step(a, ch + 1, idb[1], idb[0], wv[1], hv[1], sv[1], hb[1], wv[0], hv[0], sv[0], hb[0]);
       if (ch + 2 >= nch) break;
+    }
+  }
+
+  // The LDS-list form: batches of KB rows per lane, ids (from LDS),
+  // weights and coefficients requested together and used at once; no
+  // requests carried from one batch to the next (a carried buffer makes the
+  // compiler drain every load at the loop head anyway).
+  __device__ __forceinline__ void loop_batches(const DownArgs& a) {
+    for (int ch = 0; ch < nch; ++ch) {
+      int id[KB];
+      u32x4 w[KB];
+      float h[KB][NT];
+      float sc[KB];
+      uint32_t b[KB][HEADS ? NT : 1];
+      issue_ids(a, ch, id);
+      issue_w(a, ch, id, w, h, sc, b);
+      use(a, ch, id, w, h, sc, b);
     }
   }
 
@@ -382,14 +455,19 @@ struct DownTile {
   }
 };
 
-// One work item on its own (k_down).
-template <int WT, int NT, int LPR, int CO, bool LISTED>
+// One work item on its own (k_down; with LDSL, after the workgroup built its
+// row list).
+template <int WT, int NT, int LPR, int CO, bool LISTED, int LDSL = 0>
 __device__ __forceinline__ void down_body(const DownArgs& a, int tile, int grp, float* red) {
-  DownTile<WT, NT, LPR, CO, LISTED> D;
+  DownTile<WT, NT, LPR, CO, LISTED, LDSL> D;
   D.count(a, tile, grp, true);
-  D.ids01(a);
-  D.first(a);
-  D.loop(a);
+  if constexpr (LDSL != 0 && SFNN_DOWN_BATCHES) {
+    D.loop_batches(a);
+  } else {
+    D.ids01(a);
+    D.first(a);
+    D.loop(a);
+  }
   D.finish(a, red, true);
 }
 

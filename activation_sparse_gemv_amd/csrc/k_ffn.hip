@@ -168,6 +168,7 @@ DownArgs ffn_down_args(const FfnLaunch& p) {
   a.rg = 1;
   a.part = p.partial;
   a.batch = p.batch;
+  a.hmask = nullptr;
   return a;
 }
 

@@ -43,6 +43,9 @@ struct MfmaUpArgs {
   const f16* x;                // [B][d]
   const int32_t* ids;          // compacted ids, or null: slot s is neuron s
   const int32_t* count;        // |U|, or null: f
+  const uint64_t* union_mask;  // or: the union's mask words, compacted here (ids / count unused)
+  int32_t* ids_out;            // with union_mask: the union's ids (each workgroup its slots) or null
+  int32_t* count_out;          // with union_mask: |U| (workgroup 0), read by k_down_mfma
   const uint64_t* mask;        // per-token gate [B][f/64] or null
   float* h;                    // [32][f] this pass's h, token-major, slot-contiguous
   float* hmax;                 // [f / 32][32] largest |h| of each 32-slot step and token
@@ -113,9 +116,16 @@ __global__ __launch_bounds__(512) void k_up_mfma(MfmaUpArgs a) {
   constexpr int NM = ACT == ACT_REGLU ? 2 : 1;
   __shared__ f32x4 red[8][2][NB][kWave];  // one matrix's blocks at a time
   __shared__ int s_id[kUpSlots];
+  __shared__ int s_ul[kUpSlots], s_wt[8];  // the union's slots of this workgroup, scan totals
   __shared__ uint32_t s_hm[32];  // largest |h| per token (fp32 bits: non-negative floats order as integers)
-  const int cnt = slot_count(a.count, a.f);
   const int s0 = blockIdx.x * kUpSlots;
+  int cnt;
+  if (a.union_mask) {  // uniform over the launch
+    cnt = union_window<kUpSlots>(a.union_mask, a.f >> 6, s0, s_ul, s_wt);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.count_out = cnt;
+  } else {
+    cnt = slot_count(a.count, a.f);
+  }
   if (s0 >= cnt) return;  // the whole workgroup
   if (threadIdx.x < 32) s_hm[threadIdx.x] = 0u;  // ordered before the maxima by the sums' barriers
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -123,8 +133,11 @@ __global__ __launch_bounds__(512) void k_up_mfma(MfmaUpArgs a) {
   const int d = a.d;
   // Slots past |U| and ids outside [0, f) are dropped (h = 0); they re-read
   // the last listed row, so no row outside the list is touched.
+  // (compacted here: the workgroup's first slot, a listed row)
   int pad = 0;
-  if (a.ids) {
+  if (a.union_mask) {
+    pad = s_ul[0];
+  } else if (a.ids) {
     const int v = a.ids[cnt - 1];
     pad = v >= 0 && v < a.f ? v : 0;
   }
@@ -132,12 +145,13 @@ __global__ __launch_bounds__(512) void k_up_mfma(MfmaUpArgs a) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int s = s0 + t * 16 + r;
-    int id = s < cnt ? (a.ids ? a.ids[s] : s) : -1;
+    int id = a.union_mask ? s_ul[t * 16 + r] : (s < cnt ? (a.ids ? a.ids[s] : s) : -1);
     if (id >= a.f) id = -1;
     const int idc = id < 0 ? pad : id;
     if (wave == 0 && g == 0) {
       s_id[t * 16 + r] = id;
       a.sid[s] = idc;
+      if (a.union_mask && a.ids_out && s < cnt) a.ids_out[s] = id;
     }
     wr[0][t] = a.w_up + (size_t)idc * d + 8 * g;
     if constexpr (NM == 2) wr[1][t] = a.w_gate + (size_t)idc * d + 8 * g;
@@ -407,7 +421,7 @@ int mfma_groups(int d, int max_groups) {
 
 template <int ACT, int NB>
 static void mfma_pass(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int tok0, int nt, int kg,
-                      hipStream_t s) {
+                      hipStream_t s, const uint64_t* union_mask) {
   MfmaUpArgs u;
   u.w_up = (const f16*)p.w_up;
   u.w_gate = (const f16*)p.w_gate;
@@ -416,6 +430,9 @@ static void mfma_pass(const FfnLaunch& p, const int32_t* ids, const int32_t* cou
   u.x = (const f16*)p.x;
   u.ids = ids;
   u.count = count;
+  u.union_mask = union_mask;
+  u.ids_out = p.ids_out;
+  u.count_out = p.count_out;
   u.mask = p.mask;
   u.h = (float*)p.hbuf;
   u.hmax = p.hmax;
@@ -463,14 +480,15 @@ void launch_rows_mfma(const void* w_t, const int32_t* sid, const int32_t* count,
 }
 
 template <int ACT>
-static void mfma_all(const FfnLaunch& p, const int32_t* ids, const int32_t* count, hipStream_t s) {
+static void mfma_all(const FfnLaunch& p, const int32_t* ids, const int32_t* count, hipStream_t s,
+                     const uint64_t* union_mask) {
   const int kg = mfma_groups(p.d, kMfmaPartRows);
   for (int tok0 = 0; tok0 < p.batch; tok0 += 32) {
     const int nt = p.batch - tok0 < 32 ? p.batch - tok0 : 32;
     if (nt > 16)
-      mfma_pass<ACT, 2>(p, ids, count, tok0, nt, kg, s);
+      mfma_pass<ACT, 2>(p, ids, count, tok0, nt, kg, s, union_mask);
     else
-      mfma_pass<ACT, 1>(p, ids, count, tok0, nt, kg, s);
+      mfma_pass<ACT, 1>(p, ids, count, tok0, nt, kg, s, union_mask);
   }
 }
 
@@ -481,22 +499,25 @@ hipError_t launch_ffn_mfma(const FfnLaunch& p, hipStream_t s) {
     const int kg = mfma_groups(p.d, kMfmaPartRows);
     if ((p.f / 32 + kg - 1) / kg * 32 > kMfmaI4MaxGroupSlots) return hipErrorInvalidValue;  // not for d_ff <= 65536
   }
-  if (p.src == SRC_UNION) {
-    // the union's ids in ascending order (and |U|), as the FFN kernels write them
-    const hipError_t e = launch_compact(p.union_mask, 1, p.f, p.ids_out, p.count_out, nullptr, s);
-    if (e != hipSuccess) return e;
-    ids = p.ids_out;
+  const uint64_t* um = nullptr;
+  if (p.src == SRC_UNION && p.count_out) {
+    // the union compacted inside the up kernel (each workgroup its slots):
+    // ids_out / count_out, which the down kernel then reads
+    um = p.union_mask;
     count = p.count_out;
+  } else if (p.src == SRC_UNION) {
+    // no place for |U| given: the compaction launch into the workspace
+    return hipErrorInvalidValue;
   } else if (p.src == SRC_IDS) {
     ids = p.ids;
     count = p.count;
   }
   if (p.wt == WT_I4)
-    mfma_all_i4(p, ids, count, mfma_groups(p.d, kMfmaPartRows), s);
+    mfma_all_i4(p, ids, count, mfma_groups(p.d, kMfmaPartRows), s, um);
   else if (p.act == ACT_RELU)
-    mfma_all<ACT_RELU>(p, ids, count, s);
+    mfma_all<ACT_RELU>(p, ids, count, s, um);
   else
-    mfma_all<ACT_REGLU>(p, ids, count, s);
+    mfma_all<ACT_REGLU>(p, ids, count, s, um);
   if (p.y || p.r_out) return launch_sum(p, mfma_groups(p.d, kMfmaPartRows), s);
   return hipGetLastError();
 }

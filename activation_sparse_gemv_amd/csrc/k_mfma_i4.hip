@@ -48,6 +48,9 @@ struct MfmaUpI4Args {
   const f16* x;                  // [B][d]
   const int32_t* ids;            // compacted ids, or null: slot s is neuron s
   const int32_t* count;          // |U|, or null: f
+  const uint64_t* union_mask;    // or: the union's mask words, compacted here (ids / count unused)
+  int32_t* ids_out;              // with union_mask: the union's ids (each workgroup its slots) or null
+  int32_t* count_out;            // with union_mask: |U| (workgroup 0), read by k_down_mfma_i4
   const uint64_t* mask;          // per-token gate [B][f/64] or null
   float* h;                      // [32][f] this pass's h, token-major, slot-contiguous
   float* hmax;                   // [f / 32][32] largest |h| of each 32-slot step and token
@@ -103,22 +106,33 @@ __global__ __launch_bounds__(512) void k_up_mfma_i4(MfmaUpI4Args a) {
   __shared__ int s_id[ROWS];   // neuron of each row, -1 for a dropped slot
   __shared__ int s_idc[ROWS];  // the row actually read (dropped slots: the pad row)
   __shared__ uint32_t s_hm[RT / 2][32];  // largest |h| per step and token (fp32 bits)
-  const int cnt = slot_count_i4(a.count, a.f);
+  __shared__ int s_ul[ROWS], s_wt[8];    // the union's slots of this workgroup, scan totals
   const int s0 = blockIdx.x * ROWS;
+  int cnt;
+  if (a.union_mask) {  // uniform over the launch
+    cnt = union_window<ROWS>(a.union_mask, a.f >> 6, s0, s_ul, s_wt);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.count_out = cnt;
+  } else {
+    cnt = slot_count_i4(a.count, a.f);
+  }
   if (s0 >= cnt) return;  // the whole workgroup
   if (threadIdx.x < RT / 2 * 32) s_hm[threadIdx.x / 32][threadIdx.x % 32] = 0u;  // before the first barrier
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   const int r = lane & 15, g = lane >> 4;
   const int d = a.d, G = d >> 7;
   // this lane's rows (one per tile); slots past |U| and ids outside [0, f)
-  // are dropped (h = 0) and re-read the last listed row.  All id loads go
-  // out together (slots past |U| re-read the last one).
+  // are dropped (h = 0) and re-read the last listed row (compacted here: the
+  // workgroup's first slot, a listed row).  All id loads go out together
+  // (slots past |U| re-read the last one).
   int raw[RT + 1];
 #pragma unroll
   for (int t = 0; t <= RT; ++t) {
     const int s = t < RT ? s0 + t * 16 + r : cnt - 1;
     const int sc = s < cnt ? s : cnt - 1;
-    raw[t] = a.ids ? a.ids[sc] : sc;
+    if (a.union_mask)
+      raw[t] = t < RT ? s_ul[t * 16 + r] : s_ul[0];
+    else
+      raw[t] = a.ids ? a.ids[sc] : sc;
   }
   const int pad = raw[RT] >= 0 && raw[RT] < a.f ? raw[RT] : 0;
   const uint8_t* wr[NM][RT];
@@ -132,6 +146,7 @@ __global__ __launch_bounds__(512) void k_up_mfma_i4(MfmaUpI4Args a) {
       s_id[t * 16 + r] = id;
       s_idc[t * 16 + r] = idc;
       if (s < a.f) a.sid[s] = idc;  // the last workgroup's rows may run past d_ff
+      if (a.union_mask && a.ids_out && s < cnt) a.ids_out[s] = id;
     }
     wr[0][t] = a.q_up + (size_t)idc * (d >> 1) + 16 * g;
     if constexpr (NM == 2) wr[1][t] = a.q_gate + (size_t)idc * (d >> 1) + 16 * g;
@@ -499,7 +514,7 @@ constexpr int up_rt_i4() { return (ACT == ACT_REGLU ? 4 : 8) / NB; }
 
 template <int ACT, int NB>
 static void mfma_pass_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int tok0, int nt, int kg,
-                         hipStream_t s) {
+                         hipStream_t s, const uint64_t* union_mask) {
   constexpr int RT = up_rt_i4<ACT, NB>();
   MfmaUpI4Args u;
   u.q_up = (const uint8_t*)p.w_up;
@@ -511,6 +526,9 @@ static void mfma_pass_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* 
   u.x = (const f16*)p.x;
   u.ids = ids;
   u.count = count;
+  u.union_mask = union_mask;
+  u.ids_out = p.ids_out;
+  u.count_out = p.count_out;
   u.mask = p.mask;
   u.h = (float*)p.hbuf;
   u.hmax = p.hmax;
@@ -538,21 +556,23 @@ static void mfma_pass_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* 
 }
 
 template <int ACT>
-static void mfma_all_i4_act(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int kg, hipStream_t s) {
+static void mfma_all_i4_act(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int kg, hipStream_t s,
+                            const uint64_t* union_mask) {
   for (int tok0 = 0; tok0 < p.batch; tok0 += 32) {
     const int nt = p.batch - tok0 < 32 ? p.batch - tok0 : 32;
     if (nt > 16)
-      mfma_pass_i4<ACT, 2>(p, ids, count, tok0, nt, kg, s);
+      mfma_pass_i4<ACT, 2>(p, ids, count, tok0, nt, kg, s, union_mask);
     else
-      mfma_pass_i4<ACT, 1>(p, ids, count, tok0, nt, kg, s);
+      mfma_pass_i4<ACT, 1>(p, ids, count, tok0, nt, kg, s, union_mask);
   }
 }
 
-void mfma_all_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int kg, hipStream_t s) {
+void mfma_all_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int kg, hipStream_t s,
+                 const uint64_t* union_mask) {
   if (p.act == ACT_RELU)
-    mfma_all_i4_act<ACT_RELU>(p, ids, count, kg, s);
+    mfma_all_i4_act<ACT_RELU>(p, ids, count, kg, s, union_mask);
   else
-    mfma_all_i4_act<ACT_REGLU>(p, ids, count, kg, s);
+    mfma_all_i4_act<ACT_REGLU>(p, ids, count, kg, s, union_mask);
 }
 
 }  // namespace sfnn

@@ -110,11 +110,18 @@ static void launch_b_lpr(const DownArgs& da, const DownShape& ds, const Pred2Arg
   }
 }
 
+// Down work items of launch B: 0, one row group of the narrowest tiles (y and
+// the residual row written directly); else whole 128-byte lines in row
+// groups aiming at this many items, their partial rows added by a sum launch
+// after it.
+#ifndef SFNN_LA_B_ITEMS
+#define SFNN_LA_B_ITEMS 0
+#endif
 template <int WT, int PWT, int NT2>
 static void launch_b(DownArgs da, int batch, const PredLaunch& next, hipStream_t s) {
   const int gp = next.f / 64;
-  const DownShape ds = down_shape(WT, da.d, batch, 0);  // one row group: y and the residual row directly
-  da.rg = 1;
+  const DownShape ds = down_shape(WT, da.d, batch, SFNN_LA_B_ITEMS);
+  da.rg = ds.rg;
   const Pred2Args pa = pred2_args(next, 0, next.batch);
   const int vpl = pred2_vpl(PWT, next.r);
   if (ds.nt == 1) {
@@ -126,6 +133,7 @@ static void launch_b(DownArgs da, int batch, const PredLaunch& next, hipStream_t
     else if (vpl == 2) launch_b_lpr<WT, 2, PWT, NT2, 2>(da, ds, pa, gp, s);
     else launch_b_lpr<WT, 2, PWT, NT2, 4>(da, ds, pa, gp, s);
   }
+  if (ds.rg > 1) (void)launch_down_sum(da, s);  // errors surface through hipGetLastError
 }
 
 template <int WT, int ACT>

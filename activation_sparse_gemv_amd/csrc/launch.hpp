@@ -104,7 +104,10 @@ hipError_t launch_ffn_mfma(const FfnLaunch& p, hipStream_t s);
 // scales); launch_ffn_mfma refuses a shape whose groups would hold more.
 constexpr int kMfmaI4MaxGroupSlots = 8192;
 // INT4 passes of that path (h in the workspace as fp32 [32][f]).
-void mfma_all_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int kg, hipStream_t s);
+// union_mask: the union compacted inside the up kernel (ids / count then the
+// launch's ids_out / count_out), else null.
+void mfma_all_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int kg, hipStream_t s,
+                 const uint64_t* union_mask);
 int ffn_groups(int d, int f);
 // The fixed-order sum of `rows` partial rows per token (p.partial) into y
 // and / or the residual add, with b_down.
@@ -153,6 +156,12 @@ struct IsgLaunch {
   int32_t* sidbuf = nullptr;  // matrix-core path: [n_in] slot -> input
 };
 hipError_t launch_isg(const IsgLaunch& p, hipStream_t s);
+// The single-launch form (each workgroup lists the rows itself) applies to p.
+bool isg_single_launch(const IsgLaunch& p);
+// Head-gated output projection in the single-launch form: the rows of the
+// heads some token uses, x[t][j] taken where head j / hd is on for token t
+// (isg_single_launch(p) must hold; p.x is the ungated attention output).
+hipError_t launch_isg_heads(const IsgLaunch& p, const uint64_t* head_mask, int H, int hd, hipStream_t s);
 
 // ---- head-gated attention projections ----------------------------------------
 

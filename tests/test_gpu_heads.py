@@ -104,3 +104,18 @@ def test_heads_deterministic():
     a = _case(4096, 32, 128, 8, 0.3, seed=11)
     b = _case(4096, 32, 128, 8, 0.3, seed=11)
     assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
+
+
+# The output projection runs as one launch (the GEMV's workgroups list the used
+# heads' rows and take each token's entries only where its head is on) up to
+# 16384 attention inputs on the per-row path; past that, the gate launch and
+# the GEMV.  Both sides, with unused heads' rows and off entries NaN-poisoned.
+@pytest.mark.parametrize("wtype,d,H,hd,B", [
+    ("f16", 1024, 96, 128, 1),    # OPT-175B's 96 heads of 128, d_model cut for the oracle
+    ("f16", 1024, 128, 128, 2),   # 16384 inputs: the largest single-launch list
+    ("f16", 1024, 130, 128, 1),   # 16640 inputs: gate + GEMV
+    ("f32", 1024, 64, 128, 6),    # fp32, 6 tokens in one pass
+    ("f16", 2048, 40, 8, 3),      # head_dim 8: 8 heads per mask word of 64 rows
+])
+def test_heads_out_single_launch_limits(wtype, d, H, hd, B):
+    _case(d, H, hd, B, 0.3, wtype=wtype, seed=H + B)

@@ -140,3 +140,41 @@ def test_isg_deterministic():
     a = _run(w_t, b, x)[0]
     c = _run(w_t, b, x)[0]
     assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+
+
+# Single-launch form: every workgroup lists the nonzero inputs itself (per-row
+# path, n_in <= 16384, no row groups); past those limits the mask, compaction
+# and GEMV launches.  Both sides of each limit, with the list reported.
+@pytest.mark.parametrize("wtype,n_in,n_out,B", [
+    ("f16", 16384, 256, 1),    # largest list the LDS holds
+    ("f16", 16448, 256, 1),    # one mask word more: three launches
+    ("f16", 8192, 16384, 2),   # long rows: 8192 x 128-byte tiles stay within one row group
+    ("f16", 9216, 12288, 1),   # 9216 x 128-byte tiles pass 1 MB: row groups, three launches
+    ("f32", 8192, 512, 8),     # fp32, eight tokens a pass
+    ("f32", 8192, 4352, 8),    # fp32 128-byte tiles x eight tokens: the largest reduction buffer
+    ("f16", 64, 128, 3),       # one mask word
+])
+def test_isg_single_launch_limits(wtype, n_in, n_out, B):
+    w_t, b, x = _case(n_in, n_out, B, 0.3, wtype, seed=n_in + B)
+    y, cols, c = _run(w_t, b, x)
+    ref, J = oracle.input_sparse_gemv(w_t, x, b)
+    assert c == len(J) and np.array_equal(cols[:c], J)
+    assert np.all(cols[c:] == -7)
+    for t in range(B):
+        assert rel_err(y[t], ref[t]) <= TOL, t
+
+
+def test_isg_single_launch_all_zero_and_nan_inputs():
+    """An all-zero batch lists nothing (y = bias bitwise); a NaN input is not a
+    zero, so its row is listed; -0.0 is a zero."""
+    w_t, b, x = _case(1024, 512, 1, 0.3, "f16", seed=71)
+    z = np.zeros_like(x)
+    y, cols, c = _run(w_t, b, z)
+    assert c == 0 and np.array_equal(y[0], b.astype(np.float32))
+    x2 = np.zeros_like(x)
+    x2[0, 5] = np.float16(-0.0)
+    x2[0, 700] = np.float16(np.nan)
+    x2[0, 1023] = np.float16(2.0)
+    y2, cols2, c2 = _run(w_t, b, x2)
+    assert c2 == 2 and np.array_equal(cols2[:2], [700, 1023])
+    assert np.isnan(y2[0]).all()

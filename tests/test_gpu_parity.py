@@ -289,6 +289,35 @@ def _layer_case(lay, x, check_tokens=None, max_flip_frac=1e-4, mfma_min_batch=0)
     return out
 
 
+# The matrix-core FFN compacts the union inside its first kernel (every
+# workgroup scans the mask words for its own slots): an empty union, a full
+# one, an odd number of mask words (d_ff 1088: 17), ragged last slots and
+# several 32-token passes, fp16 (32-slot workgroups) and INT4 (64- and
+# 128-slot workgroups).
+@pytest.mark.parametrize("wtype,act,B", [("f16", "relu", 8), ("f16", "reglu", 40), ("i4g128", "relu", 3),
+                                         ("i4g128", "relu", 20), ("i4g128", "reglu", 33)])
+@pytest.mark.parametrize("tau", ["empty", "full", "calibrated"])
+def test_layer_matrix_core_union_edges(wtype, act, B, tau):
+    spec = synth.config("c4" if act == "reglu" else "c2", d_model=640, d_ff=1088, rank=64, wtype=wtype, act=act)
+    lay = synth.make_layer(spec, layer=2)
+    f = spec.d_ff
+    if tau == "empty":
+        lay.tau = np.full(f, np.inf, dtype=np.float32)
+        lay.b_down = ((np.arange(spec.d_model) % 7 - 3) * 0.25).astype(lay.b_down.dtype)
+    elif tau == "full":
+        lay.tau = np.full(f, -np.inf, dtype=np.float32)
+    x = synth.make_tokens(spec, B, stream=120 + B)
+    out = _layer_case(lay, x)
+    if tau == "empty":
+        assert out["count"] == 0
+        assert np.array_equal(out["y"], np.tile(lay.b_down.astype(np.float32), (B, 1)))
+    elif tau == "full":
+        assert out["count"] == f and np.array_equal(out["ids"], np.arange(f, dtype=np.int32))
+        ref = oracle.dense_ffn(lay, x)
+        for b in range(B):
+            assert rel_err(out["y"][b], ref[b]) <= TOL, b
+
+
 def test_layer_opt125m_64_decode_vectors():
     spec = synth.config("c1")
     lay = synth.make_layer(spec, layer=0)
