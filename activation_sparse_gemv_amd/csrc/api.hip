@@ -703,10 +703,6 @@ sfnn_status sfnn_head_out(const sfnn_heads* op, const void* attn, int32_t batch,
   char* w = (char*)ws;
   const hipStream_t s = as_stream(stream);
   const IsgLayout Lw = isg_layout(&g, batch);
-  // one launch where the GEMV's workgroups can list the heads' rows
-  // themselves; else the gate (gated copy + row list) and the GEMV
-  const IsgLaunch one = isg_launch_of(&g, attn, batch, y, nullptr, nullptr, w + gated, Lw, true);
-  if (isg_single_launch(one)) return hip_status(launch_isg_heads(one, head_mask, op->n_heads, op->head_dim, s));
   int32_t* ids = reinterpret_cast<int32_t*>(w + gated + Lw.ids);
   int32_t* cnt = reinterpret_cast<int32_t*>(w + gated + Lw.count);
   if (launch_head_gate(wt, attn, batch, op->n_heads, op->head_dim, head_mask, w, ids, cnt, s) != hipSuccess)

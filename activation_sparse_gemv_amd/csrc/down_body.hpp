@@ -33,11 +33,8 @@
 
 namespace sfnn {
 
-// Source of the coefficient of slot j for token t: h[t][j] fp32 | x[t][row_j]
-// fp16 | fp32 | the same x entries taken only where the row's head (row_j /
-// hd) is on for token t, else 0 (a select: the entries of heads that are off
-// may hold anything).
-enum { CO_H = 0, CO_X16 = 1, CO_X32 = 2, CO_X16H = 3, CO_X32H = 4 };
+// Source of the coefficient of slot j for token t.
+enum { CO_H = 0, CO_X16 = 1, CO_X32 = 2 };  // h[t][j] fp32 | x[t][row_j] fp16 | fp32
 
 // A row list a workgroup builds in its own LDS (the input-sparse GEMV's
 // single-launch form): the count in the first word of the dynamic LDS, the
@@ -68,8 +65,6 @@ struct DownArgs {
   int rg;                // row groups (>= 1)
   float* part;           // rg > 1: partial rows [rg][batch][d] (k_sum's layout)
   int batch;             // tokens of the whole call (the partial rows' stride)
-  const uint32_t* hmask; // CO_X16H / CO_X32H: per-token head bits [B][hw32] (32-bit words)
-  int hd, hw32;          // rows per head, 32-bit mask words per token
 };
 
 template <int WT>
@@ -139,9 +134,8 @@ struct DownRed {
 // break.
 template <int WT, int NT, int LPR, int CO, bool LISTED, int LDSL = 0>
 struct DownTile {
-  static_assert(LDSL != 2 || (NT == 1 && WT == WT_F16 && (CO == CO_X16 || CO == CO_X16H)),
+  static_assert(LDSL != 2 || (NT == 1 && WT == WT_F16 && CO == CO_X16),
                 "packed list entries carry one fp16 coefficient");
-  static constexpr bool HEADS = CO == CO_X16H || CO == CO_X32H;
   static constexpr int CPL = cols_per_vec<WT>();
   static constexpr int NW = kDownThreads / kWave;
   static constexpr int RPW = kWave / LPR;  // rows per wavefront per step
@@ -155,7 +149,6 @@ struct DownTile {
   u32x4 wv[2][KB];      // weights of the chunk in use and the next one
   float hv[2][KB][NT];  // coefficients
   float sv[2][KB];      // INT4 scales
-  uint32_t hb[2][KB][HEADS ? NT : 1];  // CO_X16H / CO_X32H: the mask word holding the row's head bit
   float acc[NT][CPL];
   float sb[WT == WT_I4 ? NT : 1];
 
@@ -229,8 +222,7 @@ struct DownTile {
   }
 
   __device__ __forceinline__ void issue_w(const DownArgs& a, int ch, const int (&id)[KB], u32x4 (&w)[KB],
-                                          float (&h)[KB][NT], float (&sc)[KB],
-                                          uint32_t (&hbw)[KB][HEADS ? NT : 1]) const {
+                                          float (&h)[KB][NT], float (&sc)[KB]) const {
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
       const int i = row_of(id[k]);
@@ -250,34 +242,28 @@ struct DownTile {
         const int tc = t < a.nt ? a.tok0 + t : a.tok0;
         if constexpr (LDSL == 2) {
           h[k][t] = (float)__builtin_bit_cast(f16, (uint16_t)((uint32_t)id[k] >> 16));
-          continue;  // the coefficient came with the id (the row's head is on)
+          continue;  // the coefficient came with the id
         }
         if constexpr (CO == CO_H) {
           h[k][t] = reinterpret_cast<const float*>(a.co)[(size_t)tc * a.co_stride + jc];
-        } else if constexpr (CO == CO_X16 || CO == CO_X16H) {
+        } else if constexpr (CO == CO_X16) {
           h[k][t] = (float)reinterpret_cast<const f16*>(a.co)[(size_t)tc * a.co_stride + ic];
         } else {
           h[k][t] = reinterpret_cast<const float*>(a.co)[(size_t)tc * a.co_stride + ic];
         }
-        if constexpr (HEADS && LDSL != 2) hbw[k][t] = a.hmask[(size_t)tc * a.hw32 + (ic / a.hd >> 5)];
       }
     }
   }
 
   __device__ __forceinline__ void use(const DownArgs& a, int ch, const int (&id)[KB], const u32x4 (&w)[KB],
-                                      const float (&h)[KB][NT], const float (&sc)[KB],
-                                      const uint32_t (&hbw)[KB][HEADS ? NT : 1]) {
+                                      const float (&h)[KB][NT], const float (&sc)[KB]) {
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
       const int j = (ch * KB + k) * RPS + rr;
       const bool ok = j < n && (unsigned)row_of(id[k]) < (unsigned)a.n_rows;
       float hk[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        bool on = ok && t < a.nt;
-        if constexpr (HEADS && LDSL != 2) on = on && ((hbw[k][t] >> ((id[k] / a.hd) & 31)) & 1u);
-        hk[t] = on ? h[k][t] : 0.0f;  // a select: nothing else enters
-      }
+      for (int t = 0; t < NT; ++t) hk[t] = (ok && t < a.nt) ? h[k][t] : 0.0f;  // a select: nothing else enters
       if constexpr (WT == WT_I4) {
         // nibbles in offset binary (n = t + 8) enter as fp16 subnormals with
         // no conversion: masked in place in bits 0-3 of a half a nibble is the
@@ -344,29 +330,28 @@ struct DownTile {
     issue_ids(a, 1, idb[1]);
   }
 
-  __device__ __forceinline__ void first(const DownArgs& a) { issue_w(a, 0, idb[0], wv[0], hv[0], sv[0], hb[0]); }
+  __device__ __forceinline__ void first(const DownArgs& a) { issue_w(a, 0, idb[0], wv[0], hv[0], sv[0]); }
 
   // one chunk: idc holds chunk cc's ids (replaced by chunk cc+2's), idn chunk
   // cc+1's
   __device__ __forceinline__ void step(const DownArgs& a, int cc, int (&idc)[KB], const int (&idn)[KB],
                                        const u32x4 (&wc)[KB], const float (&hc)[KB][NT], const float (&sc)[KB],
-                                       const uint32_t (&bc)[KB][HEADS ? NT : 1], u32x4 (&wn)[KB],
-                                       float (&hn)[KB][NT], float (&sn)[KB], uint32_t (&bn)[KB][HEADS ? NT : 1]) {
+                                       u32x4 (&wn)[KB], float (&hn)[KB][NT], float (&sn)[KB]) {
     int cur[KB];
 #pragma unroll
     for (int k = 0; k < KB; ++k) cur[k] = idc[k];
     issue_ids(a, cc + 2, idc);
-    issue_w(a, cc + 1, idn, wn, hn, sn, bn);
+    issue_w(a, cc + 1, idn, wn, hn, sn);
     __builtin_amdgcn_sched_barrier(0);  // the next requests go out before this chunk is used
-    use(a, cc, cur, wc, hc, sc, bc);
+    use(a, cc, cur, wc, hc, sc);
   }
 
   // every chunk (at least one: with n = 0 it adds nothing)
   __device__ __forceinline__ void loop(const DownArgs& a) {
     for (int ch = 0;; ch += 2) {
-      step(a, ch, idb[0], idb[1], wv[0], hv[0], sv[0], hb[0], wv[1], hv[1], sv[1], hb[1]);
+      step(a, ch, idb[0], idb[1], wv[0], hv[0], sv[0], wv[1], hv[1], sv[1]);
       if (ch + 1 >= nch) break;
-      step(a, ch + 1, idb[1], idb[0], wv[1], hv[1], sv[1], hb[1], wv[0], hv[0], sv[0], hb[0]);
+      step(a, ch + 1, idb[1], idb[0], wv[1], hv[1], sv[1], wv[0], hv[0], sv[0]);
       if (ch + 2 >= nch) break;
     }
   }
@@ -381,10 +366,9 @@ struct DownTile {
       u32x4 w[KB];
       float h[KB][NT];
       float sc[KB];
-      uint32_t b[KB][HEADS ? NT : 1];
       issue_ids(a, ch, id);
-      issue_w(a, ch, id, w, h, sc, b);
-      use(a, ch, id, w, h, sc, b);
+      issue_w(a, ch, id, w, h, sc);
+      use(a, ch, id, w, h, sc);
     }
   }
 

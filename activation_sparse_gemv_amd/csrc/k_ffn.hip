@@ -168,7 +168,6 @@ DownArgs ffn_down_args(const FfnLaunch& p) {
   a.rg = 1;
   a.part = p.partial;
   a.batch = p.batch;
-  a.hmask = nullptr;
   return a;
 }
 

@@ -21,10 +21,9 @@
 //   k_isg_self   every workgroup lists the rows itself, in its own LDS (one
 //                ballot per 64 inputs, a popcount scan, the set bits written
 //                in ascending order), then runs its k_down tile over that
-//                list; workgroup 0 also writes the list and its count.  The
-//                head-gated output projection uses it with the rows of the
-//                heads some token uses as the list and each token's attention
-//                entries taken only where its head is on (no gated copy).
+//                list; workgroup 0 also writes the list and its count.  One
+//                fp16 token packs its input into the list entry, so the
+//                loop's only global loads are weights.
 // fp16 inputs from kIsgMfmaMinBatch tokens on take the matrix cores instead of
 // k_down: k_isg_gather lays the listed inputs' x out as the h operand of the
 // FFN's matrix-core down-projection kernel (k_down_mfma), which multiplies
@@ -55,9 +54,7 @@ constexpr int kIsgSelfMaxIn = 16384;  // 16-bit ids, 32 KB of LDS for the list; 
 constexpr int kIsgPackedMaxIn = 8192;  // one fp16 token: id | coefficient entries, 32 KB
 
 struct SelfList {
-  const void* x;            // inputs [B][n_in] (HEADS == false: the nonzero ones are listed)
-  const uint64_t* hmask;    // HEADS: [B][hw] per-token head bits (rows of heads some token uses are listed)
-  int hd, hw;               // HEADS: rows per head, mask words per token
+  const void* x;            // inputs [B][n_in]: the nonzero ones are listed
   int n_in, batch;
   int32_t* cols_out;        // [n_in] or null: the list, written by workgroup 0
   int32_t* count_out;       // [1] or null
@@ -67,16 +64,15 @@ struct SelfList {
 // first, 16-bit ids after it, or PACKED: 32-bit entries id | the one token's
 // fp16 input << 16); every thread of the workgroup calls it.  Thread i owns
 // inputs 32 i .. 32 i + 31 (n_in <= 16384 = 512 x 32): their nonzero bits
-// from independent 16-byte loads of every token (HEADS: from the union of
-// the tokens' head words), an exclusive prefix sum of the threads' popcounts
+// from independent 16-byte loads of every token, an exclusive prefix sum of
+// the threads' popcounts
 // (lane scan per wavefront, wavefront totals through LDS), then each thread
 // writes its own entries in ascending order.
-template <typename XT, bool HEADS, bool PACKED>
+template <typename XT, bool PACKED>
 __device__ __forceinline__ void isg_build_list(const SelfList& L) {
   constexpr int NW = kDownThreads / kWave;
   constexpr int E = 16 / (int)sizeof(XT);  // inputs per 16-byte vector
   constexpr int VPT = 32 / E;              // vectors per thread
-  __shared__ unsigned long long s_hu[kIsgSelfMaxIn / 8 / 64];  // HEADS: union head words (hd >= 8)
   __shared__ int s_wt[NW];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -84,32 +80,14 @@ __device__ __forceinline__ void isg_build_list(const SelfList& L) {
   const bool mine = j0 < L.n_in;
   uint32_t m = 0;
   u32x4 v[PACKED ? VPT : 1];  // PACKED: the one token's inputs, kept for the entries
-  if constexpr (HEADS) {
-    if (tid < L.hw) {
-      unsigned long long u = 0;
-      for (int t = 0; t < L.batch; ++t) u |= L.hmask[(size_t)t * L.hw + tid];
-      s_hu[tid] = u;
-    }
-    __syncthreads();
-    if (mine) {
-      int h = j0 / L.hd, r = j0 - h * L.hd;  // head of input j0 + e, and its row in the head
-      for (int e = 0; e < 32; ++e) {
-        m |= (uint32_t)((s_hu[h >> 6] >> (h & 63)) & 1ull) << e;
-        if (++r == L.hd) {
-          r = 0;
-          ++h;
-        }
-      }
-    }
-  }
   if constexpr (PACKED) {
-    // one fp16 token: its inputs are the coefficients (HEADS: m set above)
+    // one fp16 token: its inputs are the coefficients
 #pragma unroll
     for (int q = 0; q < VPT; ++q)
       v[q] = mine ? ld16(reinterpret_cast<const uint8_t*>(L.x) + ((size_t)j0 + q * E) * sizeof(XT))
                   : u32x4{0u, 0u, 0u, 0u};
   }
-  if constexpr (!HEADS) {
+  {
     // nonzero: magnitude bits set (-0.0 is a zero, NaN is not)
     for (int t = 0; t < L.batch; ++t) {
       u32x4 w[VPT];
@@ -181,7 +159,7 @@ template <int WT, int NT, int LPR, int CO, bool PACKED>
 __global__ __launch_bounds__(kDownThreads) void k_isg_self(DownArgs a, SelfList L, int ntiles) {
   using XT = typename std::conditional<WT == WT_F32, float, f16>::type;
   __shared__ __align__(16) float red[DownRed<WT, NT, LPR>::floats];
-  isg_build_list<XT, CO == CO_X16H || CO == CO_X32H, PACKED>(L);
+  isg_build_list<XT, PACKED>(L);
   int tile, grp;
   down_item(blockIdx.x, ntiles, 8 / LPR, tile, grp);
   down_body<WT, NT, LPR, CO, true, PACKED ? 2 : 1>(a, tile, grp, red);
@@ -231,7 +209,6 @@ static DownArgs isg_down_args(const IsgLaunch& p) {
   a.rg = 1;
   a.part = p.partial;  // at least kDownMaxGroups partial rows per token (isg_groups)
   a.batch = p.batch;
-  a.hmask = nullptr;
   return a;
 }
 
@@ -254,7 +231,7 @@ static bool isg_self_fits(const IsgLaunch& p) {
 
 template <int WT, int NT, int CO, bool PACKED = false>
 static void isg_self_pass(const DownArgs& a, const SelfList& L, const DownShape& sh, hipStream_t s) {
-  const dim3 grid(sh.tiles * sh.rg), blk(kDownThreads);
+  const dim3 grid(sh.tiles), blk(kDownThreads);
   const size_t lds = 16 + (size_t)L.n_in * (PACKED ? 4 : 2);
   switch (sh.lpr) {
     case 1: hipLaunchKernelGGL((k_isg_self<WT, NT, 1, CO, PACKED>), grid, blk, lds, s, a, L, sh.tiles); break;
@@ -266,24 +243,18 @@ static void isg_self_pass(const DownArgs& a, const SelfList& L, const DownShape&
 
 // Every token group of the batch; each launch lists the rows of the whole batch.
 // One fp16 token with a short list: the packed entries (no coefficient loads).
-// Tiles narrower than a 128-byte line stream poorly (a read probe of the same
-// rows: 1.7 TB/s with 32-byte tiles against 4.7 TB/s with whole lines in row
-// groups), so rows shorter than 256 lines take whole lines in row groups and a
-// sum launch after the passes.
+// (Rows whose narrowest tiles fall under a 128-byte line were also tried in
+// whole lines over row groups plus a sum launch: slower, the sum launch
+// costing more than the wider tiles save at these sizes.)
 template <int WT, int CO>
 static void isg_self_all(DownArgs a, const SelfList& L, int batch, hipStream_t s) {
-  DownShape sh = down_shape(WT, a.d, batch, 0);
-  if (sh.lpr < 8) {
-    const DownShape wide = down_shape(WT, a.d, batch, kDownItemsListed);
-    if (wide.lpr == 8 && wide.rg > 1) sh = wide;
-  }
-  a.rg = sh.rg;
+  const DownShape sh = down_shape(WT, a.d, batch, 0);
+  a.rg = 1;
   if constexpr (WT == WT_F16) {
     if (batch == 1 && L.n_in <= kIsgPackedMaxIn) {
       a.tok0 = 0;
       a.nt = 1;
-      isg_self_pass<WT, 1, CO == CO_X16H ? CO_X16H : CO_X16, true>(a, L, sh, s);
-      if (sh.rg > 1) (void)launch_down_sum(a, s);  // errors surface through hipGetLastError
+      isg_self_pass<WT, 1, CO, true>(a, L, sh, s);
       return;
     }
   }
@@ -297,36 +268,20 @@ static void isg_self_all(DownArgs a, const SelfList& L, int batch, hipStream_t s
       default: isg_self_pass<WT, 8, CO>(a, L, sh, s); break;
     }
   }
-  if (sh.rg > 1) (void)launch_down_sum(a, s);
 }
 
-static void isg_self(const IsgLaunch& p, const uint64_t* head_mask, int H, int hd, hipStream_t s) {
-  DownArgs a = isg_down_args(p);
+static void isg_self(const IsgLaunch& p, hipStream_t s) {
+  const DownArgs a = isg_down_args(p);
   SelfList L{};
   L.x = p.x;
-  L.hmask = head_mask;
-  L.hd = hd;
-  L.hw = (H + 63) / 64;
   L.n_in = p.n_in;
   L.batch = p.batch;
-  L.cols_out = head_mask ? nullptr : p.ids;
-  L.count_out = head_mask ? nullptr : p.count;
-  if (head_mask) {
-    a.hmask = reinterpret_cast<const uint32_t*>(head_mask);
-    a.hd = hd;
-    a.hw32 = 2 * L.hw;
-  }
-  if (p.wt == WT_F32) {
-    if (head_mask)
-      isg_self_all<WT_F32, CO_X32H>(a, L, p.batch, s);
-    else
-      isg_self_all<WT_F32, CO_X32>(a, L, p.batch, s);
-  } else {
-    if (head_mask)
-      isg_self_all<WT_F16, CO_X16H>(a, L, p.batch, s);
-    else
-      isg_self_all<WT_F16, CO_X16>(a, L, p.batch, s);
-  }
+  L.cols_out = p.ids;
+  L.count_out = p.count;
+  if (p.wt == WT_F32)
+    isg_self_all<WT_F32, CO_X32>(a, L, p.batch, s);
+  else
+    isg_self_all<WT_F16, CO_X16>(a, L, p.batch, s);
 }
 
 int isg_groups(int n_out, int max_groups) {
@@ -343,17 +298,9 @@ static void isg_rows(const IsgLaunch& p, hipStream_t s) {
   down_all<WT, WT == WT_F32 ? CO_X32 : CO_X16>(isg_down_args(p), p.batch, s);
 }
 
-bool isg_single_launch(const IsgLaunch& p) { return isg_self_fits(p); }
-
-hipError_t launch_isg_heads(const IsgLaunch& p, const uint64_t* head_mask, int H, int hd, hipStream_t s) {
-  if (!isg_self_fits(p)) return hipErrorInvalidValue;
-  isg_self(p, head_mask, H, hd, s);
-  return hipGetLastError();
-}
-
 hipError_t launch_isg(const IsgLaunch& p, hipStream_t s) {
   if (!p.listed && isg_self_fits(p)) {
-    isg_self(p, nullptr, 0, 1, s);
+    isg_self(p, s);
     return hipGetLastError();
   }
   if (!p.listed) {

@@ -156,12 +156,7 @@ struct IsgLaunch {
   int32_t* sidbuf = nullptr;  // matrix-core path: [n_in] slot -> input
 };
 hipError_t launch_isg(const IsgLaunch& p, hipStream_t s);
-// The single-launch form (each workgroup lists the rows itself) applies to p.
-bool isg_single_launch(const IsgLaunch& p);
-// Head-gated output projection in the single-launch form: the rows of the
-// heads some token uses, x[t][j] taken where head j / hd is on for token t
-// (isg_single_launch(p) must hold; p.x is the ungated attention output).
-hipError_t launch_isg_heads(const IsgLaunch& p, const uint64_t* head_mask, int H, int hd, hipStream_t s);
+
 
 // ---- head-gated attention projections ----------------------------------------
 

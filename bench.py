@@ -76,10 +76,17 @@ def _parse():
 
 
 HBM_PEAK_GBS = 8000.0
-# Union share of d_ff from which the dense FFN beats predictor + sparse FFN
-# (the sparse-vs-dense sweeps on MI355X: OPT-6.7B fp16 and OPT-175B INT4-g128
-# shapes; the fp32 figure is the fp16 one, not measured on its own).
-DENSE_CROSSOVER = {"f16": 0.45, "i4g128": 0.65, "f32": 0.45}
+# Union share of d_ff from which the dense FFN beats predictor + sparse FFN,
+# measured on MI355X: fp16 ReLU 0.45 (OPT-6.7B sweep: the layer wins on a 34%
+# union, loses on 57%), INT4-g128 0.65 (OPT-175B sweep: wins at 56%, loses at
+# 72%), fp16 ReGLU 0.85 (three matrices per neuron, so the predictor weighs
+# less: the LLaMA-ReGLU-70B stack ran sparse on a 58% union at batch 16 in 266
+# us against 317 dense, and on a 78% union at batch 32 in 350 against 372);
+# fp32 takes the fp16 ReLU figure (not measured on its own).
+def dense_crossover(spec):
+    if spec.wtype == "i4g128":
+        return 0.65
+    return 0.85 if spec.act == "reglu" else 0.45
 COPY_PROBE_BYTES = 1 << 30
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 
@@ -841,7 +848,7 @@ def _switch_thresholds(sg, counts, n_prof, spec):
     the device) over n_prof[k] tokens: the smallest batch whose expected union
     share reaches the weight type's crossover, -1 if none up to 64 does."""
     ch = counts.cpu().numpy().view(np.uint32)
-    return [sg.sfnn_dense_min_batch(np.ascontiguousarray(c), n, spec.d_ff, DENSE_CROSSOVER[spec.wtype], 64)
+    return [sg.sfnn_dense_min_batch(np.ascontiguousarray(c), n, spec.d_ff, dense_crossover(spec), 64)
             for c, n in zip(ch, n_prof)]
 
 
@@ -891,7 +898,7 @@ def _auto_dense_switch(sg, distinct, spec, dev, flags, steps=64):
     thr = _switch_thresholds(sg, counts, n_prof, spec)
     for (pred, _), t in zip(distinct, thr):
         pred.dense_min_batch = t
-    print(f"# dense switch per distinct layer (auto, crossover {DENSE_CROSSOVER[spec.wtype]}): {thr}",
+    print(f"# dense switch per distinct layer (auto, crossover {dense_crossover(spec)}): {thr}",
           file=sys.stderr, flush=True)
     return thr
 

@@ -106,10 +106,9 @@ def test_heads_deterministic():
     assert np.array_equal(a[1], b[1]) and np.array_equal(a[2], b[2])
 
 
-# The output projection runs as one launch (the GEMV's workgroups list the used
-# heads' rows and take each token's entries only where its head is on) up to
-# 16384 attention inputs on the per-row path; past that, the gate launch and
-# the GEMV.  Both sides, with unused heads' rows and off entries NaN-poisoned.
+# The output projection around the input-sparse GEMV's size limits (16384
+# attention inputs, 96 heads of 128 as in OPT-175B, head_dim 8), fp16 and
+# fp32, with unused heads' rows and off entries NaN-poisoned.
 @pytest.mark.parametrize("wtype,d,H,hd,B", [
     ("f16", 1024, 96, 128, 1),    # OPT-175B's 96 heads of 128, d_model cut for the oracle
     ("f16", 1024, 128, 128, 2),   # 16384 inputs: the largest single-launch list
