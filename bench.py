@@ -72,6 +72,9 @@ def _parse():
                          "from fire counts profiled on the stack, the union law and the measured crossover)")
     ap.add_argument("--isg", action="store_true",
                     help="time the input-sparse GEMV (ReLU after the norm) over input densities and batches")
+    ap.add_argument("--only", default="",
+                    help="with --isg or --heads: one point, 'shape,batch,density' (e.g. 'up,1,0.5' or "
+                         "'opt6.7b,1,1.0'), for profiling a single workload")
     return ap.parse_args()
 
 
@@ -159,7 +162,7 @@ def main():
         _isg_sweep(args)
         return
     if args.heads:
-        _heads_sweep()
+        _heads_sweep(args)
         return
     if args.sweep:
         _sweep(args, spec)
@@ -637,18 +640,21 @@ def _isg_sweep(args):
     import activation_sparse_gemv_amd as sg
     from activation_sparse_gemv_amd.device import to_dev
     points = []
+    only = args.only.split(",") if args.only else None
     for name, n_in, n_out in (("up 4096->16384", 4096, 16384), ("qkv 4096->12288", 4096, 12288)):
+        if only and not name.startswith(only[0]):
+            continue
         nc = max(2, int(np.ceil(1.0e9 / (n_in * n_out * 2))))
         ops = []
         for c in range(nc):
             w_t, b = synth.make_isg_weights(n_in, n_out, "f16", seed=0, key=c)
             ops.append(sg.Isg(to_dev(w_t), to_dev(b)))
-        for B in (1, 4, 16):
+        for B in ((int(only[1]),) if only else (1, 4, 16)):
             ws = torch.empty(sg.sfnn_isg_workspace_bytes(ops[0], B), dtype=torch.uint8, device="cuda")
             y = torch.empty((B, n_out), dtype=torch.float32, device="cuda")
             cols = torch.empty((nc, n_in), dtype=torch.int32, device="cuda")
             cnt = torch.zeros((nc,), dtype=torch.int32, device="cuda")
-            for dens in (1.0, 0.5, 0.3, 0.1):
+            for dens in ((float(only[2]),) if only else (1.0, 0.5, 0.3, 0.1)):
                 xs = [to_dev(synth.make_relu_inputs(n_in, B, dens, seed=0, stream=700 + c)) for c in range(nc)]
 
                 def calls():
@@ -678,13 +684,14 @@ def _isg_sweep(args):
         del ops
         torch.cuda.empty_cache()
     for pt in points:
-        dense = next(q for q in points if q["shape"] == pt["shape"] and q["batch"] == pt["batch"]
-                     and q["input_density"] == 1.0)
-        pt["speedup_vs_all_rows"] = round(dense["us"] / pt["us"], 2)
+        dense = next((q for q in points if q["shape"] == pt["shape"] and q["batch"] == pt["batch"]
+                      and q["input_density"] == 1.0), None)
+        if dense is not None:
+            pt["speedup_vs_all_rows"] = round(dense["us"] / pt["us"], 2)
     print(json.dumps({"isg_sweep": points}), flush=True)
 
 
-def _heads_sweep():
+def _heads_sweep(args):
     """Head-gated attention projections: sfnn_head_qkv and sfnn_head_out at the
     OPT-6.7B (d 4096, 32 heads of 128) and OPT-175B (d 12288, 96 heads of 128)
     attention shapes, over the fraction of heads each token uses (1.0 = every
@@ -696,20 +703,23 @@ def _heads_sweep():
     import activation_sparse_gemv_amd as sg
     from activation_sparse_gemv_amd.device import to_dev
     points = []
+    only = args.only.split(",") if args.only else None
     for name, d, H, hd in (("opt6.7b", 4096, 32, 128), ("opt175b", 12288, 96, 128)):
+        if only and name != only[0]:
+            continue
         n = H * hd
         nc = max(2, int(np.ceil(1.0e9 / (4 * n * d * 2))))
         ops = []
         for c in range(nc):
             w_qkv, b_qkv, w_o_t, b_o = synth.make_head_weights(d, H, hd, "f16", seed=c)
             ops.append(sg.Heads(to_dev(w_qkv), to_dev(w_o_t), hd, to_dev(b_qkv), to_dev(b_o)))
-        for B in (1, 8):
+        for B in ((int(only[1]),) if only else (1, 8)):
             ws = torch.empty(sg.sfnn_heads_workspace_bytes(ops[0], B), dtype=torch.uint8, device="cuda")
             qkv = torch.empty((B, 3 * n), dtype=torch.float32, device="cuda")
             y = torch.empty((B, d), dtype=torch.float32, device="cuda")
             x = to_dev(synth.make_relu_inputs(d, B, 1.0, seed=1, stream=B))
             attn = to_dev(synth.make_relu_inputs(n, B, 1.0, seed=2, stream=B))
-            for dens in (1.0, 0.5, 0.2):
+            for dens in ((float(only[2]),) if only else (1.0, 0.5, 0.2)):
                 masks = []
                 used = []
                 for c in range(nc):
@@ -745,10 +755,11 @@ def _heads_sweep():
         del ops
         torch.cuda.empty_cache()
     for pt in points:
-        dense = next(q for q in points if q["shape"] == pt["shape"] and q["batch"] == pt["batch"]
-                     and q["head_density"] == 1.0)
-        pt["speedup_qkv_vs_all_heads"] = round(dense["us_qkv"] / pt["us_qkv"], 2)
-        pt["speedup_out_vs_all_heads"] = round(dense["us_out"] / pt["us_out"], 2)
+        dense = next((q for q in points if q["shape"] == pt["shape"] and q["batch"] == pt["batch"]
+                      and q["head_density"] == 1.0), None)
+        if dense is not None:
+            pt["speedup_qkv_vs_all_heads"] = round(dense["us_qkv"] / pt["us_qkv"], 2)
+            pt["speedup_out_vs_all_heads"] = round(dense["us_out"] / pt["us_out"], 2)
     print(json.dumps({"heads_sweep": points}), flush=True)
 
 
