@@ -506,11 +506,13 @@ __global__ __launch_bounds__(512) void k_down_mfma_i4(MfmaDownI4Args a) {
 // ---- host side ---------------------------------------------------------------
 
 // Row tiles per up workgroup.  Every workgroup reads all of the pass's x, so
-// the more rows it takes the less x traffic per weight byte: 128 rows for
-// ReLU and 64 for ReGLU (two matrices) with one token tile, half that with two
-// (registers).
+// the more rows it takes the less x traffic per weight byte, but the grid
+// should also come out at a whole number of workgroups per CU.  ReLU: 64 rows
+// with one token tile, 96 with two (OPT-175B's d_ff: 768 and 512 workgroups;
+// measured 6-8% faster than 128 and 64 rows at batches 4-8 and 4% at 32);
+// ReGLU (two matrices): 64 rows, half that with two token tiles (registers).
 template <int ACT, int NB>
-constexpr int up_rt_i4() { return (ACT == ACT_REGLU ? 4 : 8) / NB; }
+constexpr int up_rt_i4() { return ACT == ACT_REGLU ? 4 / NB : (NB == 1 ? 4 : 6); }
 
 template <int ACT, int NB>
 static void mfma_pass_i4(const FfnLaunch& p, const int32_t* ids, const int32_t* count, int tok0, int nt, int kg,
