@@ -352,8 +352,12 @@ __device__ __forceinline__ void up_body(const FfnArgs& a, int vb, int vg) {
 // one per wavefront, so every wavefront carries the same share; a pass of PR
 // rows has all its loads in flight at once (issued before the prologue
 // waits), and the wavefronts' partial dots are added in LDS in wavefront
-// order.  RV as in up_body.
-template <int WT, int NT, int NTH, int RV>
+// order.  RV as in up_body.  LATE: the first pass of W1^T rows is requested
+// only once x is built.  The up workgroups that share the CUs then get their
+// mask words and first up rows through the memory pipeline before the W1
+// stream fills it; worth it where their prologue is long (INT4 rows with
+// their scales: OPT-175B layer 47.1 -> 45.2 us; at fp16 OPT-6.7B it costs 5%).
+template <int WT, int NT, int NTH, int RV, bool LATE = false>
 __device__ __forceinline__ void p1_body(const FfnArgs& a, int vb, int vg) {
   using XT = typename std::conditional<WT == WT_F32, float, f16>::type;
   constexpr int NW = NTH / kWave;
@@ -388,12 +392,12 @@ __device__ __forceinline__ void p1_body(const FfnArgs& a, int vb, int vg) {
       }
     }
   };
-  issue(0);
+  if constexpr (!LATE) issue(0);
   __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the prologue waits
   chain_finish<XT, NT, false, CV>(rv, xs, s_red, nullptr, false, a.eps, d, a.tok0, a.nt);
   __syncthreads();
   for (int k0 = 0; k0 < pr; k0 += PR) {  // workgroup-uniform
-    if (k0 > 0) issue(k0);
+    if (k0 > 0 || LATE) issue(k0);
     float pacc[PR][NT];
 #pragma unroll
     for (int k = 0; k < PR; ++k) {

@@ -17,7 +17,7 @@ __global__ __launch_bounds__(NTH) void k_la_up_pred1(FfnArgs fa, int gup) {
   if ((int)blockIdx.x < gup)  // workgroup-uniform
     up_body<WT, ACT, NT, SRC_UNION, NTH, RV, true, UW>(fa, blockIdx.x, gup);
   else
-    p1_body<WT == WT_F32 ? WT_F32 : WT_F16, NT, NTH, RV>(fa, blockIdx.x - gup, gridDim.x - gup);
+    p1_body<WT == WT_F32 ? WT_F32 : WT_F16, NT, NTH, RV, WT == WT_I4>(fa, blockIdx.x - gup, gridDim.x - gup);
 }
 
 // Predictor-stage-1 workgroups of launch A: about SFNN_LA_P1_ROWS rows of W1^T each.
