@@ -144,6 +144,7 @@ struct DownTile {
   static_assert(LPR == 1 || LPR == 2 || LPR == 4 || LPR == 8, "lanes per row");
 
   int tile, grp, rr, j0, n, nch, sgrp, ngrp;  // n: slots of this row group, from slot j0
+  int craw;              // the slot count as read (used by run())
   size_t rowb, cofs;
   int idb[2][KB];       // ids of the chunks ahead
   u32x4 wv[2][KB];      // weights of the chunk in use and the next one
@@ -151,10 +152,16 @@ struct DownTile {
   float sv[2][KB];      // INT4 scales
   float acc[NT][CPL];
   float sb[WT == WT_I4 ? NT : 1];
+  float ob, orv;        // with one row group: this thread's output column's bias and residual
+  static_assert(NT * LPR * CPL <= kDownThreads, "one output column per thread at most");
 
-  // has == false: a workgroup with no tile of its own (n = 0: it reads slot
-  // 0's row of tile 0 and writes nothing)
-  __device__ __forceinline__ void count(const DownArgs& a, int tile_, int grp_, bool has) {
+  // What does not wait for the count: the tile, this lane's rows and column,
+  // the count's own load, and (one row group) the bias and residual of the
+  // output column this thread writes in finish(), so that neither load waits
+  // at the end.  The run starts at slot j0 = 0 here; run() sets it for row
+  // groups.  has == false: a workgroup with no tile of its own (n = 0: it
+  // reads slot 0's row of tile 0 and writes nothing).
+  __device__ __forceinline__ void setup(const DownArgs& a, int tile_, int grp_, bool has) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int c = lane % LPR;
     tile = has ? tile_ : 0;
@@ -165,15 +172,34 @@ struct DownTile {
     cofs = (size_t)down_row_bytes(WT, col);  // byte offset of the lane's 16 bytes
     sgrp = col / 128;
     ngrp = a.d / 128;
-    int na = a.n_slots;
-    if constexpr (LDSL) {
-      const int cn = lds_list_base()[0];
-      na = cn < 0 ? 0 : (cn > a.n_slots ? a.n_slots : cn);
-    } else if (a.count) {
-      const int cn = *a.count;
-      na = cn < 0 ? 0 : (cn > a.n_slots ? a.n_slots : cn);
+    if constexpr (LDSL)
+      craw = lds_list_base()[0];
+    else
+      craw = a.count ? *a.count : a.n_slots;
+    j0 = 0;
+    n = 0;
+    nch = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) acc[t][k] = 0.0f;
+      if constexpr (WT == WT_I4) sb[t] = 0.0f;
     }
-    // this row group's run: slots j0 .. j0 + n - 1
+    ob = orv = 0.0f;
+    constexpr int TE = LPR * CPL;
+    const int e = threadIdx.x, t = e / TE;
+    if (a.rg == 1 && e < NT * TE && t < a.nt) {
+      const int cidx = tile * TE + e % TE;
+      if (a.bias)
+        ob = a.bias_f32 ? reinterpret_cast<const float*>(a.bias)[cidx]
+                        : (float)reinterpret_cast<const f16*>(a.bias)[cidx];
+      if (a.r_in) orv = a.r_in[(size_t)(a.tok0 + t) * a.d + cidx];
+    }
+  }
+
+  // This row group's run of slots, j0 .. j0 + n - 1, from the count.
+  __device__ __forceinline__ void run(const DownArgs& a, bool has) {
+    const int na = craw < 0 ? 0 : (craw > a.n_slots ? a.n_slots : craw);
     const int spr = (na + a.rg - 1) / a.rg;
     j0 = grp * spr;
     n = na - j0 < spr ? na - j0 : spr;
@@ -181,12 +207,6 @@ struct DownTile {
     if (!has) n = 0;
     if (j0 >= a.n_slots) j0 = a.n_slots - 1;  // an empty run past the list (its reads stay in bounds)
     nch = (n + RPS * KB - 1) / (RPS * KB);  // chunks of KB steps
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) acc[t][k] = 0.0f;
-      if constexpr (WT == WT_I4) sb[t] = 0.0f;
-    }
   }
 
   // the row of an id register (packed entries: the low 16 bits)
@@ -419,23 +439,17 @@ struct DownTile {
         for (int r = 0; r < 4; ++r) s += red[((((size_t)w * 4 + r) * LPR + cl) * NT + t) * CPL + k];
       if (t < a.nt) {
         const int cidx = tile * TE + ce;
-        if (whole)
-          write_out(a, t, cidx, s);
-        else
+        if (whole) {
+          // y / the residual row from the bias and residual read in setup()
+          const float v = ob + s;
+          const size_t o = (size_t)(a.tok0 + t) * a.d + cidx;
+          if (a.y) a.y[o] = v;
+          if (a.r_in) a.r_out[o] = orv + v;
+        } else {
           a.part[((size_t)grp * a.batch + a.tok0 + t) * a.d + cidx] = s;
+        }
       }
     }
-  }
-
-  // y / the residual row of token t, column c, from the column sum s
-  __device__ __forceinline__ static void write_out(const DownArgs& a, int t, int c, float s) {
-    float b = 0.0f;
-    if (a.bias)
-      b = a.bias_f32 ? reinterpret_cast<const float*>(a.bias)[c] : (float)reinterpret_cast<const f16*>(a.bias)[c];
-    const float v = b + s;
-    const size_t o = (size_t)(a.tok0 + t) * a.d + c;
-    if (a.y) a.y[o] = v;
-    if (a.r_in) a.r_out[o] = a.r_in[o] + v;
   }
 };
 
@@ -444,11 +458,18 @@ struct DownTile {
 template <int WT, int NT, int LPR, int CO, bool LISTED, int LDSL = 0>
 __device__ __forceinline__ void down_body(const DownArgs& a, int tile, int grp, float* red) {
   DownTile<WT, NT, LPR, CO, LISTED, LDSL> D;
-  D.count(a, tile, grp, true);
+  D.setup(a, tile, grp, true);
   if constexpr (LDSL != 0 && SFNN_DOWN_BATCHES) {
+    D.run(a, true);
     D.loop_batches(a);
   } else {
-    D.ids01(a);
+    if (a.rg == 1) {  // the run starts at slot 0: its first ids go out before the count is in
+      D.ids01(a);
+      D.run(a, true);
+    } else {
+      D.run(a, true);
+      D.ids01(a);
+    }
     D.first(a);
     D.loop(a);
   }
