@@ -20,9 +20,11 @@ __global__ __launch_bounds__(NTH) void k_la_up_pred1(FfnArgs fa, int gup) {
     p1_body<WT == WT_F32 ? WT_F32 : WT_F16, NT, NTH, RV, WT == WT_I4>(fa, blockIdx.x - gup, gridDim.x - gup);
 }
 
-// Predictor-stage-1 workgroups of launch A: about SFNN_LA_P1_ROWS rows of W1^T each.
+// Predictor-stage-1 workgroups of launch A: about SFNN_LA_P1_ROWS rows of W1^T each
+// (8: 128 workgroups at rank 1024, one pass of rows each; 1-5% faster than 4 on
+// the fp16 stacks at batches 1-2, the same on INT4; 16 rows, in two passes, lose).
 #ifndef SFNN_LA_P1_ROWS
-#define SFNN_LA_P1_ROWS 4
+#define SFNN_LA_P1_ROWS 8
 #endif
 inline int la_p1_groups(int r) { return r / SFNN_LA_P1_ROWS > 0 ? r / SFNN_LA_P1_ROWS : 1; }
 
