@@ -33,7 +33,7 @@ def _up(lay, thr):
 def test_mfma_i4_sparse_ffn_random_masks(act, B):
     # d 640: 5 scale groups over 8 wavefronts (3 idle) and 5 column
     # workgroups (an odd count: the XCD pairing leaves the tail unpaired);
-    # d_ff 1088: |U| ragged against the 64-row up workgroups and 32-slot steps
+    # d_ff 1088: |U| ragged against the 64- and 96-row up workgroups and 32-slot steps
     lay = _ffn_layer("i4g128", act)
     x = synth.make_tokens(lay.spec, B, stream=240 + B)
     words = synth.random_masks(B, lay.spec.d_ff, 0.1, seed=200 + B)
