@@ -14,10 +14,15 @@ namespace sfnn {
 // registers for predictor rows.
 template <int WT, int ACT, int NT, int NTH, int RV, int UW>
 __global__ __launch_bounds__(NTH) void k_la_up_pred1(FfnArgs fa, int gup) {
-  if ((int)blockIdx.x < gup)  // workgroup-uniform
+  if ((int)blockIdx.x < gup) {  // workgroup-uniform
+    // the FFN's workgroups, whose rows end the layer, issue ahead of the
+    // stage-1 workgroups sharing their CU (with launch B's down workgroups
+    // raised the same way, 1-4% faster stacks than at equal priority)
+    __builtin_amdgcn_s_setprio(3);
     up_body<WT, ACT, NT, SRC_UNION, NTH, RV, true, UW>(fa, blockIdx.x, gup);
-  else
+  } else {
     p1_body<WT == WT_F32 ? WT_F32 : WT_F16, NT, NTH, RV, WT == WT_I4>(fa, blockIdx.x - gup, gridDim.x - gup);
+  }
 }
 
 // Predictor-stage-1 workgroups of launch A: about SFNN_LA_P1_ROWS rows of W1^T each
@@ -51,6 +56,7 @@ __global__ __launch_bounds__(512, SFNN_LA_B_WAVES) void k_la_down_pred2(DownArgs
     return;
   }
   int tile, grp;
+  __builtin_amdgcn_s_setprio(3);  // the down tiles, the launch's long pole, issue ahead of stage 2
   down_item(vb, tiles, 8 / LPR, tile, grp);
   down_body<WT, NTD, LPR, CO_H, true>(da, tile, grp, red);
 }
