@@ -471,6 +471,9 @@ __device__ __forceinline__ void down_body(const DownArgs& a, int tile, int grp, 
       D.ids01(a);
     }
     D.first(a);
+    // the first requests are out: the loop runs at a normal priority (in
+    // launch B the tile's prologue ran at a raised one)
+    __builtin_amdgcn_s_setprio(1);
     D.loop(a);
   }
   D.finish(a, red, true);

@@ -244,6 +244,9 @@ __device__ __forceinline__ void up_body(const FfnArgs& a, int vb, int vg) {
 #pragma unroll
   for (int j = 1; j < NBUF - 1; ++j) up_next(Bq[j]);
   __builtin_amdgcn_sched_barrier(0);  // every load above is issued before the staging waits
+  // in the look-ahead launch the prologue up to here ran at a raised wave
+  // priority; the rest runs at the stage-1 workgroups' level or just above
+  if constexpr (CHAIN) __builtin_amdgcn_s_setprio(1);
 
   // ---- 4. x into LDS: staged activations, or the residual chain -------------
   if constexpr (CHAIN)

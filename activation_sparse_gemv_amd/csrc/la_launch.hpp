@@ -15,9 +15,10 @@ namespace sfnn {
 template <int WT, int ACT, int NT, int NTH, int RV, int UW>
 __global__ __launch_bounds__(NTH) void k_la_up_pred1(FfnArgs fa, int gup) {
   if ((int)blockIdx.x < gup) {  // workgroup-uniform
-    // the FFN's workgroups, whose rows end the layer, issue ahead of the
-    // stage-1 workgroups sharing their CU (with launch B's down workgroups
-    // raised the same way, 1-4% faster stacks than at equal priority)
+    // the FFN's workgroups, whose rows end the layer, issue their prologue
+    // ahead of the stage-1 workgroups sharing their CU (with launch B's down
+    // workgroups raised the same way, 1-4% faster stacks than at equal
+    // priority; the bodies lower it again once their first rows are requested)
     __builtin_amdgcn_s_setprio(3);
     up_body<WT, ACT, NT, SRC_UNION, NTH, RV, true, UW>(fa, blockIdx.x, gup);
   } else {
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(512, SFNN_LA_B_WAVES) void k_la_down_pred2(DownArgs
     return;
   }
   int tile, grp;
-  __builtin_amdgcn_s_setprio(3);  // the down tiles, the launch's long pole, issue ahead of stage 2
+  __builtin_amdgcn_s_setprio(3);  // the down tiles, the launch's long pole, start ahead of stage 2
   down_item(vb, tiles, 8 / LPR, tile, grp);
   down_body<WT, NTD, LPR, CO_H, true>(da, tile, grp, red);
 }
