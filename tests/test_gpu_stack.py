@@ -158,6 +158,30 @@ def test_stack_lookahead_int4_wide():
     _stack_case(synth.config("c5", d_ff=4096, rank=256, n_layers=2), 2, 1, lookahead=True)
 
 
+@pytest.mark.parametrize("cfg,kw,B", [
+    ("c2", dict(d_model=1024, d_ff=4096, rank=128, n_layers=3), 1),
+    ("c4", dict(d_model=768, d_ff=2048, rank=64, n_layers=3), 2),
+    ("c5", dict(d_model=1536, d_ff=3072, rank=128, n_layers=3), 1),
+    ("c5", dict(d_model=1536, d_ff=3072, rank=128, n_layers=3), 4),
+])
+def test_stack_lookahead_deterministic(cfg, kw, B):
+    """Two runs of the look-ahead stack on the same inputs agree bit for bit
+    (every reduction has a fixed order; how the launches' workgroups are
+    scheduled on the CUs must not show in the results)."""
+    spec = synth.config(cfg, **kw)
+    lays = [synth.make_layer(spec, layer=l) for l in range(spec.n_layers)]
+    dev = [upload_layer(lay) for lay in lays]
+    for pred, ffn in dev:
+        pred.dense_min_batch = -1
+    r_in = synth.make_tokens(spec, B, stream=310 + B, dtype=np.float32) * np.float32(3.0)
+    xdt = torch.float32 if spec.wtype == "f32" else torch.float16
+    a = gpu_stack(dev, r_in, 1e-6, xdt, flags=1)
+    b = gpu_stack(dev, r_in, 1e-6, xdt, flags=1)
+    assert np.isfinite(a["r_out"]).all()
+    for k in ("r_out", "x", "y", "mask", "ids", "count"):
+        assert np.array_equal(a[k], b[k], equal_nan=(k in ("x", "y"))), k
+
+
 # dense hot prefix (the first neurons taken for every token): per-layer and
 # look-ahead schedules, per-row and matrix-core batches
 @pytest.mark.parametrize("B", [1, 9])
