@@ -21,10 +21,17 @@ pytestmark = pytest.mark.gpu
 TOL = 2e-3
 
 
-def _stack_case(spec, L, B, seed=0, lookahead=False, mfma_min_batch=0, hot_prefix=0, dense_layers=()):
+def _stack_case(spec, L, B, seed=0, lookahead=False, mfma_min_batch=0, hot_prefix=0, dense_layers=(),
+                down_bias=False):
     """dense_layers: layers whose dense switch is set at this batch (the
-    others stay sparse)."""
+    others stay sparse).  down_bias: a nonzero b_down on every layer (the
+    generated layers have none), so the bias and the residual meet in the
+    same output columns."""
     lays = [synth.make_layer(spec, layer=l, seed=seed) for l in range(L)]
+    if down_bias:
+        for l, lay in enumerate(lays):
+            g = np.random.default_rng(900 + l)
+            lay.b_down = (g.normal(0.0, 0.1, spec.d_model)).astype(lay.b_down.dtype)
     dev = [upload_layer(lay) for lay in lays]
     for l, (pred, ffn) in enumerate(dev):
         ffn.mfma_min_batch = mfma_min_batch
@@ -156,6 +163,19 @@ def test_stack_lookahead_opt6_7b_full_width():
 def test_stack_lookahead_int4_wide():
     """d_model 12288 INT4 (32 columns per thread in the down projection), 2 layers."""
     _stack_case(synth.config("c5", d_ff=4096, rank=256, n_layers=2), 2, 1, lookahead=True)
+
+
+@pytest.mark.parametrize("lookahead", [False, True])
+@pytest.mark.parametrize("cfg,kw,B", [
+    ("c2", dict(d_model=1024, d_ff=4096, rank=128, n_layers=3), 1),
+    ("c2", dict(d_model=1024, d_ff=4096, rank=128, n_layers=3), 2),
+    ("c5", dict(d_model=1536, d_ff=3072, rank=128, n_layers=3), 1),
+    ("c4", dict(d_model=768, d_ff=2048, rank=64, n_layers=3), 9),
+])
+def test_stack_down_bias(cfg, kw, B, lookahead):
+    """A nonzero down-projection bias through the whole stack: y_l = b_down +
+    the gated rows, r_{l+1} = r_l + y_l, per-row and matrix-core batches."""
+    _stack_case(synth.config(cfg, **kw), 3, B, lookahead=lookahead, down_bias=True)
 
 
 @pytest.mark.parametrize("cfg,kw,B", [
