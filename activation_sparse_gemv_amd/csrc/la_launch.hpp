@@ -26,13 +26,21 @@ __global__ __launch_bounds__(NTH) void k_la_up_pred1(FfnArgs fa, int gup) {
   }
 }
 
-// Predictor-stage-1 workgroups of launch A: about SFNN_LA_P1_ROWS rows of W1^T each
-// (8: 128 workgroups at rank 1024, one pass of rows each; 1-5% faster than 4 on
-// the fp16 stacks at batches 1-2, the same on INT4; 16 rows, in two passes, lose).
+// Predictor-stage-1 workgroups of launch A: about SFNN_LA_P1_ROWS rows of W1^T
+// each with fp16 / fp32 FFN weights, SFNN_LA_P1_ROWS_I4 with INT4 ones (at rank
+// 1024: 128 and 256 workgroups; 8 rows were 1-5% faster than 4 on the fp16
+// stacks at batches 1-2, 4 rows 1-2% faster than 8 on OPT-175B INT4, with the
+// FFN workgroups at a raised priority; 16 rows, in two passes, lose).
 #ifndef SFNN_LA_P1_ROWS
 #define SFNN_LA_P1_ROWS 8
 #endif
-inline int la_p1_groups(int r) { return r / SFNN_LA_P1_ROWS > 0 ? r / SFNN_LA_P1_ROWS : 1; }
+#ifndef SFNN_LA_P1_ROWS_I4
+#define SFNN_LA_P1_ROWS_I4 4
+#endif
+inline int la_p1_groups(int r, int wt) {
+  const int rows = wt == WT_I4 ? SFNN_LA_P1_ROWS_I4 : SFNN_LA_P1_ROWS;
+  return r / rows > 0 ? r / rows : 1;
+}
 
 // Launch B of layer l: the first tiles * rg workgroups compute the down-
 // projection work items of FFN_l (one tile of one row group each; y_l and
@@ -78,7 +86,7 @@ static void launch_a(const FfnLaunch& F, const float* r_l, float eps, const Pred
     fa.r = next->r;
   }
   const size_t sh = (size_t)NT * F.d * sizeof(XT) + (WT == WT_I4 ? (size_t)NT * (F.d / 32) * 4 : 0);  // + vec_i4's m8
-  const int grid = F.groups + (next ? la_p1_groups(next->r) : 0);
+  const int grid = F.groups + (next ? la_p1_groups(next->r, WT) : 0);
   if (union_words_per_lane(F.f) == 4)
     hipLaunchKernelGGL((k_la_up_pred1<WT, ACT, NT, NTH, RV, 4>), dim3(grid), dim3(NTH), sh, s, fa, F.groups);
   else
